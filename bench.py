@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MTP draft chain + greedy verify on one MI355X.
+
+One step = one round of the hot path on the Gemma-4-26B-like workload: a
+draft block of B-1 = 3 chained steps (embed + pre-projection, 4 blocks of
+RMSNorm/Q/split-K cross-attention into an 8192-position bf16 KV/O/MLP, final
+norm + 262144-row bf16 LM head + argmax, post-projection) for one sequence,
+then the greedy verify over the target's [1, 4, 262144] fp32 logits.  Inputs
+are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints one JSON line: draft tokens/s (= S * N / time per round), the
+whole-round algorithmic HBM GB/s, the LM-head kernel's roofline (algorithmic
+bytes per launch / its average launch time, measured with HIP events on the
+library's stream during the timed region) and the CPU oracle's throughput on
+a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD published
+METRIC = "draft tokens/s of fused MTP chain (B-1 steps) + verify; HBM GB/s vs peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def weight_bytes(m):
+    """Algorithmic bytes of the drafter weights read once per draft step."""
+    import mtp_synth as syn
+    es = 4 if m.w_dtype == syn.F32 else 2
+    d, dh, qd, F, V = m.d_model, m.d_hprev, m.n_head_q * m.head_dim, m.d_ff, m.n_vocab
+    mats = d * (d + dh) + dh * d + m.n_blocks * (2 * qd * d + 2 * F * d)
+    if m.head_dtype == syn.Q8_0:
+        head = V * (d // 32) * 34
+    else:
+        head = V * d * (4 if m.head_dtype == syn.F32 else 2)
+    gains = 4 * ((2 * m.n_blocks + 1) * d + m.n_blocks * m.head_dim)
+    return mats * es, head, gains
+
+
+def kv_bytes(m, seqs):
+    import mtp_synth as syn
+    es = 4 if m.kv_dtype == syn.F32 else 2
+    tot = 0
+    for s in seqs:
+        for l in range(m.n_blocks):
+            if m.block_src[l] == syn.KV_FULL:
+                n_vis = s.attn_pos + 1
+            else:
+                n_vis = s.attn_pos - max(0, s.attn_pos - m.swa_window + 1) + 1
+            tot += n_vis * m.n_head_kv * m.head_dim * 2 * es
+    return tot
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands on the same workload: whole rounds (draft block
+    + greedy verify) until about budget_s seconds of host time."""
+    from oracle import oracle as orc
+    orc.build(force=False)
+    S, N = len(w.draft.seqs), w.draft.n_steps
+    rounds, t0 = 0, time.perf_counter()
+    while True:
+        out = orc.draft_block(w.model, w.draft, want_logits=False)
+        orc.verify_greedy(w.greedy.logits, out["drafts"])
+        rounds += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or rounds >= 50:
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    return {"value": rounds * S * N / el, "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rounds} full rounds of the same workload (draft block of {N} steps for {S} sequence(s) "
+                      f"+ greedy verify), {el:.1f} s wall on the host, OpenMP threads={threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU form (sequences shard with no exchange; "
+              "see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mtp_draft_verify_amd as mtp
+    import mtp_synth as syn
+    from mtp_synth.device import to_dev, upload_model, upload_seqs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating the Gemma-4-26B-like workload (seed 1)")
+    w = syn.c2_gemma_bf16()
+    m, dr = w.model, w.draft
+    S, N, V = len(dr.seqs), dr.n_steps, m.n_vocab
+    desc, wts, keep_w = upload_model(m, dev, S, N)
+    seqs, last_tok, h_prev, keep_kv = upload_seqs(m, dr, dev)
+    stream = torch.cuda.current_stream()
+    ctx = mtp.Context(desc, wts, stream=stream, keepalive=keep_w)
+    seq_arr = mtp.make_seqs(seqs)
+    drafts = torch.zeros((S, N), dtype=torch.int32, device=dev)
+    h_last = torch.zeros((S, m.d_hprev), dtype=torch.float32, device=dev)
+    toks = torch.zeros((S, N + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.zeros((S,), dtype=torch.int32, device=dev)
+
+    # target logits with the drafter's own drafts planted (p_accept 0.8)
+    ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
+    torch.cuda.synchronize()
+    gv = syn.make_greedy_verify(1, S, N, V, w.p_accept, "max5", drafts=drafts.cpu().numpy())
+    w.greedy = gv
+    logits = to_dev(gv.logits, dev)
+
+    def step():
+        ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
+        ctx.verify_greedy(logits, drafts, toks, n_acc)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    ctx.profile(1 << mtp.MTP_PROF_HEAD)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    head_ms, head_n = ctx.profile_read(mtp.MTP_PROF_HEAD)
+    ctx.profile(0)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-class breakdown over a second, separately profiled pass (diagnostic)
+    ctx.profile(0xF)
+    n_diag = min(args.steps, 20)
+    for _ in range(n_diag):
+        step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for name, cls in (("head", mtp.MTP_PROF_HEAD), ("attn", mtp.MTP_PROF_ATTN), ("gemv", mtp.MTP_PROF_GEMV),
+                      ("verify", mtp.MTP_PROF_VERIFY)):
+        t, n = ctx.profile_read(cls)
+        breakdown[name] = {"ms_per_step": t / n_diag, "launches_per_step": n / n_diag}
+    ctx.profile(0)
+    log(f"bench: breakdown {breakdown}")
+
+    wb, hb, gb = weight_bytes(m)
+    kvb = kv_bytes(m, dr.seqs)
+    step_bytes = wb + hb + gb + kvb + S * m.d_model * 2
+    round_bytes = N * step_bytes + S * (N + 1) * V * 4
+    head_launch_bytes = hb + m.d_hprev * m.d_model * 2 + 2 * S * m.d_model * 4
+    head_avg_ms = head_ms / max(head_n, 1)
+    achieved = head_launch_bytes / (head_avg_ms * 1e-3) / 1e9
+    value = S * N / (ms_per_step * 1e-3)
+    acc = n_acc.cpu().numpy()
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Gemma-4-26B-like assistant drafter, bf16 weights/KV, fp32 arithmetic: 4 blocks "
+                               "d_model 1024, h_prev 2816, 8 q / 2 kv heads of 256, MLP 4096, full KV 8192, "
+                               "tied head V=262144; 1 sequence, B=4 (3 draft steps) + greedy verify",
+                   "n_seq": S, "draft_steps": N, "n_vocab": V, "kv_positions": dr.seqs[0].attn_pos + 1},
+        "hbm_gbps_round": round_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "bytes_per_round": round_bytes,
+        "roofline": {"bound": "hbm", "kernel": "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "bytes_per_launch": head_launch_bytes, "avg_launch_ms": head_avg_ms,
+                     "launches": head_n},
+        "breakdown": breakdown,
+        "accepted_per_round": float(acc.mean()),
+    }
+    ctx.close()
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle time)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

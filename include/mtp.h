@@ -1,0 +1,218 @@
+/*
+ * mtp.h -- C ABI of the MI355X (gfx950) library for the data-parallel hot path
+ * of Multi-Token-Prediction speculative decoding: the fused on-device draft
+ * chain and the verify step.
+ *
+ * Sources (page title, section):
+ *   [G4]  "Gemma 4 MTP -- Multi-Token Prediction speculative decoding":
+ *         s.1 (assistant drafter fed the target's h_prev and last token, B-1
+ *         chained steps, cross-attention into the target KV, no draft KV),
+ *         s.3 (pre/post projection shapes, n_embd_backbone check),
+ *         s.4 (per-step graph, in-graph argmax), s.5 (KV read contract),
+ *         s.6 (async submit/wait, step positions), s.8 (h_idx rule).
+ *   [FUS] "Fused NextN draft graph": N steps as one launch sequence with an
+ *         on-device argmax -> embed -> hidden chain and one readback
+ *         (I32[N] + embedding).
+ *   [MTP] "MTP decoding (--mtp)": "How it is wired" (greedy acceptance of the
+ *         longest argmax-matching prefix; the free token of the first
+ *         unverified row; next h_prev from row min(n_accepted, n_rows-1)).
+ *   [AUD] "opus-mtp-turbo: Track 1 report": s.4 (exact temperature>0
+ *         speculative sampling, sampling chain order).
+ *
+ * Conventions for every entry point
+ *   - All tensors are caller-owned DEVICE memory unless marked "host".  The
+ *     library never writes weights, KV caches or inputs.
+ *   - Matrices are row-major [out, in].  bf16 is stored as raw 16-bit bf16
+ *     patterns.  A Q8_0 matrix is row-major blocks of 34 bytes: a
+ *     little-endian fp16 scale d followed by 32 int8 values q (value = d*q).
+ *   - Every call enqueues work on the context's HIP stream and returns
+ *     without waiting (the stream-ordered form of [G4] s.6's async submit;
+ *     the caller's stream synchronisation is the "wait").  Inputs are read
+ *     when the work runs.
+ *   - Errors are negative mtp_status codes.  Every check runs on the host
+ *     BEFORE anything is enqueued: a failing call has no device side effects.
+ *     A context is used by one host thread at a time.
+ */
+#ifndef MTP_H
+#define MTP_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTP_MAX_BLOCKS 8
+#define MTP_MAX_SPLITS 128   /* split-K partitions per (sequence, kv head) */
+
+typedef struct mtp_ctx mtp_ctx;
+
+typedef enum mtp_status {
+    MTP_OK = 0,
+    MTP_E_INVAL = -1,       /* null pointer, bad enum, bad scalar */
+    MTP_E_SHAPE = -2,       /* dimension mismatch or limit exceeded */
+    MTP_E_DTYPE = -3,       /* unsupported dtype combination */
+    MTP_E_NOMEM = -4,       /* device or pinned allocation failed */
+    MTP_E_DEVICE = -5,      /* HIP runtime error */
+    MTP_E_NOWEIGHTS = -6,   /* draft call on a verify-only context */
+    MTP_E_BUSY = -7         /* reserved: second in-flight request ([G4] s.6) */
+} mtp_status;
+
+typedef enum mtp_dtype { MTP_F32 = 0, MTP_BF16 = 1, MTP_Q8_0 = 2 } mtp_dtype;
+
+/* KV source kinds ([G4] s.1 twist 2: each drafter block reads the last target
+   layer of its own attention type) */
+typedef enum mtp_src { MTP_SRC_FULL = 0, MTP_SRC_SWA = 1 } mtp_src;
+
+/* Drafter description ([G4] s.3-4).  d_hprev is the target's backbone width
+   (n_embd_backbone); the pre-projection maps [embed_scale*E[tok]; h_prev]
+   (d_model + d_hprev) to d_model, the post-projection maps the final-normed
+   d_model vector to the next step's h_prev (d_hprev). */
+typedef struct mtp_model_desc {
+    int32_t d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab;
+    int32_t w_dtype;      /* MTP_F32 | MTP_BF16: w_pre, w_post, block matrices */
+    int32_t head_dtype;   /* MTP_F32 | MTP_BF16 | MTP_Q8_0: tied LM head = token embedding [n_vocab, d_model] */
+    int32_t kv_dtype;     /* MTP_F32 | MTP_BF16: target K and V */
+    int32_t swa_window;   /* positions visible through an SWA source (0: no SWA block) */
+    int32_t block_src[MTP_MAX_BLOCKS];   /* MTP_SRC_FULL or MTP_SRC_SWA per block */
+    float rms_eps;        /* RMSNorm epsilon */
+    float rope_theta;     /* RoPE base (half-split pairs (i, i + head_dim/2)) */
+    float attn_scale;     /* softmax scale, normally 1/sqrt(head_dim) */
+    float embed_scale;    /* token-embedding scale, sqrt(d_model) in [G4] s.4 */
+    int32_t max_seqs;     /* largest n_seq of any later call (sizes scratch) */
+    int32_t max_steps;    /* largest n_steps / n_draft of any later call */
+} mtp_model_desc;
+
+/* Borrowed device pointers; must stay valid and unchanged for the context's
+   lifetime.  Gains are fp32 [n] vectors.  w_q [n_head_q*head_dim, d_model],
+   g_q [head_dim] (per-head query RMSNorm), w_o [d_model, n_head_q*head_dim],
+   w_up [d_ff, d_model], w_down [d_model, d_ff]. */
+typedef struct mtp_weights {
+    const void *w_pre;          /* [d_model, d_model + d_hprev] */
+    const void *w_post;         /* [d_hprev, d_model] */
+    const void *head;           /* [n_vocab, d_model] in head_dtype */
+    const float *g_final;       /* [d_model] */
+    const float *g_attn[MTP_MAX_BLOCKS];
+    const void *w_q[MTP_MAX_BLOCKS];
+    const float *g_q[MTP_MAX_BLOCKS];
+    const void *w_o[MTP_MAX_BLOCKS];
+    const float *g_mlp[MTP_MAX_BLOCKS];
+    const void *w_up[MTP_MAX_BLOCKS];
+    const void *w_down[MTP_MAX_BLOCKS];
+} mtp_weights;
+
+/* One KV source of one sequence, read-only.  K and V hold n_cells cells;
+   cell c of kv head j starts at element c*cell_stride + j*head_dim.  A full
+   source holds position p at cell p; an SWA ring holds position p at cell
+   p mod n_cells (n_cells >= swa_window). */
+typedef struct mtp_kv_view {
+    const void *k, *v;
+    int64_t n_cells;
+    int64_t cell_stride;        /* elements; >= n_head_kv * head_dim */
+} mtp_kv_view;
+
+/* Host-side per-sequence draft descriptor ([G4] s.5): the drafter attends to
+   every position <= attn_pos (full) or the last swa_window of them (SWA);
+   step k runs RoPE at position pos0 + k (pos0 = attn_pos + 1 in [G4] s.6). */
+typedef struct mtp_seq {
+    mtp_kv_view src[2];         /* [MTP_SRC_FULL], [MTP_SRC_SWA]; unused ones may be zero */
+    int32_t attn_pos;
+    int32_t pos0;
+} mtp_seq;
+
+/* Sampling chain of the temperature>0 verify ([AUD] s.4): top-k, penalties
+   over the context window, temperature, min-p, top-p. */
+typedef struct mtp_sampler {
+    float temp, top_p, min_p;
+    float rep_penalty, presence_penalty, freq_penalty;
+    int32_t top_k;              /* 0 = off */
+    int32_t penalty_last_n;     /* context window length (0 = no penalties) */
+    uint64_t seed;
+} mtp_sampler;
+
+/* Create a context on the current HIP device, bound to hip_stream (a
+   hipStream_t; NULL = the null stream).  Allocates all scratch once
+   (vocabulary-sized buffers included).  weights == NULL makes a verify-only
+   context (then only n_vocab, max_seqs and max_steps of desc are used).
+   A Q8_0 head is re-laid out once into a context-owned copy (int8 plane plus
+   fp16 scale plane, the same bytes per weight).  Returns MTP_OK and *out. */
+int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *weights, void *hip_stream, mtp_ctx **out);
+
+/* Waits for the context's stream, then frees everything the context owns. */
+void mtp_ctx_destroy(mtp_ctx *ctx);
+
+/* Draft chain ([G4] s.4; [FUS]): for every sequence s, n_steps chained steps
+   starting from token last_tok[s] and hidden state h_prev[s, :d_hprev] (fp32).
+   Step k: x = W_pre [embed_scale*E[tok_k]; h_k]; per block: RMSNorm -> Q ->
+   per-head RMSNorm -> RoPE(pos0+k) -> cross-attention into the block's KV
+   source -> W_o + residual -> RMSNorm -> W_down silu(W_up .) + residual; final
+   RMSNorm f; logits z = E f; tok_{k+1} = argmax z (lowest id on ties);
+   h_{k+1} = W_post f.  No host round trip between steps.
+     seqs       host array [n_seq]
+     last_tok   int32 [n_seq]
+     h_prev     fp32 [n_seq, d_hprev]
+     out_drafts int32 [n_seq, n_steps]      tok_1 .. tok_n_steps
+     out_h_last fp32 [n_seq, d_hprev] or NULL  (h_{n_steps})
+     out_logits fp32 [n_seq, n_steps, n_vocab] or NULL
+   Requires 1 <= n_seq <= max_seqs, 1 <= n_steps <= max_steps,
+   0 <= attn_pos < n_cells for each full source read, n_cells >= swa_window
+   for each SWA source read.  The KV must not be rewritten at positions <=
+   attn_pos until the work completes; appending past attn_pos is allowed. */
+int mtp_draft_block(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
+                    const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
+                    float *out_logits);
+
+/* Greedy verify ([MTP] "How it is wired"; [G4] s.8).  logits fp32
+   [n_seq, n_draft+1, n_vocab] are the target's rows for [confirmed, drafts...];
+   t_i = argmax row i (lowest id on ties); a = the longest prefix with
+   drafts[s, j] == t_j; out_tokens[s, 0..a] = t_0..t_a and -1 after;
+   out_n_accept[s] = a, which is also the target row whose hidden state seeds
+   the next round's h_prev.  drafts int32 [n_seq, n_draft]. */
+int mtp_verify_greedy(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
+                      const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept);
+
+/* Exact temperature>0 verify ([AUD] s.4, after Leviathan et al. 2023 s.2.3).
+   Row i's context is the last penalty_last_n tokens of history[s, :history_len[s]]
+   ++ drafts[s, :i]; p_i and q_i are the sampling chain applied to p_logits
+   row i and q_logits row i (q_logits == NULL: q_i one-hot at drafts[s, i]).
+   Draft i is accepted when u * q_i(d_i) < p_i(d_i) with u = U(seed, s, round,
+   i, 0); at the first rejection the emitted token is drawn from
+   max(p_i - q_i, 0) and the round stops; if all are accepted a bonus token is
+   drawn from p_n_draft.  Draws use Gumbel-max over SplitMix64 counters
+   (stream 1 residual, 2 bonus).
+     p_logits fp32 [n_seq, n_draft+1, n_vocab]; q_logits fp32 [n_seq, n_draft, n_vocab]
+     history int32 [n_seq, history_stride]; history_len int32 [n_seq]
+     sampler host pointer
+     out_tokens int32 [n_seq, n_draft+1] (-1 past the emitted ones); out_n_accept int32 [n_seq] */
+int mtp_verify_sample(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
+                      const float *q_logits, const int32_t *drafts, const int32_t *history,
+                      int32_t history_stride, const int32_t *history_len, const mtp_sampler *sampler,
+                      uint64_t round, int32_t *out_tokens, int32_t *out_n_accept);
+
+/* Optional HIP-event timing of the kernels one context launches, for
+   measurement tools.  mtp_profile_enable waits for the stream, clears all
+   counters and enables the classes whose bit (1 << class) is set in mask
+   (0 disables timing).  While enabled, every launch of an enabled class is
+   bracketed by two events on the context's stream.  mtp_profile_read waits
+   for the stream, returns the summed duration (ms) and launch count of one
+   class since the last enable/read, and resets that class. */
+typedef enum mtp_prof_class {
+    MTP_PROF_HEAD = 0,      /* final norm + LM head + argmax + post-projection */
+    MTP_PROF_ATTN = 1,      /* split-K attention + merge */
+    MTP_PROF_GEMV = 2,      /* pre-projection, Q, O, up, down GEMVs */
+    MTP_PROF_VERIFY = 3,    /* greedy or sampling verify */
+    MTP_PROF_N = 4
+} mtp_prof_class;
+int mtp_profile_enable(mtp_ctx *ctx, int mask);
+int mtp_profile_read(mtp_ctx *ctx, int cls, double *total_ms, int64_t *count);
+
+/* Static string for a status code. */
+const char *mtp_strerror(int code);
+
+/* Host-only validation of a drafter description (no device calls); the same
+   checks mtp_ctx_create runs first. */
+int mtp_check_desc(const mtp_model_desc *desc);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,269 @@
+// attn_kernels.hip -- split-K GQA decode cross-attention of the drafter query
+// into the target's read-only KV cache ("Gemma 4 MTP" doc s.1, s.4-5), and the
+// log-sum-exp merge of the split partials.
+#include "widen.h"
+
+namespace mtp {
+
+// ----------------------------------------------------------------------------
+// split-K GQA cross-attention into the target KV ("Gemma 4 MTP" s.4-5)
+// ----------------------------------------------------------------------------
+// Workgroup = (split, kv head, sequence).  Prologue: the G = Hq/Hkv query
+// heads of this kv head get their per-head RMSNorm and RoPE at pos0 + step
+// (angles and sin/cos in fp64, rounded to fp32), staged in LDS.  Main loop:
+// 16 lane groups of 16 lanes; a group scores one cell at a time (each lane
+// holds DPL = hd/16 dims; the dot finishes with a 16-lane DPP sum) and keeps
+// an online softmax (m, l, acc) in base 2.  Groups merge through shuffles and
+// LDS; the workgroup writes one partial (m, l, acc[hd]) per query head.
+static constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename KT> struct KVTr;
+template <> struct KVTr<float> { static constexpr int EPV = 4; };
+template <> struct KVTr<uint16_t> { static constexpr int EPV = 8; };
+
+template <typename KT, int DPL, int G>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+    constexpr int EPV = KVTr<KT>::EPV;
+    constexpr int NVL = DPL / EPV;          // 16-byte vectors per lane per row
+    constexpr int HD = DPL * 16;
+    constexpr int T = 4;                    // cells per group per chunk
+    static_assert(DPL % EPV == 0, "lane slice must be whole 16-byte vectors");
+    __shared__ float qs[G][HD];
+    __shared__ float cs[HD / 2], sn[HD / 2];
+    __shared__ float wm[4][G], wl[4][G];
+    __shared__ float wacc[4][G][HD];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const SeqParams &sqp = a.seqs[s];
+    const SrcParams &sp = sqp.src[a.src];
+    if (split >= sp.n_split) return;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int gi = tid >> 4, li = tid & 15;
+
+    // --- prologue: per-head q RMSNorm, RoPE ---------------------------------
+    const int64_t pos = (int64_t)sqp.pos0 + a.step;
+    if (tid < HD / 2) {
+        double freq = pow((double)a.theta, -2.0 * (double)tid / (double)HD);
+        double ang = (double)pos * freq;
+        double sv, cv;
+        sincos(ang, &sv, &cv);
+        cs[tid] = (float)cv;
+        sn[tid] = (float)sv;
+    }
+    for (int j = wid; j < G; j += 4) {
+        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvh * G + j) * HD;
+        float ss = 0.f;
+        for (int c = lane; c < HD; c += 64) ss = fmaf(qh[c], qh[c], ss);
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+        for (int c = lane; c < HD; c += 64) qs[j][c] = qh[c] * r * a.g_q[c];
+    }
+    __syncthreads();
+    for (int i = tid; i < G * (HD / 2); i += kBlock) {
+        const int j = i / (HD / 2), c = i - j * (HD / 2);
+        const float x0 = qs[j][c], x1 = qs[j][c + HD / 2];
+        const float y0 = x0 * cs[c] - x1 * sn[c];
+        const float y1 = x0 * sn[c] + x1 * cs[c];
+        qs[j][c] = y0;            // each (j, c) pair is owned by one thread
+        qs[j][c + HD / 2] = y1;
+    }
+    __syncthreads();
+
+    float qr[G][DPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) qr[j][e] = qs[j][li * DPL + e] * (a.scale * kLog2e);
+
+    float m[G], l[G], acc[G][DPL];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[j][e] = 0.f;
+    }
+
+    const int pbeg = split * sp.split_len;
+    const int npos = min(sp.split_len, sp.n_vis - pbeg);
+    const KT *kbase = (const KT *)sp.k + (int64_t)kvh * HD + li * DPL;
+    const KT *vbase = (const KT *)sp.v + (int64_t)kvh * HD + li * DPL;
+
+    for (int cb = 0; cb < npos; cb += 16 * T) {
+        uint4 kv[T][NVL], vv[T][NVL];
+        bool ok[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int pi = cb + t * 16 + gi;
+            ok[t] = pi < npos;
+            int cell = sp.c0 + pbeg + pi;
+            if (cell >= sp.n_cells) cell -= sp.n_cells;
+            const int64_t off = (int64_t)cell * sp.cell_stride;
+#pragma unroll
+            for (int v = 0; v < NVL; ++v) {
+                kv[t][v] = ok[t] ? *(const uint4 *)(kbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
+                vv[t][v] = ok[t] ? *(const uint4 *)(vbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
+            }
+        }
+        float sc[T][G];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float part[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) part[j] = 0.f;
+#pragma unroll
+            for (int v = 0; v < NVL; ++v) {
+                float kf[EPV];
+                widen(kv[t][v], kf);
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) part[j] = fmaf(qr[j][v * EPV + e], kf[e], part[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float r = row_sum16(part[j]);   // all lanes take part in the DPP sum
+                sc[t][j] = ok[t] ? r : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            float mx = sc[0][j];
+#pragma unroll
+            for (int t = 1; t < T; ++t) mx = fmaxf(mx, sc[t][j]);
+            const float mn = fmaxf(m[j], mx);
+            if (mn == -INFINITY) continue;          // nothing visible yet in this group
+            const float corr = exp2f(m[j] - mn);    // m = -inf gives 0
+            m[j] = mn;
+            l[j] *= corr;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[j][e] *= corr;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                const float p = exp2f(sc[t][j] - mn);
+                l[j] += p;
+#pragma unroll
+                for (int v = 0; v < NVL; ++v) {
+                    float vf[EPV];
+                    widen(vv[t][v], vf);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc[j][v * EPV + e] = fmaf(p, vf[e], acc[j][v * EPV + e]);
+                }
+            }
+        }
+    }
+
+    // merge the 4 lane groups (rows) of each wave: xor 16, then xor 32
+#pragma unroll
+    for (int step = 16; step <= 32; step *= 2) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float mo = __shfl_xor(m[j], step);
+            const float lo = __shfl_xor(l[j], step);
+            const float mn = fmaxf(m[j], mo);
+            const float cself = (mn == -INFINITY) ? 0.f : exp2f(m[j] - mn);
+            const float coth = (mn == -INFINITY) ? 0.f : exp2f(mo - mn);
+            l[j] = l[j] * cself + lo * coth;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) {
+                const float ao = __shfl_xor(acc[j][e], step);
+                acc[j][e] = acc[j][e] * cself + ao * coth;
+            }
+            m[j] = mn;
+        }
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if (lane == 0) {
+                wm[wid][j] = m[j];
+                wl[wid][j] = l[j];
+            }
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) wacc[wid][j][li * DPL + e] = acc[j][e];
+        }
+    }
+    __syncthreads();
+    // merge the 4 waves and write the partial of each query head
+    for (int i = tid; i < G * HD; i += kBlock) {
+        const int j = i / HD, c = i - j * HD;
+        float mn = fmaxf(fmaxf(wm[0][j], wm[1][j]), fmaxf(wm[2][j], wm[3][j]));
+        float av = 0.f, lv = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float cw = (wm[w][j] == -INFINITY) ? 0.f : exp2f(wm[w][j] - mn);
+            av += wacc[w][j][c] * cw;
+            lv += wl[w][j] * cw;
+        }
+        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + 2);
+        pp[2 + c] = av;
+        if (c == 0) {
+            pp[0] = mn;
+            pp[1] = lv;
+        }
+    }
+}
+
+hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st) {
+    dim3 grid(max_split, a.Hkv, a.S);
+    const int G = a.Hq / a.Hkv;
+#define MTP_ATTN_CASE(KT, HDV, GV)                                                                  \
+    if (a.hd == HDV && G == GV) {                                                                   \
+        hipLaunchKernelGGL((attn_kernel<KT, HDV / 16, GV>), grid, dim3(kBlock), 0, st, a);          \
+        return hipGetLastError();                                                                   \
+    }
+    if (kv_dtype == MTP_BF16) {
+        MTP_ATTN_CASE(uint16_t, 256, 4)
+        MTP_ATTN_CASE(uint16_t, 256, 2)
+        MTP_ATTN_CASE(uint16_t, 256, 1)
+        MTP_ATTN_CASE(uint16_t, 128, 8)
+        MTP_ATTN_CASE(uint16_t, 128, 4)
+        MTP_ATTN_CASE(uint16_t, 128, 2)
+        MTP_ATTN_CASE(uint16_t, 128, 1)
+    } else if (kv_dtype == MTP_F32) {
+        MTP_ATTN_CASE(float, 64, 4)
+        MTP_ATTN_CASE(float, 64, 8)
+        MTP_ATTN_CASE(float, 64, 2)
+        MTP_ATTN_CASE(float, 64, 1)
+        MTP_ATTN_CASE(float, 128, 4)
+        MTP_ATTN_CASE(float, 256, 4)
+    }
+#undef MTP_ATTN_CASE
+    return hipErrorInvalidValue;
+}
+
+// log-sum-exp merge of the split partials: o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    __shared__ float red_num[4][64], red_den[4][64];
+    const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
+    const int tid = threadIdx.x, dl = tid & 63, slice = tid >> 6;
+    const int hd = a.hd;
+    const int dim = chunk * 64 + dl;
+    const int ns = a.seqs[s].src[a.src].n_split;
+    const float *base = a.part + ((int64_t)s * a.Hq + h) * MTP_MAX_SPLITS * (hd + 2);
+    float M = -INFINITY;
+    for (int j = 0; j < ns; ++j) M = fmaxf(M, base[(int64_t)j * (hd + 2)]);
+    float num = 0.f, den = 0.f;
+    for (int j = slice; j < ns; j += 4) {
+        const float *pj = base + (int64_t)j * (hd + 2);
+        const float w = (pj[0] == -INFINITY) ? 0.f : exp2f(pj[0] - M);
+        den = fmaf(w, pj[1], den);
+        if (dim < hd) num = fmaf(w, pj[2 + dim], num);
+    }
+    red_num[slice][dl] = num;
+    red_den[slice][dl] = den;
+    __syncthreads();
+    if (slice == 0 && dim < hd) {
+        const float n = (red_num[0][dl] + red_num[1][dl]) + (red_num[2][dl] + red_num[3][dl]);
+        const float dd = (red_den[0][dl] + red_den[1][dl]) + (red_den[2][dl] + red_den[3][dl]);
+        a.o[((int64_t)s * a.Hq + h) * hd + dim] = n / dd;
+    }
+}
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
+    dim3 grid((a.hd + 63) / 64, a.Hq, a.S);
+    hipLaunchKernelGGL(merge_kernel, grid, dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace mtp

@@ -1,0 +1,54 @@
+// misc_kernels.hip -- small helpers of the draft chain: draft-id hand-off, Q8_0
+// re-layout at context creation, key clearing.
+#include "widen.h"
+
+namespace mtp {
+
+// ----------------------------------------------------------------------------
+// small helpers
+// ----------------------------------------------------------------------------
+__global__ void finish_drafts_kernel(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col) {
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s < S) drafts[(int64_t)s * stride + col] = key_index(keys[s]);
+}
+
+hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(finish_drafts_kernel, dim3((S + 63) / 64), dim3(64), 0, st, keys, S, drafts, stride, col);
+    return hipGetLastError();
+}
+
+// Q8_0 blocks (fp16 scale + 32 int8) -> int8 plane [rows, cols] + fp16 scale plane [rows, cols/32]
+__global__ void q8_repack_kernel(const uint8_t *blocks, int64_t n_blocks, int8_t *q, uint16_t *s) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const uint8_t *src = blocks + b * 34;
+    s[b] = (uint16_t)(src[0] | (src[1] << 8));
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        w[i] = (uint32_t)src[2 + 4 * i] | ((uint32_t)src[3 + 4 * i] << 8) | ((uint32_t)src[4 + 4 * i] << 16) |
+               ((uint32_t)src[5 + 4 * i] << 24);
+    uint4 *dst = (uint4 *)(q + b * 32);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
+                            hipStream_t st) {
+    const int64_t nb = rows * (cols / 32);
+    hipLaunchKernelGGL(q8_repack_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, blocks, nb, q, s);
+    return hipGetLastError();
+}
+
+__global__ void clear_u64_kernel(uint64_t *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0ull;
+}
+
+hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st) {
+    hipLaunchKernelGGL(clear_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace mtp

@@ -1,0 +1,466 @@
+// mtp_api.hip -- host runtime behind include/mtp.h.
+//
+// Responsibilities: validate every argument on the host before anything is
+// enqueued, own the scratch (allocated once at create, sized by max_seqs,
+// max_steps and the drafter shape), compute the per-call attention geometry
+// (visible positions, split-K partition) and hand it to the device in one
+// small copy, then enqueue the kernel sequence of the draft chain or verify
+// step on the context's stream.  No device-to-host traffic happens inside a
+// call.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "mtp_internal.h"
+
+using namespace mtp;
+
+namespace {
+
+constexpr int kParamSlots = 8;
+
+int elem_size(int dt) { return dt == MTP_F32 ? 4 : 2; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+bool attn_supported(int kv_dtype, int hd, int g) {
+    if (kv_dtype == MTP_BF16) {
+        if (hd == 256) return g == 1 || g == 2 || g == 4;
+        if (hd == 128) return g == 1 || g == 2 || g == 4 || g == 8;
+        return false;
+    }
+    if (kv_dtype == MTP_F32) {
+        if (hd == 64) return g == 1 || g == 2 || g == 4 || g == 8;
+        if (hd == 128 || hd == 256) return g == 4;
+        return false;
+    }
+    return false;
+}
+
+int64_t pow2ceil(int64_t v) {
+    int64_t p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+}  // namespace
+
+struct mtp_ctx {
+    mtp_model_desc desc{};
+    mtp_weights w{};
+    bool has_weights = false;
+    int device = 0;
+    hipStream_t stream = nullptr;
+    // draft scratch
+    float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
+    uint64_t *dkeys = nullptr;          // [2][max_seqs]
+    int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
+    uint16_t *head_qs = nullptr;        //   and fp16 scale plane
+    SeqParams *d_params = nullptr;      // [kParamSlots][max_seqs]
+    SeqParams *h_params = nullptr;      // pinned, same shape
+    hipEvent_t ev[kParamSlots]{};
+    bool ev_pending[kParamSlots]{};
+    int slot = 0;
+    // optional event timing per kernel class
+    int prof_mask = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pool;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pending[MTP_PROF_N];
+    // verify scratch
+    uint64_t *vkeys = nullptr;          // [max_seqs][max_steps + 1]
+    float *s_rowmax = nullptr;
+    int32_t *s_cand_n = nullptr, *s_cand_id = nullptr;
+    float *s_cand_z = nullptr;
+};
+
+extern "C" const char *mtp_strerror(int code) {
+    switch (code) {
+    case MTP_OK: return "ok";
+    case MTP_E_INVAL: return "invalid argument";
+    case MTP_E_SHAPE: return "shape mismatch or limit exceeded";
+    case MTP_E_DTYPE: return "unsupported dtype combination";
+    case MTP_E_NOMEM: return "out of device or pinned memory";
+    case MTP_E_DEVICE: return "HIP runtime error";
+    case MTP_E_NOWEIGHTS: return "draft call on a verify-only context";
+    case MTP_E_BUSY: return "context busy";
+    default: return "unknown status";
+    }
+}
+
+extern "C" int mtp_check_desc(const mtp_model_desc *d) {
+    if (!d) return MTP_E_INVAL;
+    if (d->d_model <= 0 || d->d_hprev <= 0 || d->n_blocks <= 0 || d->n_head_q <= 0 || d->n_head_kv <= 0 ||
+        d->head_dim <= 0 || d->d_ff <= 0 || d->n_vocab <= 0 || d->max_seqs <= 0 || d->max_steps <= 0)
+        return MTP_E_SHAPE;
+    if (d->n_blocks > MTP_MAX_BLOCKS || d->n_head_q % d->n_head_kv) return MTP_E_SHAPE;
+    if (d->w_dtype != MTP_F32 && d->w_dtype != MTP_BF16) return MTP_E_DTYPE;
+    if (d->kv_dtype != MTP_F32 && d->kv_dtype != MTP_BF16) return MTP_E_DTYPE;
+    if (d->head_dtype != MTP_F32 && d->head_dtype != MTP_BF16 && d->head_dtype != MTP_Q8_0) return MTP_E_DTYPE;
+    if (!attn_supported(d->kv_dtype, d->head_dim, d->n_head_q / d->n_head_kv)) return MTP_E_SHAPE;
+    // 16-byte vectors over every matrix row; Q8_0 blocks of 32
+    if (d->d_model % 32 || d->d_hprev % 8 || d->d_ff % 8) return MTP_E_SHAPE;
+    const int64_t qd = (int64_t)d->n_head_q * d->head_dim;
+    const int64_t kmax = d->w_dtype == MTP_BF16 ? 4096 : 2048;        // <= 8 vectors per lane
+    if (d->d_model + d->d_hprev > kmax || d->d_ff > kmax || qd > kmax || d->d_model > kmax) return MTP_E_SHAPE;
+    const int64_t hmax = d->head_dtype == MTP_F32 ? 2048 : 4096;        // head kernel: <= 8 vectors per lane
+    if (d->d_model > hmax) return MTP_E_SHAPE;
+    if (d->max_seqs > 16 || (int64_t)d->max_seqs * d->d_model > 16384) return MTP_E_SHAPE;
+    if (d->max_steps > 64) return MTP_E_SHAPE;
+    bool swa = false;
+    for (int l = 0; l < d->n_blocks; ++l) {
+        if (d->block_src[l] != MTP_SRC_FULL && d->block_src[l] != MTP_SRC_SWA) return MTP_E_INVAL;
+        swa |= d->block_src[l] == MTP_SRC_SWA;
+    }
+    if (swa && d->swa_window <= 0) return MTP_E_SHAPE;
+    if (!(d->rms_eps >= 0.f) || !(d->attn_scale > 0.f) || !(d->rope_theta > 0.f) || !std::isfinite(d->embed_scale))
+        return MTP_E_INVAL;
+    return MTP_OK;
+}
+
+static int check_weights(const mtp_model_desc *d, const mtp_weights *w) {
+    const void *mats[] = {w->w_pre, w->w_post, w->head};
+    for (const void *p : mats)
+        if (!p || !aligned16(p)) return MTP_E_INVAL;
+    if (!w->g_final) return MTP_E_INVAL;
+    for (int l = 0; l < d->n_blocks; ++l) {
+        const void *bm[] = {w->w_q[l], w->w_o[l], w->w_up[l], w->w_down[l]};
+        for (const void *p : bm)
+            if (!p || !aligned16(p)) return MTP_E_INVAL;
+        if (!w->g_attn[l] || !w->g_q[l] || !w->g_mlp[l]) return MTP_E_INVAL;
+    }
+    return MTP_OK;
+}
+
+static void free_ctx(mtp_ctx *c) {
+    if (!c) return;
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->dkeys, c->head_q, c->head_qs, c->d_params,
+                    c->vkeys, c->s_rowmax, c->s_cand_n, c->s_cand_id, c->s_cand_z};
+    for (void *b : bufs)
+        if (b) (void)hipFree(b);
+    if (c->h_params) (void)hipHostFree(c->h_params);
+    for (int i = 0; i < kParamSlots; ++i)
+        if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
+    for (int k = 0; k < MTP_PROF_N; ++k)
+        for (auto &pr : c->prof_pending[k]) c->prof_pool.push_back(pr);
+    for (auto &pr : c->prof_pool) {
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
+    }
+    delete c;
+}
+
+template <typename T>
+static bool dalloc(T **p, size_t n) {
+    return hipMalloc((void **)p, sizeof(T) * std::max<size_t>(n, 1)) == hipSuccess;
+}
+
+extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *weights, void *hip_stream,
+                              mtp_ctx **out) {
+    if (!desc || !out) return MTP_E_INVAL;
+    *out = nullptr;
+    if (weights) {
+        int rc = mtp_check_desc(desc);
+        if (rc) return rc;
+        rc = check_weights(desc, weights);
+        if (rc) return rc;
+    } else if (desc->n_vocab <= 0 || desc->max_seqs <= 0 || desc->max_steps <= 0 || desc->max_steps > 64) {
+        return MTP_E_SHAPE;
+    }
+    mtp_ctx *c = new (std::nothrow) mtp_ctx();
+    if (!c) return MTP_E_NOMEM;
+    c->desc = *desc;
+    c->stream = (hipStream_t)hip_stream;
+    if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+    const mtp_model_desc &d = c->desc;
+    const size_t S = d.max_seqs, R = (size_t)d.max_steps + 1;
+    bool ok = dalloc(&c->vkeys, S * R);
+    if (weights) {
+        c->w = *weights;
+        c->has_weights = true;
+        const size_t qd = (size_t)d.n_head_q * d.head_dim;
+        ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
+             dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
+             dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
+             dalloc(&c->dkeys, 2 * S) && dalloc(&c->d_params, kParamSlots * S);
+        if (ok && d.head_dtype == MTP_Q8_0)
+            ok = dalloc(&c->head_q, (size_t)d.n_vocab * d.d_model) &&
+                 dalloc(&c->head_qs, (size_t)d.n_vocab * (d.d_model / 32));
+        if (ok) ok = hipHostMalloc((void **)&c->h_params, sizeof(SeqParams) * kParamSlots * S) == hipSuccess;
+        for (int i = 0; ok && i < kParamSlots; ++i)
+            ok = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) == hipSuccess;
+    }
+    if (!ok) { free_ctx(c); return MTP_E_NOMEM; }
+    if (hipMemset(c->vkeys, 0, sizeof(uint64_t) * S * R) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+    if (c->has_weights) {
+        if (hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+        if (d.head_dtype == MTP_Q8_0 &&
+            launch_q8_repack((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_q, c->head_qs, c->stream) !=
+                hipSuccess) {
+            free_ctx(c);
+            return MTP_E_DEVICE;
+        }
+    }
+    *out = c;
+    return MTP_OK;
+}
+
+extern "C" void mtp_ctx_destroy(mtp_ctx *c) {
+    if (!c) return;
+    (void)hipStreamSynchronize(c->stream);
+    free_ctx(c);
+}
+
+// ---------------------------------------------------------------------------
+// optional event timing
+// ---------------------------------------------------------------------------
+namespace {
+struct ProfScope {
+    mtp_ctx *c;
+    int cls;
+    std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+    ProfScope(mtp_ctx *ctx, int k) : c(ctx), cls(k) {
+        if (!(c->prof_mask & (1 << cls))) return;
+        if (c->prof_pool.empty()) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess) return;
+            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+            c->prof_pool.emplace_back(a, b);
+        }
+        ev = c->prof_pool.back();
+        c->prof_pool.pop_back();
+        (void)hipEventRecord(ev.first, c->stream);
+    }
+    ~ProfScope() {
+        if (!ev.first) return;
+        (void)hipEventRecord(ev.second, c->stream);
+        c->prof_pending[cls].push_back(ev);
+    }
+};
+}  // namespace
+
+extern "C" int mtp_profile_enable(mtp_ctx *c, int mask) {
+    if (!c) return MTP_E_INVAL;
+    if (hipStreamSynchronize(c->stream) != hipSuccess) return MTP_E_DEVICE;
+    for (int k = 0; k < MTP_PROF_N; ++k) {
+        for (auto &pr : c->prof_pending[k]) c->prof_pool.push_back(pr);
+        c->prof_pending[k].clear();
+    }
+    c->prof_mask = mask & ((1 << MTP_PROF_N) - 1);
+    return MTP_OK;
+}
+
+extern "C" int mtp_profile_read(mtp_ctx *c, int cls, double *total_ms, int64_t *count) {
+    if (!c || cls < 0 || cls >= MTP_PROF_N || !total_ms || !count) return MTP_E_INVAL;
+    if (hipStreamSynchronize(c->stream) != hipSuccess) return MTP_E_DEVICE;
+    double t = 0.0;
+    for (auto &pr : c->prof_pending[cls]) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return MTP_E_DEVICE;
+        t += ms;
+        c->prof_pool.push_back(pr);
+    }
+    *total_ms = t;
+    *count = (int64_t)c->prof_pending[cls].size();
+    c->prof_pending[cls].clear();
+    return MTP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// draft chain
+// ---------------------------------------------------------------------------
+static int src_geometry(const mtp_model_desc &d, const mtp_seq &sq, int src, SrcParams &p) {
+    const mtp_kv_view &kv = sq.src[src];
+    const int es = elem_size(d.kv_dtype);
+    if (!kv.k || !kv.v || !aligned16(kv.k) || !aligned16(kv.v)) return MTP_E_INVAL;
+    if (kv.n_cells <= 0 || kv.n_cells > 0x7FFFFFFF) return MTP_E_SHAPE;
+    if (kv.cell_stride < (int64_t)d.n_head_kv * d.head_dim || (kv.cell_stride * es) % 16) return MTP_E_SHAPE;
+    p.k = kv.k;
+    p.v = kv.v;
+    p.cell_stride = kv.cell_stride;
+    p.n_cells = (int32_t)kv.n_cells;
+    if (src == MTP_SRC_FULL) {
+        if (sq.attn_pos >= kv.n_cells) return MTP_E_SHAPE;
+        p.lo = 0;
+        p.n_vis = sq.attn_pos + 1;
+        p.c0 = 0;
+    } else {
+        if (kv.n_cells < d.swa_window) return MTP_E_SHAPE;
+        p.lo = std::max(0, sq.attn_pos - d.swa_window + 1);
+        p.n_vis = sq.attn_pos - p.lo + 1;
+        p.c0 = (int32_t)(p.lo % kv.n_cells);
+    }
+    const int64_t per = (p.n_vis + MTP_MAX_SPLITS - 1) / MTP_MAX_SPLITS;
+    p.split_len = (int32_t)std::max<int64_t>(64, pow2ceil(per));
+    p.n_split = (p.n_vis + p.split_len - 1) / p.split_len;
+    return MTP_OK;
+}
+
+static int gemv_rows_per_wg(int M) {
+    int r = (M + 511) / 512;
+    r = ((r + 3) / 4) * 4;
+    return std::max(4, r);
+}
+
+static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a) {
+    ProfScope ps(c, MTP_PROF_GEMV);
+    a.rows_per_wg = gemv_rows_per_wg(a.M);
+    const int n_wg = (a.M + a.rows_per_wg - 1) / a.rows_per_wg;
+    return launch_gemv(c->desc.w_dtype, in_mode, epi, a, n_wg, c->stream);
+}
+
+extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
+                               const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
+                               float *out_logits) {
+    if (!c) return MTP_E_INVAL;
+    if (!c->has_weights) return MTP_E_NOWEIGHTS;
+    const mtp_model_desc &d = c->desc;
+    if (n_seq < 1 || n_seq > d.max_seqs || n_steps < 1 || n_steps > d.max_steps) return MTP_E_SHAPE;
+    if (!seqs || !last_tok || !h_prev || !out_drafts) return MTP_E_INVAL;
+    bool use_src[2] = {false, false};
+    for (int l = 0; l < d.n_blocks; ++l) use_src[d.block_src[l]] = true;
+
+    // per-call geometry into the next pinned slot
+    const int slot = c->slot;
+    if (c->ev_pending[slot] && hipEventSynchronize(c->ev[slot]) != hipSuccess) return MTP_E_DEVICE;
+    c->ev_pending[slot] = false;
+    SeqParams *hp = c->h_params + (size_t)slot * d.max_seqs;
+    int max_split[2] = {0, 0};
+    for (int s = 0; s < n_seq; ++s) {
+        const mtp_seq &sq = seqs[s];
+        SeqParams &p = hp[s];
+        std::memset(&p, 0, sizeof(p));
+        if (sq.attn_pos < 0 || sq.pos0 < 0 || (int64_t)sq.pos0 + n_steps > 0x7FFFFFFF) return MTP_E_INVAL;
+        p.pos0 = sq.pos0;
+        for (int src = 0; src < 2; ++src) {
+            if (!use_src[src]) continue;
+            int rc = src_geometry(d, sq, src, p.src[src]);
+            if (rc) return rc;
+            max_split[src] = std::max(max_split[src], p.src[src].n_split);
+        }
+    }
+    SeqParams *dp = c->d_params + (size_t)slot * d.max_seqs;
+    if (hipMemcpyAsync(dp, hp, sizeof(SeqParams) * n_seq, hipMemcpyHostToDevice, c->stream) != hipSuccess)
+        return MTP_E_DEVICE;
+    if (hipEventRecord(c->ev[slot], c->stream) != hipSuccess) return MTP_E_DEVICE;
+    c->ev_pending[slot] = true;
+    c->slot = (slot + 1) % kParamSlots;
+
+    const int D = d.d_model, DH = d.d_hprev, QD = d.n_head_q * d.head_dim, F = d.d_ff, V = d.n_vocab;
+    const int S = n_seq;
+    hipError_t e = hipSuccess;
+    for (int k = 0; k < n_steps && e == hipSuccess; ++k) {
+        uint64_t *key_cur = c->dkeys + (size_t)(k & 1) * d.max_seqs;
+        uint64_t *key_prev = c->dkeys + (size_t)((k + 1) & 1) * d.max_seqs;
+        // a1: x = W_pre [embed_scale * E[tok]; h]
+        GemvArgs ga{};
+        ga.W = c->w.w_pre; ga.M = D; ga.K = D + DH; ga.S = S;
+        ga.embed = c->w.head; ga.embed_dtype = d.head_dtype; ga.d_embed = D; ga.embed_rows = V;
+        ga.embed_q = c->head_q; ga.embed_qs = c->head_qs; ga.embed_scale = d.embed_scale;
+        ga.tok_in = k == 0 ? last_tok : nullptr;
+        ga.key_in = key_prev;
+        ga.h = k == 0 ? h_prev : c->h; ga.dh = DH;
+        ga.key_reset = key_cur;
+        ga.drafts_out = k > 0 ? out_drafts : nullptr; ga.drafts_stride = n_steps; ga.drafts_col = k - 1;
+        ga.dst = c->x; ga.dst_stride = D;
+        e = run_gemv(c, IN_EMBED, EPI_STORE, ga);
+        for (int l = 0; l < d.n_blocks && e == hipSuccess; ++l) {
+            // a2: q = W_q rmsnorm(x)
+            GemvArgs gq{};
+            gq.W = c->w.w_q[l]; gq.M = QD; gq.K = D; gq.S = S;
+            gq.src = c->x; gq.src_stride = D; gq.gain = c->w.g_attn[l]; gq.eps = d.rms_eps;
+            gq.dst = c->q; gq.dst_stride = QD;
+            e = run_gemv(c, IN_NORM, EPI_STORE, gq);
+            // a3: split-K attention + merge
+            const int src = d.block_src[l];
+            {
+                ProfScope ps_attn(c, MTP_PROF_ATTN);
+                if (e == hipSuccess) {
+                    AttnArgs aa{};
+                    aa.q = c->q; aa.g_q = c->w.g_q[l]; aa.eps = d.rms_eps; aa.theta = d.rope_theta;
+                    aa.scale = d.attn_scale; aa.Hq = d.n_head_q; aa.Hkv = d.n_head_kv; aa.hd = d.head_dim;
+                    aa.S = S; aa.src = src; aa.step = k; aa.seqs = dp; aa.part = c->part;
+                    e = launch_attn(d.kv_dtype, aa, max_split[src], c->stream);
+                }
+                if (e == hipSuccess) {
+                    MergeArgs ma{};
+                    ma.part = c->part; ma.o = c->o; ma.Hq = d.n_head_q; ma.Hkv = d.n_head_kv;
+                    ma.hd = d.head_dim; ma.S = S; ma.src = src; ma.seqs = dp;
+                    e = launch_merge(ma, c->stream);
+                }
+            }
+            // a4: x += W_o o
+            if (e == hipSuccess) {
+                GemvArgs go{};
+                go.W = c->w.w_o[l]; go.M = D; go.K = QD; go.S = S;
+                go.src = c->o; go.src_stride = QD; go.dst = c->x; go.dst_stride = D;
+                e = run_gemv(c, IN_PLAIN, EPI_ADD, go);
+            }
+            // a5: u = silu(W_up rmsnorm(x)); x += W_down u
+            if (e == hipSuccess) {
+                GemvArgs gu{};
+                gu.W = c->w.w_up[l]; gu.M = F; gu.K = D; gu.S = S;
+                gu.src = c->x; gu.src_stride = D; gu.gain = c->w.g_mlp[l]; gu.eps = d.rms_eps;
+                gu.dst = c->u; gu.dst_stride = F;
+                e = run_gemv(c, IN_NORM, EPI_SILU, gu);
+            }
+            if (e == hipSuccess) {
+                GemvArgs gd{};
+                gd.W = c->w.w_down[l]; gd.M = D; gd.K = F; gd.S = S;
+                gd.src = c->u; gd.src_stride = F; gd.dst = c->x; gd.dst_stride = D;
+                e = run_gemv(c, IN_PLAIN, EPI_ADD, gd);
+            }
+        }
+        // a6 + a7: final norm, LM head + argmax, post-projection
+        if (e == hipSuccess) {
+            HeadArgs ha{};
+            ha.x = c->x; ha.g_final = c->w.g_final; ha.eps = d.rms_eps; ha.d = D; ha.S = S; ha.V = V;
+            ha.head = c->w.head; ha.head_q = c->head_q; ha.head_qs = c->head_qs;
+            const int n_head_wg = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (V + 15) / 16));
+            int rpw = (V + n_head_wg - 1) / n_head_wg;
+            rpw = ((rpw + 15) / 16) * 16;
+            ha.rows_per_wg = rpw;
+            ha.n_head_wg = (V + rpw - 1) / rpw;
+            ha.keys = key_cur;
+            ha.logits = out_logits ? out_logits + (size_t)k * V : nullptr;
+            ha.logits_stride = (int64_t)n_steps * V;
+            ha.w_post = c->w.w_post; ha.dh = DH;
+            ha.post_rows_per_wg = 4;
+            ha.h_out = (k == n_steps - 1 && out_h_last) ? out_h_last : c->h;
+            const int n_post_wg = (DH + ha.post_rows_per_wg - 1) / ha.post_rows_per_wg;
+            ProfScope ps(c, MTP_PROF_HEAD);
+            e = launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, c->stream);
+        }
+    }
+    if (e == hipSuccess)
+        e = launch_finish_drafts(c->dkeys + (size_t)((n_steps - 1) & 1) * d.max_seqs, S, out_drafts, n_steps,
+                                 n_steps - 1, c->stream);
+    return e == hipSuccess ? MTP_OK : MTP_E_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// verify
+// ---------------------------------------------------------------------------
+extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
+                                 const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept) {
+    if (!c) return MTP_E_INVAL;
+    if (n_seq < 1 || n_seq > c->desc.max_seqs || n_draft < 0 || n_draft > c->desc.max_steps || n_vocab < 1)
+        return MTP_E_SHAPE;
+    if (!logits || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept) return MTP_E_INVAL;
+    ProfScope ps(c, MTP_PROF_VERIFY);
+    hipError_t e = launch_verify_greedy(logits, drafts, n_seq, n_draft, n_vocab, c->vkeys, out_tokens, out_n_accept,
+                                        c->stream);
+    return e == hipSuccess ? MTP_OK : MTP_E_DEVICE;
+}
+
+extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
+                                 const float *q_logits, const int32_t *drafts, const int32_t *history,
+                                 int32_t history_stride, const int32_t *history_len, const mtp_sampler *sp,
+                                 uint64_t round, int32_t *out_tokens, int32_t *out_n_accept) {
+    (void)q_logits; (void)drafts; (void)history; (void)history_stride; (void)history_len; (void)sp; (void)round;
+    (void)out_tokens; (void)out_n_accept; (void)p_logits; (void)n_vocab; (void)n_draft; (void)n_seq;
+    if (!c) return MTP_E_INVAL;
+    return MTP_E_DTYPE;
+}

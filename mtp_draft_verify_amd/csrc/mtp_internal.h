@@ -1,0 +1,134 @@
+// mtp_internal.h -- structures shared by the host runtime and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mtp.h"
+
+namespace mtp {
+
+// Per-(sequence, source) attention geometry, computed on the host per call and
+// copied to the device once per call.  Positions lo .. lo+n_vis-1 are visible;
+// position lo + j lives at cell c0 + j (wrapped once at n_cells for a ring).
+struct SrcParams {
+    const void *k;
+    const void *v;
+    int64_t cell_stride;
+    int32_t n_cells;
+    int32_t lo;
+    int32_t n_vis;
+    int32_t c0;
+    int32_t split_len;
+    int32_t n_split;
+};
+
+struct SeqParams {
+    SrcParams src[2];
+    int32_t pos0;
+    int32_t pad[3];
+};
+
+// Input transforms applied while a GEMV stages its input vector.
+enum GemvIn : int { IN_PLAIN = 0, IN_NORM = 1, IN_EMBED = 2 };
+// Output transforms.
+enum GemvEpi : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SILU = 2 };
+
+struct GemvArgs {
+    const void *W;          // [M, K] row-major
+    int32_t M, K, S;
+    int32_t rows_per_wg;
+    // input
+    const float *src;       // [S, src_stride] (IN_PLAIN / IN_NORM)
+    int32_t src_stride;
+    const float *gain;      // IN_NORM
+    float eps;
+    // IN_EMBED: [embed_scale * E[tok]; h]
+    const void *embed;      // head / embedding table [V, d]
+    int32_t embed_dtype, d_embed, embed_rows;
+    const int8_t *embed_q;  // Q8_0 plane [V, d]
+    const uint16_t *embed_qs;   // Q8_0 scales [V, d/32]
+    float embed_scale;
+    const int32_t *tok_in;  // step 0: caller's last_tok
+    const uint64_t *key_in; // later steps: argmax keys of the previous step
+    const float *h;         // [S, dh]
+    int32_t dh;
+    uint64_t *key_reset;    // keys to clear for this step's head
+    int32_t *drafts_out;    // write drafts[s, step-1] (nullptr: none)
+    int32_t drafts_stride, drafts_col;
+    // output
+    float *dst;             // [S, dst_stride]
+    int32_t dst_stride;
+};
+
+struct HeadArgs {
+    // final norm
+    const float *x;         // [S, d]
+    const float *g_final;
+    float eps;
+    int32_t d, S, V;
+    // head
+    const void *head;       // bf16 / f32 [V, d]
+    const int8_t *head_q;   // Q8_0 plane [V, d]
+    const uint16_t *head_qs;    // Q8_0 scales [V, d/32]
+    int32_t rows_per_wg, n_head_wg;
+    uint64_t *keys;         // [S] argmax keys (cleared before)
+    float *logits;          // [S, logits_stride] at this step's offset, or nullptr
+    int64_t logits_stride;
+    // post-projection: h = W_post f
+    const void *w_post;     // [dh, d] (w dtype)
+    int32_t dh, post_rows_per_wg;
+    float *h_out;           // [S, dh]
+};
+
+struct AttnArgs {
+    const float *q;         // [S, Hq*hd] raw projections
+    const float *g_q;       // [hd]
+    float eps, theta, scale;
+    int32_t Hq, Hkv, hd, S, src, step;
+    const SeqParams *seqs;
+    float *part;            // [S, Hq, MTP_MAX_SPLITS, hd + 2]  (m, l, o[hd])
+};
+
+struct MergeArgs {
+    const float *part;
+    float *o;               // [S, Hq*hd]
+    int32_t Hq, Hkv, hd, S, src;
+    const SeqParams *seqs;
+};
+
+// launchers (defined with their kernels; all enqueue on `st`)
+hipError_t launch_gemv(int w_dtype, int in_mode, int epi, const GemvArgs &a, int n_wg, hipStream_t st);
+hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, hipStream_t st);
+hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
+hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col,
+                                hipStream_t st);
+hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
+                            hipStream_t st);
+hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
+
+// verify
+hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,
+                                uint64_t *keys, int32_t *out_tokens, int32_t *out_n_accept, hipStream_t st);
+
+struct SampleArgs {
+    const float *p_logits;  // [S, N+1, V]
+    const float *q_logits;  // [S, N, V] or nullptr
+    const int32_t *drafts;  // [S, N]
+    const int32_t *history; // [S, hstride]
+    const int32_t *history_len;
+    int32_t hstride, S, N, V;
+    float temp, top_p, min_p, rep, presence, freq;
+    int32_t top_k, last_n;
+    uint64_t seed, round;
+    // scratch
+    float *row_max;         // [S, 2, N+1]  (0: p rows, 1: q rows)
+    int32_t *cand_n;        // [S, 2, N+1]
+    int32_t *cand_id;       // [S, 2, N+1, cap]
+    float *cand_z;          // [S, 2, N+1, cap]
+    int32_t cap;
+    int32_t *out_tokens, *out_n_accept;
+};
+hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st);
+
+}  // namespace mtp

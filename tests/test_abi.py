@@ -1,0 +1,82 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and host-only validation rejects bad descriptions and
+arguments without touching a device."""
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def mtp():
+    import mtp_draft_verify_amd as m
+    if not m.LIB_PATH.exists():
+        from mtp_draft_verify_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def test_every_declared_symbol_is_exported(mtp):
+    header = (ROOT / "include" / "mtp.h").read_text()
+    declared = set(re.findall(r"^(?:int|void|const char \*)\s*\*?\s*(mtp_\w+)\s*\(", header, re.M))
+    assert {"mtp_ctx_create", "mtp_draft_block", "mtp_verify_greedy", "mtp_verify_sample"} <= declared
+    assert declared == set(mtp.EXPORTS)
+    L = C.CDLL(str(mtp.LIB_PATH))
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_strerror_names_every_status(mtp):
+    for code in range(0, -8, -1):
+        assert mtp.mtp_strerror(code) != "unknown status"
+    assert mtp.mtp_strerror(-99) == "unknown status"
+
+
+def _c2_desc(mtp, **over):
+    kw = dict(d_model=1024, d_hprev=2816, n_blocks=4, n_head_q=8, n_head_kv=2, head_dim=256, d_ff=4096,
+              n_vocab=262144, w_dtype=mtp.MTP_BF16, head_dtype=mtp.MTP_BF16, kv_dtype=mtp.MTP_BF16,
+              max_seqs=16, max_steps=4)
+    kw.update(over)
+    return mtp.make_desc(**kw)
+
+
+def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
+    assert mtp.mtp_check_desc(_c2_desc(mtp)) == mtp.MTP_OK
+    assert mtp.mtp_check_desc(_c2_desc(mtp, head_dtype=mtp.MTP_Q8_0, max_seqs=8, max_steps=4)) == mtp.MTP_OK
+    assert mtp.mtp_check_desc(_c2_desc(mtp, swa_window=1024, block_src=[1, 1, 1, 0])) == mtp.MTP_OK
+    tiny = dict(d_model=256, d_hprev=256, n_blocks=1, n_head_q=4, n_head_kv=1, head_dim=64, d_ff=1024, n_vocab=4096,
+                w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32, max_seqs=1, max_steps=3)
+    assert mtp.mtp_check_desc(mtp.make_desc(**tiny)) == mtp.MTP_OK
+    bad = [
+        dict(n_head_kv=3),                        # Hq % Hkv
+        dict(n_blocks=9),                         # > MTP_MAX_BLOCKS
+        dict(d_model=1000),                       # not a multiple of 32
+        dict(w_dtype=mtp.MTP_Q8_0),               # Q8_0 only for the head
+        dict(kv_dtype=7),
+        dict(max_seqs=17),                        # > 16 sequences
+        dict(block_src=[1, 0, 0, 0]),             # SWA block without a window
+        dict(head_dim=96),                        # no attention instantiation
+        dict(d_ff=8192),                          # GEMV row longer than supported
+        dict(max_steps=0),
+    ]
+    for b in bad:
+        rc = mtp.mtp_check_desc(_c2_desc(mtp, **b))
+        assert rc < 0, b
+    assert mtp.lib().mtp_check_desc(None) == mtp.MTP_E_INVAL
+
+
+def test_entry_points_reject_null_context_without_device_work(mtp):
+    L = mtp.lib()
+    assert L.mtp_draft_block(None, 1, None, None, None, 1, None, None, None) == mtp.MTP_E_INVAL
+    assert L.mtp_verify_greedy(None, 1, 1, 10, None, None, None, None) == mtp.MTP_E_INVAL
+    sp = mtp.make_sampler(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4)
+    assert L.mtp_verify_sample(None, 1, 1, 10, None, None, None, None, 0, None, C.byref(sp), 0, None,
+                               None) == mtp.MTP_E_INVAL
+    assert L.mtp_ctx_create(None, None, None, None) == mtp.MTP_E_INVAL
+    assert L.mtp_profile_enable(None, 1) == mtp.MTP_E_INVAL
+    assert L.mtp_profile_read(None, 0, None, None) == mtp.MTP_E_INVAL
+    L.mtp_ctx_destroy(None)

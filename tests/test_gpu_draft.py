@@ -1,0 +1,146 @@
+"""GPU parity of the draft chain (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+
+import mtp_synth as syn
+from tests.gpu_harness import GpuDrafter, compare_draft, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, gpu_out, orc_out, idx=None, max_near=1):
+    c = compare_draft(w.model, gpu_out, orc_out, idx)
+    log(f"  {w.name}: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
+        f"max_h_err={c.max_h_err:.3g}")
+    assert c.near_ties <= max_near
+    return c
+
+
+def test_c1_tiny_fp32_matches_oracle(orc):
+    log("case c1 tiny fp32: S=1 N=3 ctx=512")
+    w = syn.c1_tiny()
+    g = GpuDrafter(w.model, 1, 3)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
+def test_c1_shapes_ragged_multi_seq(orc):
+    log("case c1 shapes: S=3 N=5 ctx=300 (ragged split tail)")
+    w = syn.c1_tiny(n_seq=3, n_steps=5, ctx=300)
+    g = GpuDrafter(w.model, 4, 6)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
+def test_c2_gemma_bf16_full_size_matches_oracle(orc):
+    log("case c2 full: bf16, V=262144, ctx=8192, S=1 N=3")
+    w = syn.c2_gemma_bf16()
+    g = GpuDrafter(w.model, 1, 3)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
+def test_c2_shapes_ragged_vocab_and_context(orc):
+    log("case c2 shapes: V=262144-123, ctx=1000, S=3 N=2")
+    w = syn.c2_gemma_bf16(n_vocab=262144 - 123, ctx=1000, n_seq=3, n_steps=2)
+    g = GpuDrafter(w.model, 3, 2)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
+def test_c3_interleaved_swa_full_small_contexts(orc):
+    log("case c3 small: 16 seqs, ctx U[700, 5000], SWA window 1024 ring")
+    w = syn.c3_interleaved(ctx_range=(700, 5000), full_cap=5000)
+    g = GpuDrafter(w.model, 16, 3)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft), max_near=2)
+
+
+def test_c3_full_size_sampled_sequences(orc):
+    log("case c3 full: 16 seqs, ctx U[4096, 32768]; oracle on 4 sampled sequences")
+    w = syn.c3_interleaved()
+    g = GpuDrafter(w.model, 16, 3)
+    gpu = g.run(w.draft)
+    idx = [0, 5, 10, 15]
+    _check(w, gpu, orc.draft_block(w.model, w.draft, seq_idx=idx), idx)
+
+
+def test_c4_q8_head_small_context(orc):
+    log("case c4 small: Q8_0 head, 8 seqs, ctx 3000, N=4")
+    w = syn.c4_longctx_q8(ctx=3000)
+    g = GpuDrafter(w.model, 8, 4)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
+def test_chained_equals_step_by_step_on_gpu():
+    """One N-step call == N one-step calls chained through (token, h), bit for
+    bit (the fused-vs-sequential check of the evaluation record)."""
+    log("case chain==steps: c3 small shapes")
+    w = syn.c3_interleaved(ctx_range=(700, 3000), full_cap=3000, n_seq=5)
+    g = GpuDrafter(w.model, 5, 3)
+    full = g.run(w.draft)
+    tok, h = w.draft.last_tok.copy(), w.draft.h_prev.copy()
+    for k in range(3):
+        one = g.run(w.draft, n_steps=1, last_tok=tok, h_prev=h, pos0_shift=k)
+        assert np.array_equal(one["drafts"][:, 0], full["drafts"][:, k])
+        assert np.array_equal(one["logits"][:, 0], full["logits"][:, k])
+        tok, h = one["drafts"][:, 0].copy(), one["h_last"].copy()
+    assert np.array_equal(h, full["h_last"])
+
+
+def test_sequence_alone_equals_sequence_in_batch():
+    """Per-sequence reductions do not depend on the batch: a sequence drafted
+    alone gives the same bits as inside a batch of 6."""
+    log("case alone==batch")
+    w = syn.c3_interleaved(ctx_range=(700, 3000), full_cap=3000, n_seq=6)
+    g = GpuDrafter(w.model, 6, 3)
+    batch = g.run(w.draft)
+    for s in (0, 4):
+        one = g.run(w.draft, seq_idx=[s])
+        assert np.array_equal(one["drafts"][0], batch["drafts"][s])
+        assert np.array_equal(one["logits"][0], batch["logits"][s])
+        assert np.array_equal(one["h_last"][0], batch["h_last"][s])
+
+
+def test_kv_is_read_only_and_unseen_cells_are_never_read():
+    """The drafter never writes the target KV, and cells outside the visible
+    range (past attn_pos, outside the SWA window) can hold NaN without any
+    effect ("Gemma 4 MTP" s.5; the audit page's no-invalid-read check)."""
+    import torch
+    from mtp_synth.device import upload_seqs
+    log("case kv read-only + poisoned cells")
+    w = syn.c3_interleaved(ctx_range=(1500, 2500), full_cap=4096, n_seq=4)
+    g = GpuDrafter(w.model, 4, 3)
+    ref = g.run(w.draft)
+    # poison: full cells > attn_pos; SWA ring cells are all visible when ctx >= W,
+    # so rebuild each ring with extra capacity and poison the unused cells
+    for s in w.draft.seqs:
+        full, swa = s.src
+        k, v = full.k.copy(), full.v.copy()
+        k[s.attn_pos + 1:] = 0x7FC0
+        v[s.attn_pos + 1:] = 0x7FC0
+        C = swa.n_cells + 77
+        k2 = np.full((C,) + swa.k.shape[1:], 0x7FC0, np.uint16)
+        v2 = np.full((C,) + swa.v.shape[1:], 0x7FC0, np.uint16)
+        W = w.model.swa_window
+        for p in range(s.attn_pos - W + 1, s.attn_pos + 1):
+            k2[p % C], v2[p % C] = swa.k[p % swa.n_cells], swa.v[p % swa.n_cells]
+        s.src = [syn.KVSource(k, v), syn.KVSource(k2, v2)]
+    seqs, lt, hp, keep = upload_seqs(w.model, w.draft, "cuda")
+    before = [torch.cat([t.view(torch.int16).flatten().to(torch.int64) for t in keep]).sum().item()]
+    import mtp_draft_verify_amd as mtp
+    drafts = torch.zeros((4, 3), dtype=torch.int32, device="cuda")
+    h = torch.zeros((4, w.model.d_hprev), device="cuda")
+    logits = torch.zeros((4, 3, w.model.n_vocab), device="cuda")
+    g.ctx.draft_block(seqs, lt, hp, 3, drafts, h, logits)
+    torch.cuda.synchronize()
+    after = torch.cat([t.view(torch.int16).flatten().to(torch.int64) for t in keep]).sum().item()
+    assert before[0] == after
+    assert np.array_equal(drafts.cpu().numpy(), ref["drafts"])
+    assert np.array_equal(logits.cpu().numpy(), ref["logits"])
+    assert np.array_equal(h.cpu().numpy(), ref["h_last"])
+
+
+def test_repeated_calls_are_deterministic():
+    log("case determinism")
+    w = syn.c2_gemma_bf16(ctx=2000, n_vocab=65536)
+    g = GpuDrafter(w.model, 1, 3)
+    a = g.run(w.draft)
+    b = g.run(w.draft)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
