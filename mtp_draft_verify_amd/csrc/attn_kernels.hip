@@ -8,12 +8,14 @@ namespace mtp {
 // ----------------------------------------------------------------------------
 // split-K GQA cross-attention into the target KV ("Gemma 4 MTP" s.4-5)
 // ----------------------------------------------------------------------------
-// Workgroup = (split, kv head, sequence).  Prologue: the G = Hq/Hkv query
-// heads of this kv head get their per-head RMSNorm and RoPE at pos0 + step
-// (angles and sin/cos in fp64, rounded to fp32), staged in LDS.  Main loop:
-// 16 lane groups of 16 lanes; a group scores one cell at a time (each lane
-// holds DPL = hd/16 dims; the dot finishes with a 16-lane DPP sum) and keeps
-// an online softmax (m, l, acc) in base 2.  Groups merge through shuffles and
+// Workgroup = (split, kv head, sequence).  The first chunk of K/V is loaded
+// before anything else (it does not depend on the query), so its HBM latency
+// overlaps the prologue: per-head RMSNorm of the G = Hq/Hkv query heads of
+// this kv head, then RoPE at pos0 + step (angle pos * inv_freq in fp64, reduced
+// mod 2*pi in fp64, sin/cos in fp32), staged in LDS.  Main loop: 16 lane
+// groups of 16 lanes; a group scores one cell at a time (each lane holds
+// DPL = hd/16 dims; the dot finishes with a 16-lane DPP sum) and keeps an
+// online softmax (m, l, acc) in base 2.  Groups merge through shuffles and
 // LDS; the workgroup writes one partial (m, l, acc[hd]) per query head.
 static constexpr float kLog2e = 1.4426950408889634f;
 
@@ -40,23 +42,66 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int gi = tid >> 4, li = tid & 15;
 
-    // --- prologue: per-head q RMSNorm, RoPE ---------------------------------
+    const int pbeg = split * sp.split_len;
+    const int npos = min(sp.split_len, sp.n_vis - pbeg);
+    const KT *kbase = (const KT *)sp.k + (int64_t)kvh * HD + li * DPL;
+    const KT *vbase = (const KT *)sp.v + (int64_t)kvh * HD + li * DPL;
+    uint4 kv[T][NVL], vv[T][NVL];
+    bool ok[T];
+    auto load_chunk = [&](int cb) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int pi = cb + t * 16 + gi;
+            ok[t] = pi < npos;
+            int cell = sp.c0 + pbeg + pi;
+            if (cell >= sp.n_cells) cell -= sp.n_cells;
+            const int64_t off = (int64_t)cell * sp.cell_stride;
+#pragma unroll
+            for (int v = 0; v < NVL; ++v) {
+                kv[t][v] = ok[t] ? *(const uint4 *)(kbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
+                vv[t][v] = ok[t] ? *(const uint4 *)(vbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    load_chunk(0);
+
+    // --- prologue: per-head q RMSNorm, RoPE (all its loads issued first) -----
+    constexpr int QPL = (HD + 63) / 64;     // query values per lane per head
+    constexpr int GW = (G + 3) / 4;         // heads per wave
+    float qv[GW][QPL], gq[QPL];
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) gq[i] = (lane + 64 * i < HD) ? a.g_q[lane + 64 * i] : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < GW; ++jj) {
+        const int j = wid + 4 * jj;
+        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvh * G + min(j, G - 1)) * HD;
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) qv[jj][i] = (lane + 64 * i < HD) ? qh[lane + 64 * i] : 0.f;
+    }
+    const double invf = (tid < HD / 2) ? a.inv_freq[tid] : 0.0;
     const int64_t pos = (int64_t)sqp.pos0 + a.step;
     if (tid < HD / 2) {
-        double freq = pow((double)a.theta, -2.0 * (double)tid / (double)HD);
-        double ang = (double)pos * freq;
-        double sv, cv;
-        sincos(ang, &sv, &cv);
-        cs[tid] = (float)cv;
-        sn[tid] = (float)sv;
+        const double kTwoPi = 6.283185307179586476925;
+        const double ang = (double)pos * invf;
+        const double red = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
+        float sv, cv;
+        sincosf((float)red, &sv, &cv);
+        cs[tid] = cv;
+        sn[tid] = sv;
     }
-    for (int j = wid; j < G; j += 4) {
-        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvh * G + j) * HD;
-        float ss = 0.f;
-        for (int c = lane; c < HD; c += 64) ss = fmaf(qh[c], qh[c], ss);
-        ss = wave_sum(ss);
-        const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
-        for (int c = lane; c < HD; c += 64) qs[j][c] = qh[c] * r * a.g_q[c];
+#pragma unroll
+    for (int jj = 0; jj < GW; ++jj) {
+        const int j = wid + 4 * jj;
+        if (j < G) {                        // wave-uniform
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < QPL; ++i) ss = fmaf(qv[jj][i], qv[jj][i], ss);
+            ss = wave_sum(ss);
+            const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+            for (int i = 0; i < QPL; ++i)
+                if (lane + 64 * i < HD) qs[j][lane + 64 * i] = qv[jj][i] * r * gq[i];
+        }
     }
     __syncthreads();
     for (int i = tid; i < G * (HD / 2); i += kBlock) {
@@ -84,27 +129,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int e = 0; e < DPL; ++e) acc[j][e] = 0.f;
     }
 
-    const int pbeg = split * sp.split_len;
-    const int npos = min(sp.split_len, sp.n_vis - pbeg);
-    const KT *kbase = (const KT *)sp.k + (int64_t)kvh * HD + li * DPL;
-    const KT *vbase = (const KT *)sp.v + (int64_t)kvh * HD + li * DPL;
-
     for (int cb = 0; cb < npos; cb += 16 * T) {
-        uint4 kv[T][NVL], vv[T][NVL];
-        bool ok[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int pi = cb + t * 16 + gi;
-            ok[t] = pi < npos;
-            int cell = sp.c0 + pbeg + pi;
-            if (cell >= sp.n_cells) cell -= sp.n_cells;
-            const int64_t off = (int64_t)cell * sp.cell_stride;
-#pragma unroll
-            for (int v = 0; v < NVL; ++v) {
-                kv[t][v] = ok[t] ? *(const uint4 *)(kbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
-                vv[t][v] = ok[t] ? *(const uint4 *)(vbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
-            }
-        }
+        if (cb > 0) load_chunk(cb);
         float sc[T][G];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -232,31 +258,51 @@ hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream
     return hipErrorInvalidValue;
 }
 
-// log-sum-exp merge of the split partials: o = sum_j 2^(m_j - M) acc_j / sum_j 2^(m_j - M) l_j
+// Log-sum-exp merge of the split partials of one query head, online form:
+// (m, l, acc) <- (M, l*2^(m-M) + l_j*2^(m_j-M), acc*2^(m-M) + acc_j*2^(m_j-M)),
+// M = max(m, m_j).  Workgroup = (64-dim chunk, query head, sequence); 4 thread
+// slices take every 4th split with 8 splits' loads in flight per thread, then
+// the slices combine through LDS in a fixed order.
+__device__ __forceinline__ void lse_combine(float &m, float &l, float &acc, float mj, float lj, float aj) {
+    const float mn = fmaxf(m, mj);
+    if (mn == -INFINITY) return;
+    const float c0 = exp2f(m - mn), c1 = exp2f(mj - mn);
+    l = l * c0 + lj * c1;
+    acc = acc * c0 + aj * c1;
+    m = mn;
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    __shared__ float red_num[4][64], red_den[4][64];
+    __shared__ float sm[4][64], sl[4][64], sa[4][64];
     const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x, dl = tid & 63, slice = tid >> 6;
     const int hd = a.hd;
-    const int dim = chunk * 64 + dl;
+    const int dim = min(chunk * 64 + dl, hd - 1);
     const int ns = a.seqs[s].src[a.src].n_split;
     const float *base = a.part + ((int64_t)s * a.Hq + h) * MTP_MAX_SPLITS * (hd + 2);
-    float M = -INFINITY;
-    for (int j = 0; j < ns; ++j) M = fmaxf(M, base[(int64_t)j * (hd + 2)]);
-    float num = 0.f, den = 0.f;
-    for (int j = slice; j < ns; j += 4) {
-        const float *pj = base + (int64_t)j * (hd + 2);
-        const float w = (pj[0] == -INFINITY) ? 0.f : exp2f(pj[0] - M);
-        den = fmaf(w, pj[1], den);
-        if (dim < hd) num = fmaf(w, pj[2 + dim], num);
+    constexpr int U = 8;
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+    for (int j0 = slice; j0 < ns; j0 += 4 * U) {
+        float mj[U], lj[U], aj[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = j0 + 4 * u;
+            const float *pj = base + (int64_t)min(j, ns - 1) * (hd + 2);
+            mj[u] = (j < ns) ? pj[0] : -INFINITY;
+            lj[u] = pj[1];
+            aj[u] = pj[2 + dim];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) lse_combine(m, l, acc, mj[u], lj[u], aj[u]);
     }
-    red_num[slice][dl] = num;
-    red_den[slice][dl] = den;
+    sm[slice][dl] = m;
+    sl[slice][dl] = l;
+    sa[slice][dl] = acc;
     __syncthreads();
-    if (slice == 0 && dim < hd) {
-        const float n = (red_num[0][dl] + red_num[1][dl]) + (red_num[2][dl] + red_num[3][dl]);
-        const float dd = (red_den[0][dl] + red_den[1][dl]) + (red_den[2][dl] + red_den[3][dl]);
-        a.o[((int64_t)s * a.Hq + h) * hd + dim] = n / dd;
+    if (slice == 0 && chunk * 64 + dl < hd) {
+#pragma unroll
+        for (int k = 1; k < 4; ++k) lse_combine(m, l, acc, sm[k][dl], sl[k][dl], sa[k][dl]);
+        a.o[((int64_t)s * a.Hq + h) * hd + chunk * 64 + dl] = acc / l;
     }
 }
 

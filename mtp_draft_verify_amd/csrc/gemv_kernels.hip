@@ -10,46 +10,83 @@
 
 namespace mtp {
 
-template <int IN>
+// Column slice of lane `lane` in a row of K values: vectors v = 0..NV-1 of EPV
+// consecutive values starting at v*64*EPV + lane*EPV.  Every sum of squares
+// (RMSNorm) runs over these slices in this order and finishes with wave_sum,
+// whether the input sits in registers (one sequence) or in LDS (several), so
+// a sequence gets the same bits alone or in a batch.
+template <int NV, int EPV>
+__device__ __forceinline__ float slice_sumsq(const float *x, int K, int lane) {
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int col = v * 64 * EPV + lane * EPV;
+        if (col < K)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) ss = fmaf(x[col + e], x[col + e], ss);
+    }
+    return wave_sum(ss);
+}
+
+__device__ __forceinline__ float embed_value(const GemvArgs &a, int s, int c) {
+    const int d = a.d_embed;
+    if (c >= d) return a.h[(int64_t)s * a.dh + (c - d)];
+    const int32_t tok = a.tok_in ? a.tok_in[s] : key_index(a.key_in[s]);
+    float e;
+    if (tok < 0 || tok >= a.embed_rows) e = 0.f;   // ids outside the vocabulary embed to zero
+    else if (a.embed_dtype == MTP_F32) e = ((const float *)a.embed)[(int64_t)tok * d + c];
+    else if (a.embed_dtype == MTP_BF16) e = bf16_to_f(((const uint16_t *)a.embed)[(int64_t)tok * d + c]);
+    else e = half_to_f(a.embed_qs[(int64_t)tok * (d / 32) + c / 32]) * (float)a.embed_q[(int64_t)tok * d + c];
+    return a.embed_scale * e;
+}
+
+// The EPV input values of sequence s at columns [col, col + EPV), loaded with
+// 16-byte vectors (EPV is 4 or 8 and divides d_model, so a slice never
+// straddles the embedding / hidden-state boundary).
+template <int IN, int EPV>
+__device__ __forceinline__ void load_x_slice(const GemvArgs &a, int s, int col, float (&x)[EPV]) {
+    if (IN != IN_EMBED) {
+        const float4 *p = (const float4 *)(a.src + (int64_t)s * a.src_stride + col);
+#pragma unroll
+        for (int e4 = 0; e4 < EPV / 4; ++e4) {
+            const float4 v = p[e4];
+            x[4 * e4 + 0] = v.x; x[4 * e4 + 1] = v.y; x[4 * e4 + 2] = v.z; x[4 * e4 + 3] = v.w;
+        }
+        return;
+    }
+    const int d = a.d_embed;
+    if (col >= d) {
+        const float4 *p = (const float4 *)(a.h + (int64_t)s * a.dh + (col - d));
+#pragma unroll
+        for (int e4 = 0; e4 < EPV / 4; ++e4) {
+            const float4 v = p[e4];
+            x[4 * e4 + 0] = v.x; x[4 * e4 + 1] = v.y; x[4 * e4 + 2] = v.z; x[4 * e4 + 3] = v.w;
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) x[e] = embed_value(a, s, col + e);
+}
+
+// Stage the transformed inputs of sequences s0 .. s0+sg-1 into LDS (several
+// sequences per call).
+template <int IN, int NV, int EPV>
 __device__ void stage_input(const GemvArgs &a, float *xs, float *rs, int s0, int sg) {
-    const int K = a.K, tid = threadIdx.x;
+    const int K = a.K, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    for (int i = tid; i < sg * K; i += kBlock) {
+        const int j = i / K, c = i - j * K;
+        xs[i] = (IN == IN_EMBED) ? embed_value(a, s0 + j, c) : a.src[(int64_t)(s0 + j) * a.src_stride + c];
+    }
     if (IN == IN_NORM) {
-        // 1 / rms per sequence: wave w reduces sequences w, w+4, ... (fixed order)
-        const int lane = tid & 63, wid = tid >> 6;
+        __syncthreads();
         for (int j = wid; j < sg; j += 4) {
-            const float *x = a.src + (int64_t)(s0 + j) * a.src_stride;
-            float ss = 0.f;
-            for (int c = lane; c < K; c += 64) ss = fmaf(x[c], x[c], ss);
-            ss = wave_sum(ss);
+            const float ss = slice_sumsq<NV, EPV>(xs + j * K, K, lane);
             if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)K + a.eps);
         }
         __syncthreads();
         for (int i = tid; i < sg * K; i += kBlock) {
             const int j = i / K, c = i - j * K;
-            xs[i] = a.src[(int64_t)(s0 + j) * a.src_stride + c] * rs[j] * a.gain[c];
-        }
-    } else if (IN == IN_PLAIN) {
-        for (int i = tid; i < sg * K; i += kBlock) {
-            const int j = i / K, c = i - j * K;
-            xs[i] = a.src[(int64_t)(s0 + j) * a.src_stride + c];
-        }
-    } else {   // IN_EMBED: [embed_scale * E[tok]; h]
-        const int d = a.d_embed;
-        for (int i = tid; i < sg * K; i += kBlock) {
-            const int j = i / K, c = i - j * K, s = s0 + j;
-            float v;
-            if (c < d) {
-                const int32_t tok = a.tok_in ? a.tok_in[s] : key_index(a.key_in[s]);
-                float e;
-                if (tok < 0 || tok >= a.embed_rows) e = 0.f;   // ids outside the vocabulary embed to zero
-                else if (a.embed_dtype == MTP_F32) e = ((const float *)a.embed)[(int64_t)tok * d + c];
-                else if (a.embed_dtype == MTP_BF16) e = bf16_to_f(((const uint16_t *)a.embed)[(int64_t)tok * d + c]);
-                else e = half_to_f(a.embed_qs[(int64_t)tok * (d / 32) + c / 32]) * (float)a.embed_q[(int64_t)tok * d + c];
-                v = a.embed_scale * e;
-            } else {
-                v = a.h[(int64_t)s * a.dh + (c - d)];
-            }
-            xs[i] = v;
+            xs[i] = xs[i] * rs[j] * a.gain[c];
         }
     }
 }
@@ -62,8 +99,32 @@ __device__ __forceinline__ void gemv_store(const GemvArgs &a, int s, int r, floa
     else *dp = silu_f(y);
 }
 
+template <typename WT, int NV, int RU>
+__device__ __forceinline__ void load_rows(const GemvArgs &a, int rb, int row1, int lane, uint4 (&wv)[RU][NV]) {
+    constexpr int EPV = WTr<WT>::EPV, CPW = 64 * EPV;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int r = rb + 4 * u;
+        const uint4 *wr = (const uint4 *)((const WT *)a.W + (int64_t)r * a.K);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int col = v * CPW + lane * EPV;
+            wv[u][v] = (r < row1 && col < a.K) ? wr[col / EPV] : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+// One workgroup = 4 waves over rows [row0, row1); wave w takes rows
+// row0 + w, row0 + w + 4, ... two at a time.  The first rows' weights are
+// requested before the input is read, so the two latencies overlap.
 template <typename WT, int NV, int IN, int EPI, bool ONE>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a_in) {
+    GemvArgs a = a_in;
+    if (IN == IN_EMBED) {   // caller buffers of this call
+        a.tok_in = a.step == 0 ? a.io->last_tok : nullptr;
+        if (a.step == 0) a.h = a.io->h_prev;
+        a.drafts_out = a.step > 0 ? a.io->out_drafts : nullptr;
+    }
     constexpr int EPV = WTr<WT>::EPV;
     constexpr int CPW = 64 * EPV;
     constexpr int RU = 2;                  // rows in flight per wave
@@ -76,52 +137,101 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         if (a.drafts_out) a.drafts_out[(int64_t)tid * a.drafts_stride + a.drafts_col] = key_index(a.key_in[tid]);
         if (a.key_reset) a.key_reset[tid] = 0ull;
     }
-    const int Sg = ONE ? 1 : min(kMaxSeqGroup, max(1, kLdsFloats / K));
     const int row0 = blockIdx.x * a.rows_per_wg;
     const int row1 = min(M, row0 + a.rows_per_wg);
 
-    for (int s0 = 0; s0 < S; s0 += Sg) {
-        const int sg = min(Sg, S - s0);
-        __syncthreads();
-        stage_input<IN>(a, xs, rs, s0, sg);
-        __syncthreads();
-        float xr[ONE ? NV : 1][EPV];
-        if (ONE) {
+    if constexpr (ONE) {
+        // One sequence: the lane's input slice lives in registers, no LDS.
+        // Every load this wave needs (weights of its first rows, input slice,
+        // gains, residual) is issued before any arithmetic.
+        int rb = row0 + wid;
+        uint4 wv[RU][NV];
+        load_rows<WT, NV, RU>(a, rb, row1, lane, wv);
+        float xr[NV][EPV], gr[NV][EPV];
 #pragma unroll
-            for (int v = 0; v < (ONE ? NV : 1); ++v) {
-                const int col = v * CPW + lane * EPV;
+        for (int v = 0; v < NV; ++v) {
+            const int col = v * CPW + lane * EPV;
+            if (col < K) {
+                load_x_slice<IN, EPV>(a, 0, col, xr[v]);
+                if (IN == IN_NORM) {
+                    const float4 *gp = (const float4 *)(a.gain + col);
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) xr[v][e] = (col < K) ? xs[col + e] : 0.f;
+                    for (int e4 = 0; e4 < EPV / 4; ++e4) {
+                        const float4 g4 = gp[e4];
+                        gr[v][4 * e4 + 0] = g4.x; gr[v][4 * e4 + 1] = g4.y;
+                        gr[v][4 * e4 + 2] = g4.z; gr[v][4 * e4 + 3] = g4.w;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) xr[v][e] = gr[v][e] = 0.f;
             }
         }
-        for (int rb = row0 + wid; rb < row1; rb += 4 * RU) {
-            uint4 wv[RU][NV];
+        float res[RU];
 #pragma unroll
-            for (int u = 0; u < RU; ++u) {
-                const int r = rb + 4 * u;
-                const uint4 *wr = (const uint4 *)((const WT *)a.W + (int64_t)r * K);
+        for (int u = 0; u < RU; ++u)
+            res[u] = (EPI == EPI_ADD && lane == 0 && rb + 4 * u < row1) ? a.dst[rb + 4 * u] : 0.f;
+        if (IN == IN_NORM) {
+            float ss = 0.f;
 #pragma unroll
-                for (int v = 0; v < NV; ++v) {
-                    const int col = v * CPW + lane * EPV;
-                    wv[u][v] = (r < row1 && col < K) ? wr[col / EPV] : make_uint4(0, 0, 0, 0);
-                }
-            }
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) ss = fmaf(xr[v][e], xr[v][e], ss);
+            const float r = 1.0f / sqrtf(wave_sum(ss) / (float)K + a.eps);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) xr[v][e] = xr[v][e] * r * gr[v][e];
+        }
+        for (; rb < row1; rb += 4 * RU) {
+            uint4 wn[RU][NV];
+            if (rb + 4 * RU < row1) load_rows<WT, NV, RU>(a, rb + 4 * RU, row1, lane, wn);
 #pragma unroll
             for (int u = 0; u < RU; ++u) {
                 const int r = rb + 4 * u;
                 if (r >= row1) break;          // wave-uniform
-                float w[NV][EPV];
+                float acc = 0.f;
 #pragma unroll
-                for (int v = 0; v < NV; ++v) widen(wv[u][v], w[v]);
-                if (ONE) {
-                    float acc = 0.f;
+                for (int v = 0; v < NV; ++v) {
+                    float w[EPV];
+                    widen(wv[u][v], w);
 #pragma unroll
-                    for (int v = 0; v < NV; ++v)
+                    for (int e = 0; e < EPV; ++e) acc = fmaf(w[e], xr[v][e], acc);
+                }
+                const float y = wave_sum(acc);
+                if (lane == 0) {
+                    if (EPI == EPI_ADD) a.dst[r] = res[u] + y;
+                    else gemv_store<EPI>(a, 0, r, y);
+                }
+            }
 #pragma unroll
-                        for (int e = 0; e < EPV; ++e) acc = fmaf(w[v][e], xr[ONE ? v : 0][e], acc);
-                    const float y = wave_sum(acc);
-                    if (lane == 0) gemv_store<EPI>(a, s0, r, y);
-                } else {
+            for (int u = 0; u < RU; ++u) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) wv[u][v] = wn[u][v];
+                res[u] = (EPI == EPI_ADD && lane == 0 && rb + 4 * RU + 4 * u < row1) ? a.dst[rb + 4 * RU + 4 * u] : 0.f;
+            }
+        }
+        return;
+    } else {
+        const int Sg = min(kMaxSeqGroup, max(1, kLdsFloats / K));
+        for (int s0 = 0; s0 < S; s0 += Sg) {
+            const int sg = min(Sg, S - s0);
+            int rb = row0 + wid;
+            uint4 wv[RU][NV];
+            load_rows<WT, NV, RU>(a, rb, row1, lane, wv);
+            __syncthreads();
+            stage_input<IN, NV, EPV>(a, xs, rs, s0, sg);
+            __syncthreads();
+            for (; rb < row1; rb += 4 * RU) {
+                uint4 wn[RU][NV];
+                if (rb + 4 * RU < row1) load_rows<WT, NV, RU>(a, rb + 4 * RU, row1, lane, wn);
+#pragma unroll
+                for (int u = 0; u < RU; ++u) {
+                    const int r = rb + 4 * u;
+                    if (r >= row1) break;          // wave-uniform
+                    float w[NV][EPV];
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) widen(wv[u][v], w[v]);
                     for (int j = 0; j < sg; ++j) {
                         float acc = 0.f;
 #pragma unroll
@@ -143,6 +253,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
                         if (lane == 0) gemv_store<EPI>(a, s0 + j, r, y);
                     }
                 }
+#pragma unroll
+                for (int u = 0; u < RU; ++u)
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) wv[u][v] = wn[u][v];
             }
         }
     }

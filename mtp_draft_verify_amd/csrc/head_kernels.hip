@@ -12,7 +12,7 @@
 namespace mtp {
 
 template <typename WT>
-__device__ void post_rows(const HeadArgs &a, const float *fs) {
+__device__ void post_rows(const HeadArgs &a, const float *fs, float *h_out) {
     constexpr int EPV = WTr<WT>::EPV, CPW = 64 * EPV;
     const int d = a.d, S = a.S;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -36,7 +36,7 @@ __device__ void post_rows(const HeadArgs &a, const float *fs) {
                 }
             }
             const float y = wave_sum(acc);
-            if (lane == 0) a.h_out[(int64_t)s * a.dh + r] = y;
+            if (lane == 0) h_out[(int64_t)s * a.dh + r] = y;
         }
     }
 }
@@ -50,6 +50,33 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
     __shared__ uint64_t wbest[4][kMaxSeqGroup];
     const int d = a.d, S = a.S;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int r0 = blockIdx.x * a.rows_per_wg;
+    const int r1 = min(a.V, r0 + a.rows_per_wg);
+    const int nblk = d / 32;
+    uint4 wv[RU][NV];
+    float sc[RU][NV];
+    auto load_head_rows = [&](int rb) {
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int r = rb + u;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int col = v * CPW + lane * EPV;
+                const bool ok = (r < r1) && (col < d);
+                if constexpr (sizeof(HT) == 1) {
+                    wv[u][v] = ok ? ld_nt((const uint4 *)(a.head_q + (int64_t)r * d + col)) : make_uint4(0, 0, 0, 0);
+                    sc[u][v] = ok ? half_to_f(a.head_qs[(int64_t)r * nblk + col / 32]) : 0.f;
+                } else {
+                    wv[u][v] = ok ? ld_nt((const uint4 *)((const HT *)a.head + (int64_t)r * d + col))
+                                  : make_uint4(0, 0, 0, 0);
+                    sc[u][v] = 1.f;
+                }
+            }
+        }
+    };
+    // the first rows' weights do not depend on x: request them before the prologue
+    const bool head_wg = (int)blockIdx.x < a.n_head_wg;
+    if (head_wg) load_head_rows(r0 + wid * RU);
 
     // f = rmsnorm(x; g_final)
     for (int j = wid; j < S; j += 4) {
@@ -68,10 +95,13 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
     __syncthreads();
 
     if ((int)blockIdx.x >= a.n_head_wg) {
-        if (w_dtype == MTP_BF16) post_rows<uint16_t>(a, fs);
-        else post_rows<float>(a, fs);
+        float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
+        if (w_dtype == MTP_BF16) post_rows<uint16_t>(a, fs, h_out);
+        else post_rows<float>(a, fs, h_out);
         return;
     }
+    float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : nullptr;
+    const int64_t logits_stride = (int64_t)a.n_steps * a.V;
 
     float fr[ONE ? NV : 1][EPV];
     if (ONE) {
@@ -83,29 +113,8 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
         }
     }
     uint64_t best1 = 0ull;                  // one-sequence path keeps its best in a register
-    const int r0 = blockIdx.x * a.rows_per_wg;
-    const int r1 = min(a.V, r0 + a.rows_per_wg);
-    const int nblk = d / 32;
     for (int rb = r0 + wid * RU; rb < r1; rb += 4 * RU) {
-        uint4 wv[RU][NV];
-        float sc[RU][NV];
-#pragma unroll
-        for (int u = 0; u < RU; ++u) {
-            const int r = rb + u;
-#pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int col = v * CPW + lane * EPV;
-                const bool ok = (r < r1) && (col < d);
-                if constexpr (sizeof(HT) == 1) {
-                    wv[u][v] = ok ? ld_nt((const uint4 *)(a.head_q + (int64_t)r * d + col)) : make_uint4(0, 0, 0, 0);
-                    sc[u][v] = ok ? half_to_f(a.head_qs[(int64_t)r * nblk + col / 32]) : 0.f;
-                } else {
-                    wv[u][v] = ok ? ld_nt((const uint4 *)((const HT *)a.head + (int64_t)r * d + col))
-                                  : make_uint4(0, 0, 0, 0);
-                    sc[u][v] = 1.f;
-                }
-            }
-        }
+        if (rb != r0 + wid * RU) load_head_rows(rb);
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
             const int r = rb + u;
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
                     acc = fmaf(part, sc[u][v], acc);
                 }
                 const float z = wave_sum(acc);
-                if (a.logits && lane == 0) a.logits[(int64_t)j * a.logits_stride + r] = z;
+                if (logits && lane == 0) logits[(int64_t)j * logits_stride + r] = z;
                 const uint64_t k = argmax_key(z, (uint32_t)r);
                 if (ONE) {
                     best1 = k > best1 ? k : best1;

@@ -7,14 +7,14 @@ namespace mtp {
 // ----------------------------------------------------------------------------
 // small helpers
 // ----------------------------------------------------------------------------
-__global__ void finish_drafts_kernel(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col) {
+__global__ void finish_drafts_kernel(const uint64_t *keys, int32_t S, const CallIO *io, int32_t stride, int32_t col) {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s < S) drafts[(int64_t)s * stride + col] = key_index(keys[s]);
+    if (s < S) io->out_drafts[(int64_t)s * stride + col] = key_index(keys[s]);
 }
 
-hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col,
+hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *io, int32_t stride, int32_t col,
                                 hipStream_t st) {
-    hipLaunchKernelGGL(finish_drafts_kernel, dim3((S + 63) / 64), dim3(64), 0, st, keys, S, drafts, stride, col);
+    hipLaunchKernelGGL(finish_drafts_kernel, dim3((S + 63) / 64), dim3(64), 0, st, keys, S, io, stride, col);
     return hipGetLastError();
 }
 
@@ -48,6 +48,17 @@ __global__ void clear_u64_kernel(uint64_t *p, int64_t n) {
 
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st) {
     hipLaunchKernelGGL(clear_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+// RoPE frequencies theta^(-2i/hd), i < hd/2, in fp64 (once per context)
+__global__ void rope_init_kernel(double *inv_freq, int32_t hd, double theta) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < hd / 2) inv_freq[i] = pow(theta, -2.0 * (double)i / (double)hd);
+}
+
+hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st) {
+    hipLaunchKernelGGL(rope_init_kernel, dim3((hd / 2 + 63) / 64), dim3(64), 0, st, inv_freq, hd, (double)theta);
     return hipGetLastError();
 }
 

@@ -58,13 +58,22 @@ struct mtp_ctx {
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
     uint64_t *dkeys = nullptr;          // [2][max_seqs]
+    double *inv_freq = nullptr;         // [head_dim / 2] RoPE frequencies
     int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
     uint16_t *head_qs = nullptr;        //   and fp16 scale plane
-    SeqParams *d_params = nullptr;      // [kParamSlots][max_seqs]
-    SeqParams *h_params = nullptr;      // pinned, same shape
+    // per-call parameter block: CallIO then SeqParams[max_seqs], at one fixed
+    // device address; staged through a ring of pinned host slots
+    uint8_t *d_block = nullptr;
+    uint8_t *h_block = nullptr;         // [kParamSlots][block_bytes], pinned
+    size_t block_bytes = 0;
     hipEvent_t ev[kParamSlots]{};
     bool ev_pending[kParamSlots]{};
     int slot = 0;
+    // captured draft chains, one per launch shape
+    hipStream_t cap_stream = nullptr;
+    struct Graph { int key[4]; hipGraph_t g; hipGraphExec_t exec; };
+    std::vector<Graph> graphs;
+    bool graph_failed = false;          // capture unsupported: launch directly
     // optional event timing per kernel class
     int prof_mask = 0;
     std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pool;
@@ -136,11 +145,16 @@ static int check_weights(const mtp_model_desc *d, const mtp_weights *w) {
 
 static void free_ctx(mtp_ctx *c) {
     if (!c) return;
-    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->dkeys, c->head_q, c->head_qs, c->d_params,
+    for (auto &g : c->graphs) {
+        (void)hipGraphExecDestroy(g.exec);
+        (void)hipGraphDestroy(g.g);
+    }
+    if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
                     c->vkeys, c->s_rowmax, c->s_cand_n, c->s_cand_id, c->s_cand_z};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
-    if (c->h_params) (void)hipHostFree(c->h_params);
+    if (c->h_block) (void)hipHostFree(c->h_block);
     for (int i = 0; i < kParamSlots; ++i)
         if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
     for (int k = 0; k < MTP_PROF_N; ++k)
@@ -184,18 +198,25 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
-             dalloc(&c->dkeys, 2 * S) && dalloc(&c->d_params, kParamSlots * S);
+             dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2);
+        c->block_bytes = sizeof(CallIO) + sizeof(SeqParams) * S;
+        ok = ok && dalloc(&c->d_block, c->block_bytes);
         if (ok && d.head_dtype == MTP_Q8_0)
             ok = dalloc(&c->head_q, (size_t)d.n_vocab * d.d_model) &&
                  dalloc(&c->head_qs, (size_t)d.n_vocab * (d.d_model / 32));
-        if (ok) ok = hipHostMalloc((void **)&c->h_params, sizeof(SeqParams) * kParamSlots * S) == hipSuccess;
+        if (ok) ok = hipHostMalloc((void **)&c->h_block, c->block_bytes * kParamSlots) == hipSuccess;
+        if (ok) ok = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) == hipSuccess;
         for (int i = 0; ok && i < kParamSlots; ++i)
             ok = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) == hipSuccess;
     }
     if (!ok) { free_ctx(c); return MTP_E_NOMEM; }
     if (hipMemset(c->vkeys, 0, sizeof(uint64_t) * S * R) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
     if (c->has_weights) {
-        if (hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+        if (hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S) != hipSuccess ||
+            launch_rope_init(c->inv_freq, d.head_dim, d.rope_theta, c->stream) != hipSuccess) {
+            free_ctx(c);
+            return MTP_E_DEVICE;
+        }
         if (d.head_dtype == MTP_Q8_0 &&
             launch_q8_repack((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_q, c->head_qs, c->stream) !=
                 hipSuccess) {
@@ -304,54 +325,30 @@ static int gemv_rows_per_wg(int M) {
     return std::max(4, r);
 }
 
-static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a) {
+static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStream_t st) {
     ProfScope ps(c, MTP_PROF_GEMV);
     a.rows_per_wg = gemv_rows_per_wg(a.M);
     const int n_wg = (a.M + a.rows_per_wg - 1) / a.rows_per_wg;
-    return launch_gemv(c->desc.w_dtype, in_mode, epi, a, n_wg, c->stream);
+    return launch_gemv(c->desc.w_dtype, in_mode, epi, a, n_wg, st);
 }
 
-extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
-                               const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
-                               float *out_logits) {
-    if (!c) return MTP_E_INVAL;
-    if (!c->has_weights) return MTP_E_NOWEIGHTS;
+// Launch shape of one draft call: everything the kernel sequence depends on
+// besides the parameter block.
+struct ChainShape {
+    int S, N, split[2];
+};
+
+// Enqueue the whole draft chain (N steps of a1..a7, then the hand-off of the
+// last draft ids) on `st`.  Every argument is a context-owned or weight
+// address, so the same sequence can be captured once and replayed.
+static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st) {
     const mtp_model_desc &d = c->desc;
-    if (n_seq < 1 || n_seq > d.max_seqs || n_steps < 1 || n_steps > d.max_steps) return MTP_E_SHAPE;
-    if (!seqs || !last_tok || !h_prev || !out_drafts) return MTP_E_INVAL;
-    bool use_src[2] = {false, false};
-    for (int l = 0; l < d.n_blocks; ++l) use_src[d.block_src[l]] = true;
-
-    // per-call geometry into the next pinned slot
-    const int slot = c->slot;
-    if (c->ev_pending[slot] && hipEventSynchronize(c->ev[slot]) != hipSuccess) return MTP_E_DEVICE;
-    c->ev_pending[slot] = false;
-    SeqParams *hp = c->h_params + (size_t)slot * d.max_seqs;
-    int max_split[2] = {0, 0};
-    for (int s = 0; s < n_seq; ++s) {
-        const mtp_seq &sq = seqs[s];
-        SeqParams &p = hp[s];
-        std::memset(&p, 0, sizeof(p));
-        if (sq.attn_pos < 0 || sq.pos0 < 0 || (int64_t)sq.pos0 + n_steps > 0x7FFFFFFF) return MTP_E_INVAL;
-        p.pos0 = sq.pos0;
-        for (int src = 0; src < 2; ++src) {
-            if (!use_src[src]) continue;
-            int rc = src_geometry(d, sq, src, p.src[src]);
-            if (rc) return rc;
-            max_split[src] = std::max(max_split[src], p.src[src].n_split);
-        }
-    }
-    SeqParams *dp = c->d_params + (size_t)slot * d.max_seqs;
-    if (hipMemcpyAsync(dp, hp, sizeof(SeqParams) * n_seq, hipMemcpyHostToDevice, c->stream) != hipSuccess)
-        return MTP_E_DEVICE;
-    if (hipEventRecord(c->ev[slot], c->stream) != hipSuccess) return MTP_E_DEVICE;
-    c->ev_pending[slot] = true;
-    c->slot = (slot + 1) % kParamSlots;
-
     const int D = d.d_model, DH = d.d_hprev, QD = d.n_head_q * d.head_dim, F = d.d_ff, V = d.n_vocab;
-    const int S = n_seq;
+    const int S = sh.S, N = sh.N;
+    const CallIO *io = (const CallIO *)c->d_block;
+    const SeqParams *dp = (const SeqParams *)(c->d_block + sizeof(CallIO));
     hipError_t e = hipSuccess;
-    for (int k = 0; k < n_steps && e == hipSuccess; ++k) {
+    for (int k = 0; k < N && e == hipSuccess; ++k) {
         uint64_t *key_cur = c->dkeys + (size_t)(k & 1) * d.max_seqs;
         uint64_t *key_prev = c->dkeys + (size_t)((k + 1) & 1) * d.max_seqs;
         // a1: x = W_pre [embed_scale * E[tok]; h]
@@ -359,36 +356,37 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
         ga.W = c->w.w_pre; ga.M = D; ga.K = D + DH; ga.S = S;
         ga.embed = c->w.head; ga.embed_dtype = d.head_dtype; ga.d_embed = D; ga.embed_rows = V;
         ga.embed_q = c->head_q; ga.embed_qs = c->head_qs; ga.embed_scale = d.embed_scale;
-        ga.tok_in = k == 0 ? last_tok : nullptr;
+        ga.io = io; ga.step = k;
         ga.key_in = key_prev;
-        ga.h = k == 0 ? h_prev : c->h; ga.dh = DH;
+        ga.h = c->h; ga.dh = DH;
         ga.key_reset = key_cur;
-        ga.drafts_out = k > 0 ? out_drafts : nullptr; ga.drafts_stride = n_steps; ga.drafts_col = k - 1;
+        ga.drafts_stride = N; ga.drafts_col = k - 1;
         ga.dst = c->x; ga.dst_stride = D;
-        e = run_gemv(c, IN_EMBED, EPI_STORE, ga);
+        e = run_gemv(c, IN_EMBED, EPI_STORE, ga, st);
         for (int l = 0; l < d.n_blocks && e == hipSuccess; ++l) {
             // a2: q = W_q rmsnorm(x)
             GemvArgs gq{};
             gq.W = c->w.w_q[l]; gq.M = QD; gq.K = D; gq.S = S;
             gq.src = c->x; gq.src_stride = D; gq.gain = c->w.g_attn[l]; gq.eps = d.rms_eps;
             gq.dst = c->q; gq.dst_stride = QD;
-            e = run_gemv(c, IN_NORM, EPI_STORE, gq);
+            e = run_gemv(c, IN_NORM, EPI_STORE, gq, st);
             // a3: split-K attention + merge
             const int src = d.block_src[l];
             {
                 ProfScope ps_attn(c, MTP_PROF_ATTN);
                 if (e == hipSuccess) {
                     AttnArgs aa{};
-                    aa.q = c->q; aa.g_q = c->w.g_q[l]; aa.eps = d.rms_eps; aa.theta = d.rope_theta;
+                    aa.q = c->q; aa.g_q = c->w.g_q[l]; aa.inv_freq = c->inv_freq; aa.eps = d.rms_eps;
+                    aa.theta = d.rope_theta;
                     aa.scale = d.attn_scale; aa.Hq = d.n_head_q; aa.Hkv = d.n_head_kv; aa.hd = d.head_dim;
                     aa.S = S; aa.src = src; aa.step = k; aa.seqs = dp; aa.part = c->part;
-                    e = launch_attn(d.kv_dtype, aa, max_split[src], c->stream);
+                    e = launch_attn(d.kv_dtype, aa, sh.split[src], st);
                 }
                 if (e == hipSuccess) {
                     MergeArgs ma{};
                     ma.part = c->part; ma.o = c->o; ma.Hq = d.n_head_q; ma.Hkv = d.n_head_kv;
                     ma.hd = d.head_dim; ma.S = S; ma.src = src; ma.seqs = dp;
-                    e = launch_merge(ma, c->stream);
+                    e = launch_merge(ma, st);
                 }
             }
             // a4: x += W_o o
@@ -396,7 +394,7 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
                 GemvArgs go{};
                 go.W = c->w.w_o[l]; go.M = D; go.K = QD; go.S = S;
                 go.src = c->o; go.src_stride = QD; go.dst = c->x; go.dst_stride = D;
-                e = run_gemv(c, IN_PLAIN, EPI_ADD, go);
+                e = run_gemv(c, IN_PLAIN, EPI_ADD, go, st);
             }
             // a5: u = silu(W_up rmsnorm(x)); x += W_down u
             if (e == hipSuccess) {
@@ -404,13 +402,13 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
                 gu.W = c->w.w_up[l]; gu.M = F; gu.K = D; gu.S = S;
                 gu.src = c->x; gu.src_stride = D; gu.gain = c->w.g_mlp[l]; gu.eps = d.rms_eps;
                 gu.dst = c->u; gu.dst_stride = F;
-                e = run_gemv(c, IN_NORM, EPI_SILU, gu);
+                e = run_gemv(c, IN_NORM, EPI_SILU, gu, st);
             }
             if (e == hipSuccess) {
                 GemvArgs gd{};
                 gd.W = c->w.w_down[l]; gd.M = D; gd.K = F; gd.S = S;
                 gd.src = c->u; gd.src_stride = F; gd.dst = c->x; gd.dst_stride = D;
-                e = run_gemv(c, IN_PLAIN, EPI_ADD, gd);
+                e = run_gemv(c, IN_PLAIN, EPI_ADD, gd, st);
             }
         }
         // a6 + a7: final norm, LM head + argmax, post-projection
@@ -424,19 +422,115 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
             ha.rows_per_wg = rpw;
             ha.n_head_wg = (V + rpw - 1) / rpw;
             ha.keys = key_cur;
-            ha.logits = out_logits ? out_logits + (size_t)k * V : nullptr;
-            ha.logits_stride = (int64_t)n_steps * V;
+            ha.io = io; ha.step = k; ha.n_steps = N;
             ha.w_post = c->w.w_post; ha.dh = DH;
             ha.post_rows_per_wg = 4;
-            ha.h_out = (k == n_steps - 1 && out_h_last) ? out_h_last : c->h;
+            ha.h_out = c->h;
             const int n_post_wg = (DH + ha.post_rows_per_wg - 1) / ha.post_rows_per_wg;
             ProfScope ps(c, MTP_PROF_HEAD);
-            e = launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, c->stream);
+            e = launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
         }
     }
     if (e == hipSuccess)
-        e = launch_finish_drafts(c->dkeys + (size_t)((n_steps - 1) & 1) * d.max_seqs, S, out_drafts, n_steps,
-                                 n_steps - 1, c->stream);
+        e = launch_finish_drafts(c->dkeys + (size_t)((N - 1) & 1) * d.max_seqs, S, io, N, N - 1, st);
+    return e;
+}
+
+// The captured chain for a launch shape (built on first use).
+static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
+    const int key[4] = {sh.S, sh.N, sh.split[0], sh.split[1]};
+    for (auto &g : c->graphs)
+        if (std::memcmp(g.key, key, sizeof(key)) == 0) return g.exec;
+    if (c->graph_failed) return nullptr;
+    if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeRelaxed) != hipSuccess) {
+        c->graph_failed = true;
+        return nullptr;
+    }
+    const hipError_t e = enqueue_chain(c, sh, c->cap_stream);
+    hipGraph_t g = nullptr;
+    const hipError_t e2 = hipStreamEndCapture(c->cap_stream, &g);
+    if (e != hipSuccess || e2 != hipSuccess || !g) {
+        if (g) (void)hipGraphDestroy(g);
+        (void)hipGetLastError();
+        c->graph_failed = true;
+        return nullptr;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess) {
+        (void)hipGraphDestroy(g);
+        (void)hipGetLastError();
+        c->graph_failed = true;
+        return nullptr;
+    }
+    if (c->graphs.size() >= 16) {       // keep the cache bounded
+        (void)hipGraphExecDestroy(c->graphs.front().exec);
+        (void)hipGraphDestroy(c->graphs.front().g);
+        c->graphs.erase(c->graphs.begin());
+    }
+    mtp_ctx::Graph ent;
+    std::memcpy(ent.key, key, sizeof(key));
+    ent.g = g;
+    ent.exec = exec;
+    c->graphs.push_back(ent);
+    return exec;
+}
+
+extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
+                               const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
+                               float *out_logits) {
+    if (!c) return MTP_E_INVAL;
+    if (!c->has_weights) return MTP_E_NOWEIGHTS;
+    const mtp_model_desc &d = c->desc;
+    if (n_seq < 1 || n_seq > d.max_seqs || n_steps < 1 || n_steps > d.max_steps) return MTP_E_SHAPE;
+    if (!seqs || !last_tok || !h_prev || !out_drafts) return MTP_E_INVAL;
+    if (!aligned16(h_prev)) return MTP_E_INVAL;
+    bool use_src[2] = {false, false};
+    for (int l = 0; l < d.n_blocks; ++l) use_src[d.block_src[l]] = true;
+
+    // per-call parameter block into the next pinned slot
+    const int slot = c->slot;
+    if (c->ev_pending[slot] && hipEventSynchronize(c->ev[slot]) != hipSuccess) return MTP_E_DEVICE;
+    c->ev_pending[slot] = false;
+    uint8_t *hb = c->h_block + (size_t)slot * c->block_bytes;
+    CallIO *hio = (CallIO *)hb;
+    SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
+    std::memset(hio, 0, sizeof(CallIO));
+    ChainShape sh{n_seq, n_steps, {0, 0}};
+    for (int s = 0; s < n_seq; ++s) {
+        const mtp_seq &sq = seqs[s];
+        SeqParams &p = hp[s];
+        std::memset(&p, 0, sizeof(p));
+        if (sq.attn_pos < 0 || sq.pos0 < 0 || (int64_t)sq.pos0 + n_steps > 0x7FFFFFFF) return MTP_E_INVAL;
+        p.pos0 = sq.pos0;
+        for (int src = 0; src < 2; ++src) {
+            if (!use_src[src]) continue;
+            int rc = src_geometry(d, sq, src, p.src[src]);
+            if (rc) return rc;
+            sh.split[src] = std::max(sh.split[src], p.src[src].n_split);
+        }
+    }
+    // grids are sized for a power-of-two split count so one captured chain
+    // serves a range of context lengths (surplus workgroups exit at once)
+    for (int src = 0; src < 2; ++src)
+        if (sh.split[src]) sh.split[src] = (int)std::min<int64_t>(MTP_MAX_SPLITS, pow2ceil(sh.split[src]));
+    hio->last_tok = last_tok;
+    hio->h_prev = h_prev;
+    hio->out_drafts = out_drafts;
+    hio->out_h_last = out_h_last;
+    hio->out_logits = out_logits;
+    const size_t bytes = sizeof(CallIO) + sizeof(SeqParams) * n_seq;
+    if (hipMemcpyAsync(c->d_block, hb, bytes, hipMemcpyHostToDevice, c->stream) != hipSuccess) return MTP_E_DEVICE;
+    if (hipEventRecord(c->ev[slot], c->stream) != hipSuccess) return MTP_E_DEVICE;
+    c->ev_pending[slot] = true;
+    c->slot = (slot + 1) % kParamSlots;
+
+    hipError_t e;
+    if (c->prof_mask) {
+        e = enqueue_chain(c, sh, c->stream);        // event timing needs individual launches
+    } else {
+        hipGraphExec_t exec = chain_graph(c, sh);
+        e = exec ? hipGraphLaunch(exec, c->stream) : enqueue_chain(c, sh, c->stream);
+    }
     return e == hipSuccess ? MTP_OK : MTP_E_DEVICE;
 }
 

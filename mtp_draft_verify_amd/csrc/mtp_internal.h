@@ -28,6 +28,18 @@ struct SeqParams {
     int32_t pad[3];
 };
 
+// Caller buffers of one draft call.  They sit in device memory at a fixed
+// address (followed by the SeqParams array), so the kernels of a captured
+// chain never change: each call only rewrites this block.
+struct CallIO {
+    const int32_t *last_tok;
+    const float *h_prev;
+    int32_t *out_drafts;
+    float *out_h_last;
+    float *out_logits;
+    int64_t pad[3];
+};
+
 // Input transforms applied while a GEMV stages its input vector.
 enum GemvIn : int { IN_PLAIN = 0, IN_NORM = 1, IN_EMBED = 2 };
 // Output transforms.
@@ -48,12 +60,14 @@ struct GemvArgs {
     const int8_t *embed_q;  // Q8_0 plane [V, d]
     const uint16_t *embed_qs;   // Q8_0 scales [V, d/32]
     float embed_scale;
-    const int32_t *tok_in;  // step 0: caller's last_tok
+    const CallIO *io;       // caller buffers (IN_EMBED)
+    int32_t step;           // draft step: 0 reads io->last_tok / io->h_prev
+    const int32_t *tok_in;  // resolved in the kernel from io / step
     const uint64_t *key_in; // later steps: argmax keys of the previous step
-    const float *h;         // [S, dh]
+    const float *h;         // [S, dh] hidden state of later steps
     int32_t dh;
     uint64_t *key_reset;    // keys to clear for this step's head
-    int32_t *drafts_out;    // write drafts[s, step-1] (nullptr: none)
+    int32_t *drafts_out;    // resolved in the kernel: io->out_drafts for step > 0
     int32_t drafts_stride, drafts_col;
     // output
     float *dst;             // [S, dst_stride]
@@ -72,17 +86,18 @@ struct HeadArgs {
     const uint16_t *head_qs;    // Q8_0 scales [V, d/32]
     int32_t rows_per_wg, n_head_wg;
     uint64_t *keys;         // [S] argmax keys (cleared before)
-    float *logits;          // [S, logits_stride] at this step's offset, or nullptr
-    int64_t logits_stride;
+    const CallIO *io;       // io->out_logits (nullable), io->out_h_last (nullable)
+    int32_t step, n_steps;  // logits land at out_logits[s, step, :]
     // post-projection: h = W_post f
     const void *w_post;     // [dh, d] (w dtype)
     int32_t dh, post_rows_per_wg;
-    float *h_out;           // [S, dh]
+    float *h_out;           // [S, dh] context buffer (the last step writes io->out_h_last when given)
 };
 
 struct AttnArgs {
     const float *q;         // [S, Hq*hd] raw projections
     const float *g_q;       // [hd]
+    const double *inv_freq; // [hd/2] RoPE frequencies theta^(-2i/hd)
     float eps, theta, scale;
     int32_t Hq, Hkv, hd, S, src, step;
     const SeqParams *seqs;
@@ -101,11 +116,12 @@ hipError_t launch_gemv(int w_dtype, int in_mode, int epi, const GemvArgs &a, int
 hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, hipStream_t st);
 hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
-hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, int32_t *drafts, int32_t stride, int32_t col,
+hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *io, int32_t stride, int32_t col,
                                 hipStream_t st);
 hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
                             hipStream_t st);
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
+hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st);
 
 // verify
 hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,

@@ -144,3 +144,30 @@ def test_repeated_calls_are_deterministic():
     b = g.run(w.draft)
     for k in a:
         assert np.array_equal(a[k], b[k])
+
+
+def test_captured_chain_replays_match_direct_launches():
+    """The chain captured once per launch shape and replayed with new
+    per-call parameters (other context lengths in the same split bucket,
+    other tokens and hidden states) gives the same bits as individually
+    launched kernels (a stale-parameter replay would not)."""
+    import mtp_draft_verify_amd as mtp
+    log("case graph replay == direct launches")
+    w = syn.c3_interleaved(ctx_range=(2100, 2600), full_cap=3000, n_seq=3)
+    g = GpuDrafter(w.model, 3, 3)
+    outs = []
+    for shift in (0, 7, 19):
+        for s in w.draft.seqs:
+            s.attn_pos += shift
+            s.pos0 += shift
+        g.ctx.profile(0)
+        replay = g.run(w.draft, last_tok=(w.draft.last_tok + shift) % w.model.n_vocab,
+                       h_prev=w.draft.h_prev * (1 + 0.1 * shift))
+        g.ctx.profile(1 << mtp.MTP_PROF_GEMV)     # event timing forces individual launches
+        direct = g.run(w.draft, last_tok=(w.draft.last_tok + shift) % w.model.n_vocab,
+                       h_prev=w.draft.h_prev * (1 + 0.1 * shift))
+        g.ctx.profile(0)
+        for k in replay:
+            assert np.array_equal(replay[k], direct[k]), (shift, k)
+        outs.append(replay["drafts"])
+    assert not all(np.array_equal(outs[0], o) for o in outs[1:])
