@@ -208,6 +208,10 @@ int mtp_profile_read(mtp_ctx *ctx, int cls, double *total_ms, int64_t *count);
 /* Static string for a status code. */
 const char *mtp_strerror(int code);
 
+/* Text of the last HIP failure seen by this thread (the HIP call and its
+   error string), or "" if none. */
+const char *mtp_last_error(void);
+
 /* Host-only validation of a drafter description (no device calls); the same
    checks mtp_ctx_create runs first. */
 int mtp_check_desc(const mtp_model_desc *desc);

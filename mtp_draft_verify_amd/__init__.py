@@ -25,14 +25,15 @@ MTP_SRC_FULL, MTP_SRC_SWA = 0, 1
 MAX_BLOCKS = 8
 MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_verify_greedy", "mtp_verify_sample",
-           "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read")
+           "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read", "mtp_last_error")
 MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY = 0, 1, 2, 3
 
 
 class MTPError(RuntimeError):
     def __init__(self, code: int, where: str):
         self.code = code
-        super().__init__(f"{where}: {mtp_strerror(code)} ({code})")
+        detail = mtp_last_error() if code == MTP_E_DEVICE or code == MTP_E_NOMEM else ""
+        super().__init__(f"{where}: {mtp_strerror(code)} ({code})" + (f" [{detail}]" if detail else ""))
 
 
 class ModelDesc(C.Structure):
@@ -72,6 +73,11 @@ def lib() -> C.CDLL:
         if not LIB_PATH.exists():
             raise RuntimeError(f"{LIB_PATH} is missing: build it with mtp_draft_verify_amd/build.py "
                                "(or __graft_entry__.build()); there is no fallback path")
+        # torch first: libmtp.so then binds to the HIP runtime torch already
+        # loaded (same soname), so device pointers and streams from torch and
+        # the library's kernels live in one runtime.  Loading the library
+        # first would bring a second HIP/HSA runtime into the process.
+        import torch  # noqa: F401
         L = C.CDLL(str(LIB_PATH))
         P = C.c_void_p
         L.mtp_ctx_create.argtypes = [C.POINTER(ModelDesc), C.POINTER(Weights), P, C.POINTER(P)]
@@ -87,6 +93,8 @@ def lib() -> C.CDLL:
         L.mtp_verify_sample.restype = C.c_int
         L.mtp_strerror.argtypes = [C.c_int]
         L.mtp_strerror.restype = C.c_char_p
+        L.mtp_last_error.argtypes = []
+        L.mtp_last_error.restype = C.c_char_p
         L.mtp_check_desc.argtypes = [C.POINTER(ModelDesc)]
         L.mtp_check_desc.restype = C.c_int
         L.mtp_profile_enable.argtypes = [P, C.c_int]
@@ -117,6 +125,10 @@ def _stream_handle(stream) -> Optional[int]:
 # --------------------------------------------------------------------------- C names
 def mtp_strerror(code: int) -> str:
     return lib().mtp_strerror(code).decode()
+
+
+def mtp_last_error() -> str:
+    return lib().mtp_last_error().decode()
 
 
 def mtp_check_desc(desc: ModelDesc) -> int:

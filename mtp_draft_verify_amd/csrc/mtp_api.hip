@@ -23,6 +23,15 @@ namespace {
 
 constexpr int kParamSlots = 8;
 
+thread_local char g_last_error[256] = "";
+
+// Record a failing HIP call (readable through mtp_last_error) and map it to
+// MTP_E_DEVICE.
+int hip_fail(const char *what, hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+    return MTP_E_DEVICE;
+}
+
 int elem_size(int dt) { return dt == MTP_F32 ? 4 : 2; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
@@ -80,10 +89,16 @@ struct mtp_ctx {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pending[MTP_PROF_N];
     // verify scratch
     uint64_t *vkeys = nullptr;          // [max_seqs][max_steps + 1]
-    float *s_rowmax = nullptr;
+    // temperature>0 verify scratch, per row (target rows then draft rows)
+    int32_t s_cap = 0;                  // candidate slots per row
+    uint32_t *s_maxkey = nullptr;
+    uint64_t *s_topk = nullptr;
     int32_t *s_cand_n = nullptr, *s_cand_id = nullptr;
-    float *s_cand_z = nullptr;
+    float *s_cand_v = nullptr;
+    void *s_state = nullptr;
 };
+
+extern "C" const char *mtp_last_error(void) { return g_last_error; }
 
 extern "C" const char *mtp_strerror(int code) {
     switch (code) {
@@ -151,7 +166,7 @@ static void free_ctx(mtp_ctx *c) {
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
-                    c->vkeys, c->s_rowmax, c->s_cand_n, c->s_cand_id, c->s_cand_z};
+                    c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_block) (void)hipHostFree(c->h_block);
@@ -187,10 +202,21 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
     if (!c) return MTP_E_NOMEM;
     c->desc = *desc;
     c->stream = (hipStream_t)hip_stream;
-    if (hipGetDevice(&c->device) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+    g_last_error[0] = 0;
+    {
+        const hipError_t e = hipGetDevice(&c->device);
+        if (e != hipSuccess) { free_ctx(c); return hip_fail("hipGetDevice", e); }
+    }
     const mtp_model_desc &d = c->desc;
     const size_t S = d.max_seqs, R = (size_t)d.max_steps + 1;
     bool ok = dalloc(&c->vkeys, S * R);
+    {
+        const size_t rows = S * (2 * (size_t)d.max_steps + 1);
+        c->s_cap = std::min(4096, d.n_vocab);
+        ok = ok && dalloc(&c->s_maxkey, rows) && dalloc(&c->s_topk, rows) && dalloc(&c->s_cand_n, rows) &&
+             dalloc(&c->s_cand_id, rows * c->s_cap) && dalloc(&c->s_cand_v, rows * c->s_cap) &&
+             dalloc((uint8_t **)&c->s_state, rows * sample_row_state_bytes());
+    }
     if (weights) {
         c->w = *weights;
         c->has_weights = true;
@@ -209,19 +235,26 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         for (int i = 0; ok && i < kParamSlots; ++i)
             ok = hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming) == hipSuccess;
     }
-    if (!ok) { free_ctx(c); return MTP_E_NOMEM; }
-    if (hipMemset(c->vkeys, 0, sizeof(uint64_t) * S * R) != hipSuccess) { free_ctx(c); return MTP_E_DEVICE; }
+    if (!ok) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "allocation failed: %s", hipGetErrorString(hipGetLastError()));
+        free_ctx(c);
+        return MTP_E_NOMEM;
+    }
+    {
+        const size_t rows = S * (2 * (size_t)d.max_steps + 1);
+        hipError_t e = hipMemset(c->vkeys, 0, sizeof(uint64_t) * S * R);
+        if (e == hipSuccess) e = hipMemset(c->s_maxkey, 0, sizeof(uint32_t) * rows);
+        if (e == hipSuccess) e = hipMemset(c->s_cand_n, 0, sizeof(int32_t) * rows);
+        if (e != hipSuccess) { free_ctx(c); return hip_fail("hipMemset (verify scratch)", e); }
+    }
     if (c->has_weights) {
-        if (hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S) != hipSuccess ||
-            launch_rope_init(c->inv_freq, d.head_dim, d.rope_theta, c->stream) != hipSuccess) {
-            free_ctx(c);
-            return MTP_E_DEVICE;
-        }
-        if (d.head_dtype == MTP_Q8_0 &&
-            launch_q8_repack((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_q, c->head_qs, c->stream) !=
-                hipSuccess) {
-            free_ctx(c);
-            return MTP_E_DEVICE;
+        hipError_t e = hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S);
+        if (e != hipSuccess) { free_ctx(c); return hip_fail("hipMemset (draft keys)", e); }
+        e = launch_rope_init(c->inv_freq, d.head_dim, d.rope_theta, c->stream);
+        if (e != hipSuccess) { free_ctx(c); return hip_fail("rope table kernel", e); }
+        if (d.head_dtype == MTP_Q8_0) {
+            e = launch_q8_repack((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_q, c->head_qs, c->stream);
+            if (e != hipSuccess) { free_ctx(c); return hip_fail("Q8_0 re-layout kernel", e); }
         }
     }
     *out = c;
@@ -519,8 +552,12 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
     hio->out_h_last = out_h_last;
     hio->out_logits = out_logits;
     const size_t bytes = sizeof(CallIO) + sizeof(SeqParams) * n_seq;
-    if (hipMemcpyAsync(c->d_block, hb, bytes, hipMemcpyHostToDevice, c->stream) != hipSuccess) return MTP_E_DEVICE;
-    if (hipEventRecord(c->ev[slot], c->stream) != hipSuccess) return MTP_E_DEVICE;
+    {
+        hipError_t e0 = hipMemcpyAsync(c->d_block, hb, bytes, hipMemcpyHostToDevice, c->stream);
+        if (e0 != hipSuccess) return hip_fail("hipMemcpyAsync (parameter block)", e0);
+        e0 = hipEventRecord(c->ev[slot], c->stream);
+        if (e0 != hipSuccess) return hip_fail("hipEventRecord", e0);
+    }
     c->ev_pending[slot] = true;
     c->slot = (slot + 1) % kParamSlots;
 
@@ -531,7 +568,7 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
         hipGraphExec_t exec = chain_graph(c, sh);
         e = exec ? hipGraphLaunch(exec, c->stream) : enqueue_chain(c, sh, c->stream);
     }
-    return e == hipSuccess ? MTP_OK : MTP_E_DEVICE;
+    return e == hipSuccess ? MTP_OK : hip_fail("draft chain launch", e);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,15 +583,37 @@ extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     ProfScope ps(c, MTP_PROF_VERIFY);
     hipError_t e = launch_verify_greedy(logits, drafts, n_seq, n_draft, n_vocab, c->vkeys, out_tokens, out_n_accept,
                                         c->stream);
-    return e == hipSuccess ? MTP_OK : MTP_E_DEVICE;
+    return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch", e);
 }
 
 extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
                                  const float *q_logits, const int32_t *drafts, const int32_t *history,
                                  int32_t history_stride, const int32_t *history_len, const mtp_sampler *sp,
                                  uint64_t round, int32_t *out_tokens, int32_t *out_n_accept) {
-    (void)q_logits; (void)drafts; (void)history; (void)history_stride; (void)history_len; (void)sp; (void)round;
-    (void)out_tokens; (void)out_n_accept; (void)p_logits; (void)n_vocab; (void)n_draft; (void)n_seq;
-    if (!c) return MTP_E_INVAL;
-    return MTP_E_DTYPE;
+    if (!c || !sp) return MTP_E_INVAL;
+    const mtp_model_desc &d = c->desc;
+    if (n_seq < 1 || n_seq > d.max_seqs || n_draft < 0 || n_draft > d.max_steps || n_vocab < 1 ||
+        n_vocab > d.n_vocab)
+        return MTP_E_SHAPE;
+    if (!p_logits || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept) return MTP_E_INVAL;
+    if (q_logits && n_draft == 0) q_logits = nullptr;
+    if (!(sp->temp > 0.f) || !(sp->top_p > 0.f && sp->top_p <= 1.f) || !(sp->min_p >= 0.f && sp->min_p < 1.f) ||
+        !(sp->rep_penalty > 0.f) || !std::isfinite(sp->presence_penalty) || !std::isfinite(sp->freq_penalty) ||
+        sp->top_k < 0 || sp->penalty_last_n < 0 || sp->penalty_last_n > 1024)
+        return MTP_E_INVAL;
+    if (sp->penalty_last_n > 0 && (!history_len || (history_stride > 0 && !history) || history_stride < 0))
+        return MTP_E_INVAL;
+    SampleArgs a{};
+    a.p_logits = p_logits; a.q_logits = q_logits; a.drafts = drafts;
+    a.history = history; a.history_len = sp->penalty_last_n > 0 ? history_len : nullptr;
+    a.hstride = history_stride; a.S = n_seq; a.N = n_draft; a.V = n_vocab;
+    a.temp = sp->temp; a.top_p = sp->top_p; a.min_p = sp->min_p;
+    a.rep = sp->rep_penalty; a.presence = sp->presence_penalty; a.freq = sp->freq_penalty;
+    a.top_k = sp->top_k; a.last_n = sp->penalty_last_n; a.seed = sp->seed; a.round = round;
+    a.row_maxkey = c->s_maxkey; a.topk_key = c->s_topk; a.cand_n = c->s_cand_n; a.cand_id = c->s_cand_id;
+    a.cand_v = c->s_cand_v; a.row_state = c->s_state; a.cap = std::min(c->s_cap, n_vocab);
+    a.out_tokens = out_tokens; a.out_n_accept = out_n_accept;
+    ProfScope ps(c, MTP_PROF_VERIFY);
+    const hipError_t e = launch_verify_sample(a, c->stream);
+    return e == hipSuccess ? MTP_OK : hip_fail("sampling verify launch", e);
 }

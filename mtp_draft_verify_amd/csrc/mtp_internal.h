@@ -137,14 +137,17 @@ struct SampleArgs {
     float temp, top_p, min_p, rep, presence, freq;
     int32_t top_k, last_n;
     uint64_t seed, round;
-    // scratch
-    float *row_max;         // [S, 2, N+1]  (0: p rows, 1: q rows)
-    int32_t *cand_n;        // [S, 2, N+1]
-    int32_t *cand_id;       // [S, 2, N+1, cap]
-    float *cand_z;          // [S, 2, N+1, cap]
+    // scratch, per row (S*(N+1) target rows, then S*N draft rows)
+    uint32_t *row_maxkey;   // zero between calls
+    uint64_t *topk_key;
+    int32_t *cand_n;        // zero between calls
+    int32_t *cand_id;       // [rows, cap]
+    float *cand_v;          // [rows, cap]
+    void *row_state;        // [rows] RowState
     int32_t cap;
     int32_t *out_tokens, *out_n_accept;
 };
 hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st);
+size_t sample_row_state_bytes();
 
 }  // namespace mtp

@@ -1,0 +1,541 @@
+// sample_kernels.hip -- exact temperature>0 speculative verification on gfx950.
+//
+// "opus-mtp-turbo: Track 1 report" s.4 (after Leviathan et al. 2023 s.2.3):
+// row i's distribution p_i is the sampling chain (top-k, penalties over the
+// history plus drafts[0..i), temperature, min-p, top-p) of the target's row;
+// draft d_i is accepted when u * q_i(d_i) < p_i(d_i); at the first rejection
+// the emitted token is drawn from max(p_i - q_i, 0); if every draft is
+// accepted, a bonus token is drawn from p_N.  A missing q means the drafts
+// are deterministic (q one-hot at d_i).
+//
+// Kernels (rows = S*(N+1) target rows followed by S*N draft rows):
+//   topk   (only when top_k > 0) one workgroup per row: radix select of the
+//          k-th largest raw (logit, -id) key
+//   max    per (row, 8192-token chunk): max of the penalised, tempered logit
+//   cand   per (row, chunk): tokens with exp(v - M) >= min_p join the row's
+//          candidate list (order fixed later by sorting)
+//   row    one workgroup per row: sort candidates by (prob desc, id asc),
+//          cumulative sums in a fixed tree order, top-p cut, normaliser; when
+//          the candidates overflow their slots the row switches to an implicit
+//          form (a 64-bit threshold key found by radix select over the whole
+//          row, exact for any distribution)
+//   seq    one workgroup per sequence: accept tests, residual or bonus draw by
+//          Gumbel-max over counter-based SplitMix64 uniforms, outputs, and the
+//          reset of the per-row scratch for the next call
+// All floating point is fp32; every sum runs in a fixed order, so a call is
+// deterministic.
+#include "dev_common.h"
+
+namespace mtp {
+
+static constexpr int kChunk = 8192;
+static constexpr int kMaxCtx = 1024;
+
+struct RowState {
+    float M;          // max of the penalised, tempered logits (kept set)
+    float Z;          // normaliser of the final kept set
+    uint64_t tau;     // kept iff key(e, id) >= tau (after the min-p test)
+    int32_t n_keep;   // compact form: number of kept entries in the row's list; -1: implicit form
+    int32_t pad;
+};
+
+// ---------------------------------------------------------------------------
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): golden-gamma step and the
+// 30/27/31 shift-xor-multiply finaliser.  A coordinate tuple is folded in by
+// xor into the state, one step per coordinate.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t sm64_step(uint64_t state) {
+    uint64_t z = state + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+__device__ __forceinline__ float counter_uniform(uint64_t seed, uint64_t s, uint64_t round, uint64_t i, uint64_t stream,
+                                                 uint64_t t) {
+    uint64_t h = sm64_step(seed);
+    h = sm64_step(h ^ s);
+    h = sm64_step(h ^ round);
+    h = sm64_step(h ^ i);
+    h = sm64_step(h ^ stream);
+    h = sm64_step(h ^ t);
+    return ((float)(h >> 41) + 0.5f) * (1.0f / 8388608.0f);   // (k + 1/2) / 2^23, exact in fp32
+}
+
+__device__ __forceinline__ uint32_t fkey(float v) {            // monotone fp32 -> u32
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_inv(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t tok_key(float v, int32_t id) {  // larger value, then lower id
+    return ((uint64_t)fkey(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+
+struct RowRef {
+    const float *z;   // logits row
+    int kind;         // 0: target row, 1: draft row
+    int s, i;
+};
+
+__device__ __forceinline__ RowRef row_ref(const SampleArgs &a, int row) {
+    RowRef r;
+    const int np = a.S * (a.N + 1);
+    if (row < np) {
+        r.kind = 0;
+        r.s = row / (a.N + 1);
+        r.i = row - r.s * (a.N + 1);
+        r.z = a.p_logits + (int64_t)row * a.V;
+    } else {
+        const int qr = row - np;
+        r.kind = 1;
+        r.s = qr / a.N;
+        r.i = qr - r.s * a.N;
+        r.z = a.q_logits + (int64_t)qr * a.V;
+    }
+    return r;
+}
+
+// context of row (s, i): the last last_n tokens of history[s] ++ drafts[s][0..i)
+__device__ __forceinline__ int ctx_len(const SampleArgs &a, int s, int i) {
+    const int total = (a.history_len ? a.history_len[s] : 0) + i;
+    return a.last_n <= 0 ? 0 : min(a.last_n, total);
+}
+__device__ __forceinline__ int32_t ctx_token(const SampleArgs &a, int s, int i, int n_ctx, int j) {
+    const int hlen = a.history_len ? a.history_len[s] : 0;
+    const int pos = hlen + i - n_ctx + j;
+    return pos < hlen ? a.history[(int64_t)s * a.hstride + pos] : a.drafts[(int64_t)s * a.N + (pos - hlen)];
+}
+
+__device__ __forceinline__ float chain_value(const SampleArgs &a, float z, int cnt) {
+    if (cnt > 0) {
+        z = z > 0.f ? z / a.rep : z * a.rep;
+        z -= a.presence + a.freq * (float)cnt;
+    }
+    return z / a.temp;
+}
+
+// block-wide helpers (256 threads)
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Context of one row in LDS: token list, and a bitmap over [c0, c0 + nbits).
+struct CtxLds {
+    int32_t tok[kMaxCtx];
+    uint32_t bits[kChunk / 32];
+};
+
+__device__ void load_ctx(const SampleArgs &a, int s, int i, int c0, int nbits, CtxLds &cl, int &n_ctx) {
+    n_ctx = ctx_len(a, s, i);
+    for (int w = threadIdx.x; w < kChunk / 32; w += kBlock) cl.bits[w] = 0u;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n_ctx; j += kBlock) {
+        const int32_t t = ctx_token(a, s, i, n_ctx, j);
+        cl.tok[j] = t;
+        if (t >= c0 && t < c0 + nbits) atomicOr(&cl.bits[(t - c0) >> 5], 1u << ((t - c0) & 31));
+    }
+    __syncthreads();
+}
+
+// sort a context list of n <= kMaxCtx tokens ascending in place (LDS, bitonic)
+__device__ void sort_ctx(int32_t *tok, int n) {
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    for (int j = n + threadIdx.x; j < np2; j += kBlock) tok[j] = 0x7FFFFFFF;
+    __syncthreads();
+    for (int k = 2; k <= np2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int x = threadIdx.x; x < np2; x += kBlock) {
+                const int y = x ^ j;
+                if (y > x) {
+                    const bool up = (x & k) == 0;
+                    const int32_t a = tok[x], b = tok[y];
+                    if (up ? (a > b) : (a < b)) { tok[x] = b; tok[y] = a; }
+                }
+            }
+            __syncthreads();
+        }
+}
+// occurrences of t in a sorted list
+__device__ __forceinline__ int sorted_count(const int32_t *tok, int n, int32_t t) {
+    int lo = 0, hi = n;
+    while (lo < hi) { const int m = (lo + hi) >> 1; if (tok[m] < t) lo = m + 1; else hi = m; }
+    int c = 0;
+    while (lo + c < n && tok[lo + c] == t) ++c;
+    return c;
+}
+
+__device__ __forceinline__ int ctx_count(const CtxLds &cl, int n_ctx, int32_t t) {
+    int c = 0;
+    for (int j = 0; j < n_ctx; ++j) c += cl.tok[j] == t;
+    return c;
+}
+
+// value of token t of a row after top-k and penalties (NaN when top-k drops it)
+__device__ __forceinline__ float token_value(const SampleArgs &a, const float *z, int32_t t, bool member,
+                                             const CtxLds &cl, int n_ctx, uint64_t topk_key) {
+    const float raw = z[t];
+    if (a.top_k > 0 && tok_key(raw, t) < topk_key) return __int_as_float(0x7FC00000);
+    return chain_value(a, raw, member ? ctx_count(cl, n_ctx, t) : 0);
+}
+
+// ---------------------------------------------------------------------------
+// radix select over one row: the largest 64-bit key K with W(key >= K) >= target,
+// where W sums weight(t) over the row's eligible tokens.  8 passes of 8 bits.
+// ---------------------------------------------------------------------------
+template <typename KeyW>
+__device__ uint64_t radix_select(int V, uint64_t target, KeyW key_weight, uint64_t *hist /* [256] LDS */,
+                                 uint64_t *scal /* [4] LDS */) {
+    uint64_t prefix = 0, mask = 0;
+    for (int pass = 0; pass < 8; ++pass) {
+        const int shift = 56 - 8 * pass;
+        for (int b = threadIdx.x; b < 256; b += kBlock) hist[b] = 0;
+        __syncthreads();
+        for (int t = threadIdx.x; t < V; t += kBlock) {
+            uint64_t k, wgt;
+            if (!key_weight(t, k, wgt)) continue;
+            if ((k & mask) != prefix) continue;
+            atomicAdd((unsigned long long *)&hist[(k >> shift) & 0xFF], (unsigned long long)wgt);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t above = 0;
+            int dsel = 0;
+            for (int b = 255; b >= 0; --b) {
+                if (above + hist[b] >= target) { dsel = b; break; }
+                above += hist[b];
+            }
+            scal[0] = (uint64_t)dsel;
+            scal[1] = above;
+        }
+        __syncthreads();
+        prefix |= scal[0] << shift;
+        mask |= (uint64_t)0xFF << shift;
+        target -= scal[1];
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// top-k threshold on raw logits (ties: lower id first)
+__global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
+    __shared__ uint64_t hist[256], scal[4];
+    const int row = blockIdx.x;
+    const RowRef rr = row_ref(a, row);
+    if (a.top_k >= a.V) {
+        if (threadIdx.x == 0) a.topk_key[row] = 0;
+        return;
+    }
+    auto kw = [&](int t, uint64_t &k, uint64_t &w) {
+        k = tok_key(rr.z[t], t);
+        w = 1;
+        return true;
+    };
+    const uint64_t K = radix_select(a.V, (uint64_t)a.top_k, kw, hist, scal);
+    if (threadIdx.x == 0) a.topk_key[row] = K;
+}
+
+// pass 1: row max of the chain values
+__global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chunk) {
+    __shared__ CtxLds cl;
+    __shared__ float red[4];
+    const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
+    const RowRef rr = row_ref(a, row);
+    const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
+    int n_ctx;
+    load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
+    const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
+    float mx = -INFINITY;
+    for (int t = c0 + threadIdx.x; t < c1; t += kBlock) {
+        const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+        const float v = token_value(a, rr.z, t, member, cl, n_ctx, tk);
+        if (v == v) mx = fmaxf(mx, v);
+    }
+    mx = block_max(mx, red);
+    if (threadIdx.x == 0 && mx > -INFINITY) atomicMax(&a.row_maxkey[row], fkey(mx));
+}
+
+// pass 2: min-p survivors join the candidate list
+__global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_chunk) {
+    __shared__ CtxLds cl;
+    const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
+    const RowRef rr = row_ref(a, row);
+    const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
+    int n_ctx;
+    load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
+    const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
+    const float M = fkey_inv(a.row_maxkey[row]);
+    for (int t = c0 + threadIdx.x; t < c1; t += kBlock) {
+        const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+        const float v = token_value(a, rr.z, t, member, cl, n_ctx, tk);
+        if (!(v == v)) continue;
+        const float e = expf(v - M);
+        if (e >= a.min_p) {
+            const int slot = atomicAdd(&a.cand_n[row], 1);
+            if (slot < a.cap) {
+                a.cand_id[(int64_t)row * a.cap + slot] = t;
+                a.cand_v[(int64_t)row * a.cap + slot] = e;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// row finalisation
+// ---------------------------------------------------------------------------
+static constexpr int kSortMax = 4096;
+
+__global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
+    __shared__ uint64_t keys[kSortMax];
+    __shared__ float part[kBlock];
+    __shared__ float red[4];
+    __shared__ int cut_sh;
+    __shared__ uint64_t hist[256], scal[4];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n_all = a.cand_n[row];
+    const float M = fkey_inv(a.row_maxkey[row]);
+    RowState st;
+    st.M = M;
+    st.pad = 0;
+    if (n_all <= a.cap) {
+        // ---- compact form: sort the candidates ----
+        const int n = n_all;
+        int np2 = 1;
+        while (np2 < n) np2 <<= 1;
+        for (int j = tid; j < np2; j += kBlock)
+            keys[j] = j < n ? tok_key(a.cand_v[(int64_t)row * a.cap + j], a.cand_id[(int64_t)row * a.cap + j]) : 0ull;
+        __syncthreads();
+        for (int k = 2; k <= np2; k <<= 1) {           // bitonic sort, descending
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int x = tid; x < np2; x += kBlock) {
+                    const int y = x ^ j;
+                    if (y > x) {
+                        const bool desc = (x & k) == 0;
+                        const uint64_t kx = keys[x], ky = keys[y];
+                        if (desc ? (kx < ky) : (kx > ky)) { keys[x] = ky; keys[y] = kx; }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // inclusive prefix sums of e in sorted order: contiguous per-thread
+        // blocks, then a serial scan of the block totals (fixed order)
+        const int per = (n + kBlock - 1) / kBlock;
+        const int b0 = tid * per, b1 = min(n, b0 + per);
+        float run = 0.f;
+        for (int j = b0; j < b1; ++j) run += fkey_inv((uint32_t)(keys[j] >> 32));
+        part[tid] = run;
+        if (tid == 0) cut_sh = n - 1;
+        __syncthreads();
+        if (tid == 0) {
+            float acc = 0.f;
+            for (int b = 0; b < kBlock; ++b) { const float t = part[b]; part[b] = acc; acc += t; }
+            red[0] = acc;
+        }
+        __syncthreads();
+        const float Z2 = red[0];
+        if (a.top_p < 1.f) {
+            float cum = part[tid];
+            for (int j = b0; j < b1; ++j) {
+                cum += fkey_inv((uint32_t)(keys[j] >> 32));
+                if (cum / Z2 >= a.top_p) { atomicMin(&cut_sh, j); break; }
+            }
+        }
+        __syncthreads();
+        const int cut = cut_sh;
+        // normaliser of the kept prefix, in the same summation order
+        if (tid == 0) {
+            const int tb = cut / per;
+            float z = part[tb];
+            for (int j = tb * per; j <= cut; ++j) z += fkey_inv((uint32_t)(keys[j] >> 32));
+            st.Z = z;
+            st.tau = keys[cut];
+            st.n_keep = cut + 1;
+            ((RowState *)a.row_state)[row] = st;
+        }
+        for (int j = tid; j <= cut; j += kBlock) {
+            a.cand_id[(int64_t)row * a.cap + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)keys[j]);
+            a.cand_v[(int64_t)row * a.cap + j] = fkey_inv((uint32_t)(keys[j] >> 32));
+        }
+        return;
+    }
+    // ---- implicit form: thresholds over the whole row ----
+    const RowRef rr = row_ref(a, row);
+    __shared__ int32_t ctx_tok[kMaxCtx];
+    const int n_ctx = ctx_len(a, rr.s, rr.i);
+    for (int j = tid; j < n_ctx; j += kBlock) ctx_tok[j] = ctx_token(a, rr.s, rr.i, n_ctx, j);
+    __syncthreads();
+    sort_ctx(ctx_tok, n_ctx);
+    const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
+    auto e_of = [&](int t, float &e) {
+        const float raw = rr.z[t];
+        if (a.top_k > 0 && tok_key(raw, t) < tk) return false;
+        e = expf(chain_value(a, raw, sorted_count(ctx_tok, n_ctx, t)) - M);
+        return e >= a.min_p;
+    };
+    float z2 = 0.f;
+    for (int t = tid; t < a.V; t += kBlock) {
+        float e;
+        if (e_of(t, e)) z2 += e;
+    }
+    const float Z2 = block_sum(z2, red);
+    uint64_t tau = 0;
+    if (a.top_p < 1.f) {
+        // fixed-point weights (2^40 per unit) keep the histogram sums exact
+        const double scale = 1099511627776.0;
+        const uint64_t target = (uint64_t)ceil((double)a.top_p * (double)Z2 * scale);
+        auto kw = [&](int t, uint64_t &k, uint64_t &w) {
+            float e;
+            if (!e_of(t, e)) return false;
+            k = tok_key(e, t);
+            w = (uint64_t)((double)e * scale);
+            return true;
+        };
+        tau = radix_select(a.V, target, kw, hist, scal);
+    }
+    float z3 = 0.f;
+    for (int t = tid; t < a.V; t += kBlock) {
+        float e;
+        if (e_of(t, e) && tok_key(e, t) >= tau) z3 += e;
+    }
+    const float Z3 = block_sum(z3, red);
+    if (tid == 0) {
+        st.Z = Z3;
+        st.tau = tau;
+        st.n_keep = -1;
+        ((RowState *)a.row_state)[row] = st;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// per-sequence accept / resample
+// ---------------------------------------------------------------------------
+// probability of token t under row `row` (its RowState already final);
+// ctx_tok is the row's context, sorted
+__device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t *ctx_tok, int n_ctx) {
+    if (t < 0 || t >= a.V) return 0.f;
+    const RowRef rr = row_ref(a, row);
+    const RowState st = ((const RowState *)a.row_state)[row];
+    const float raw = rr.z[t];
+    if (a.top_k > 0 && tok_key(raw, t) < a.topk_key[row]) return 0.f;
+    const float e = expf(chain_value(a, raw, sorted_count(ctx_tok, n_ctx, t)) - st.M);
+    if (!(e >= a.min_p) || tok_key(e, t) < st.tau) return 0.f;
+    return e / st.Z;
+}
+
+__global__ __launch_bounds__(256) void sample_seq_kernel(SampleArgs a) {
+    __shared__ int32_t ctx_tok[kMaxCtx];
+    __shared__ uint64_t best_w[4];
+    __shared__ int decision;
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int N = a.N, R = N + 1;
+    int n_acc = N;
+    for (int i = 0; i <= N; ++i) {
+        const int prow = s * R + i;
+        const int n_ctx = ctx_len(a, s, i);
+        __syncthreads();
+        for (int j = tid; j < n_ctx; j += kBlock) ctx_tok[j] = ctx_token(a, s, i, n_ctx, j);
+        __syncthreads();
+        sort_ctx(ctx_tok, n_ctx);
+        const int32_t d = i < N ? a.drafts[(int64_t)s * N + i] : -1;
+        const int qrow = a.q_logits ? a.S * R + s * N + i : -1;
+        if (i < N) {
+            if (tid == 0) {
+                const float pd = row_prob(a, prow, d, ctx_tok, n_ctx);
+                const float qd = a.q_logits ? row_prob(a, qrow, d, ctx_tok, n_ctx) : ((d >= 0 && d < a.V) ? 1.f : 0.f);
+                const float u = counter_uniform(a.seed, s, a.round, i, 0, 0);
+                decision = (u * qd < pd) ? 1 : 0;
+            }
+            __syncthreads();
+            if (decision) {
+                if (tid == 0) a.out_tokens[(int64_t)s * R + i] = d;
+                continue;
+            }
+        }
+        // draw from max(p - q, 0) (rejection at row i) or from p_N (bonus)
+        const uint64_t stream = i < N ? 1 : 2;
+        const RowState st = ((const RowState *)a.row_state)[prow];
+        uint64_t best = 0;
+        auto consider = [&](int32_t t, float pt) {
+            float r = pt;
+            if (i < N) r -= a.q_logits ? row_prob(a, qrow, t, ctx_tok, n_ctx) : (t == d ? 1.f : 0.f);
+            if (!(r > 0.f)) return;
+            const float u = counter_uniform(a.seed, s, a.round, i, stream, (uint64_t)t);
+            const float key = logf(r) - logf(-logf(u));
+            const uint64_t k = tok_key(key, t);
+            best = k > best ? k : best;
+        };
+        if (st.n_keep >= 0) {
+            for (int j = tid; j < st.n_keep; j += kBlock)
+                consider(a.cand_id[(int64_t)prow * a.cap + j], a.cand_v[(int64_t)prow * a.cap + j] / st.Z);
+        } else {
+            for (int t = tid; t < a.V; t += kBlock) {
+                const float pt = row_prob(a, prow, t, ctx_tok, n_ctx);
+                if (pt > 0.f) consider(t, pt);
+            }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m) << 32) |
+                               (uint32_t)__shfl_xor((int)(uint32_t)best, m);
+            best = o > best ? o : best;
+        }
+        if (lane == 0) best_w[wid] = best;
+        __syncthreads();
+        if (tid == 0) {
+            uint64_t b = best_w[0];
+            for (int w = 1; w < 4; ++w) b = best_w[w] > b ? best_w[w] : b;
+            a.out_tokens[(int64_t)s * R + i] = b ? (int32_t)(0xFFFFFFFFu - (uint32_t)b) : -1;
+        }
+        n_acc = i < N ? i : N;
+        if (i < N) {
+            for (int j = i + 1 + tid; j < R; j += kBlock) a.out_tokens[(int64_t)s * R + j] = -1;
+        }
+        break;
+    }
+    if (tid == 0) a.out_n_accept[s] = n_acc;
+    // clear this sequence's row scratch for the next call
+    for (int i = tid; i < R; i += kBlock) {
+        a.row_maxkey[s * R + i] = 0u;
+        a.cand_n[s * R + i] = 0;
+    }
+    if (a.q_logits)
+        for (int i = tid; i < N; i += kBlock) {
+            a.row_maxkey[a.S * R + s * N + i] = 0u;
+            a.cand_n[a.S * R + s * N + i] = 0;
+        }
+}
+
+hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st) {
+    const int rows = a.S * (a.N + 1) + (a.q_logits ? a.S * a.N : 0);
+    const int n_chunk = (a.V + kChunk - 1) / kChunk;
+    if ((int64_t)rows * n_chunk > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (a.top_k > 0) {
+        hipLaunchKernelGGL(sample_topk_kernel, dim3(rows), dim3(kBlock), 0, st, a);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    hipLaunchKernelGGL(sample_max_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    hipLaunchKernelGGL(sample_cand_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+size_t sample_row_state_bytes() { return sizeof(RowState); }
+
+}  // namespace mtp

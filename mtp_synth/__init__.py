@@ -303,7 +303,7 @@ def make_sample_verify(seed: int, S: int, N: int, V: int, *, logit_var: float = 
     q = None
     if not one_hot:
         q = p[:, :N] + normal(seed, "sample.q_noise", (S, N, V))
-    n_top = hist // 4
+    n_top = min(hist // 4, 32)
     r = rng_for(seed, "sample.history")
     history = np.empty((S, hist), dtype=np.int32)
     for s in range(S):
