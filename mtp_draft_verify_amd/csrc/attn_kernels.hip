@@ -32,8 +32,11 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     static_assert(DPL % EPV == 0, "lane slice must be whole 16-byte vectors");
     __shared__ float qs[G][HD];
     __shared__ float cs[HD / 2], sn[HD / 2];
-    __shared__ float wm[4][G], wl[4][G];
-    __shared__ float wacc[4][G][HD];
+    // per lane-group state, merged in LDS; padded (lane stride DPL+1, group
+    // stride +16) so the 64 lanes of a store hit 64 different banks
+    constexpr int JS = 16 * (DPL + 1), GS = G * JS + 16;
+    __shared__ float gm[16][G], gl[16][G], gw[16][G], gL[G], gM[G];
+    __shared__ float gacc[16 * GS];
 
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const SeqParams &sqp = a.seqs[s];
@@ -179,53 +182,43 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         }
     }
 
-    // merge the 4 lane groups (rows) of each wave: xor 16, then xor 32
+    // merge the 16 lane groups through LDS: each group stores (m, l, acc),
+    // 64 threads turn the m's into per-group weights 2^(m_g - M) and the
+    // normaliser, then every thread writes merged (head, dim) outputs
 #pragma unroll
-    for (int step = 16; step <= 32; step *= 2) {
+    for (int j = 0; j < G; ++j) {
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const float mo = __shfl_xor(m[j], step);
-            const float lo = __shfl_xor(l[j], step);
-            const float mn = fmaxf(m[j], mo);
-            const float cself = (mn == -INFINITY) ? 0.f : exp2f(m[j] - mn);
-            const float coth = (mn == -INFINITY) ? 0.f : exp2f(mo - mn);
-            l[j] = l[j] * cself + lo * coth;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) {
-                const float ao = __shfl_xor(acc[j][e], step);
-                acc[j][e] = acc[j][e] * cself + ao * coth;
-            }
-            m[j] = mn;
-        }
-    }
-    if (lane < 16) {
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            if (lane == 0) {
-                wm[wid][j] = m[j];
-                wl[wid][j] = l[j];
-            }
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) wacc[wid][j][li * DPL + e] = acc[j][e];
+        for (int e = 0; e < DPL; ++e) gacc[gi * GS + j * JS + li * (DPL + 1) + e] = acc[j][e];
+        if (li == 0) {
+            gm[gi][j] = m[j];
+            gl[gi][j] = l[j];
         }
     }
     __syncthreads();
-    // merge the 4 waves and write the partial of each query head
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int g = 0; g < 16; ++g) M = fmaxf(M, gm[g][tid]);
+        float L = 0.f;
+        for (int g = 0; g < 16; ++g) {
+            const float w = (gm[g][tid] == -INFINITY) ? 0.f : exp2f(gm[g][tid] - M);
+            gw[g][tid] = w;
+            L += gl[g][tid] * w;
+        }
+        gM[tid] = M;
+        gL[tid] = L;
+    }
+    __syncthreads();
     for (int i = tid; i < G * HD; i += kBlock) {
         const int j = i / HD, c = i - j * HD;
-        float mn = fmaxf(fmaxf(wm[0][j], wm[1][j]), fmaxf(wm[2][j], wm[3][j]));
-        float av = 0.f, lv = 0.f;
+        float av = 0.f;
+        const int cl = (c / DPL) * (DPL + 1) + (c % DPL);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float cw = (wm[w][j] == -INFINITY) ? 0.f : exp2f(wm[w][j] - mn);
-            av += wacc[w][j][c] * cw;
-            lv += wl[w][j] * cw;
-        }
+        for (int g = 0; g < 16; ++g) av = fmaf(gw[g][j], gacc[g * GS + j * JS + cl], av);
         float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + 2);
         pp[2 + c] = av;
         if (c == 0) {
-            pp[0] = mn;
-            pp[1] = lv;
+            pp[0] = gM[j];
+            pp[1] = gL[j];
         }
     }
 }
@@ -260,9 +253,9 @@ hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream
 
 // Log-sum-exp merge of the split partials of one query head, online form:
 // (m, l, acc) <- (M, l*2^(m-M) + l_j*2^(m_j-M), acc*2^(m-M) + acc_j*2^(m_j-M)),
-// M = max(m, m_j).  Workgroup = (64-dim chunk, query head, sequence); 4 thread
-// slices take every 4th split with 8 splits' loads in flight per thread, then
-// the slices combine through LDS in a fixed order.
+// M = max(m, m_j).  Workgroup = (16-dim chunk, query head, sequence): 16
+// thread slices take every 16th split (at most 8 each, all loads in flight at
+// once), then 16 threads combine the slices through LDS in a fixed order.
 __device__ __forceinline__ void lse_combine(float &m, float &l, float &acc, float mj, float lj, float aj) {
     const float mn = fmaxf(m, mj);
     if (mn == -INFINITY) return;
@@ -273,41 +266,38 @@ __device__ __forceinline__ void lse_combine(float &m, float &l, float &acc, floa
 }
 
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    __shared__ float sm[4][64], sl[4][64], sa[4][64];
+    constexpr int DC = 16, SL = 16, U = MTP_MAX_SPLITS / SL;
+    __shared__ float sm[SL][DC], sl[SL][DC], sa[SL][DC];
     const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
-    const int tid = threadIdx.x, dl = tid & 63, slice = tid >> 6;
+    const int tid = threadIdx.x, dl = tid % DC, slice = tid / DC;
     const int hd = a.hd;
-    const int dim = min(chunk * 64 + dl, hd - 1);
+    const int dim = min(chunk * DC + dl, hd - 1);
     const int ns = a.seqs[s].src[a.src].n_split;
     const float *base = a.part + ((int64_t)s * a.Hq + h) * MTP_MAX_SPLITS * (hd + 2);
-    constexpr int U = 8;
-    float m = -INFINITY, l = 0.f, acc = 0.f;
-    for (int j0 = slice; j0 < ns; j0 += 4 * U) {
-        float mj[U], lj[U], aj[U];
+    float mj[U], lj[U], aj[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = j0 + 4 * u;
-            const float *pj = base + (int64_t)min(j, ns - 1) * (hd + 2);
-            mj[u] = (j < ns) ? pj[0] : -INFINITY;
-            lj[u] = pj[1];
-            aj[u] = pj[2 + dim];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) lse_combine(m, l, acc, mj[u], lj[u], aj[u]);
+    for (int u = 0; u < U; ++u) {
+        const int j = slice + SL * u;
+        const float *pj = base + (int64_t)min(j, ns - 1) * (hd + 2);
+        mj[u] = (j < ns) ? pj[0] : -INFINITY;
+        lj[u] = pj[1];
+        aj[u] = pj[2 + dim];
     }
+    float m = -INFINITY, l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) lse_combine(m, l, acc, mj[u], lj[u], aj[u]);
     sm[slice][dl] = m;
     sl[slice][dl] = l;
     sa[slice][dl] = acc;
     __syncthreads();
-    if (slice == 0 && chunk * 64 + dl < hd) {
-#pragma unroll
-        for (int k = 1; k < 4; ++k) lse_combine(m, l, acc, sm[k][dl], sl[k][dl], sa[k][dl]);
-        a.o[((int64_t)s * a.Hq + h) * hd + chunk * 64 + dl] = acc / l;
+    if (slice == 0 && chunk * DC + dl < hd) {
+        for (int k = 1; k < SL; ++k) lse_combine(m, l, acc, sm[k][dl], sl[k][dl], sa[k][dl]);
+        a.o[((int64_t)s * a.Hq + h) * hd + chunk * DC + dl] = acc / l;
     }
 }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
-    dim3 grid((a.hd + 63) / 64, a.Hq, a.S);
+    dim3 grid((a.hd + 15) / 16, a.Hq, a.S);
     hipLaunchKernelGGL(merge_kernel, grid, dim3(kBlock), 0, st, a);
     return hipGetLastError();
 }
