@@ -102,6 +102,62 @@ def cpu_baseline(w, budget_s):
                       f"+ greedy verify), {el:.1f} s wall on the host, OpenMP threads={threads}"}
 
 
+WORKLOADS = {
+    "c2": ("c2_gemma_bf16", "Gemma-4-26B-like assistant drafter, bf16 weights/KV, fp32 arithmetic: 4 blocks "
+           "d_model 1024, h_prev 2816, 8 q / 2 kv heads of 256, MLP 4096, full KV 8192, tied head V=262144; "
+           "1 sequence, B=4 (3 draft steps) + greedy verify"),
+    "c3": ("c3_interleaved", "same drafter; blocks 0-2 read a 1024-position SWA ring, block 3 a full KV of "
+           "ctx ~ U{4096..32768}; 16 sequences, B=4 + greedy verify"),
+    "c4": ("c4_longctx_q8", "same drafter with a Q8_0 tied head; full KV of 131072 positions; 8 sequences, "
+           "B=5 (4 draft steps) + greedy verify"),
+    "c5": ("c5_sample", "exact temperature>0 verify only: V=248320, 32 sequences x 4 drafts, q = perturbed copy, "
+           "temp 0.6, top-p 0.95, min-p 0.05, repetition 1.08, presence 0.4 over the last 64 tokens"),
+}
+
+
+def bench_sample(args, dev):
+    """Extra measurement: the temperature>0 verify on its own."""
+    import torch
+    import mtp_draft_verify_amd as mtp
+    import mtp_synth as syn
+    from mtp_synth.device import to_dev
+    w = syn.c5_sample()
+    sv = w.sample
+    S, R, V = sv.p_logits.shape
+    desc = mtp.make_desc(d_model=32, d_hprev=8, n_blocks=1, n_head_q=1, n_head_kv=1, head_dim=64, d_ff=8,
+                         n_vocab=V, w_dtype=0, head_dtype=0, kv_dtype=0, max_seqs=S, max_steps=R - 1)
+    ctx = mtp.Context(desc, None, stream=torch.cuda.current_stream())
+    p, q = to_dev(sv.p_logits, dev), to_dev(sv.q_logits, dev)
+    dr, hist, hl = to_dev(sv.drafts, dev), to_dev(sv.history, dev), to_dev(sv.history_len, dev)
+    sp = sv.sampler
+    smp = mtp.make_sampler(temp=sp.temp, top_p=sp.top_p, min_p=sp.min_p, rep_penalty=sp.rep_penalty,
+                           presence_penalty=sp.presence_penalty, freq_penalty=sp.freq_penalty, top_k=sp.top_k,
+                           penalty_last_n=sp.penalty_last_n, seed=sp.seed)
+    toks = torch.zeros((S, R), dtype=torch.int32, device=dev)
+    na = torch.zeros((S,), dtype=torch.int32, device=dev)
+    rnd = [0]
+
+    def step():
+        ctx.verify_sample(p, q, dr, hist, hl, smp, rnd[0], toks, na)
+        rnd[0] += 1
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    bytes_step = 2 * (p.numel() + q.numel()) * 4
+    out = {"metric": "verified draft tokens/s of exact temperature>0 verify", "value": S * (R - 1) / (ms * 1e-3),
+           "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": WORKLOADS["c5"][1], "n_seq": S, "n_draft": R - 1, "n_vocab": V},
+           "hbm_gbps_step": bytes_step / (ms * 1e-3) / 1e9, "accepted_per_round": float(na.float().mean())}
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -111,6 +167,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 3 times (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS),
+                    help="c2 (default, the headline line); c3, c4, c5 are extra measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU form (sequences shard with no exchange; "
@@ -135,8 +193,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4}), flush=True)
         return
-    log("bench: generating the Gemma-4-26B-like workload (seed 1)")
-    w = syn.c2_gemma_bf16()
+    if args.workload == "c5":
+        bench_sample(args, dev)
+        return
+    log(f"bench: generating workload {args.workload}")
+    w = getattr(syn, WORKLOADS[args.workload][0])()
     m, dr = w.model, w.draft
     S, N, V = len(dr.seqs), dr.n_steps, m.n_vocab
     desc, wts, keep_w = upload_model(m, dev, S, N)
@@ -220,14 +281,14 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Gemma-4-26B-like assistant drafter, bf16 weights/KV, fp32 arithmetic: 4 blocks "
-                               "d_model 1024, h_prev 2816, 8 q / 2 kv heads of 256, MLP 4096, full KV 8192, "
-                               "tied head V=262144; 1 sequence, B=4 (3 draft steps) + greedy verify",
-                   "n_seq": S, "draft_steps": N, "n_vocab": V, "kv_positions": dr.seqs[0].attn_pos + 1},
+        "config": {"workload": WORKLOADS[args.workload][1],
+                   "n_seq": S, "draft_steps": N, "n_vocab": V,
+                   "kv_positions": [s_.attn_pos + 1 for s_ in dr.seqs][:16]},
         "hbm_gbps_round": round_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "kernel": "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)",
+                     "note": None if args.workload == "c2" else "traffic counters were taken on the c2 workload",
                      "timing": f"HIP events around each head launch over {args.steps} steps after the timed region",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": head_traffic_from_counters(), "bytes_per_launch": head_launch_bytes,
@@ -237,7 +298,9 @@ def main():
         "accepted_per_round": float(acc.mean()),
     }
     ctx.close()
-    if not args.no_cpu_baseline:
+    if args.workload != "c2":
+        out["roofline"]["traffic"] = None
+    if not args.no_cpu_baseline and args.workload == "c2":
         log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle time)")
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(out), flush=True)
