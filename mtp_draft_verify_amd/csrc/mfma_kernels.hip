@@ -1,0 +1,504 @@
+// mfma_kernels.hip -- the draft chain's GEMVs and LM head for several
+// sequences at once, on the gfx950 matrix cores.
+//
+// With S >= 2 sequences a weight pass is a real (if skinny) contraction,
+// Y[s, r] = sum_c W[r, c] X[s, c], so each 16-row weight tile meets all S
+// sequences in v_mfma_f32_16x16x32_bf16 instead of S wave reductions.  The
+// fp32 activations enter as an exact-to-2^-18 pair of bf16 halves (hi + lo,
+// two MFMAs, two fp32 accumulators), so the products keep fp32 accuracy; bf16
+// weights enter as they are and Q8_0 quants widen exactly to bf16, the block
+// scale being applied to each 32-column MFMA result in fp32.
+//
+// Operand layout of the 16x16x32 bf16 MFMA (one wave, lane l = 16 g + j):
+//   A: lane l holds row j, columns 8 g .. 8 g + 7 of the 32-column step
+//   B: lane l holds column j (a sequence), the same 8 step columns
+//   D: lane l holds rows 4 g .. 4 g + 3 of column j
+// Each output column is a separate dot product, so a sequence gets the same
+// bits whatever else is in the batch.
+#include <algorithm>
+
+#include "widen.h"
+
+namespace mtp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t mfma(const bf16x8_t a, const bf16x8_t b, const f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// v ~= hi + lo with |v - hi - lo| <= 2^-18 |v| (both halves round to nearest).
+__device__ __forceinline__ void split_bf16(const float (&v)[8], u32x4_t &hi, u32x4_t &lo) {
+    bf16x8_t h, l;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 b = (__bf16)v[i];
+        h[i] = b;
+        l[i] = (__bf16)(v[i] - (float)b);
+    }
+    hi = __builtin_bit_cast(u32x4_t, h);
+    lo = __builtin_bit_cast(u32x4_t, l);
+}
+
+// 8 Q8_0 quants (one lane's share of a step) as exact bf16 values.
+__device__ __forceinline__ u32x4_t q8_to_bf16(const u32x2_t q) {
+    u32x4_t r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t w = q[h];
+        const uint32_t f0 = __float_as_uint((float)(int8_t)(w & 0xFF));
+        const uint32_t f1 = __float_as_uint((float)(int8_t)((w >> 8) & 0xFF));
+        const uint32_t f2 = __float_as_uint((float)(int8_t)((w >> 16) & 0xFF));
+        const uint32_t f3 = __float_as_uint((float)(int8_t)(w >> 24));
+        r[2 * h + 0] = (f0 >> 16) | (f1 & 0xFFFF0000u);
+        r[2 * h + 1] = (f2 >> 16) | (f3 & 0xFFFF0000u);
+    }
+    return r;
+}
+
+__device__ __forceinline__ u32x4_t ld_nt4(const void *p) { return __builtin_nontemporal_load((const u32x4_t *)p); }
+__device__ __forceinline__ u32x2_t ld_nt2(const void *p) { return __builtin_nontemporal_load((const u32x2_t *)p); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const int lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// ============================================================================
+// GEMV tile kernel: one 16-row tile per workgroup, the K steps dealt out
+// round-robin to the NW waves (step t = w + NW i), partial tiles summed over
+// the waves in a fixed order.  All weight loads are issued first.
+// ============================================================================
+static constexpr int kMmSteps = 8;     // K steps per wave (K <= NW * 8 * 32)
+
+template <int IN>
+__device__ __forceinline__ void mm_load_x(const GemvArgs &a, int s, int col, float (&x)[8]) {
+    if (IN != IN_EMBED) {
+        const float4 *p = (const float4 *)(a.src + (int64_t)s * a.src_stride + col);
+        const float4 u = p[0], v = p[1];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+        return;
+    }
+    const int d = a.d_embed;
+    if (col >= d) {
+        const float4 *p = (const float4 *)(a.h + (int64_t)s * a.dh + (col - d));
+        const float4 u = p[0], v = p[1];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+        return;
+    }
+    const int32_t tok = a.tok_in ? a.tok_in[s] : key_index(a.key_in[s]);
+    if (tok < 0 || tok >= a.embed_rows) {   // ids outside the vocabulary embed to zero
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+        return;
+    }
+    float e[8];
+    if (a.embed_dtype == MTP_F32) {
+        const float4 *p = (const float4 *)((const float *)a.embed + (int64_t)tok * d + col);
+        const float4 u = p[0], v = p[1];
+        e[0] = u.x; e[1] = u.y; e[2] = u.z; e[3] = u.w; e[4] = v.x; e[5] = v.y; e[6] = v.z; e[7] = v.w;
+    } else if (a.embed_dtype == MTP_BF16) {
+        widen(*(const uint4 *)((const uint16_t *)a.embed + (int64_t)tok * d + col), e);
+    } else {
+        const float sc = half_to_f(a.embed_qs[(int64_t)tok * (d / 32) + col / 32]);
+        const uint2 q = *(const uint2 *)(a.embed_q + (int64_t)tok * d + col);
+        const uint32_t qw[2] = {q.x, q.y};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e[i] = sc * (float)(int8_t)((qw[i / 4] >> (8 * (i % 4))) & 0xFF);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = a.embed_scale * e[i];
+}
+
+template <int NW, int IN, int EPI>
+__global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in) {
+    GemvArgs a = a_in;
+    if (IN == IN_EMBED) {   // caller buffers of this call
+        a.tok_in = a.step == 0 ? a.io->last_tok : nullptr;
+        if (a.step == 0) a.h = a.io->h_prev;
+        a.drafts_out = a.step > 0 ? a.io->out_drafts : nullptr;
+    }
+    __shared__ float ssw[NW][16];
+    __shared__ f32x4_t red[NW][64];
+    const int K = a.K, M = a.M, S = a.S, KS = K / 32;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int j16 = lane & 15, g = lane >> 4;
+    const int R0 = blockIdx.x * 16;
+
+    if (IN == IN_EMBED && blockIdx.x == 0 && tid < S) {
+        if (a.drafts_out) a.drafts_out[(int64_t)tid * a.drafts_stride + a.drafts_col] = key_index(a.key_in[tid]);
+        if (a.key_reset) a.key_reset[tid] = 0ull;
+    }
+
+    // weights of this wave's steps (row R0 + j16)
+    u32x4_t wa[kMmSteps];
+    {
+        const int row = R0 + j16;
+        const uint16_t *wr = (const uint16_t *)a.W + (int64_t)row * K + 8 * g;
+#pragma unroll
+        for (int i = 0; i < kMmSteps; ++i) {
+            const int t = wid + NW * i;
+            wa[i] = (row < M && t < KS) ? ld_nt4(wr + 32 * t) : u32x4_t{0, 0, 0, 0};
+        }
+    }
+    // activations of sequence j16 at the same columns
+    const bool sok = j16 < S;
+    float x[kMmSteps][8];
+    float gn[IN == IN_NORM ? kMmSteps : 1][8];
+#pragma unroll
+    for (int i = 0; i < kMmSteps; ++i) {
+        const int t = wid + NW * i;
+        const int col = 32 * t + 8 * g;
+        if (sok && t < KS) {
+            mm_load_x<IN>(a, j16, col, x[i]);
+            if (IN == IN_NORM) {
+                const float4 *gp = (const float4 *)(a.gain + col);
+                const float4 u = gp[0], v = gp[1];
+                float *gi = gn[IN == IN_NORM ? i : 0];
+                gi[0] = u.x; gi[1] = u.y; gi[2] = u.z; gi[3] = u.w; gi[4] = v.x; gi[5] = v.y; gi[6] = v.z; gi[7] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = 0.f;
+            if (IN == IN_NORM)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) gn[IN == IN_NORM ? i : 0][e] = 0.f;
+        }
+    }
+    if (IN == IN_NORM) {
+        // sum of squares of sequence j16: lane (steps, then values), then the
+        // four lane groups, then the waves in order
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kMmSteps; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(x[i][e], x[i][e], ss);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (g == 0) ssw[wid][j16] = ss;
+        __syncthreads();
+        float tot = 0.f;
+        for (int w = 0; w < NW; ++w) tot += ssw[w][j16];
+        const float r = 1.0f / sqrtf(tot / (float)K + a.eps);
+#pragma unroll
+        for (int i = 0; i < kMmSteps; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[i][e] = x[i][e] * r * gn[IN == IN_NORM ? i : 0][e];
+    }
+    f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kMmSteps; ++i) {
+        if (wid + NW * i >= KS) break;      // wave-uniform
+        u32x4_t bh, bl;
+        split_bf16(x[i], bh, bl);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wa[i]);
+        acc_h = mfma(av, __builtin_bit_cast(bf16x8_t, bh), acc_h);
+        acc_l = mfma(av, __builtin_bit_cast(bf16x8_t, bl), acc_l);
+    }
+    red[wid][lane] = acc_h + acc_l;
+    __syncthreads();
+    // thread -> (sequence s, row rho): 16 consecutive threads own 16 consecutive rows
+    for (int o = tid; o < 256; o += NW * 64) {
+        const int s = o >> 4, rho = o & 15;
+        const int row = R0 + rho;
+        if (s >= S || row >= M) continue;
+        const int l = s + 16 * (rho >> 2), q = rho & 3;
+        float y = 0.f;
+        for (int w = 0; w < NW; ++w) y += red[w][l][q];
+        float *dp = a.dst + (int64_t)s * a.dst_stride + row;
+        if (EPI == EPI_STORE) *dp = y;
+        else if (EPI == EPI_ADD) *dp = *dp + y;
+        else *dp = silu_f(y);
+    }
+}
+
+// ============================================================================
+// LM head tile kernel: f = rmsnorm(x; g_final) is staged once per workgroup
+// in LDS as the B operand (hi and lo halves); the four waves then stream
+// their 16-row head tiles with several 8-step units of weights in flight,
+// store the logits, and keep a per-sequence argmax key.  Workgroups past
+// n_head_wg run the post-projection h' = W_post f over the same staged f.
+// ============================================================================
+static constexpr int kHeadUnit = 8;     // K steps per unit: 16 rows x 256 columns
+static constexpr int kHeadDepth = 4;    // units in flight per wave
+
+template <typename HT>
+struct HeadUnit;
+template <> struct HeadUnit<uint16_t> {
+    u32x4_t w[kHeadUnit];
+};
+template <> struct HeadUnit<int8_t> {
+    u32x2_t w[kHeadUnit];
+    u32x4_t sc;             // fp16 scales of the lane's row for the unit's 8 blocks
+};
+
+// Staged-activation slot of (step t, half h, lane group g, sequence s): one
+// 1 KiB block per (t, h) in lane order, so a wave reads it with a single
+// conflict-free ds_read_b128 at a compile-time offset from its lane base.
+__device__ __forceinline__ int bslot(int t, int h, int g, int s) { return ((2 * t + h) * 4 + g) * 16 + s; }
+
+// Unit c (steps 8c .. 8c+7) of the 16-row tile at row0.  Rows are clamped
+// into the matrix (rows past the end are computed but never stored).
+template <typename HT>
+__device__ __forceinline__ void head_load_unit(const void *W, const uint16_t *qs, int rows, int d, int row0, int c,
+                                               int j16, int g, HeadUnit<HT> &u) {
+    const int KS = d / 32;
+    const int row = min(row0 + j16, rows - 1);
+    if constexpr (sizeof(HT) == 2) {
+        const uint16_t *wr = (const uint16_t *)W + (int64_t)row * d + 8 * g + 32 * kHeadUnit * c;
+#pragma unroll
+        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt4(wr + 32 * k);
+    } else {
+        const int8_t *wr = (const int8_t *)W + (int64_t)row * d + 8 * g + 32 * kHeadUnit * c;
+#pragma unroll
+        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt2(wr + 32 * k);
+        u.sc = ld_nt4(qs + (int64_t)row * KS + c * kHeadUnit);
+    }
+}
+
+__device__ __forceinline__ float sc_at(const u32x4_t &v, int k) {
+    const uint32_t w = v[k >> 1];
+    return half_to_f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFF)));
+}
+
+// MFMAs of one unit; acc_h / acc_l carry the tile's running sums.  The
+// activations are the A operand (rows = sequences) and the weights the B
+// operand (columns = vocabulary rows), so a lane's four results share its
+// weight row j16 and one Q8_0 scale per block.
+template <typename HT>
+__device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4_t *bsm, int c, int g, int j16,
+                                              f32x4_t &acc_h, f32x4_t &acc_l) {
+    const u32x4_t *xb = bsm + bslot(c * kHeadUnit, 0, g, j16);
+#pragma unroll
+    for (int k = 0; k < kHeadUnit; ++k) {
+        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, xb[128 * k]);
+        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, xb[128 * k + 64]);
+        if constexpr (sizeof(HT) == 2) {
+            const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, u.w[k]);
+            acc_h = mfma(xh, wv, acc_h);
+            acc_l = mfma(xl, wv, acc_l);
+        } else {
+            // Each block's products are scaled before the next block starts:
+            // the empty volatile asm statements keep their order, which
+            // keeps one block's conversion and MFMA results live at a time.
+            u32x2_t q = u.w[k];
+            asm volatile("" : "+v"(q));
+            const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t ph = mfma(xh, wv, z), pl = mfma(xl, wv, z);
+            const float sc = sc_at(u.sc, k);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc_h[i] = fmaf(sc, ph[i], acc_h[i]);
+                acc_l[i] = fmaf(sc, pl[i], acc_l[i]);
+            }
+            asm volatile("" : "+v"(acc_h), "+v"(acc_l));
+        }
+    }
+}
+
+// The 16-row tiles [T0, T1) of one workgroup: wave w takes T0 + w, T0 + w + 4,
+// ...  UPT units make a tile and kHeadDepth is a multiple of UPT, so a tile's
+// epilogue sits at a fixed ring position; loads and stores are unconditional
+// (tiles past the wave's last one load the matrix's first unit and store to
+// `sink`), which keeps the loop body straight-line and lets the compiler
+// wait for exactly the unit it is about to use.
+//   HEAD: argmax key over valid rows, logits to `out` when LOGITS
+//   else: rows stored to `out` (the post-projection)
+template <typename HT, int UPT, bool HEAD, bool LOGITS>
+__device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs, int rows, int T0, int T1,
+                           const u32x4_t *bsm, float *out, int64_t out_stride, uint64_t (&best)[4]) {
+    constexpr int TPI = kHeadDepth / UPT;   // tiles per loop iteration
+    static_assert(kHeadDepth % UPT == 0, "ring must hold whole tiles");
+    const int d = a.d, S = a.S;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j16 = lane & 15, g = lane >> 4;
+    const int nt = T1 - T0 > wid ? (T1 - T0 - wid + 3) / 4 : 0;
+    const int nit = (nt + TPI - 1) / TPI;
+    auto load = [&](int i, int c, HeadUnit<HT> &dst) {
+        const bool real = i < nt;
+        head_load_unit<HT>(W, qs, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, j16, g, dst);
+    };
+    HeadUnit<HT> buf[kHeadDepth];
+#pragma unroll
+    for (int p = 0; p < kHeadDepth; ++p) load(p / UPT, p % UPT, buf[p]);
+    f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < nit; ++it) {
+#pragma unroll
+        for (int p = 0; p < kHeadDepth; ++p) {
+            const int i = it * TPI + p / UPT, c = p % UPT;
+            head_unit_mma<HT>(buf[p], bsm, c, g, j16, acc_h, acc_l);
+            load(i + TPI, c, buf[p]);
+            if (c == UPT - 1) {
+                // lane (j16, g) holds row 16 tile + j16 for sequences 4g .. 4g+3
+                const int r = 16 * (T0 + wid + 4 * i) + j16;
+                const f32x4_t z = acc_h + acc_l;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int sq = 4 * g + q;
+                    const bool ok = i < nt && sq < S && r < rows;
+                    if (HEAD) {
+                        const uint64_t k = ok ? argmax_key(z[q], (uint32_t)r) : 0ull;
+                        best[q] = k > best[q] ? k : best[q];
+                    }
+                    if (!HEAD || LOGITS) *(ok ? out + (int64_t)sq * out_stride + r : a.sink + lane) = z[q];
+                }
+                acc_h = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                acc_l = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep each unit's LDS reads next to its MFMAs
+        }
+    }
+}
+
+template <typename HT, int UPT, bool LOGITS>
+__global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_wg) {
+    extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
+    __shared__ float rs[kMaxSeqGroup];
+    __shared__ uint64_t wbest[4][16];
+    const int d = a.d, S = a.S, KS = d / 32;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const bool head_wg = (int)blockIdx.x < a.n_head_wg;
+
+    // f = rmsnorm(x; g_final) -> activation halves (sequences >= S stay zero)
+    for (int j = wid; j < S; j += 4) {
+        const float *x = a.x + (int64_t)j * d;
+        float ss = 0.f;
+        for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
+    }
+    __syncthreads();
+    for (int it = tid; it < KS * 64; it += 256) {
+        const int s = it & 15, g = (it >> 4) & 3, t = it >> 6;
+        u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
+        if (s < S) {
+            const int col = 32 * t + 8 * g;
+            const float4 *xp = (const float4 *)(a.x + (int64_t)s * d + col);
+            const float4 *gp = (const float4 *)(a.g_final + col);
+            const float4 x0 = xp[0], x1 = xp[1], g0 = gp[0], g1 = gp[1];
+            const float r = rs[s];
+            const float v[8] = {x0.x * r * g0.x, x0.y * r * g0.y, x0.z * r * g0.z, x0.w * r * g0.w,
+                                x1.x * r * g1.x, x1.y * r * g1.y, x1.z * r * g1.z, x1.w * r * g1.w};
+            split_bf16(v, hi, lo);
+        }
+        mm_bsm[bslot(t, 0, g, s)] = hi;
+        mm_bsm[bslot(t, 1, g, s)] = lo;
+    }
+    __syncthreads();
+
+    uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};   // sequences 4g .. 4g+3 of this lane
+    if (head_wg) {
+        float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : a.sink;
+        const int64_t logits_stride = (int64_t)a.n_steps * a.V;
+        const int n_tiles = (a.V + 15) / 16;
+        const int T0 = blockIdx.x * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
+        const void *W = sizeof(HT) == 1 ? (const void *)a.head_q : a.head;
+        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, logits, logits_stride, best);
+        // best over the 16 rows of each lane group: xor-shuffles within 16 lanes
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+                const uint64_t o = shfl_xor_u64(best[q], m);
+                best[q] = o > best[q] ? o : best[q];
+            }
+        }
+        if ((lane & 15) == 0)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wbest[wid][4 * (lane >> 4) + q] = best[q];
+        __syncthreads();
+        if (tid < S) {
+            uint64_t k = wbest[0][tid];
+            for (int w = 1; w < 4; ++w) k = wbest[w][tid] > k ? wbest[w][tid] : k;
+            atomicMax((unsigned long long *)&a.keys[tid], (unsigned long long)k);
+        }
+    } else {
+        float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
+        const int n_tiles = (a.dh + 15) / 16;
+        const int T0 = ((int)blockIdx.x - a.n_head_wg) * 4, T1 = min(n_tiles, T0 + 4);
+        head_tiles<uint16_t, UPT, false, false>(a, a.w_post, nullptr, a.dh, T0, T1, mm_bsm, h_out, a.dh, best);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// host side
+// ----------------------------------------------------------------------------
+bool mm_gemv_supported(int w_dtype, const GemvArgs &a) {
+    return w_dtype == MTP_BF16 && a.S >= kMmMinSeqs && a.S <= 16 && a.K % 32 == 0 && a.K <= 16 * kMmSteps * 32;
+}
+
+hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, hipStream_t st) {
+    const int KS = a.K / 32;
+    const int nw = KS <= 4 * kMmSteps ? 4 : KS <= 8 * kMmSteps ? 8 : 16;
+    const dim3 grid((a.M + 15) / 16);
+#define MTP_MM_CASE(NW, I, E)                                                                          \
+    if (nw == NW && in_mode == I && epi == E) {                                                        \
+        hipLaunchKernelGGL((mm_gemv_kernel<NW, I, E>), grid, dim3(NW * 64), 0, st, a);                 \
+        return hipGetLastError();                                                                      \
+    }
+#define MTP_MM_NW(NW)                          \
+    MTP_MM_CASE(NW, IN_EMBED, EPI_STORE)       \
+    MTP_MM_CASE(NW, IN_NORM, EPI_STORE)        \
+    MTP_MM_CASE(NW, IN_NORM, EPI_SILU)         \
+    MTP_MM_CASE(NW, IN_PLAIN, EPI_ADD)
+    MTP_MM_NW(4)
+    MTP_MM_NW(8)
+    MTP_MM_NW(16)
+#undef MTP_MM_NW
+#undef MTP_MM_CASE
+    return hipErrorInvalidValue;
+}
+
+bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a) {
+    const int upt = a.d / (32 * kHeadUnit);
+    return w_dtype == MTP_BF16 && (head_dtype == MTP_BF16 || head_dtype == MTP_Q8_0) && a.S >= kMmMinSeqs &&
+           a.S <= 16 && a.d % (32 * kHeadUnit) == 0 && (upt == 1 || upt == 2 || upt == 4) && a.sink;
+}
+
+template <typename HT, int UPT>
+static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 grid, size_t lds, bool logits,
+                                   hipStream_t st) {
+    if (logits) {
+        hipError_t e = allow_dynamic_lds(mm_head_kernel<HT, UPT, true>, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((mm_head_kernel<HT, UPT, true>), grid, dim3(256), lds, st, a, tiles_per_wg);
+    } else {
+        hipError_t e = allow_dynamic_lds(mm_head_kernel<HT, UPT, false>, lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((mm_head_kernel<HT, UPT, false>), grid, dim3(256), lds, st, a, tiles_per_wg);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mm_head(int head_dtype, const HeadArgs &a_in, bool logits, hipStream_t st) {
+    HeadArgs a = a_in;
+    const int KS = a.d / 32, upt = a.d / (32 * kHeadUnit);
+    const size_t lds = sizeof(u32x4_t) * (size_t)128 * KS;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
+    const int n_tiles = (a.V + 15) / 16;
+    int n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
+    const int tiles_per_wg = (n_tiles + n_wg - 1) / n_wg;
+    n_wg = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+    a.n_head_wg = n_wg;
+    const int n_post_wg = ((a.dh + 15) / 16 + 3) / 4;
+    const dim3 grid(n_wg + n_post_wg);
+#define MTP_MMH(HT, U)                                                                                 \
+    if (upt == U) return launch_mm_head_t<HT, U>(a, tiles_per_wg, grid, lds, logits, st);
+    if (head_dtype == MTP_BF16) {
+        MTP_MMH(uint16_t, 1)
+        MTP_MMH(uint16_t, 2)
+        MTP_MMH(uint16_t, 4)
+    } else {
+        MTP_MMH(int8_t, 1)
+        MTP_MMH(int8_t, 2)
+        MTP_MMH(int8_t, 4)
+    }
+#undef MTP_MMH
+    return hipErrorInvalidValue;
+}
+
+}  // namespace mtp

@@ -66,6 +66,7 @@ struct mtp_ctx {
     hipStream_t stream = nullptr;
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
+    float *sink = nullptr;              // [64] stores that carry nothing land here
     uint64_t *dkeys = nullptr;          // [2][max_seqs]
     double *inv_freq = nullptr;         // [head_dim / 2] RoPE frequencies
     int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
@@ -80,7 +81,7 @@ struct mtp_ctx {
     int slot = 0;
     // captured draft chains, one per launch shape
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[4]; hipGraph_t g; hipGraphExec_t exec; };
+    struct Graph { int key[5]; hipGraph_t g; hipGraphExec_t exec; };
     std::vector<Graph> graphs;
     bool graph_failed = false;          // capture unsupported: launch directly
     // optional event timing per kernel class
@@ -165,7 +166,7 @@ static void free_ctx(mtp_ctx *c) {
         (void)hipGraphDestroy(g.g);
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
@@ -224,7 +225,7 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
-             dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2);
+             dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64);
         c->block_bytes = sizeof(CallIO) + sizeof(SeqParams) * S;
         ok = ok && dalloc(&c->d_block, c->block_bytes);
         if (ok && d.head_dtype == MTP_Q8_0)
@@ -360,6 +361,7 @@ static int gemv_rows_per_wg(int M) {
 
 static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStream_t st) {
     ProfScope ps(c, MTP_PROF_GEMV);
+    if (mm_gemv_supported(c->desc.w_dtype, a)) return launch_mm_gemv(in_mode, epi, a, st);
     a.rows_per_wg = gemv_rows_per_wg(a.M);
     const int n_wg = (a.M + a.rows_per_wg - 1) / a.rows_per_wg;
     return launch_gemv(c->desc.w_dtype, in_mode, epi, a, n_wg, st);
@@ -369,6 +371,7 @@ static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStre
 // besides the parameter block.
 struct ChainShape {
     int S, N, split[2];
+    int logits;     // the caller asked for draft logits
 };
 
 // Enqueue the whole draft chain (N steps of a1..a7, then the hand-off of the
@@ -459,9 +462,11 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             ha.w_post = c->w.w_post; ha.dh = DH;
             ha.post_rows_per_wg = 4;
             ha.h_out = c->h;
+            ha.sink = c->sink;
             const int n_post_wg = (DH + ha.post_rows_per_wg - 1) / ha.post_rows_per_wg;
             ProfScope ps(c, MTP_PROF_HEAD);
-            e = launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
+            e = mm_head_supported(d.head_dtype, d.w_dtype, ha) ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
+                                                                : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
         }
     }
     if (e == hipSuccess)
@@ -471,7 +476,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
 
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
-    const int key[4] = {sh.S, sh.N, sh.split[0], sh.split[1]};
+    const int key[5] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.logits};
     for (auto &g : c->graphs)
         if (std::memcmp(g.key, key, sizeof(key)) == 0) return g.exec;
     if (c->graph_failed) return nullptr;
@@ -528,7 +533,7 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
     CallIO *hio = (CallIO *)hb;
     SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
     std::memset(hio, 0, sizeof(CallIO));
-    ChainShape sh{n_seq, n_steps, {0, 0}};
+    ChainShape sh{n_seq, n_steps, {0, 0}, out_logits != nullptr};
     for (int s = 0; s < n_seq; ++s) {
         const mtp_seq &sq = seqs[s];
         SeqParams &p = hp[s];

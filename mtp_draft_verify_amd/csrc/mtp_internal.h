@@ -92,6 +92,7 @@ struct HeadArgs {
     const void *w_post;     // [dh, d] (w dtype)
     int32_t dh, post_rows_per_wg;
     float *h_out;           // [S, dh] context buffer (the last step writes io->out_h_last when given)
+    float *sink;            // [64] target of stores that carry nothing (matrix-core head)
 };
 
 struct AttnArgs {
@@ -122,6 +123,13 @@ hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, i
                             hipStream_t st);
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
 hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st);
+
+// several sequences: GEMVs and the LM head on the matrix cores
+static constexpr int kMmMinSeqs = 2;
+bool mm_gemv_supported(int w_dtype, const GemvArgs &a);
+hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, hipStream_t st);
+bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a);
+hipError_t launch_mm_head(int head_dtype, const HeadArgs &a, bool logits, hipStream_t st);
 
 // verify
 hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,
