@@ -223,6 +223,272 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 }
 
+// ----------------------------------------------------------------------------
+// bf16 KV: scores on the matrix cores, softmax and P.V on the vector ALUs
+// ----------------------------------------------------------------------------
+// Workgroup = (split, kv head, sequence) as above; each wave owns 16-cell
+// tiles w, w+4, ... of the split.  Per tile the G query heads meet the 16
+// K rows in v_mfma_f32_16x16x32_bf16 (A = K, cells as rows, straight from
+// HBM; B = the scaled query as bf16 hi and lo halves, 2G of the 16
+// columns), so a score costs no vector work.  Lane j < G of each 16-lane
+// row then owns head j for 4 cells: it adds the lo column, keeps the online
+// softmax (m, l) in base 2 and publishes p through LDS; every lane then
+// accumulates P.V for its HD/64 dims of all G heads from the tile's V rows,
+// which it loads as one coalesced 512-byte row per cell.  The next tile's
+// K and V are loaded before the current one is used; loads past the
+// wave's last tile re-read its first tile (cached) so the loop body stays
+// straight-line.  Positions past the split end are clamped to its last
+// position (never an unseen cell) and masked to -inf.
+typedef __bf16 abf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t au32x2_t __attribute__((ext_vector_type(2)));
+
+template <int DPL> struct VRow;
+template <> struct VRow<4> { typedef au32x2_t T; };   // 4 bf16 per lane per cell
+template <> struct VRow<2> { typedef uint32_t T; };   // 2 bf16
+
+// KV addresses come from the per-call parameter block, so the compiler
+// cannot see that they are global memory; flat loads would count against
+// the LDS counter too and force full waits.  Load through global pointers.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
+template <int HD, int G>
+struct AttnTile {
+    static constexpr int KS = HD / 32, DPL = HD / 64;
+    u32x4_t k[KS];
+    typename VRow<DPL>::T v[16];
+};
+
+__device__ __forceinline__ void bf16_pair(uint32_t w, float &lo, float &hi) {
+    lo = __uint_as_float(w << 16);
+    hi = __uint_as_float(w & 0xFFFF0000u);
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
+    constexpr int KS = HD / 32, DPL = HD / 64;
+    static_assert(2 * G <= 16, "hi and lo query columns must fit one MFMA tile");
+    __shared__ float qs[G][HD];
+    __shared__ float cs[HD / 2], sn[HD / 2];
+    __shared__ float wm[4][G], wl[4][G];
+    __shared__ float wacc[4][G][HD];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const SeqParams &sqp = a.seqs[s];
+    const SrcParams &sp = sqp.src[a.src];
+    if (split >= sp.n_split) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j16 = lane & 15, g = lane >> 4;
+    const int pbeg = split * sp.split_len;
+    const int npos = min(sp.split_len, sp.n_vis - pbeg);
+    const int ntile = (npos + 15) / 16;
+    const int nt = ntile > wid ? (ntile - wid + 3) / 4 : 0;     // this wave's tiles
+
+    const uint16_t *kb = (const uint16_t *)sp.k + (int64_t)kvh * HD;
+    const uint16_t *vb = (const uint16_t *)sp.v + (int64_t)kvh * HD;
+    auto cell_of = [&](int pi) {
+        int c = sp.c0 + pbeg + min(pi, npos - 1);
+        return c >= sp.n_cells ? c - sp.n_cells : c;
+    };
+    auto load = [&](int i, AttnTile<HD, G> &t) {
+        const int p0 = i < nt ? 16 * (wid + 4 * i) : 16 * wid;
+        const uint16_t *kp = kb + (int64_t)cell_of(p0 + j16) * sp.cell_stride + 8 * g;
+#pragma unroll
+        for (int u = 0; u < KS; ++u) t.k[u] = ld_global<u32x4_t>(kp + 32 * u);
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+            t.v[c] = ld_global<typename VRow<DPL>::T>(vb + (int64_t)cell_of(p0 + c) * sp.cell_stride + DPL * lane);
+    };
+    // the first two tiles do not depend on the query: request them first
+    AttnTile<HD, G> buf[2];
+    if (nt > 0) load(0, buf[0]);
+    if (nt > 1) load(1, buf[1]);
+
+    // --- prologue: per-head q RMSNorm and RoPE, as in attn_kernel ----------
+    constexpr int QPL = (HD + 63) / 64;
+    constexpr int GW = (G + 3) / 4;
+    float qv[GW][QPL], gq[QPL];
+#pragma unroll
+    for (int i = 0; i < QPL; ++i) gq[i] = (lane + 64 * i < HD) ? a.g_q[lane + 64 * i] : 0.f;
+#pragma unroll
+    for (int jj = 0; jj < GW; ++jj) {
+        const int j = wid + 4 * jj;
+        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvh * G + min(j, G - 1)) * HD;
+#pragma unroll
+        for (int i = 0; i < QPL; ++i) qv[jj][i] = (lane + 64 * i < HD) ? qh[lane + 64 * i] : 0.f;
+    }
+    const double invf = (tid < HD / 2) ? a.inv_freq[tid] : 0.0;
+    const int64_t pos = (int64_t)sqp.pos0 + a.step;
+    if (tid < HD / 2) {
+        const double kTwoPi = 6.283185307179586476925;
+        const double ang = (double)pos * invf;
+        const double red = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
+        float sv, cv;
+        sincosf((float)red, &sv, &cv);
+        cs[tid] = cv;
+        sn[tid] = sv;
+    }
+#pragma unroll
+    for (int jj = 0; jj < GW; ++jj) {
+        const int j = wid + 4 * jj;
+        if (j < G) {
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < QPL; ++i) ss = fmaf(qv[jj][i], qv[jj][i], ss);
+            ss = wave_sum(ss);
+            const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
+#pragma unroll
+            for (int i = 0; i < QPL; ++i)
+                if (lane + 64 * i < HD) qs[j][lane + 64 * i] = qv[jj][i] * r * gq[i];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * (HD / 2); i += kBlock) {
+        const int j = i / (HD / 2), c = i - j * (HD / 2);
+        const float x0 = qs[j][c], x1 = qs[j][c + HD / 2];
+        qs[j][c] = x0 * cs[c] - x1 * sn[c];
+        qs[j][c + HD / 2] = x0 * sn[c] + x1 * cs[c];
+    }
+    __syncthreads();
+
+    // B operand: column h < G holds the hi half of query head h, column 8 + h
+    // its lo half (scaled by scale * log2(e)); the other columns are zero.
+    abf16x8_t qb[KS];
+    {
+        const int h = j16 & 7;
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (h < G) ? qs[h][32 * u + 8 * g + e] * (a.scale * kLog2e) : 0.f;
+                const __bf16 hb = (__bf16)x;
+                qb[u][e] = j16 < 8 ? hb : (__bf16)(x - (float)hb);
+            }
+        }
+    }
+
+    float m = -INFINITY, l = 0.f;           // head j16 (lanes j16 < G)
+    float acc[G][DPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
+
+    // (x, y) of lanes l and l ^ 32 (and l ^ 16) in the same order in both lanes
+    auto xmax = [](float v) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+        r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    };
+    auto xsum = [](float v) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    };
+    auto tile = [&](int i, const AttnTile<HD, G> &t) {
+        // two independent MFMA chains over the even / odd head-dim steps
+        f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < KS; u += 2) {
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, t.k[u]), qb[u], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, t.k[u + 1]), qb[u + 1], d1, 0, 0, 0);
+        }
+        const f32x4_t d = d0 + d1;
+        // lane (j16 < G, g): head j16, cells 4g .. 4g+3; its lo column sits
+        // 8 lanes away in the same row (a rotate by 8 either way)
+        const int pt = 16 * (wid + 4 * i) + 4 * g;
+        float sc[4], mt = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            sc[q] = (pt + q < npos) ? d[q] + dpp<0x128>(d[q]) : -INFINITY;
+            mt = fmaxf(mt, sc[q]);
+        }
+        mt = xmax(mt);
+        const float mn = fmaxf(m, mt);
+        const float corr = mn == -INFINITY ? 1.f : exp2f(m - mn);
+        float p[4], ps = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            p[q] = mn == -INFINITY ? 0.f : exp2f(sc[q] - mn);
+            ps += p[q];
+        }
+        l = l * corr + xsum(ps);
+        m = mn;
+        // P.V: p and the rescale are read out of the owning lanes as scalars
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float cr = lane_read(corr, h);
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[h][e] *= cr;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            float vf[DPL];
+            if constexpr (DPL == 4) {
+                bf16_pair(t.v[c][0], vf[0], vf[1]);
+                bf16_pair(t.v[c][1], vf[2], vf[3]);
+            } else {
+                bf16_pair(t.v[c], vf[0], vf[1]);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float ph = lane_read(p[c & 3], h + 16 * (c >> 2));
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+            }
+        }
+    };
+    // Two tiles in flight.  The steady-state body issues its loads without
+    // conditions; the last one to three tiles are peeled, so no load is
+    // issued past the wave's last tile.
+    int i = 0;
+    for (; i + 3 < nt; i += 2) {
+        tile(i, buf[0]);
+        load(i + 2, buf[0]);
+        tile(i + 1, buf[1]);
+        load(i + 3, buf[1]);
+    }
+    if (i < nt) tile(i, buf[0]);
+    if (i + 2 < nt) load(i + 2, buf[0]);
+    if (i + 1 < nt) tile(i + 1, buf[1]);
+    if (i + 2 < nt) tile(i + 2, buf[0]);
+
+    // --- merge the four waves' states -> one partial per query head --------
+    if (j16 < G && g == 0) {
+        wm[wid][j16] = m;
+        wl[wid][j16] = l;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) wacc[wid][h][DPL * lane + e] = acc[h][e];
+    __syncthreads();
+    for (int i = tid; i < G * HD; i += kBlock) {
+        const int j = i / HD, c = i - j * HD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][j]);
+        float L = 0.f, av = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float wt = wm[w][j] == -INFINITY ? 0.f : exp2f(wm[w][j] - M);
+            L = fmaf(wl[w][j], wt, L);
+            av = fmaf(wacc[w][j][c], wt, av);
+        }
+        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + 2);
+        pp[2 + c] = av;
+        if (c == 0) {
+            pp[0] = M;
+            pp[1] = L;
+        }
+    }
+}
+
 hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st) {
     dim3 grid(max_split, a.Hkv, a.S);
     const int G = a.Hq / a.Hkv;
@@ -231,6 +497,22 @@ hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream
         hipLaunchKernelGGL((attn_kernel<KT, HDV / 16, GV>), grid, dim3(kBlock), 0, st, a);          \
         return hipGetLastError();                                                                   \
     }
+#define MTP_ATTN_MM(HDV, GV)                                                                        \
+    if (a.hd == HDV && G == GV) {                                                                   \
+        hipLaunchKernelGGL((attn_mm_kernel<HDV, GV>), grid, dim3(kBlock), 0, st, a);                \
+        return hipGetLastError();                                                                   \
+    }
+    if (kv_dtype == MTP_BF16) {
+        MTP_ATTN_MM(256, 4)
+        MTP_ATTN_MM(256, 2)
+        MTP_ATTN_MM(256, 1)
+        MTP_ATTN_MM(256, 8)
+        MTP_ATTN_MM(128, 8)
+        MTP_ATTN_MM(128, 4)
+        MTP_ATTN_MM(128, 2)
+        MTP_ATTN_MM(128, 1)
+    }
+#undef MTP_ATTN_MM
     if (kv_dtype == MTP_BF16) {
         MTP_ATTN_CASE(uint16_t, 256, 4)
         MTP_ATTN_CASE(uint16_t, 256, 2)
