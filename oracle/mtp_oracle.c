@@ -183,6 +183,43 @@ int32_t orc_argmax_f32(int64_t n, const float *z, double *margin) {
     return (int32_t)best;
 }
 
+/* Draft confidence ("MTP decoding", section "Stopping early when the head is
+   unsure"; "Fused NextN draft graph", risks: the per-step softmax maximum
+   read back beside the argmax).  The largest softmax probability is
+   exp(max - max) / sum exp(z - max) = 1 / sum exp(z - max). */
+double orc_confidence(int64_t n, const float *z) {
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n; ++t)
+        if ((double)z[t] > m) m = z[t];
+    double sum = 0.0;
+    for (int64_t t = 0; t < n; ++t) sum += exp((double)z[t] - m);
+    return 1.0 / sum;
+}
+
+/* p_min trim ("MTP decoding", "Stopping early ...": drafting stops as soon
+   as the confidence falls below p_min; at 0 it never stops; the step that
+   falls below is not proposed).  The chain itself always runs every step
+   (one captured launch); the trim is applied to what it returns. */
+int orc_pmin_trim(int32_t n_seq, int32_t n_steps, const double *conf, double p_min, double tol, int32_t *drafts,
+                  int32_t *out_n_keep, int32_t *out_near) {
+    if (n_seq <= 0 || n_steps <= 0 || !conf || !drafts || !out_n_keep) return -1;
+    for (int32_t s = 0; s < n_seq; ++s) {
+        int32_t keep = n_steps, near = 0;
+        for (int32_t k = 0; k < n_steps; ++k) {
+            const double c = conf[(int64_t)s * n_steps + k];
+            if (fabs(c - p_min) <= tol) near = 1;
+            if (c < p_min) {
+                keep = k;
+                break;
+            }
+        }
+        for (int32_t k = keep; k < n_steps; ++k) drafts[(int64_t)s * n_steps + k] = -1;
+        out_n_keep[s] = keep;
+        if (out_near) out_near[s] = near;
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* draft chain ([G4] s.4 steps 1-8, s.6 positions; [FUS] on-device chain)    */
 /* ------------------------------------------------------------------------ */
@@ -200,7 +237,7 @@ static int check_model(const orc_model *m, const orc_weights *w) {
 
 int orc_draft_block(const orc_model *m, const orc_weights *w, int32_t n_seq, const orc_seq *seqs,
                     const int32_t *last_tok, const float *h_prev, int32_t n_steps, int32_t *out_drafts,
-                    float *out_h_last, float *out_logits, double *out_margin) {
+                    float *out_h_last, float *out_logits, double *out_margin, double *out_conf) {
     int rc = check_model(m, w);
     if (rc) return rc;
     if (n_seq <= 0 || n_steps <= 0 || !seqs || !last_tok || !h_prev || !out_drafts) return -1;
@@ -291,6 +328,7 @@ int orc_draft_block(const orc_model *m, const orc_weights *w, int32_t n_seq, con
             int32_t nt = orc_argmax_f32(V, zf, &margin);
             if (out_logits) memcpy(out_logits + ((int64_t)s * n_steps + k) * V, zf, sizeof(float) * (size_t)V);
             if (out_margin) out_margin[(int64_t)s * n_steps + k] = margin;
+            if (out_conf) out_conf[(int64_t)s * n_steps + k] = orc_confidence(V, zf);
             out_drafts[(int64_t)s * n_steps + k] = nt;
             tok[s] = nt;   /* the argmax feeds the next step ([FUS] chain) */
             /* h is handed over as F32 ([G4] s.4 input inp_h_prev F32) */

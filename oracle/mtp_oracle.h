@@ -75,9 +75,24 @@ uint64_t orc_rng_u64(uint64_t seed, uint64_t s, uint64_t round, uint64_t i, uint
 float orc_uniform(uint64_t seed, uint64_t s, uint64_t round, uint64_t i, uint64_t stream, uint64_t t);
 
 /* ---- the path ---- */
+/* out_conf (nullable): per-step draft confidence [S, n_steps], see
+   orc_confidence */
 int orc_draft_block(const orc_model *m, const orc_weights *w, int32_t n_seq, const orc_seq *seqs,
                     const int32_t *last_tok, const float *h_prev, int32_t n_steps,
-                    int32_t *out_drafts, float *out_h_last, float *out_logits, double *out_margin);
+                    int32_t *out_drafts, float *out_h_last, float *out_logits, double *out_margin,
+                    double *out_conf);
+
+/* Draft confidence of one step: the largest probability of the draft head's
+   softmax over its (fp32) logit row, 1 / sum_t exp(z_t - max z). */
+double orc_confidence(int64_t n, const float *z);
+
+/* p_min trim of a drafted block: drafting stops at the first step whose
+   confidence is below p_min, so n_keep[s] = number of leading steps with
+   conf >= p_min (n_steps if none falls below; p_min <= 0 never trims).
+   Drafts at k >= n_keep[s] become -1.  near[s] = 1 when some conf of the
+   sequence up to and including its stopping step lies within tol of p_min. */
+int orc_pmin_trim(int32_t n_seq, int32_t n_steps, const double *conf, double p_min, double tol,
+                  int32_t *drafts, int32_t *out_n_keep, int32_t *out_near);
 
 int orc_verify_greedy(int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
                       const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept);

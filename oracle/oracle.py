@@ -83,7 +83,10 @@ def lib():
         L.orc_uniform.restype = C.c_float
         L.orc_uniform.argtypes = [C.c_uint64] * 6
         L.orc_draft_block.argtypes = [C.POINTER(OrcModel), C.POINTER(OrcWeights), C.c_int32, P, P, P, C.c_int32,
-                                      P, P, P, P]
+                                      P, P, P, P, P]
+        L.orc_confidence.restype = C.c_double
+        L.orc_confidence.argtypes = [C.c_int64, P]
+        L.orc_pmin_trim.argtypes = [C.c_int32, C.c_int32, P, C.c_double, C.c_double, P, P, P]
         L.orc_verify_greedy.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.orc_sample_dist.argtypes = [C.c_int32, P, P, C.c_int32, C.POINTER(OrcSampler), P, P]
         L.orc_verify_sample.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
@@ -152,11 +155,30 @@ def draft_block(m: syn.Model, dr: syn.DraftInputs, seq_idx=None, want_logits: bo
     h_last = np.zeros((S, m.d_hprev), np.float32)
     logits = np.zeros((S, N, m.n_vocab), np.float32) if want_logits else None
     margin = np.zeros((S, N), np.float64)
+    conf = np.zeros((S, N), np.float64)
     rc = lib().orc_draft_block(C.byref(om), C.byref(ow), S, C.cast(sa, C.c_void_p), _p(lt), _p(hp), N, _p(drafts),
-                               _p(h_last), _p(logits), _p(margin))
+                               _p(h_last), _p(logits), _p(margin), _p(conf))
     if rc != 0:
         raise RuntimeError(f"orc_draft_block failed: {rc}")
-    return dict(drafts=drafts, h_last=h_last, logits=logits, margin=margin)
+    return dict(drafts=drafts, h_last=h_last, logits=logits, margin=margin, conf=conf)
+
+
+def confidence(z: np.ndarray) -> float:
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    return float(lib().orc_confidence(len(z), _p(z)))
+
+
+def pmin_trim(drafts: np.ndarray, conf: np.ndarray, p_min: float, tol: float = 0.0):
+    """-> (trimmed drafts, n_keep, near flags)"""
+    d = np.ascontiguousarray(drafts, dtype=np.int32).copy()
+    c = np.ascontiguousarray(conf, dtype=np.float64)
+    S, N = d.shape
+    keep = np.zeros(S, np.int32)
+    near = np.zeros(S, np.int32)
+    rc = lib().orc_pmin_trim(S, N, _p(c), C.c_double(p_min), C.c_double(tol), _p(d), _p(keep), _p(near))
+    if rc != 0:
+        raise RuntimeError(f"orc_pmin_trim failed: {rc}")
+    return d, keep, near
 
 
 def verify_greedy(logits: np.ndarray, drafts: np.ndarray):

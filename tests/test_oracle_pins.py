@@ -230,6 +230,67 @@ def test_chain_embedding_path_follows_a_permutation(orc):
     np.testing.assert_allclose(out["h_last"][0], np.eye(d)[t] * fval, rtol=2e-7)
 
 
+def test_draft_confidence_closed_forms(orc):
+    """The draft confidence is the largest softmax probability of the step's
+    logit row ("MTP decoding", stopping early when the head is unsure):
+    three tokens with weights 1:2:3 give 3/6; a flat row gives 1/V; two
+    tokens a gap g apart give the logistic 1/(1 + e^-g)."""
+    z = np.log(np.array([1.0, 2.0, 3.0])).astype(np.float32)
+    assert abs(orc.confidence(z) - 0.5) < 1e-7
+    for V in (1, 7, 262144):
+        assert orc.confidence(np.full(V, -3.25, np.float32)) == 1.0 / V
+    for g in (0.0, 0.5, 4.0, 30.0):
+        z = np.array([1.0, 1.0 + g], np.float32)
+        assert abs(orc.confidence(z) - 1.0 / (1.0 + math.exp(-g))) < 1e-7
+    # shift invariance: adding a constant to every logit changes nothing
+    r = np.random.default_rng(5).standard_normal(1000).astype(np.float32)
+    assert abs(orc.confidence(r) - orc.confidence(r + np.float32(8.0))) < 1e-6
+
+
+def test_pmin_trim_hand_cases(orc):
+    """Drafting stops at the first step whose confidence is below p_min and
+    that step is not proposed; p_min = 0 never stops; p_min above 1 keeps
+    nothing."""
+    d = np.array([[11, 12, 13], [21, 22, 23], [31, 32, 33]], np.int32)
+    c = np.array([[0.9, 0.5, 0.95], [0.7, 0.8, 0.9], [0.2, 0.99, 0.99]])
+    t, keep, _ = orc.pmin_trim(d, c, 0.6)
+    assert keep.tolist() == [1, 3, 0]
+    assert t.tolist() == [[11, -1, -1], [21, 22, 23], [-1, -1, -1]]
+    t, keep, _ = orc.pmin_trim(d, c, 0.0)
+    assert keep.tolist() == [3, 3, 3] and np.array_equal(t, d)
+    t, keep, _ = orc.pmin_trim(d, c, 1.01)
+    assert keep.tolist() == [0, 0, 0] and (t == -1).all()
+    # equality keeps the step (stops only strictly below)
+    _, keep, near = orc.pmin_trim(d, c, 0.7, tol=1e-9)
+    assert keep.tolist() == [1, 3, 0] and near.tolist() == [0, 1, 0]
+
+
+def test_chain_confidence_of_a_one_hot_logit_row(orc):
+    """Permutation drafter of the embedding-path pin: every step's logits are
+    a single value z* at the draft token and 0 elsewhere, so the confidence
+    is 1 / (1 + (V-1) e^-z*); a zero head gives 1/V at every step."""
+    d = V = dh = 8
+    m = toys.blank_model(d=d, dh=dh, V=V)
+    toys.zero_blocks(m)
+    perm = [3, 6, 0, 7, 1, 2, 5, 4]
+    a = 0.5
+    m.weights["head"] = (a * np.eye(V, d)).astype(np.float32)
+    m.weights["w_pre"] = np.concatenate([toys.perm_matrix(perm), np.zeros((d, dh), np.float32)], 1)
+    m.weights["w_post"] = np.eye(dh, d, dtype=np.float32)
+    g = m.weights["g_final"]
+    dr = toys.one_seq_inputs(m, 4, 3, last_tok=2, h_prev=np.ones(dh), n_steps=3)
+    out = orc.draft_block(m, dr)
+    t = 2
+    for k in range(3):
+        t = perm[t]
+        xval = math.sqrt(d) * a
+        zstar = float(np.float32(a * xval * toys.rms_scale(np.eye(d)[t] * xval, m.rms_eps) * g[t]))
+        assert abs(out["conf"][0, k] - 1.0 / (1.0 + (V - 1) * math.exp(-zstar))) < 1e-7
+    m.weights["head"] = np.zeros((V, d), np.float32)
+    out = orc.draft_block(m, dr)
+    assert (out["conf"] == 1.0 / V).all() and (out["drafts"] == 0).all()
+
+
 def test_chain_hidden_path_follows_the_post_projection(orc):
     """W_pre = [0 | I]: x = h.  W_post = P: next h = P f.  The drafts walk the
     permutation through h alone, and h_last = P f of the last step (handed
