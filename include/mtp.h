@@ -161,6 +161,24 @@ int mtp_draft_block(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const int3
                     const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
                     float *out_logits);
 
+/* Draft chain with per-step confidence and the p_min trim ("MTP decoding",
+   section "Stopping early when the head is unsure"; "Fused NextN draft
+   graph", risks: the per-step softmax maximum read back beside the argmax,
+   then the draft block trimmed by p_min before verify).  The same chain as
+   mtp_draft_block, always n_steps steps in one launch sequence, plus:
+     out_conf   fp32 [n_seq, n_steps]  conf[s, k] = the largest softmax
+                probability of step k's logits, 1 / sum_t exp(z_t - max z)
+                (required whenever p_min > 0 or out_n_keep is given)
+     p_min      trim threshold: drafting stops at the first step whose
+                confidence is below p_min and that step is not proposed;
+                out_drafts[s, k] = -1 for k >= n_keep[s] (-1 never matches
+                in mtp_verify_greedy).  p_min <= 0 keeps every draft.
+     out_n_keep int32 [n_seq] or NULL  leading drafts kept
+   Returns MTP_E_INVAL for a NaN p_min or a trim request without out_conf. */
+int mtp_draft_block_conf(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
+                         const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
+                         float *out_logits, float *out_conf, float p_min, int32_t *out_n_keep);
+
 /* Greedy verify ([MTP] "How it is wired"; [G4] s.8).  logits fp32
    [n_seq, n_draft+1, n_vocab] are the target's rows for [confirmed, drafts...];
    t_i = argmax row i (lowest id on ties); a = the longest prefix with

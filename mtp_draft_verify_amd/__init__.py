@@ -5,7 +5,7 @@ this module only builds the C structs from torch tensors (device memory and
 the current HIP stream) and raises on a non-zero status.  It fails loudly when
 the library is missing: there is no fallback path.
 
-The module-level functions carry the C names (mtp_ctx_create, mtp_draft_block,
+The module-level functions carry the C names (mtp_ctx_create, mtp_draft_block, mtp_draft_block_conf,
 mtp_verify_greedy, mtp_verify_sample, mtp_ctx_destroy, mtp_strerror,
 mtp_check_desc); `Context` is a small owner around them.
 """
@@ -24,8 +24,9 @@ MTP_F32, MTP_BF16, MTP_Q8_0 = 0, 1, 2
 MTP_SRC_FULL, MTP_SRC_SWA = 0, 1
 MAX_BLOCKS = 8
 MAX_SPLITS = 128
-EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_verify_greedy", "mtp_verify_sample",
-           "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read", "mtp_last_error")
+EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
+           "mtp_verify_sample", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
+           "mtp_last_error")
 MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY = 0, 1, 2, 3
 
 
@@ -86,6 +87,8 @@ def lib() -> C.CDLL:
         L.mtp_ctx_destroy.restype = None
         L.mtp_draft_block.argtypes = [P, C.c_int32, C.POINTER(Seq), P, P, C.c_int32, P, P, P]
         L.mtp_draft_block.restype = C.c_int
+        L.mtp_draft_block_conf.argtypes = [P, C.c_int32, C.POINTER(Seq), P, P, C.c_int32, P, P, P, P, C.c_float, P]
+        L.mtp_draft_block_conf.restype = C.c_int
         L.mtp_verify_greedy.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.mtp_verify_greedy.restype = C.c_int
         L.mtp_verify_sample.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
@@ -155,6 +158,16 @@ def mtp_draft_block(ctx: int, seqs, last_tok, h_prev, n_steps: int, out_drafts, 
                                _ptr(out_h_last), _ptr(out_logits))
     if rc != MTP_OK:
         raise MTPError(rc, "mtp_draft_block")
+
+
+def mtp_draft_block_conf(ctx: int, seqs, last_tok, h_prev, n_steps: int, out_drafts, out_h_last=None,
+                         out_logits=None, out_conf=None, p_min: float = 0.0, out_n_keep=None) -> None:
+    arr = seqs if isinstance(seqs, C.Array) else make_seqs(seqs)
+    rc = lib().mtp_draft_block_conf(ctx, len(arr), arr, _ptr(last_tok), _ptr(h_prev), n_steps, _ptr(out_drafts),
+                                    _ptr(out_h_last), _ptr(out_logits), _ptr(out_conf), float(p_min),
+                                    _ptr(out_n_keep))
+    if rc != MTP_OK:
+        raise MTPError(rc, "mtp_draft_block_conf")
 
 
 def mtp_verify_greedy(ctx: int, n_seq: int, n_draft: int, n_vocab: int, logits, drafts, out_tokens,
@@ -251,6 +264,11 @@ class Context:
 
     def draft_block(self, seqs, last_tok, h_prev, n_steps, out_drafts, out_h_last=None, out_logits=None):
         mtp_draft_block(self.handle, seqs, last_tok, h_prev, n_steps, out_drafts, out_h_last, out_logits)
+
+    def draft_block_conf(self, seqs, last_tok, h_prev, n_steps, out_drafts, out_h_last=None, out_logits=None,
+                         out_conf=None, p_min=0.0, out_n_keep=None):
+        mtp_draft_block_conf(self.handle, seqs, last_tok, h_prev, n_steps, out_drafts, out_h_last, out_logits,
+                             out_conf, p_min, out_n_keep)
 
     def verify_greedy(self, logits, drafts, out_tokens, out_n_accept):
         S, R, V = logits.shape

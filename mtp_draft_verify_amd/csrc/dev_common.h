@@ -74,6 +74,24 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 
 __device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
 
+// Running (max m, sum s of exp(z - m)) over a stream of logits, and the merge
+// of two such pairs.  The merge is symmetric in its operands, so both lanes
+// of a butterfly exchange end with the same bits.
+__device__ __forceinline__ void conf_add(float &m, float &s, float z) {
+    if (z > m) {
+        s = s * __expf(m - z) + 1.0f;
+        m = z;
+    } else {
+        s += __expf(z - m);
+    }
+}
+__device__ __forceinline__ void conf_merge(float &m, float &s, float m2, float s2) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;
+    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
+    m = mn;
+}
+
 // non-temporal 16-byte loads for data streamed once (weights, logits)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

@@ -41,13 +41,14 @@ __device__ void post_rows(const HeadArgs &a, const float *fs, float *h_out) {
     }
 }
 
-template <typename HT, int NV, bool ONE>
+template <typename HT, int NV, bool ONE, bool CONF>
 __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
     constexpr int EPV = WTr<HT>::EPV, CPW = 64 * EPV;
     constexpr int RU = ONE ? 4 : 2;        // rows in flight per wave
     extern __shared__ float fs[];          // [S][d] final-normed activations
     __shared__ float rs[kMaxSeqGroup];
     __shared__ uint64_t wbest[4][kMaxSeqGroup];
+    __shared__ float wcm[4][kMaxSeqGroup], wcs[4][kMaxSeqGroup];   // confidence partials per wave
     const int d = a.d, S = a.S;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int r0 = blockIdx.x * a.rows_per_wg;
@@ -86,7 +87,11 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
         ss = wave_sum(ss);
         if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
     }
-    if (tid < 4 * kMaxSeqGroup) wbest[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0ull;
+    if (tid < 4 * kMaxSeqGroup) {
+        wbest[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0ull;
+        wcm[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = -INFINITY;
+        wcs[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0.f;
+    }
     __syncthreads();
     for (int i = tid; i < S * d; i += kBlock) {
         const int j = i / d, c = i - j * d;
@@ -113,6 +118,8 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
         }
     }
     uint64_t best1 = 0ull;                  // one-sequence path keeps its best in a register
+    float cm1 = -INFINITY, cs1 = 0.f;       // and its confidence partial
+    constexpr bool conf = CONF;             // confidence partials requested
     for (int rb = r0 + wid * RU; rb < r1; rb += 4 * RU) {
         if (rb != r0 + wid * RU) load_head_rows(rb);
 #pragma unroll
@@ -151,32 +158,43 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
                 const uint64_t k = argmax_key(z, (uint32_t)r);
                 if (ONE) {
                     best1 = k > best1 ? k : best1;
-                } else if (lane == 0 && k > wbest[wid][j]) {
-                    wbest[wid][j] = k;          // only lane 0 of this wave touches this slot
+                    if (conf) conf_add(cm1, cs1, z);
+                } else if (lane == 0) {         // only lane 0 of this wave touches these slots
+                    if (k > wbest[wid][j]) wbest[wid][j] = k;
+                    if (conf) conf_add(wcm[wid][j], wcs[wid][j], z);
                 }
             }
         }
     }
-    if (ONE && lane == 0) wbest[wid][0] = best1;
+    if (ONE && lane == 0) {
+        wbest[wid][0] = best1;
+        wcm[wid][0] = cm1;
+        wcs[wid][0] = cs1;
+    }
     __syncthreads();
     if (tid < S) {
         uint64_t k = wbest[0][tid];
         for (int w = 1; w < 4; ++w) k = wbest[w][tid] > k ? wbest[w][tid] : k;
         atomicMax((unsigned long long *)&a.keys[tid], (unsigned long long)k);
+        if (conf) {
+            float m = wcm[0][tid], sm = wcs[0][tid];
+            for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w][tid], wcs[w][tid]);
+            a.conf[(int64_t)tid * kConfSlots + blockIdx.x] = ConfPart{m, sm};
+        }
     }
 }
 
-template <typename HT, bool ONE>
-static hipError_t launch_head_t(const HeadArgs &a, int w_dtype, int n_post_wg, hipStream_t st) {
+template <typename HT, bool ONE, bool CONF>
+static hipError_t launch_head_c(const HeadArgs &a, int w_dtype, int n_post_wg, hipStream_t st) {
     constexpr int CPW = 64 * WTr<HT>::EPV;
     const int nv = (a.d + CPW - 1) / CPW;
     const size_t lds = sizeof(float) * (size_t)a.S * a.d;
     dim3 grid(a.n_head_wg + n_post_wg);
 #define MTP_HEAD_CASE(N)                                                                               \
     if (nv <= N) {                                                                                     \
-        hipError_t e0 = allow_dynamic_lds(head_kernel<HT, N, ONE>, lds);                               \
+        hipError_t e0 = allow_dynamic_lds(head_kernel<HT, N, ONE, CONF>, lds);                         \
         if (e0 != hipSuccess) return e0;                                                               \
-        hipLaunchKernelGGL((head_kernel<HT, N, ONE>), grid, dim3(kBlock), lds, st, a, w_dtype);        \
+        hipLaunchKernelGGL((head_kernel<HT, N, ONE, CONF>), grid, dim3(kBlock), lds, st, a, w_dtype);  \
         return hipGetLastError();                                                                      \
     }
     MTP_HEAD_CASE(1)
@@ -185,6 +203,12 @@ static hipError_t launch_head_t(const HeadArgs &a, int w_dtype, int n_post_wg, h
     MTP_HEAD_CASE(8)
 #undef MTP_HEAD_CASE
     return hipErrorInvalidValue;
+}
+
+template <typename HT, bool ONE>
+static hipError_t launch_head_t(const HeadArgs &a, int w_dtype, int n_post_wg, hipStream_t st) {
+    return a.conf ? launch_head_c<HT, ONE, true>(a, w_dtype, n_post_wg, st)
+                  : launch_head_c<HT, ONE, false>(a, w_dtype, n_post_wg, st);
 }
 
 hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, hipStream_t st) {

@@ -308,7 +308,9 @@ __device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4
 //   else: rows stored to `out` (the post-projection)
 template <typename HT, int UPT, bool HEAD, bool LOGITS>
 __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs, int rows, int T0, int T1,
-                           const u32x4_t *bsm, float *out, int64_t out_stride, uint64_t (&best)[4]) {
+                           const u32x4_t *bsm, float *out, int64_t out_stride, uint64_t (&best)[4],
+                           float (&cm)[4], float (&cs)[4]) {
+    const bool conf = HEAD && a.conf != nullptr;
     constexpr int TPI = kHeadDepth / UPT;   // tiles per loop iteration
     static_assert(kHeadDepth % UPT == 0, "ring must hold whole tiles");
     const int d = a.d, S = a.S;
@@ -342,6 +344,7 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
                     if (HEAD) {
                         const uint64_t k = ok ? argmax_key(z[q], (uint32_t)r) : 0ull;
                         best[q] = k > best[q] ? k : best[q];
+                        if (conf && ok) conf_add(cm[q], cs[q], z[q]);
                     }
                     if (!HEAD || LOGITS) *(ok ? out + (int64_t)sq * out_stride + r : a.sink + lane) = z[q];
                 }
@@ -358,6 +361,7 @@ __global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_
     extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
     __shared__ float rs[kMaxSeqGroup];
     __shared__ uint64_t wbest[4][16];
+    __shared__ float wcm[4][16], wcs[4][16];
     const int d = a.d, S = a.S, KS = d / 32;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const bool head_wg = (int)blockIdx.x < a.n_head_wg;
@@ -390,13 +394,14 @@ __global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_
     __syncthreads();
 
     uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};   // sequences 4g .. 4g+3 of this lane
+    float cm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, cs[4] = {0.f, 0.f, 0.f, 0.f};
     if (head_wg) {
         float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : a.sink;
         const int64_t logits_stride = (int64_t)a.n_steps * a.V;
         const int n_tiles = (a.V + 15) / 16;
         const int T0 = blockIdx.x * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
         const void *W = sizeof(HT) == 1 ? (const void *)a.head_q : a.head;
-        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, logits, logits_stride, best);
+        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, logits, logits_stride, best, cm, cs);
         // best over the 16 rows of each lane group: xor-shuffles within 16 lanes
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -406,20 +411,40 @@ __global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_
                 best[q] = o > best[q] ? o : best[q];
             }
         }
+        const bool conf = a.conf != nullptr;
+        if (conf) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) {
+                    const float om = __shfl_xor(cm[q], m), os = __shfl_xor(cs[q], m);
+                    conf_merge(cm[q], cs[q], om, os);
+                }
+            }
+        }
         if ((lane & 15) == 0)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) wbest[wid][4 * (lane >> 4) + q] = best[q];
+            for (int q = 0; q < 4; ++q) {
+                wbest[wid][4 * (lane >> 4) + q] = best[q];
+                wcm[wid][4 * (lane >> 4) + q] = cm[q];
+                wcs[wid][4 * (lane >> 4) + q] = cs[q];
+            }
         __syncthreads();
         if (tid < S) {
             uint64_t k = wbest[0][tid];
             for (int w = 1; w < 4; ++w) k = wbest[w][tid] > k ? wbest[w][tid] : k;
             atomicMax((unsigned long long *)&a.keys[tid], (unsigned long long)k);
+            if (conf) {
+                float m = wcm[0][tid], sm = wcs[0][tid];
+                for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w][tid], wcs[w][tid]);
+                a.conf[(int64_t)tid * kConfSlots + blockIdx.x] = ConfPart{m, sm};
+            }
         }
     } else {
         float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
         const int n_tiles = (a.dh + 15) / 16;
         const int T0 = ((int)blockIdx.x - a.n_head_wg) * 4, T1 = min(n_tiles, T0 + 4);
-        head_tiles<uint16_t, UPT, false, false>(a, a.w_post, nullptr, a.dh, T0, T1, mm_bsm, h_out, a.dh, best);
+        head_tiles<uint16_t, UPT, false, false>(a, a.w_post, nullptr, a.dh, T0, T1, mm_bsm, h_out, a.dh, best, cm, cs);
     }
 }
 
@@ -473,16 +498,29 @@ static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 gri
     return hipGetLastError();
 }
 
+// Head workgroups of a launch and the 16-row tiles each takes.
+static void mm_head_grid(const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
+    const size_t lds = sizeof(u32x4_t) * (size_t)128 * (a.d / 32);
+    const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
+    const int n_tiles = (a.V + 15) / 16;
+    n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
+    tiles_per_wg = (n_tiles + n_wg - 1) / n_wg;
+    n_wg = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+}
+
+int mm_head_groups(const HeadArgs &a) {
+    int n_wg, tpw;
+    mm_head_grid(a, n_wg, tpw);
+    return n_wg;
+}
+
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a_in, bool logits, hipStream_t st) {
     HeadArgs a = a_in;
     const int KS = a.d / 32, upt = a.d / (32 * kHeadUnit);
     const size_t lds = sizeof(u32x4_t) * (size_t)128 * KS;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
-    const int n_tiles = (a.V + 15) / 16;
-    int n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
-    const int tiles_per_wg = (n_tiles + n_wg - 1) / n_wg;
-    n_wg = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
+    int n_wg, tiles_per_wg;
+    mm_head_grid(a, n_wg, tiles_per_wg);
     a.n_head_wg = n_wg;
     const int n_post_wg = ((a.dh + 15) / 16 + 3) / 4;
     const dim3 grid(n_wg + n_post_wg);

@@ -51,6 +51,56 @@ hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Per-step draft confidence and the p_min trim ("MTP decoding", stopping
+// early when the head is unsure; "Fused NextN draft graph", risks: the
+// per-step softmax maximum read back with the argmax).  One workgroup per
+// sequence.  For each step the head workgroups' (max, sum exp) partials are
+// merged in a fixed order -- thread t takes slots t, t + 256, ..., then a
+// tree over the threads -- and conf = 1 / sum exp(z - max).  Thread 0 then
+// keeps the leading steps with conf >= p_min and writes -1 over the rest.
+__global__ __launch_bounds__(256) void conf_finish_kernel(const ConfPart *part, int32_t N, int32_t n_part,
+                                                          int64_t step_stride, const CallIO *io) {
+    __shared__ float tm[256], ts[256];
+    __shared__ float conf_s[64];
+    const int s = blockIdx.x, tid = threadIdx.x;
+    for (int k = 0; k < N; ++k) {
+        const ConfPart *p = part + k * step_stride + (int64_t)s * kConfSlots;
+        float m = -INFINITY, sm = 0.f;
+        for (int i = tid; i < n_part; i += 256) conf_merge(m, sm, p[i].m, p[i].s);
+        tm[tid] = m;
+        ts[tid] = sm;
+        __syncthreads();
+        for (int w = 128; w > 0; w >>= 1) {
+            if (tid < w) {
+                float a = tm[tid], b = ts[tid];
+                conf_merge(a, b, tm[tid + w], ts[tid + w]);
+                tm[tid] = a;
+                ts[tid] = b;
+            }
+            __syncthreads();
+        }
+        if (tid == 0) conf_s[k] = 1.0f / ts[0];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const float p_min = io->p_min;
+        int keep = N;
+        for (int k = 0; k < N; ++k) {
+            if (io->out_conf) io->out_conf[(int64_t)s * N + k] = conf_s[k];
+            if (keep == N && conf_s[k] < p_min) keep = k;
+        }
+        for (int k = keep; k < N; ++k) io->out_drafts[(int64_t)s * N + k] = -1;
+        if (io->out_n_keep) io->out_n_keep[s] = keep;
+    }
+}
+
+hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_t n_part, int64_t step_stride,
+                              const CallIO *io, hipStream_t st) {
+    if (N > 64 || n_part > kConfSlots) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(conf_finish_kernel, dim3(S), dim3(256), 0, st, part, N, n_part, step_stride, io);
+    return hipGetLastError();
+}
+
 // RoPE frequencies theta^(-2i/hd), i < hd/2, in fp64 (once per context)
 __global__ void rope_init_kernel(double *inv_freq, int32_t hd, double theta) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;

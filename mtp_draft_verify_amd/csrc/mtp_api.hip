@@ -67,6 +67,7 @@ struct mtp_ctx {
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
     float *sink = nullptr;              // [64] stores that carry nothing land here
+    ConfPart *conf_part = nullptr;      // [max_steps][max_seqs][kConfSlots] confidence partials
     uint64_t *dkeys = nullptr;          // [2][max_seqs]
     double *inv_freq = nullptr;         // [head_dim / 2] RoPE frequencies
     int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
@@ -81,7 +82,7 @@ struct mtp_ctx {
     int slot = 0;
     // captured draft chains, one per launch shape
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[5]; hipGraph_t g; hipGraphExec_t exec; };
+    struct Graph { int key[6]; hipGraph_t g; hipGraphExec_t exec; };
     std::vector<Graph> graphs;
     bool graph_failed = false;          // capture unsupported: launch directly
     // optional event timing per kernel class
@@ -166,7 +167,7 @@ static void free_ctx(mtp_ctx *c) {
         (void)hipGraphDestroy(g.g);
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
@@ -225,7 +226,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
-             dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64);
+             dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64) &&
+             dalloc(&c->conf_part, (size_t)d.max_steps * S * kConfSlots);
         c->block_bytes = sizeof(CallIO) + sizeof(SeqParams) * S;
         ok = ok && dalloc(&c->d_block, c->block_bytes);
         if (ok && d.head_dtype == MTP_Q8_0)
@@ -372,6 +374,7 @@ static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStre
 struct ChainShape {
     int S, N, split[2];
     int logits;     // the caller asked for draft logits
+    int conf;       // the caller asked for per-step confidence / the p_min trim
 };
 
 // Enqueue the whole draft chain (N steps of a1..a7, then the hand-off of the
@@ -384,6 +387,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
     const CallIO *io = (const CallIO *)c->d_block;
     const SeqParams *dp = (const SeqParams *)(c->d_block + sizeof(CallIO));
     hipError_t e = hipSuccess;
+    int n_part = 0;                     // confidence partials per (step, sequence)
     for (int k = 0; k < N && e == hipSuccess; ++k) {
         uint64_t *key_cur = c->dkeys + (size_t)(k & 1) * d.max_seqs;
         uint64_t *key_prev = c->dkeys + (size_t)((k + 1) & 1) * d.max_seqs;
@@ -463,20 +467,25 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             ha.post_rows_per_wg = 4;
             ha.h_out = c->h;
             ha.sink = c->sink;
+            ha.conf = sh.conf ? c->conf_part + (size_t)k * d.max_seqs * kConfSlots : nullptr;
             const int n_post_wg = (DH + ha.post_rows_per_wg - 1) / ha.post_rows_per_wg;
             ProfScope ps(c, MTP_PROF_HEAD);
-            e = mm_head_supported(d.head_dtype, d.w_dtype, ha) ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
-                                                                : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
+            const bool mm = mm_head_supported(d.head_dtype, d.w_dtype, ha);
+            n_part = mm ? mm_head_groups(ha) : ha.n_head_wg;
+            e = mm ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
+                   : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
         }
     }
     if (e == hipSuccess)
         e = launch_finish_drafts(c->dkeys + (size_t)((N - 1) & 1) * d.max_seqs, S, io, N, N - 1, st);
+    if (e == hipSuccess && sh.conf)
+        e = launch_conf_finish(c->conf_part, S, N, n_part, (int64_t)d.max_seqs * kConfSlots, io, st);
     return e;
 }
 
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
-    const int key[5] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.logits};
+    const int key[6] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.logits, sh.conf};
     for (auto &g : c->graphs)
         if (std::memcmp(g.key, key, sizeof(key)) == 0) return g.exec;
     if (c->graph_failed) return nullptr;
@@ -516,7 +525,15 @@ static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
 extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
                                const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
                                float *out_logits) {
+    return mtp_draft_block_conf(c, n_seq, seqs, last_tok, h_prev, n_steps, out_drafts, out_h_last, out_logits,
+                                nullptr, 0.0f, nullptr);
+}
+
+extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
+                                    const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,
+                                    float *out_logits, float *out_conf, float p_min, int32_t *out_n_keep) {
     if (!c) return MTP_E_INVAL;
+    if (!(p_min == p_min) || ((p_min > 0.0f || out_n_keep) && !out_conf)) return MTP_E_INVAL;
     if (!c->has_weights) return MTP_E_NOWEIGHTS;
     const mtp_model_desc &d = c->desc;
     if (n_seq < 1 || n_seq > d.max_seqs || n_steps < 1 || n_steps > d.max_steps) return MTP_E_SHAPE;
@@ -533,7 +550,7 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
     CallIO *hio = (CallIO *)hb;
     SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
     std::memset(hio, 0, sizeof(CallIO));
-    ChainShape sh{n_seq, n_steps, {0, 0}, out_logits != nullptr};
+    ChainShape sh{n_seq, n_steps, {0, 0}, out_logits != nullptr, out_conf != nullptr};
     for (int s = 0; s < n_seq; ++s) {
         const mtp_seq &sq = seqs[s];
         SeqParams &p = hp[s];
@@ -556,6 +573,9 @@ extern "C" int mtp_draft_block(mtp_ctx *c, int32_t n_seq, const mtp_seq *seqs, c
     hio->out_drafts = out_drafts;
     hio->out_h_last = out_h_last;
     hio->out_logits = out_logits;
+    hio->out_conf = out_conf;
+    hio->out_n_keep = out_n_keep;
+    hio->p_min = p_min;
     const size_t bytes = sizeof(CallIO) + sizeof(SeqParams) * n_seq;
     {
         hipError_t e0 = hipMemcpyAsync(c->d_block, hb, bytes, hipMemcpyHostToDevice, c->stream);

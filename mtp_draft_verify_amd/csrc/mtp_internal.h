@@ -37,7 +37,18 @@ struct CallIO {
     int32_t *out_drafts;
     float *out_h_last;
     float *out_logits;
-    int64_t pad[3];
+    float *out_conf;        // [S, N] per-step draft confidence (or null)
+    int32_t *out_n_keep;    // [S] drafts kept by the p_min trim (or null)
+    float p_min;            // trim threshold; <= 0 keeps every draft
+    int32_t pad;
+};
+static_assert(sizeof(CallIO) == 64, "the parameter block layout is fixed");
+
+// Per-workgroup partials of the draft confidence: (max, sum exp(z - max))
+// of the workgroup's logits, per (step, sequence) in slots [kConfSlots].
+static constexpr int kConfSlots = 2048;
+struct ConfPart {
+    float m, s;
 };
 
 // Input transforms applied while a GEMV stages its input vector.
@@ -93,6 +104,7 @@ struct HeadArgs {
     int32_t dh, post_rows_per_wg;
     float *h_out;           // [S, dh] context buffer (the last step writes io->out_h_last when given)
     float *sink;            // [64] target of stores that carry nothing (matrix-core head)
+    ConfPart *conf;         // this step's confidence partials [S][kConfSlots] (or null)
 };
 
 struct AttnArgs {
@@ -122,6 +134,8 @@ hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *i
 hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
                             hipStream_t st);
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
+hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_t n_part, int64_t step_stride,
+                              const CallIO *io, hipStream_t st);
 hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st);
 
 // several sequences: GEMVs and the LM head on the matrix cores
@@ -130,6 +144,7 @@ bool mm_gemv_supported(int w_dtype, const GemvArgs &a);
 hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, hipStream_t st);
 bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a);
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a, bool logits, hipStream_t st);
+int mm_head_groups(const HeadArgs &a);   // head workgroups (confidence partials) of one launch
 
 // verify
 hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,

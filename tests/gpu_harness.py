@@ -81,7 +81,7 @@ class GpuDrafter:
         self.ctx = mtp.Context(self.desc, self.w, keepalive=self.tensors)
 
     def run(self, dr: syn.DraftInputs, n_steps=None, want_logits=True, seq_idx=None, last_tok=None, h_prev=None,
-            pos0_shift=0):
+            pos0_shift=0, conf=False, p_min=0.0):
         import torch
         from mtp_synth.device import upload_seqs
         seqs, lt, hp, keep = upload_seqs(self.m, dr, self.device, seq_idx)
@@ -95,10 +95,17 @@ class GpuDrafter:
         drafts = torch.full((S, N), -7, dtype=torch.int32, device=self.device)
         h_last = torch.zeros((S, self.m.d_hprev), dtype=torch.float32, device=self.device)
         logits = torch.zeros((S, N, self.m.n_vocab), dtype=torch.float32, device=self.device) if want_logits else None
-        self.ctx.draft_block(seqs, lt, hp, N, drafts, h_last, logits)
+        if conf:
+            cf = torch.full((S, N), -7.0, dtype=torch.float32, device=self.device)
+            nk = torch.full((S,), -7, dtype=torch.int32, device=self.device)
+            self.ctx.draft_block_conf(seqs, lt, hp, N, drafts, h_last, logits, cf, p_min, nk)
+        else:
+            self.ctx.draft_block(seqs, lt, hp, N, drafts, h_last, logits)
         torch.cuda.synchronize()
         out = dict(drafts=drafts.cpu().numpy(), h_last=h_last.cpu().numpy(),
                    logits=logits.cpu().numpy() if logits is not None else None)
+        if conf:
+            out["conf"], out["n_keep"] = cf.cpu().numpy(), nk.cpu().numpy()
         del keep
         return out
 

@@ -72,6 +72,7 @@ def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
 def test_entry_points_reject_null_context_without_device_work(mtp):
     L = mtp.lib()
     assert L.mtp_draft_block(None, 1, None, None, None, 1, None, None, None) == mtp.MTP_E_INVAL
+    assert L.mtp_draft_block_conf(None, 1, None, None, None, 1, None, None, None, None, 0.5, None) == mtp.MTP_E_INVAL
     assert L.mtp_verify_greedy(None, 1, 1, 10, None, None, None, None) == mtp.MTP_E_INVAL
     sp = mtp.make_sampler(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4)
     assert L.mtp_verify_sample(None, 1, 1, 10, None, None, None, None, 0, None, C.byref(sp), 0, None,
