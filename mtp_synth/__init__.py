@@ -126,6 +126,8 @@ class Model:
     rope_theta: float = 10000.0
     attn_scale: float = 0.0      # 0 -> 1/sqrt(head_dim)
     embed_scale: float = 0.0     # 0 -> sqrt(d_model)
+    n_centroids: int = 0         # centroid LM head: 0 = dense tied head
+    centroid_top_k: int = 0
     weights: Dict[str, np.ndarray] = field(default_factory=dict)
 
     def __post_init__(self):
@@ -140,8 +142,14 @@ class Model:
 
 def make_model(seed: int, *, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab,
                w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16, swa_window=0, block_src=None,
-               head_std: Optional[float] = None) -> Model:
-    """Random drafter: matrices ~ N(0, 1/fan_in), norm gains = 1 + 0.1 N(0,1)."""
+               head_std: Optional[float] = None, n_centroids: int = 0, centroid_top_k: int = 0) -> Model:
+    """Random drafter: matrices ~ N(0, 1/fan_in), norm gains = 1 + 0.1 N(0,1).
+
+    With n_centroids > 0 the LM head is a centroid head: token_ordering is a
+    random permutation of the vocabulary cut into n_centroids lists of
+    V/n_centroids ids, and centroid c is the mean of its list's embedding
+    rows rescaled to unit RMS per entry (so the top centroids tend to hold
+    the top tokens, as a trained head's clusters do)."""
     m = Model(d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab, w_dtype, head_dtype,
               kv_dtype, swa_window, list(block_src if block_src is not None else [KV_FULL] * n_blocks))
     d, dh, qd = d_model, d_hprev, n_head_q * head_dim
@@ -157,6 +165,16 @@ def make_model(seed: int, *, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, he
     mat("w_post", dh, d)
     mat("head", n_vocab, d, std=head_std if head_std is not None else 1.0 / math.sqrt(d), dt=head_dtype)
     gain("g_final", d)
+    if n_centroids:
+        assert n_vocab % n_centroids == 0 and 1 <= centroid_top_k <= n_centroids and head_dtype != Q8_0
+        m.n_centroids, m.centroid_top_k = n_centroids, centroid_top_k
+        vsc = n_vocab // n_centroids
+        order = rng_for(seed, "token_ordering").permutation(n_vocab).astype(np.int32)
+        E = W["head"] if head_dtype == F32 else (W["head"].astype(np.uint32) << 16).view(np.float32)
+        C = E[order].reshape(n_centroids, vsc, d).astype(np.float64).mean(axis=1)
+        C /= np.sqrt((C ** 2).mean(axis=1, keepdims=True)) * math.sqrt(d)
+        W["centroids"] = store(C.astype(np.float32), w_dtype)
+        W["token_ordering"] = order
     for l in range(n_blocks):
         nm = m.block_names(l)
         gain(nm["g_attn"], d)
@@ -401,7 +419,24 @@ def c5_sample(seed: int = 4, **over) -> Workload:
     return Workload("c5_exact_sampling_verify", None, None, sample=sv)
 
 
-CONFIGS = {"c1": c1_tiny, "c2": c2_gemma_bf16, "c3": c3_interleaved, "c4": c4_longctx_q8, "c5": c5_sample}
+def c6_centroid(seed: int = 1, **over) -> Workload:
+    """The c2 drafter shape with a centroid LM head instead of the dense tied
+    head: 2048 centroids of 128 token ids each, top 32 centroids (4096
+    candidate rows) per step; full KV 8192, S=1, N=3."""
+    shape = dict(C2_SHAPE)
+    shape.update({k: v for k, v in over.items() if k in shape})
+    m = make_model(seed, **shape, w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16, head_std=1.0 / math.sqrt(1024),
+                   n_centroids=over.get("n_centroids", 2048), centroid_top_k=over.get("centroid_top_k", 32))
+    ctx = over.get("ctx", 8192)
+    S = over.get("n_seq", 1)
+    N = over.get("n_steps", 3)
+    dr = make_draft_inputs(seed, m, [ctx] * S, N)
+    gv = make_greedy_verify(seed, S, N, m.n_vocab, 0.8, "max5")
+    return Workload("c6_centroid_head_bf16", m, dr, gv, p_accept=0.8)
+
+
+CONFIGS = {"c1": c1_tiny, "c2": c2_gemma_bf16, "c3": c3_interleaved, "c4": c4_longctx_q8, "c5": c5_sample,
+           "c6": c6_centroid}
 
 
 # ----------------------------------------------------------------------------

@@ -220,11 +220,59 @@ int orc_pmin_trim(int32_t n_seq, int32_t n_steps, const double *conf, double p_m
     return 0;
 }
 
+/* Centroid / ordered-embeddings LM head ("Gemma 4 MTP" s.3): steps 1-5 of
+   the page, in its order.  The top-k choice is taken on fp32-rounded
+   centroid logits (the precision the GPU decides in). */
+double orc_centroid_logits(const orc_model *m, const orc_weights *w, const double *f, float *z_out) {
+    const int32_t d = m->d_model, V = m->n_vocab, nc = m->n_centroids, k = m->centroid_top_k;
+    const int32_t vsc = V / nc;
+    float *cl = malloc(sizeof(float) * (size_t)nc);
+    char *taken = calloc((size_t)nc, 1);
+    if (!cl || !taken) { free(cl); free(taken); return -1.0; }
+    /* 1. centroid logits */
+    for (int32_t c = 0; c < nc; ++c) {
+        double acc = 0.0;
+        for (int32_t j = 0; j < d; ++j) acc += orc_load(w->centroids, m->w_dtype, c, j, d) * f[j];
+        cl[c] = (float)acc;
+    }
+    /* 5 (prefill). the full row the verifier expects */
+    for (int32_t t = 0; t < V; ++t) z_out[t] = -1e30f;
+    double boundary = INFINITY;
+    float last = 0.0f;
+    for (int32_t i = 0; i < k; ++i) {
+        /* 2. next best centroid: largest logit, lowest id among equals */
+        int32_t best = -1;
+        for (int32_t c = 0; c < nc; ++c)
+            if (!taken[c] && (best < 0 || cl[c] > cl[best])) best = c;
+        taken[best] = 1;
+        last = cl[best];
+        /* 3. its candidate token ids; 4. their logits E[t] . f */
+        for (int32_t r = 0; r < vsc; ++r) {
+            const int32_t t = w->token_ordering[(int64_t)best * vsc + r];
+            double acc = 0.0;
+            for (int32_t j = 0; j < d; ++j) acc += orc_load(w->head, m->head_dtype, t, j, d) * f[j];
+            z_out[t] = (float)acc;
+        }
+    }
+    for (int32_t c = 0; c < nc; ++c)
+        if (!taken[c] && (double)last - (double)cl[c] < boundary) boundary = (double)last - (double)cl[c];
+    free(cl);
+    free(taken);
+    return boundary;
+}
+
 /* ------------------------------------------------------------------------ */
 /* draft chain ([G4] s.4 steps 1-8, s.6 positions; [FUS] on-device chain)    */
 /* ------------------------------------------------------------------------ */
 static int check_model(const orc_model *m, const orc_weights *w) {
     if (!m || !w) return -1;
+    if (m->n_centroids < 0) return -2;
+    if (m->n_centroids > 0) {
+        if (m->n_vocab % m->n_centroids || m->centroid_top_k < 1 || m->centroid_top_k > m->n_centroids) return -2;
+        if (!w->centroids || !w->token_ordering) return -1;
+        for (int32_t t = 0; t < m->n_vocab; ++t)
+            if (w->token_ordering[t] < 0 || w->token_ordering[t] >= m->n_vocab) return -2;
+    }
     if (m->d_model <= 0 || m->d_hprev <= 0 || m->n_blocks <= 0 || m->n_blocks > ORC_MAX_BLOCKS) return -2;
     if (m->n_head_kv <= 0 || m->n_head_q % m->n_head_kv || m->head_dim <= 0 || m->head_dim % 2) return -2;
     if (m->head_dtype == ORC_Q8_0 && m->d_model % 32) return -2;
@@ -318,14 +366,21 @@ int orc_draft_block(const orc_model *m, const orc_weights *w, int32_t n_seq, con
               argmax; post-projection gives the next step's h_prev
               ([G4] s.4 steps 5, 6, 8) */
         for (int32_t s = 0; s < S; ++s) orc_rmsnorm(d, x + (int64_t)s * d, w->g_final, m->rms_eps, f + (int64_t)s * d);
-        gemv_batch(w->head, m->head_dtype, V, d, S, f, d, zd, V);
+        if (m->n_centroids == 0) gemv_batch(w->head, m->head_dtype, V, d, S, f, d, zd, V);
         double *hn = calloc((size_t)S * dh, sizeof(double));
         if (!hn) { err = -4; goto done; }
         gemv_batch(w->w_post, m->w_dtype, dh, d, S, f, d, hn, dh);
         for (int32_t s = 0; s < S; ++s) {
-            for (int32_t t = 0; t < V; ++t) zf[t] = (float)zd[(int64_t)s * V + t];
+            double cmargin = INFINITY;
+            if (m->n_centroids == 0) {
+                for (int32_t t = 0; t < V; ++t) zf[t] = (float)zd[(int64_t)s * V + t];
+            } else {
+                cmargin = orc_centroid_logits(m, w, f + (int64_t)s * d, zf);
+                if (cmargin < 0) { err = -4; free(hn); goto done; }
+            }
             double margin;
             int32_t nt = orc_argmax_f32(V, zf, &margin);
+            if (cmargin < margin) margin = cmargin;   /* a near tie at either decision */
             if (out_logits) memcpy(out_logits + ((int64_t)s * n_steps + k) * V, zf, sizeof(float) * (size_t)V);
             if (out_margin) out_margin[(int64_t)s * n_steps + k] = margin;
             if (out_conf) out_conf[(int64_t)s * n_steps + k] = orc_confidence(V, zf);

@@ -31,6 +31,8 @@ typedef struct {
     int32_t w_dtype, head_dtype, kv_dtype, swa_window;
     int32_t block_src[ORC_MAX_BLOCKS];
     double rms_eps, rope_theta, attn_scale, embed_scale;
+    /* centroid ("ordered embeddings") LM head: 0 = dense tied head */
+    int32_t n_centroids, centroid_top_k;
 } orc_model;
 
 typedef struct {
@@ -42,6 +44,8 @@ typedef struct {
     const void *w_o[ORC_MAX_BLOCKS];
     const float *g_mlp[ORC_MAX_BLOCKS];
     const void *w_up[ORC_MAX_BLOCKS], *w_down[ORC_MAX_BLOCKS];
+    const void *centroids;          /* [n_centroids, d] (w_dtype), centroid head only */
+    const int32_t *token_ordering;  /* [n_vocab], centroid head only */
 } orc_weights;
 
 typedef struct { const void *k, *v; int64_t n_cells, cell_stride; } orc_kv;
@@ -81,6 +85,15 @@ int orc_draft_block(const orc_model *m, const orc_weights *w, int32_t n_seq, con
                     const int32_t *last_tok, const float *h_prev, int32_t n_steps,
                     int32_t *out_drafts, float *out_h_last, float *out_logits, double *out_margin,
                     double *out_conf);
+
+/* Centroid LM head of one final-normed vector f ("Gemma 4 MTP" s.3,
+   centroid / ordered-embeddings head): centroid logits C f, the top_k
+   centroids (ties -> lower id), their token lists ordering[c*vsc ..
+   (c+1)*vsc) with vsc = V / n_centroids, candidate logits E[t] f, scattered
+   into a full row z_out[V] prefilled with -1e30.  Returns the boundary
+   margin of the top-k choice (k-th minus (k+1)-th centroid logit, fp32),
+   +inf when every centroid is chosen. */
+double orc_centroid_logits(const orc_model *m, const orc_weights *w, const double *f, float *z_out);
 
 /* Draft confidence of one step: the largest probability of the draft head's
    softmax over its (fp32) logit row, 1 / sum_t exp(z_t - max z). */

@@ -37,12 +37,14 @@ class OrcModel(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("d_model", "d_hprev", "n_blocks", "n_head_q", "n_head_kv", "head_dim",
                                           "d_ff", "n_vocab", "w_dtype", "head_dtype", "kv_dtype", "swa_window")] + \
                [("block_src", C.c_int32 * MAXB)] + \
-               [(n, C.c_double) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")]
+               [(n, C.c_double) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")] + \
+               [("n_centroids", C.c_int32), ("centroid_top_k", C.c_int32)]
 
 
 class OrcWeights(C.Structure):
     _fields_ = [("w_pre", C.c_void_p), ("w_post", C.c_void_p), ("head", C.c_void_p), ("g_final", C.c_void_p)] + \
-               [(n, C.c_void_p * MAXB) for n in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down")]
+               [(n, C.c_void_p * MAXB) for n in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down")] + \
+               [("centroids", C.c_void_p), ("token_ordering", C.c_void_p)]
 
 
 class OrcKV(C.Structure):
@@ -84,6 +86,8 @@ def lib():
         L.orc_uniform.argtypes = [C.c_uint64] * 6
         L.orc_draft_block.argtypes = [C.POINTER(OrcModel), C.POINTER(OrcWeights), C.c_int32, P, P, P, C.c_int32,
                                       P, P, P, P, P]
+        L.orc_centroid_logits.restype = C.c_double
+        L.orc_centroid_logits.argtypes = [C.POINTER(OrcModel), C.POINTER(OrcWeights), P, P]
         L.orc_confidence.restype = C.c_double
         L.orc_confidence.argtypes = [C.c_int64, P]
         L.orc_pmin_trim.argtypes = [C.c_int32, C.c_int32, P, C.c_double, C.c_double, P, P, P]
@@ -112,6 +116,7 @@ def orc_model(m: syn.Model) -> OrcModel:
     for l in range(MAXB):
         om.block_src[l] = m.block_src[l] if l < len(m.block_src) else 0
     om.rms_eps, om.rope_theta, om.attn_scale, om.embed_scale = m.rms_eps, m.rope_theta, m.attn_scale, m.embed_scale
+    om.n_centroids, om.centroid_top_k = m.n_centroids, m.centroid_top_k
     return om
 
 
@@ -123,6 +128,8 @@ def orc_weights(m: syn.Model) -> OrcWeights:
         nm = m.block_names(l)
         for k in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down"):
             getattr(ow, k)[l] = _p(W[nm[k]])
+    if m.n_centroids:
+        ow.centroids, ow.token_ordering = _p(W["centroids"]), _p(W["token_ordering"])
     return ow
 
 
@@ -161,6 +168,15 @@ def draft_block(m: syn.Model, dr: syn.DraftInputs, seq_idx=None, want_logits: bo
     if rc != 0:
         raise RuntimeError(f"orc_draft_block failed: {rc}")
     return dict(drafts=drafts, h_last=h_last, logits=logits, margin=margin, conf=conf)
+
+
+def centroid_logits(m: syn.Model, f: np.ndarray):
+    """Centroid head of one final-normed vector f -> (full fp32 row, top-k boundary margin)."""
+    om, ow = orc_model(m), orc_weights(m)
+    f = np.ascontiguousarray(f, dtype=np.float64)
+    z = np.zeros(m.n_vocab, np.float32)
+    margin = lib().orc_centroid_logits(C.byref(om), C.byref(ow), _p(f), _p(z))
+    return z, margin
 
 
 def confidence(z: np.ndarray) -> float:

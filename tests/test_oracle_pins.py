@@ -291,6 +291,45 @@ def test_chain_confidence_of_a_one_hot_logit_row(orc):
     assert (out["conf"] == 1.0 / V).all() and (out["drafts"] == 0).all()
 
 
+def test_centroid_head_hand_case(orc):
+    """Centroid head ("Gemma 4 MTP" s.3): V=8 tokens in 4 centroid lists of 2
+    (ordering [5,1 | 0,7 | 2,6 | 3,4]), top-2 centroids.  With f = e_0 the
+    centroid logits are column 0 of C = [0.3, -1, 2, 0.3]: centroid 2 wins,
+    then the tie 0.3 / 0.3 goes to the lower id 0.  Candidates {2, 6, 5, 1}
+    get E[t] . f = E[t, 0]; every other token reads -1e30; the boundary
+    margin is 0.3 - 0.3 = 0."""
+    m = toys.blank_model(d=4, dh=4, V=8)
+    m.n_centroids, m.centroid_top_k = 4, 2
+    m.weights["centroids"] = np.array([[0.3, 1, 0, 0], [-1, 0, 0, 0], [2, 0, 0, 0], [0.3, 0, 5, 0]], np.float32)
+    m.weights["token_ordering"] = np.array([5, 1, 0, 7, 2, 6, 3, 4], np.int32)
+    E = np.arange(32, dtype=np.float32).reshape(8, 4) / 8 - 1
+    m.weights["head"] = E
+    z, margin = orc.centroid_logits(m, np.array([1.0, 0, 0, 0]))
+    want = np.full(8, -1e30, np.float32)
+    for t in (2, 6, 5, 1):
+        want[t] = E[t, 0]
+    assert np.array_equal(z, want) and margin == 0.0
+    # shifting f towards feature 2 promotes centroid 3 past centroid 0
+    z, margin = orc.centroid_logits(m, np.array([1.0, 0, 0.1, 0]))
+    assert sorted(np.nonzero(z > -1e29)[0].tolist()) == [2, 3, 4, 6]
+    assert abs(margin - (0.8 - 0.3)) < 1e-7
+
+
+def test_centroid_head_with_one_list_equals_the_dense_head(orc):
+    """One centroid holding the whole (permuted) vocabulary, top-1: the
+    candidate set is every token, so the chain is the dense tied head's
+    chain bit for bit."""
+    w = syn.c1_tiny()
+    dense = orc.draft_block(w.model, w.draft)
+    m = w.model
+    m.n_centroids, m.centroid_top_k = 1, 1
+    m.weights["centroids"] = np.ones((1, m.d_model), np.float32)
+    m.weights["token_ordering"] = np.random.default_rng(1).permutation(m.n_vocab).astype(np.int32)
+    cent = orc.draft_block(m, w.draft)
+    for k in ("drafts", "logits", "h_last", "conf"):
+        assert np.array_equal(dense[k], cent[k]), k
+
+
 def test_chain_hidden_path_follows_the_post_projection(orc):
     """W_pre = [0 | I]: x = h.  W_post = P: next h = P f.  The drafts walk the
     permutation through h alone, and h_last = P f of the last step (handed
