@@ -35,16 +35,21 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def weight_bytes(m):
-    """Algorithmic bytes of the drafter weights read once per draft step."""
+def weight_bytes(m, S=1):
+    """Algorithmic bytes of the drafter weights read once per draft step
+    (a centroid head reads its centroid matrix plus each sequence's
+    candidate embedding rows)."""
     import mtp_synth as syn
     es = 4 if m.w_dtype == syn.F32 else 2
     d, dh, qd, F, V = m.d_model, m.d_hprev, m.n_head_q * m.head_dim, m.d_ff, m.n_vocab
     mats = d * (d + dh) + dh * d + m.n_blocks * (2 * qd * d + 2 * F * d)
-    if m.head_dtype == syn.Q8_0:
+    hes = 4 if m.head_dtype == syn.F32 else 2
+    if m.n_centroids:
+        head = m.n_centroids * d * es + S * m.centroid_top_k * (V // m.n_centroids) * d * hes
+    elif m.head_dtype == syn.Q8_0:
         head = V * (d // 32) * 34
     else:
-        head = V * d * (4 if m.head_dtype == syn.F32 else 2)
+        head = V * d * hes
     gains = 4 * ((2 * m.n_blocks + 1) * d + m.n_blocks * m.head_dim)
     return mats * es, head, gains
 
@@ -112,6 +117,8 @@ WORKLOADS = {
            "B=5 (4 draft steps) + greedy verify"),
     "c5": ("c5_sample", "exact temperature>0 verify only: V=248320, 32 sequences x 4 drafts, q = perturbed copy, "
            "temp 0.6, top-p 0.95, min-p 0.05, repetition 1.08, presence 0.4 over the last 64 tokens"),
+    "c6": ("c6_centroid", "the c2 drafter with a centroid LM head: 2048 centroids x 128 token ids, top 32 "
+           "centroids (4096 candidate rows) per step; full KV 8192; 1 sequence, B=4 + greedy verify"),
 }
 
 
@@ -258,13 +265,17 @@ def main():
     ctx.profile(0)
     log(f"bench: breakdown {breakdown}")
 
-    wb, hb, gb = weight_bytes(m)
+    wb, hb, gb = weight_bytes(m, S)
     kvb = kv_bytes(m, dr.seqs)
     step_bytes = wb + hb + gb + kvb + S * m.d_model * 2
     round_bytes = N * step_bytes + S * (N + 1) * V * 4
     head_launch_bytes = hb + m.d_hprev * m.d_model * 2 + 2 * S * m.d_model * 4
+    if m.n_centroids:   # the head class times only the candidate-row kernel
+        head_launch_bytes -= m.n_centroids * m.d_model * (4 if m.w_dtype == syn.F32 else 2)
     head_avg_ms = head_ms / max(head_n, 1)
     achieved = head_launch_bytes / (head_avg_ms * 1e-3) / 1e9
+    kernel_name = ("cand_head_kernel (centroid head candidate rows + argmax + post-proj)" if m.n_centroids
+                   else "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)")
     value = S * N / (ms_per_step * 1e-3)
     acc = n_acc.cpu().numpy()
 
@@ -287,13 +298,19 @@ def main():
         "hbm_gbps_round": round_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_round": round_bytes,
-        "roofline": {"bound": "hbm", "kernel": "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)",
+        "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "note": None if args.workload == "c2" else "traffic counters were taken on the c2 workload",
                      "timing": f"HIP events around each head launch over {args.steps} steps after the timed region",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": head_traffic_from_counters(), "bytes_per_launch": head_launch_bytes,
                      "avg_launch_ms": head_avg_ms,
                      "launches": head_n},
+        "roofline_attn": {"bound": "hbm", "kernel": "attn_mm_kernel + merge_kernel (split-K attention, a3)",
+                          "timing": f"HIP events around each attention + merge pair over {n_diag} steps",
+                          "achieved": N * kvb / (breakdown["attn"]["ms_per_step"] * 1e-3) / 1e9,
+                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                          "frac": N * kvb / (breakdown["attn"]["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "bytes_per_round": N * kvb},
         "breakdown": breakdown,
         "accepted_per_round": float(acc.mean()),
     }

@@ -80,6 +80,14 @@ typedef struct mtp_model_desc {
     float embed_scale;    /* token-embedding scale, sqrt(d_model) in [G4] s.4 */
     int32_t max_seqs;     /* largest n_seq of any later call (sizes scratch) */
     int32_t max_steps;    /* largest n_steps / n_draft of any later call */
+    /* Centroid ("ordered embeddings") LM head ([G4] s.3): 0 = the dense tied
+       head.  Otherwise the step's logits are the token-embedding rows of the
+       centroid_top_k best centroids' token lists (n_vocab / n_centroids ids
+       each) applied to f, every other token -1e30.  Requires n_vocab %
+       n_centroids == 0, n_centroids <= 8192, 1 <= centroid_top_k <=
+       min(n_centroids, 64), head_dtype MTP_F32 or MTP_BF16. */
+    int32_t n_centroids;
+    int32_t centroid_top_k;
 } mtp_model_desc;
 
 /* Borrowed device pointers; must stay valid and unchanged for the context's
@@ -98,6 +106,9 @@ typedef struct mtp_weights {
     const float *g_mlp[MTP_MAX_BLOCKS];
     const void *w_up[MTP_MAX_BLOCKS];
     const void *w_down[MTP_MAX_BLOCKS];
+    const void *centroids;          /* [n_centroids, d_model] in w_dtype (centroid head only) */
+    const int32_t *token_ordering;  /* [n_vocab] token ids in [0, n_vocab): centroid c lists entries
+                                       [c*vsc, (c+1)*vsc), vsc = n_vocab / n_centroids (centroid head only) */
 } mtp_weights;
 
 /* One KV source of one sequence, read-only.  K and V hold n_cells cells;

@@ -42,12 +42,14 @@ class ModelDesc(C.Structure):
                                           "d_ff", "n_vocab", "w_dtype", "head_dtype", "kv_dtype", "swa_window")] + \
                [("block_src", C.c_int32 * MAX_BLOCKS)] + \
                [(n, C.c_float) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")] + \
-               [("max_seqs", C.c_int32), ("max_steps", C.c_int32)]
+               [("max_seqs", C.c_int32), ("max_steps", C.c_int32), ("n_centroids", C.c_int32),
+                ("centroid_top_k", C.c_int32)]
 
 
 class Weights(C.Structure):
     _fields_ = [("w_pre", C.c_void_p), ("w_post", C.c_void_p), ("head", C.c_void_p), ("g_final", C.c_void_p)] + \
-               [(n, C.c_void_p * MAX_BLOCKS) for n in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down")]
+               [(n, C.c_void_p * MAX_BLOCKS) for n in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down")] + \
+               [("centroids", C.c_void_p), ("token_ordering", C.c_void_p)]
 
 
 class KVView(C.Structure):
@@ -207,11 +209,12 @@ def mtp_profile_read(ctx: int, cls: int):
 # --------------------------------------------------------------------------- struct builders
 def make_desc(*, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab, w_dtype, head_dtype,
               kv_dtype, swa_window=0, block_src=(), rms_eps=1e-6, rope_theta=10000.0, attn_scale=None,
-              embed_scale=None, max_seqs=1, max_steps=4) -> ModelDesc:
+              embed_scale=None, max_seqs=1, max_steps=4, n_centroids=0, centroid_top_k=0) -> ModelDesc:
     d = ModelDesc()
     for k, v in dict(d_model=d_model, d_hprev=d_hprev, n_blocks=n_blocks, n_head_q=n_head_q, n_head_kv=n_head_kv,
                      head_dim=head_dim, d_ff=d_ff, n_vocab=n_vocab, w_dtype=w_dtype, head_dtype=head_dtype,
-                     kv_dtype=kv_dtype, swa_window=swa_window, max_seqs=max_seqs, max_steps=max_steps).items():
+                     kv_dtype=kv_dtype, swa_window=swa_window, max_seqs=max_seqs, max_steps=max_steps,
+                     n_centroids=n_centroids, centroid_top_k=centroid_top_k).items():
         setattr(d, k, int(v))
     for i in range(MAX_BLOCKS):
         d.block_src[i] = int(block_src[i]) if i < len(block_src) else 0
@@ -222,12 +225,15 @@ def make_desc(*, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff
 
 
 def make_weights(t: Dict[str, object], n_blocks: int) -> Weights:
-    """t maps 'w_pre', 'w_post', 'head', 'g_final' and 'blk{l}.<name>' to device tensors."""
+    """t maps 'w_pre', 'w_post', 'head', 'g_final' and 'blk{l}.<name>' to device tensors
+    (plus 'centroids' and 'token_ordering' for a centroid head)."""
     w = Weights()
     w.w_pre, w.w_post, w.head, w.g_final = (_ptr(t[k]) for k in ("w_pre", "w_post", "head", "g_final"))
     for l in range(n_blocks):
         for k in ("g_attn", "w_q", "g_q", "w_o", "g_mlp", "w_up", "w_down"):
             getattr(w, k)[l] = _ptr(t[f"blk{l}.{k}"])
+    if "centroids" in t:
+        w.centroids, w.token_ordering = _ptr(t["centroids"]), _ptr(t["token_ordering"])
     return w
 
 

@@ -7,6 +7,8 @@
 // their cache residency), several rows in flight per wave, and each workgroup
 // folds its best (value, lowest index) per sequence into one 64-bit key with
 // atomicMax.  Workgroups past n_head_wg compute h' = W_post f instead.
+#include <algorithm>
+
 #include "widen.h"
 
 namespace mtp {
@@ -209,6 +211,178 @@ template <typename HT, bool ONE>
 static hipError_t launch_head_t(const HeadArgs &a, int w_dtype, int n_post_wg, hipStream_t st) {
     return a.conf ? launch_head_c<HT, ONE, true>(a, w_dtype, n_post_wg, st)
                   : launch_head_c<HT, ONE, false>(a, w_dtype, n_post_wg, st);
+}
+
+// ----------------------------------------------------------------------------
+// Centroid head steps 3-5 ("Gemma 4 MTP" s.3): the candidate rows.
+// ----------------------------------------------------------------------------
+// Workgroup = (sequence, chunk of kCandChunk candidate rows).  The lane's
+// slice of f = rmsnorm(x_s; g_final) lives in registers; each wave takes
+// rows two at a time, looks up the token id through the chosen centroid's
+// list, gathers that embedding row with 16-byte loads and reduces the dot
+// across the wave.  Keys, confidence partials and (optionally) the logit
+// scatter follow the dense head.  Workgroups past S * chunks run the
+// post-projection exactly as in head_kernel.
+static constexpr int kCandChunk = 32;
+
+template <typename HT, int NV, bool CONF>
+__global__ __launch_bounds__(256) void cand_head_kernel(HeadArgs a, int w_dtype, int chunks) {
+    constexpr int EPV = WTr<HT>::EPV, CPW = 64 * EPV;
+    constexpr int RU = 2;
+    extern __shared__ float fs[];
+    __shared__ float rs[kMaxSeqGroup];
+    __shared__ uint64_t wbest[4];
+    __shared__ float wcm[4], wcs[4];
+    const int d = a.d, S = a.S;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    if ((int)blockIdx.x >= S * chunks) {         // post-projection rows
+        for (int j = wid; j < S; j += 4) {
+            const float *x = a.x + (int64_t)j * d;
+            float ss = 0.f;
+            for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
+        }
+        __syncthreads();
+        for (int i = tid; i < S * d; i += kBlock) {
+            const int j = i / d, c = i - j * d;
+            fs[i] = a.x[i] * rs[j] * a.g_final[c];
+        }
+        __syncthreads();
+        float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
+        if (w_dtype == MTP_BF16) post_rows<uint16_t>(a, fs, h_out);
+        else post_rows<float>(a, fs, h_out);
+        return;
+    }
+    const int s = blockIdx.x / chunks, ch = blockIdx.x - s * chunks;
+    const int total = a.n_cand * a.vsc;
+    const int r0 = ch * kCandChunk, r1 = min(total, r0 + kCandChunk);
+    const int32_t *cand = a.cand + (int64_t)s * a.n_cand;
+    auto row_of = [&](int r) {                  // ids outside the vocabulary are clamped into it
+        const int q = r / a.vsc;
+        return min(max(a.ordering[(int64_t)cand[q] * a.vsc + (r - q * a.vsc)], 0), a.V - 1);
+    };
+    uint4 wv[RU][NV];
+    int tok[RU];
+    auto load_rows = [&](int rb) {
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int r = rb + 4 * u;
+            tok[u] = r < r1 ? row_of(r) : 0;
+            const HT *er = (const HT *)a.head + (int64_t)tok[u] * d;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int col = v * CPW + lane * EPV;
+                wv[u][v] = (r < r1 && col < d) ? *(const uint4 *)(er + col) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    load_rows(r0 + wid);
+    // f slice of this lane (all waves compute the norm of sequence s)
+    float fr[NV][EPV];
+    {
+        const float *x = a.x + (int64_t)s * d;
+        float ss = 0.f;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int col = v * CPW + lane * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                fr[v][e] = (col < d) ? x[col + e] : 0.f;
+                ss = fmaf(fr[v][e], fr[v][e], ss);
+            }
+        }
+        const float r = 1.0f / sqrtf(wave_sum(ss) / (float)d + a.eps);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int col = v * CPW + lane * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) fr[v][e] = (col < d) ? fr[v][e] * r * a.g_final[col + e] : 0.f;
+        }
+    }
+    float *logits = a.io->out_logits ? a.io->out_logits + ((int64_t)s * a.n_steps + a.step) * a.V : nullptr;
+    uint64_t best = 0ull;
+    float cm = -INFINITY, cs = 0.f;
+    for (int rb = r0 + wid; rb < r1; rb += 4 * RU) {
+        if (rb != r0 + wid) load_rows(rb);
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            const int r = rb + 4 * u;
+            if (r >= r1) break;                  // wave-uniform
+            float acc = 0.f;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float w[EPV];
+                widen(wv[u][v], w);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc = fmaf(w[e], fr[v][e], acc);
+            }
+            const float z = wave_sum(acc);
+            const uint64_t k = argmax_key(z, (uint32_t)tok[u]);
+            best = k > best ? k : best;
+            if (CONF) conf_add(cm, cs, z);
+            if (logits && lane == 0) logits[tok[u]] = z;
+        }
+    }
+    if (lane == 0) {
+        wbest[wid] = best;
+        wcm[wid] = cm;
+        wcs[wid] = cs;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint64_t k = wbest[0];
+        for (int w = 1; w < 4; ++w) k = wbest[w] > k ? wbest[w] : k;
+        atomicMax((unsigned long long *)&a.keys[s], (unsigned long long)k);
+        if (CONF) {
+            float m = wcm[0], sm = wcs[0];
+            for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w], wcs[w]);
+            a.conf[(int64_t)s * kConfSlots + ch] = ConfPart{m, sm};
+        }
+    }
+}
+
+int cand_head_groups(const HeadArgs &a) {
+    return std::min(kConfSlots, (a.n_cand * a.vsc + kCandChunk - 1) / kCandChunk);
+}
+
+template <typename HT, bool CONF>
+static hipError_t launch_cand_t(const HeadArgs &a_in, int w_dtype, int n_post_wg, hipStream_t st) {
+    constexpr int CPW = 64 * WTr<HT>::EPV;
+    HeadArgs a = a_in;
+    const int chunks = cand_head_groups(a);
+    if ((int64_t)chunks * kCandChunk < (int64_t)a.n_cand * a.vsc) return hipErrorInvalidValue;
+    a.n_head_wg = a.S * chunks;                 // post rows follow the candidate workgroups
+    const int nv = (a.d + CPW - 1) / CPW;
+    const size_t lds = sizeof(float) * (size_t)a.S * a.d;
+    const dim3 grid(a.n_head_wg + n_post_wg);
+#define MTP_CAND_CASE(N)                                                                               \
+    if (nv <= N) {                                                                                     \
+        hipError_t e0 = allow_dynamic_lds(cand_head_kernel<HT, N, CONF>, lds);                         \
+        if (e0 != hipSuccess) return e0;                                                               \
+        hipLaunchKernelGGL((cand_head_kernel<HT, N, CONF>), grid, dim3(kBlock), lds, st, a, w_dtype, chunks); \
+        return hipGetLastError();                                                                      \
+    }
+    MTP_CAND_CASE(1)
+    MTP_CAND_CASE(2)
+    MTP_CAND_CASE(4)
+    MTP_CAND_CASE(8)
+#undef MTP_CAND_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_cand_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, bool logits,
+                            hipStream_t st) {
+    if (logits) {
+        const hipError_t e = launch_fill_logits(a.io, a.S, a.n_steps, a.V, a.step, -1e30f, st);
+        if (e != hipSuccess) return e;
+    }
+    const bool conf = a.conf != nullptr;
+    if (head_dtype == MTP_BF16) return conf ? launch_cand_t<uint16_t, true>(a, w_dtype, n_post_wg, st)
+                                            : launch_cand_t<uint16_t, false>(a, w_dtype, n_post_wg, st);
+    if (head_dtype == MTP_F32) return conf ? launch_cand_t<float, true>(a, w_dtype, n_post_wg, st)
+                                           : launch_cand_t<float, false>(a, w_dtype, n_post_wg, st);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, hipStream_t st) {

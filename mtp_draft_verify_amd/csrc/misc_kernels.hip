@@ -101,6 +101,131 @@ hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_
     return hipGetLastError();
 }
 
+// Centroid head step 2 ("Gemma 4 MTP" s.3): the top-k centroids of each
+// sequence, one workgroup per sequence.  Centroid c gets the argmax key
+// (ordered logit << 32 | ~c): larger logit first, lower id first among equal
+// logits, and every key distinct.  A radix select from the top byte down
+// finds the k-th largest key -- per byte, a histogram of the keys that still
+// match the chosen prefix, then one wave scans the 256 bins from the top --
+// stopping as soon as the chosen bin holds exactly the keys still needed.
+// The k keys at or above it are gathered and sorted (bitonic, one wave), so
+// the chosen centroids come out best first whatever order the gather took.
+static constexpr int kTopkPerThread = kMaxCentroids / 256;
+
+__global__ __launch_bounds__(256) void centroid_topk_kernel(const float *cl, int32_t nc, int32_t k, int32_t *cand) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint64_t sel[kMaxCentroidTopK];
+    __shared__ uint64_t s_prefix, s_mask;
+    __shared__ int32_t s_need, s_done, s_nsel;
+    const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    uint64_t key[kTopkPerThread];
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread; ++i) {
+        const int c = tid + 256 * i;
+        key[i] = c < nc ? argmax_key(cl[(int64_t)s * nc + c], (uint32_t)c) : 0ull;
+    }
+    if (tid == 0) {
+        s_prefix = 0ull;
+        s_mask = 0ull;
+        s_need = k;
+        s_done = 0;
+        s_nsel = 0;
+    }
+    for (int shift = 56; shift >= 0; shift -= 8) {
+        hist[tid] = 0u;
+        __syncthreads();
+        const uint64_t prefix = s_prefix, mask = s_mask;
+        if (s_done) break;                       // uniform: read after the barrier
+#pragma unroll
+        for (int i = 0; i < kTopkPerThread; ++i)
+            if (tid + 256 * i < nc && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+        __syncthreads();
+        if (tid < 64) {
+            // lane l holds bins 255-4l .. 252-4l (top down); inclusive scan over lanes
+            uint32_t part = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part += hist[255 - 4 * lane - j];
+            uint32_t cum = part;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_up(cum, off);
+                if (lane >= off) cum += o;
+            }
+            const uint32_t need = (uint32_t)s_need;
+            const uint64_t hit = __ballot(cum >= need);
+            const int l0 = __ffsll((unsigned long long)hit) - 1;     // first lane reaching need
+            if (lane == l0) {
+                uint32_t c = cum - part;                 // keys in higher bins
+                for (int j = 0; j < 4; ++j) {
+                    const int bin = 255 - 4 * lane - j;
+                    const uint32_t h = hist[bin];
+                    if (c + h >= need) {
+                        s_prefix = prefix | ((uint64_t)bin << shift);
+                        s_mask = mask | (255ull << shift);
+                        s_need = (int32_t)(need - c);
+                        s_done = (h == need - c) ? 1 : 0;
+                        break;
+                    }
+                    c += h;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // keys whose masked prefix is at or above the final prefix: exactly k
+    {
+        const uint64_t prefix = s_prefix, mask = s_mask;
+#pragma unroll
+        for (int i = 0; i < kTopkPerThread; ++i)
+            if (tid + 256 * i < nc && (key[i] & mask) >= prefix) {
+                const int slot = atomicAdd(&s_nsel, 1);
+                if (slot < kMaxCentroidTopK) sel[slot] = key[i];
+            }
+    }
+    __syncthreads();
+    if (tid < 64) {
+        uint64_t v = lane < k ? sel[lane] : 0ull;
+        // bitonic sort of 64 keys across the wave, descending
+        for (int size = 2; size <= 64; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const uint32_t lo = __shfl_xor((uint32_t)v, stride), hi = __shfl_xor((uint32_t)(v >> 32), stride);
+                const uint64_t o = ((uint64_t)hi << 32) | lo;
+                const bool desc = (lane & size) == 0;
+                const bool first = (lane & stride) == 0;
+                const bool keep_max = desc == first;
+                v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+            }
+        }
+        if (lane < k) cand[(int64_t)s * k + lane] = key_index(v);
+    }
+}
+
+hipError_t launch_centroid_topk(const float *cl, int32_t n_centroids, int32_t k, int32_t S, int32_t *cand,
+                                hipStream_t st) {
+    if (n_centroids > kMaxCentroids || k < 1 || k > n_centroids || k > kMaxCentroidTopK) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(centroid_topk_kernel, dim3(S), dim3(256), 0, st, cl, n_centroids, k, cand);
+    return hipGetLastError();
+}
+
+// The full logit row of a centroid head starts at -1e30 for every token
+// that is not a candidate ("Gemma 4 MTP" s.3 step 5); only when the caller
+// asked for logits.
+__global__ void fill_logits_kernel(const CallIO *io, int32_t S, int32_t N, int32_t V, int32_t step, float v) {
+    float *z = io->out_logits;
+    if (!z) return;
+    const int64_t n = (int64_t)S * V;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t s = i / V, t = i - s * V;
+        z[(s * N + step) * V + t] = v;
+    }
+}
+
+hipError_t launch_fill_logits(const CallIO *io, int32_t S, int32_t N, int32_t V, int32_t step, float v,
+                              hipStream_t st) {
+    hipLaunchKernelGGL(fill_logits_kernel, dim3(1024), dim3(256), 0, st, io, S, N, V, step, v);
+    return hipGetLastError();
+}
+
 // RoPE frequencies theta^(-2i/hd), i < hd/2, in fp64 (once per context)
 __global__ void rope_init_kernel(double *inv_freq, int32_t hd, double theta) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;

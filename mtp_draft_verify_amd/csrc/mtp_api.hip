@@ -68,6 +68,8 @@ struct mtp_ctx {
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
     float *sink = nullptr;              // [64] stores that carry nothing land here
     ConfPart *conf_part = nullptr;      // [max_steps][max_seqs][kConfSlots] confidence partials
+    float *cl = nullptr;                // [max_seqs, n_centroids] centroid logits (centroid head)
+    int32_t *cand = nullptr;            // [max_seqs, centroid_top_k] chosen centroids
     uint64_t *dkeys = nullptr;          // [2][max_seqs]
     double *inv_freq = nullptr;         // [head_dim / 2] RoPE frequencies
     int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
@@ -143,6 +145,12 @@ extern "C" int mtp_check_desc(const mtp_model_desc *d) {
     if (swa && d->swa_window <= 0) return MTP_E_SHAPE;
     if (!(d->rms_eps >= 0.f) || !(d->attn_scale > 0.f) || !(d->rope_theta > 0.f) || !std::isfinite(d->embed_scale))
         return MTP_E_INVAL;
+    if (d->n_centroids < 0) return MTP_E_SHAPE;
+    if (d->n_centroids > 0) {
+        if (d->n_centroids > kMaxCentroids || d->n_vocab % d->n_centroids) return MTP_E_SHAPE;
+        if (d->centroid_top_k < 1 || d->centroid_top_k > std::min(d->n_centroids, kMaxCentroidTopK)) return MTP_E_SHAPE;
+        if (d->head_dtype == MTP_Q8_0) return MTP_E_DTYPE;
+    }
     return MTP_OK;
 }
 
@@ -157,6 +165,7 @@ static int check_weights(const mtp_model_desc *d, const mtp_weights *w) {
             if (!p || !aligned16(p)) return MTP_E_INVAL;
         if (!w->g_attn[l] || !w->g_q[l] || !w->g_mlp[l]) return MTP_E_INVAL;
     }
+    if (d->n_centroids > 0 && (!w->centroids || !aligned16(w->centroids) || !w->token_ordering)) return MTP_E_INVAL;
     return MTP_OK;
 }
 
@@ -167,7 +176,7 @@ static void free_ctx(mtp_ctx *c) {
         (void)hipGraphDestroy(g.g);
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
@@ -228,6 +237,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
              dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64) &&
              dalloc(&c->conf_part, (size_t)d.max_steps * S * kConfSlots);
+        if (ok && d.n_centroids > 0)
+            ok = dalloc(&c->cl, S * d.n_centroids) && dalloc(&c->cand, S * d.centroid_top_k);
         c->block_bytes = sizeof(CallIO) + sizeof(SeqParams) * S;
         ok = ok && dalloc(&c->d_block, c->block_bytes);
         if (ok && d.head_dtype == MTP_Q8_0)
@@ -451,6 +462,15 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 e = run_gemv(c, IN_PLAIN, EPI_ADD, gd, st);
             }
         }
+        // a6 (centroid head): centroid logits C rmsnorm(x; g_final), top-k
+        if (e == hipSuccess && d.n_centroids > 0) {
+            GemvArgs gc{};
+            gc.W = c->w.centroids; gc.M = d.n_centroids; gc.K = D; gc.S = S;
+            gc.src = c->x; gc.src_stride = D; gc.gain = c->w.g_final; gc.eps = d.rms_eps;
+            gc.dst = c->cl; gc.dst_stride = d.n_centroids;
+            e = run_gemv(c, IN_NORM, EPI_STORE, gc, st);
+            if (e == hipSuccess) e = launch_centroid_topk(c->cl, d.n_centroids, d.centroid_top_k, S, c->cand, st);
+        }
         // a6 + a7: final norm, LM head + argmax, post-projection
         if (e == hipSuccess) {
             HeadArgs ha{};
@@ -470,10 +490,17 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             ha.conf = sh.conf ? c->conf_part + (size_t)k * d.max_seqs * kConfSlots : nullptr;
             const int n_post_wg = (DH + ha.post_rows_per_wg - 1) / ha.post_rows_per_wg;
             ProfScope ps(c, MTP_PROF_HEAD);
-            const bool mm = mm_head_supported(d.head_dtype, d.w_dtype, ha);
-            n_part = mm ? mm_head_groups(ha) : ha.n_head_wg;
-            e = mm ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
-                   : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
+            if (d.n_centroids > 0) {
+                ha.cand = c->cand; ha.ordering = c->w.token_ordering;
+                ha.n_cand = d.centroid_top_k; ha.vsc = V / d.n_centroids;
+                n_part = cand_head_groups(ha);
+                e = launch_cand_head(d.head_dtype, d.w_dtype, ha, n_post_wg, sh.logits, st);
+            } else {
+                const bool mm = mm_head_supported(d.head_dtype, d.w_dtype, ha);
+                n_part = mm ? mm_head_groups(ha) : ha.n_head_wg;
+                e = mm ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
+                       : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
+            }
         }
     }
     if (e == hipSuccess)

@@ -105,7 +105,14 @@ struct HeadArgs {
     float *h_out;           // [S, dh] context buffer (the last step writes io->out_h_last when given)
     float *sink;            // [64] target of stores that carry nothing (matrix-core head)
     ConfPart *conf;         // this step's confidence partials [S][kConfSlots] (or null)
+    // centroid head: candidate rows of sequence s are ordering[cand[s, i] * vsc + r]
+    const int32_t *cand;    // [S, n_cand] chosen centroids
+    const int32_t *ordering;
+    int32_t n_cand, vsc;
 };
+
+static constexpr int kMaxCentroids = 8192;
+static constexpr int kMaxCentroidTopK = 64;
 
 struct AttnArgs {
     const float *q;         // [S, Hq*hd] raw projections
@@ -137,6 +144,15 @@ hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
 hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_t n_part, int64_t step_stride,
                               const CallIO *io, hipStream_t st);
 hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st);
+
+// centroid LM head: top-k centroids per sequence, then the candidate rows
+hipError_t launch_centroid_topk(const float *cl, int32_t n_centroids, int32_t k, int32_t S, int32_t *cand,
+                                hipStream_t st);
+int cand_head_groups(const HeadArgs &a);    // candidate workgroups per sequence (confidence partials)
+hipError_t launch_fill_logits(const CallIO *io, int32_t S, int32_t N, int32_t V, int32_t step, float v,
+                              hipStream_t st);
+hipError_t launch_cand_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, bool logits,
+                            hipStream_t st);
 
 // several sequences: GEMVs and the LM head on the matrix cores
 static constexpr int kMmMinSeqs = 2;

@@ -28,7 +28,8 @@ def upload_model(m: syn.Model, device, max_seqs: int, max_steps: int):
                          n_head_kv=m.n_head_kv, head_dim=m.head_dim, d_ff=m.d_ff, n_vocab=m.n_vocab,
                          w_dtype=m.w_dtype, head_dtype=m.head_dtype, kv_dtype=m.kv_dtype, swa_window=m.swa_window,
                          block_src=m.block_src, rms_eps=m.rms_eps, rope_theta=m.rope_theta,
-                         attn_scale=m.attn_scale, embed_scale=m.embed_scale, max_seqs=max_seqs, max_steps=max_steps)
+                         attn_scale=m.attn_scale, embed_scale=m.embed_scale, max_seqs=max_seqs, max_steps=max_steps,
+                         n_centroids=m.n_centroids, centroid_top_k=m.centroid_top_k)
     w = mtp.make_weights(t, m.n_blocks)
     return desc, w, t
 

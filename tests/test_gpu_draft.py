@@ -179,3 +179,24 @@ def test_captured_chain_replays_match_direct_launches():
             assert np.array_equal(replay[k], direct[k]), (shift, k)
         outs.append(replay["drafts"])
     assert not all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_centroid_head_full_size_matches_oracle(orc):
+    log("case c6: centroid head, 2048 centroids x 128 ids, top 32; bf16 c2 drafter, ctx 8192, S=1 N=3")
+    w = syn.c6_centroid()
+    g = GpuDrafter(w.model, 1, 3)
+    gpu = g.run(w.draft)
+    o = orc.draft_block(w.model, w.draft)
+    _check(w, gpu, o)
+    # the full logit row: -1e30 outside the candidates, as the verifier expects
+    assert (gpu["logits"] == np.float32(-1e30)).sum() == (o["logits"] == np.float32(-1e30)).sum()
+
+
+def test_centroid_head_several_sequences_with_confidence(orc):
+    log("case c6 small: centroid head, S=3, N=2, ctx 1000 (+confidence)")
+    w = syn.c6_centroid(n_seq=3, n_steps=2, ctx=1000)
+    g = GpuDrafter(w.model, 3, 2)
+    gpu = g.run(w.draft, conf=True)
+    o = orc.draft_block(w.model, w.draft)
+    _check(w, gpu, o)
+    np.testing.assert_allclose(gpu["conf"], o["conf"], rtol=1e-3)
