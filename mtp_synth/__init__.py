@@ -32,7 +32,7 @@ from typing import Dict, List, Optional
 import numpy as np
 
 F32, BF16, Q8_0 = 0, 1, 2
-KV_FULL, KV_SWA = 0, 1
+KV_FULL, KV_SWA, KV_SINK_WINDOW = 0, 1, 2
 DTYPE_NAMES = {F32: "f32", BF16: "bf16", Q8_0: "q8_0"}
 
 
@@ -128,6 +128,8 @@ class Model:
     embed_scale: float = 0.0     # 0 -> sqrt(d_model)
     n_centroids: int = 0         # centroid LM head: 0 = dense tied head
     centroid_top_k: int = 0
+    sw_window: int = 0           # sink + window source: window length
+    sw_sink: int = 0             #   and sink cells
     weights: Dict[str, np.ndarray] = field(default_factory=dict)
 
     def __post_init__(self):
@@ -202,9 +204,10 @@ class KVSource:
 
 @dataclass
 class Seq:
-    src: List[Optional[KVSource]]   # [full, swa]
+    src: List[Optional[KVSource]]   # [full, swa, sink + window]
     attn_pos: int
     pos0: int
+    run_lo: int = 0                 # first valid cell of the sink + window source
 
 
 @dataclass
@@ -223,7 +226,7 @@ def make_kv(seed: int, name: str, n_cells: int, m: Model, fill_cells: Optional[i
 
 
 def make_draft_inputs(seed: int, m: Model, ctx_lens, n_steps: int, *, full_cap=None, swa_cells=None,
-                      share_kv: bool = False) -> DraftInputs:
+                      share_kv: bool = False, run_lo=None) -> DraftInputs:
     """Sequences with context lengths ctx_lens (attn_pos = ctx-1, pos0 = ctx).
 
     full_cap: cells in each sequence's full-attention source (default max ctx).
@@ -232,13 +235,16 @@ def make_draft_inputs(seed: int, m: Model, ctx_lens, n_steps: int, *, full_cap=N
     """
     S = len(ctx_lens)
     need_swa = KV_SWA in m.block_src[:m.n_blocks]
+    need_sw = KV_SINK_WINDOW in m.block_src[:m.n_blocks]
     full_cap = full_cap or max(ctx_lens)
     seqs = []
     shared = make_kv(seed, "kv.full", full_cap, m) if share_kv else None
     for s, ctx in enumerate(ctx_lens):
         full = shared if share_kv else make_kv(seed, f"kv.full.{s}", full_cap, m)
         swa = make_kv(seed, f"kv.swa.{s}", swa_cells or m.swa_window, m) if need_swa else None
-        seqs.append(Seq([full, swa], attn_pos=int(ctx) - 1, pos0=int(ctx)))
+        sw = make_kv(seed, f"kv.sw.{s}", full_cap, m) if need_sw else None
+        seqs.append(Seq([full, swa, sw], attn_pos=int(ctx) - 1, pos0=int(ctx),
+                        run_lo=int(run_lo[s]) if run_lo is not None else 0))
     last_tok = rng_for(seed, "last_tok").integers(0, m.n_vocab, size=S, dtype=np.int64).astype(np.int32)
     h_prev = normal(seed, "h_prev", (S, m.d_hprev))
     return DraftInputs(seqs, last_tok, h_prev, n_steps)
@@ -435,8 +441,29 @@ def c6_centroid(seed: int = 1, **over) -> Workload:
     return Workload("c6_centroid_head_bf16", m, dr, gv, p_accept=0.8)
 
 
+def c7_sink_window(seed: int = 1, data_seed: int = 5, **over) -> Workload:
+    """The c2 drafter with every block reading a sink + window source: 64 sink
+    cells plus a 256-position window over a 12000-cell cache; 8 sequences
+    with ctx ~ U{2000..12000}, half of them with a valid run that starts
+    inside the window (a recent prefill of fewer rows than the window), B=4."""
+    shape = dict(C2_SHAPE)
+    shape.update({k: v for k, v in over.items() if k in shape})
+    m = make_model(seed, **shape, w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16,
+                   block_src=[KV_SINK_WINDOW] * shape["n_blocks"], head_std=1.0 / math.sqrt(1024))
+    m.sw_window, m.sw_sink = over.get("sw_window", 256), over.get("sw_sink", 64)
+    S = over.get("n_seq", 8)
+    lo, hi = over.get("ctx_range", (2000, 12000))
+    r = rng_for(data_seed, "c7.ctx")
+    ctx = r.integers(lo, hi + 1, size=S)
+    run = [int(c) - int(r.integers(1, m.sw_window)) if s % 2 else 0 for s, c in enumerate(ctx)]
+    N = over.get("n_steps", 3)
+    dr = make_draft_inputs(data_seed, m, list(ctx), N, full_cap=over.get("full_cap", hi), run_lo=run)
+    gv = make_greedy_verify(data_seed, S, N, m.n_vocab, 0.8, "max5")
+    return Workload("c7_sink_window", m, dr, gv, p_accept=0.8)
+
+
 CONFIGS = {"c1": c1_tiny, "c2": c2_gemma_bf16, "c3": c3_interleaved, "c4": c4_longctx_q8, "c5": c5_sample,
-           "c6": c6_centroid}
+           "c6": c6_centroid, "c7": c7_sink_window}
 
 
 # ----------------------------------------------------------------------------

@@ -122,30 +122,69 @@ static void gemv_batch(const void *W, int32_t dtype, int64_t rows, int64_t cols,
    and its mask admits every position <= attn_pos.  A sliding-window source
    holds position p at ring cell p mod n_cells and admits the last swa_window
    positions up to attn_pos.  o_h = sum_c softmax_c(scale * q_h . K_c) V_c. */
+int64_t orc_visible_cells(const orc_model *m, const orc_seq *seq, int32_t src, int64_t *cells, int64_t cap) {
+    const orc_kv *kv = &seq->src[src];
+    const int64_t hi = seq->attn_pos;
+    int64_t n = 0;
+    if (hi < 0 || !kv->k || !kv->v) return -1;
+    if (src == ORC_SRC_FULL) {
+        if (hi >= kv->n_cells) return -2;
+        for (int64_t p = 0; p <= hi; ++p) {
+            if (n >= cap) return -3;
+            cells[n++] = p;
+        }
+    } else if (src == ORC_SRC_SWA) {
+        if (m->swa_window <= 0 || kv->n_cells < m->swa_window) return -2;
+        int64_t lo = hi - m->swa_window + 1;
+        if (lo < 0) lo = 0;
+        for (int64_t p = lo; p <= hi; ++p) {
+            if (n >= cap) return -3;
+            cells[n++] = p % kv->n_cells;
+        }
+    } else if (src == ORC_SRC_SINK_WINDOW) {
+        /* the draft attention's id list [0 .. min(sink, first) - 1] ++
+           [first .. cell0], first moved up to the valid run's start */
+        if (m->sw_window <= 0 || m->sw_sink < 0 || hi >= kv->n_cells) return -2;
+        int64_t first = hi - m->sw_window + 1;
+        if (first < seq->run_lo) first = seq->run_lo;
+        if (first < 0) first = 0;
+        if (first > hi) return -2;
+        const int64_t ns = m->sw_sink < first ? m->sw_sink : first;
+        for (int64_t p = 0; p < ns; ++p) {
+            if (n >= cap) return -3;
+            cells[n++] = p;
+        }
+        for (int64_t p = first; p <= hi; ++p) {
+            if (n >= cap) return -3;
+            cells[n++] = p;
+        }
+    } else {
+        return -1;
+    }
+    return n;
+}
+
 int orc_attend_group(const orc_model *m, const orc_seq *seq, int32_t src, int32_t kvh, const double *q_group,
                      double *o_group) {
     const orc_kv *kv = &seq->src[src];
     const int32_t hd = m->head_dim, g = m->n_head_q / m->n_head_kv;
-    int64_t hi = seq->attn_pos, lo = 0;
-    if (hi < 0 || !kv->k || !kv->v) return -1;
-    if (src == ORC_SRC_FULL) {
-        if (hi >= kv->n_cells) return -2;
-    } else {
-        if (m->swa_window <= 0 || kv->n_cells < m->swa_window) return -2;
-        lo = hi - m->swa_window + 1;
-        if (lo < 0) lo = 0;
+    const int64_t cap = (int64_t)seq->attn_pos + 1;
+    if (cap <= 0) return -1;
+    int64_t *cells = (int64_t *)malloc(sizeof(int64_t) * (size_t)cap);
+    if (!cells) return -4;
+    const int64_t n = orc_visible_cells(m, seq, src, cells, cap);
+    if (n <= 0) {
+        free(cells);
+        return n < 0 ? (int)n : -2;
     }
-    const int64_t n = hi - lo + 1;
     double *sc = (double *)malloc(sizeof(double) * (size_t)(n * g));
-    if (!sc) return -4;
-    for (int64_t p = lo; p <= hi; ++p) {
-        int64_t cell = (src == ORC_SRC_FULL) ? p : p % kv->n_cells;
+    if (!sc) { free(cells); return -4; }
+    for (int64_t c = 0; c < n; ++c)
         for (int32_t j = 0; j < g; ++j) {
             double dot = 0.0;
-            for (int32_t i = 0; i < hd; ++i) dot += q_group[j * hd + i] * kv_load(m, kv, kv->k, cell, kvh, i);
-            sc[j * n + (p - lo)] = dot * m->attn_scale;
+            for (int32_t i = 0; i < hd; ++i) dot += q_group[j * hd + i] * kv_load(m, kv, kv->k, cells[c], kvh, i);
+            sc[j * n + c] = dot * m->attn_scale;
         }
-    }
     for (int32_t j = 0; j < g; ++j) {
         double mx = -INFINITY;
         for (int64_t c = 0; c < n; ++c) mx = fmax(mx, sc[j * n + c]);
@@ -155,14 +194,14 @@ int orc_attend_group(const orc_model *m, const orc_seq *seq, int32_t src, int32_
             den += sc[j * n + c];
         }
         for (int32_t i = 0; i < hd; ++i) o_group[j * hd + i] = 0.0;
-        for (int64_t p = lo; p <= hi; ++p) {
-            int64_t cell = (src == ORC_SRC_FULL) ? p : p % kv->n_cells;
-            double wgt = sc[j * n + (p - lo)];
-            for (int32_t i = 0; i < hd; ++i) o_group[j * hd + i] += wgt * kv_load(m, kv, kv->v, cell, kvh, i);
+        for (int64_t c = 0; c < n; ++c) {
+            const double wgt = sc[j * n + c];
+            for (int32_t i = 0; i < hd; ++i) o_group[j * hd + i] += wgt * kv_load(m, kv, kv->v, cells[c], kvh, i);
         }
         for (int32_t i = 0; i < hd; ++i) o_group[j * hd + i] /= den;
     }
     free(sc);
+    free(cells);
     return 0;
 }
 

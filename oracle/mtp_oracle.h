@@ -22,7 +22,7 @@ extern "C" {
 #endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q8_0 = 2 };
-enum { ORC_SRC_FULL = 0, ORC_SRC_SWA = 1 };
+enum { ORC_SRC_FULL = 0, ORC_SRC_SWA = 1, ORC_SRC_SINK_WINDOW = 2 };
 enum { ORC_STREAM_ACCEPT = 0, ORC_STREAM_RESIDUAL = 1, ORC_STREAM_BONUS = 2 };
 #define ORC_MAX_BLOCKS 8
 
@@ -33,6 +33,8 @@ typedef struct {
     double rms_eps, rope_theta, attn_scale, embed_scale;
     /* centroid ("ordered embeddings") LM head: 0 = dense tied head */
     int32_t n_centroids, centroid_top_k;
+    /* sink + window source: window length and sink cells */
+    int32_t sw_window, sw_sink;
 } orc_model;
 
 typedef struct {
@@ -49,7 +51,16 @@ typedef struct {
 } orc_weights;
 
 typedef struct { const void *k, *v; int64_t n_cells, cell_stride; } orc_kv;
-typedef struct { orc_kv src[2]; int32_t attn_pos, pos0; } orc_seq;
+/* src[ORC_SRC_*]; run_lo = first cell of the valid run of a sink + window
+   source (cells below it, outside the sink, are stale) */
+typedef struct { orc_kv src[3]; int32_t attn_pos, pos0, run_lo; } orc_seq;
+
+/* Cells a block attends to, in order; returns the count (<= cap) or < 0.
+   full: 0..attn_pos.  SWA ring: positions max(0, attn_pos-W+1)..attn_pos at
+   cell p mod n_cells.  sink + window ("opus-mtp-turbo" report s.2): first =
+   max(attn_pos - W + 1, run_lo, 0), cells [0, min(sink, first)) ++
+   [first, attn_pos]. */
+int64_t orc_visible_cells(const orc_model *m, const orc_seq *seq, int32_t src, int64_t *cells, int64_t cap);
 
 typedef struct {
     double temp, top_p, min_p, rep_penalty, presence_penalty, freq_penalty;

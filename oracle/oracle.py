@@ -38,7 +38,8 @@ class OrcModel(C.Structure):
                                           "d_ff", "n_vocab", "w_dtype", "head_dtype", "kv_dtype", "swa_window")] + \
                [("block_src", C.c_int32 * MAXB)] + \
                [(n, C.c_double) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")] + \
-               [("n_centroids", C.c_int32), ("centroid_top_k", C.c_int32)]
+               [("n_centroids", C.c_int32), ("centroid_top_k", C.c_int32), ("sw_window", C.c_int32),
+                ("sw_sink", C.c_int32)]
 
 
 class OrcWeights(C.Structure):
@@ -52,7 +53,7 @@ class OrcKV(C.Structure):
 
 
 class OrcSeq(C.Structure):
-    _fields_ = [("src", OrcKV * 2), ("attn_pos", C.c_int32), ("pos0", C.c_int32)]
+    _fields_ = [("src", OrcKV * 3), ("attn_pos", C.c_int32), ("pos0", C.c_int32), ("run_lo", C.c_int32)]
 
 
 class OrcSampler(C.Structure):
@@ -86,6 +87,8 @@ def lib():
         L.orc_uniform.argtypes = [C.c_uint64] * 6
         L.orc_draft_block.argtypes = [C.POINTER(OrcModel), C.POINTER(OrcWeights), C.c_int32, P, P, P, C.c_int32,
                                       P, P, P, P, P]
+        L.orc_visible_cells.restype = C.c_int64
+        L.orc_visible_cells.argtypes = [C.POINTER(OrcModel), P, C.c_int32, P, C.c_int64]
         L.orc_centroid_logits.restype = C.c_double
         L.orc_centroid_logits.argtypes = [C.POINTER(OrcModel), C.POINTER(OrcWeights), P, P]
         L.orc_confidence.restype = C.c_double
@@ -117,6 +120,7 @@ def orc_model(m: syn.Model) -> OrcModel:
         om.block_src[l] = m.block_src[l] if l < len(m.block_src) else 0
     om.rms_eps, om.rope_theta, om.attn_scale, om.embed_scale = m.rms_eps, m.rope_theta, m.attn_scale, m.embed_scale
     om.n_centroids, om.centroid_top_k = m.n_centroids, m.centroid_top_k
+    om.sw_window, om.sw_sink = m.sw_window, m.sw_sink
     return om
 
 
@@ -141,7 +145,7 @@ def orc_seqs(m: syn.Model, seqs) -> C.Array:
                 arr[i].src[j].k, arr[i].src[j].v = _p(src.k), _p(src.v)
                 arr[i].src[j].n_cells = src.n_cells
                 arr[i].src[j].cell_stride = m.n_head_kv * m.head_dim
-        arr[i].attn_pos, arr[i].pos0 = s.attn_pos, s.pos0
+        arr[i].attn_pos, arr[i].pos0, arr[i].run_lo = s.attn_pos, s.pos0, s.run_lo
     return arr
 
 
@@ -177,6 +181,17 @@ def centroid_logits(m: syn.Model, f: np.ndarray):
     z = np.zeros(m.n_vocab, np.float32)
     margin = lib().orc_centroid_logits(C.byref(om), C.byref(ow), _p(f), _p(z))
     return z, margin
+
+
+def visible_cells(m: syn.Model, seq, src: int) -> np.ndarray:
+    om = orc_model(m)
+    sa = orc_seqs(m, [seq])
+    cap = seq.attn_pos + 1
+    cells = np.zeros(max(cap, 1), np.int64)
+    n = lib().orc_visible_cells(C.byref(om), C.cast(sa, C.c_void_p), src, _p(cells), cap)
+    if n < 0:
+        raise RuntimeError(f"orc_visible_cells failed: {n}")
+    return cells[:n]
 
 
 def confidence(z: np.ndarray) -> float:

@@ -110,9 +110,11 @@ def _attn_model(Hq=4, Hkv=2, hd=4, swa=0):
     return toys.blank_model(Hq=Hq, Hkv=Hkv, hd=hd, swa_window=swa)
 
 
-def _seq(m, k, v, attn_pos, src=syn.KV_FULL):
+def _seq(m, k, v, attn_pos, src=syn.KV_FULL, run_lo=0):
     kv = syn.KVSource(np.ascontiguousarray(k, np.float32), np.ascontiguousarray(v, np.float32))
-    return syn.Seq([kv, None] if src == syn.KV_FULL else [None, kv], attn_pos=attn_pos, pos0=attn_pos + 1)
+    srcs = [None, None, None]
+    srcs[src] = kv
+    return syn.Seq(srcs, attn_pos=attn_pos, pos0=attn_pos + 1, run_lo=run_lo)
 
 
 def test_attention_one_visible_cell_returns_its_value_row(orc):
@@ -135,6 +137,67 @@ def test_attention_equal_keys_or_zero_query_average_the_values(orc):
     k = r.standard_normal((n, 2, 4))
     o = orc.attend_group(m, _seq(m, k, v, 20), syn.KV_FULL, 1, np.zeros((2, 4)))
     np.testing.assert_allclose(o[0], v[:21, 1].astype(np.float64).mean(0), rtol=1e-12)
+
+
+def test_sink_window_visible_cells_hand_cases(orc):
+    """Sink + window source ("opus-mtp-turbo" report s.2): the draft attends to
+    [0 .. min(sink, first) - 1] ++ [first .. attn_pos] with first moved up to
+    the valid run's start; short contexts give one contiguous run, no cell
+    twice."""
+    m = _attn_model()
+    m.sw_window, m.sw_sink = 256, 64
+    k = np.zeros((1200, 2, 4))
+    def cells(attn_pos, run_lo=0, sink=64):
+        m.sw_sink = sink
+        return orc.visible_cells(m, _seq(m, k, k, attn_pos, syn.KV_SINK_WINDOW, run_lo), syn.KV_SINK_WINDOW).tolist()
+    assert cells(1000) == list(range(64)) + list(range(745, 1001))
+    assert cells(1000, run_lo=900) == list(range(64)) + list(range(900, 1001))
+    assert cells(1000, run_lo=10) == list(range(64)) + list(range(745, 1001))
+    assert cells(100) == list(range(101))
+    assert cells(300) == list(range(301))
+    assert cells(1000, sink=0) == list(range(745, 1001))
+    assert cells(1000, run_lo=20, sink=64) == list(range(64)) + list(range(745, 1001))
+    assert cells(200, run_lo=150) == list(range(64)) + list(range(150, 201))
+
+
+def test_sink_window_equal_keys_average_exactly_the_visible_values(orc):
+    """Equal keys give uniform weights: the output is the mean of the value
+    rows of the sink and the window, and stale cells (NaN) are never read."""
+    m = _attn_model()
+    m.sw_window, m.sw_sink = 16, 4
+    r = np.random.default_rng(9)
+    n = 64
+    k = np.tile(r.standard_normal((1, 2, 4)), (n, 1, 1))
+    v = r.standard_normal((n, 2, 4)).astype(np.float32)
+    k[4:40], v[4:40] = np.nan, np.nan           # between the sink and the valid run: stale
+    k[51:], v[51:] = np.nan, np.nan             # past attn_pos
+    o = orc.attend_group(m, _seq(m, k, v, 50, syn.KV_SINK_WINDOW, run_lo=40), syn.KV_SINK_WINDOW, 1,
+                         r.standard_normal((2, 4)))
+    want = np.concatenate([v[0:4, 1], v[40:51, 1]]).astype(np.float64).mean(0)
+    np.testing.assert_allclose(o, np.tile(want, (2, 1)), rtol=1e-12)
+
+
+def test_sink_window_without_sink_equals_a_sliding_window_ring(orc):
+    """With no sink and no stale cells, a sink + window block over a full cache
+    attends to the same positions as an SWA block over a ring of capacity W
+    holding them (cell p mod W): the chains agree bit for bit."""
+    W, ctx = 8, 21
+    m = toys.blank_model(d=8, dh=8, V=16, swa_window=W, block_src=[syn.KV_SWA])
+    m.sw_window, m.sw_sink = W, 0
+    r = np.random.default_rng(4)
+    k = r.standard_normal((ctx, m.n_head_kv, m.head_dim)).astype(np.float32)
+    v = r.standard_normal((ctx, m.n_head_kv, m.head_dim)).astype(np.float32)
+    ring_k, ring_v = np.zeros((W,) + k.shape[1:], np.float32), np.zeros((W,) + v.shape[1:], np.float32)
+    for p in range(ctx):
+        ring_k[p % W], ring_v[p % W] = k[p], v[p]
+    lt, hp = np.array([3], np.int32), r.standard_normal((1, 8)).astype(np.float32)
+    swa = syn.DraftInputs([syn.Seq([None, syn.KVSource(ring_k, ring_v), None], ctx - 1, ctx)], lt, hp, 3)
+    a = orc.draft_block(m, swa)
+    m.block_src = [syn.KV_SINK_WINDOW]
+    sw = syn.DraftInputs([syn.Seq([None, None, syn.KVSource(k, v)], ctx - 1, ctx)], lt, hp, 3)
+    b = orc.draft_block(m, sw)
+    for key in ("drafts", "logits", "h_last"):
+        assert np.array_equal(a[key], b[key]), key
 
 
 def test_attention_two_cells_logistic_weights_and_scale(orc):
