@@ -62,8 +62,11 @@ def kv_bytes(m, seqs):
         for l in range(m.n_blocks):
             if m.block_src[l] == syn.KV_FULL:
                 n_vis = s.attn_pos + 1
-            else:
+            elif m.block_src[l] == syn.KV_SWA:
                 n_vis = s.attn_pos - max(0, s.attn_pos - m.swa_window + 1) + 1
+            else:   # sink + window: [0, min(sink, first)) ++ [first, attn_pos]
+                first = max(s.attn_pos - m.sw_window + 1, s.run_lo, 0)
+                n_vis = min(m.sw_sink, first) + s.attn_pos - first + 1
             tot += n_vis * m.n_head_kv * m.head_dim * 2 * es
     return tot
 
@@ -119,6 +122,9 @@ WORKLOADS = {
            "temp 0.6, top-p 0.95, min-p 0.05, repetition 1.08, presence 0.4 over the last 64 tokens"),
     "c6": ("c6_centroid", "the c2 drafter with a centroid LM head: 2048 centroids x 128 token ids, top 32 "
            "centroids (4096 candidate rows) per step; full KV 8192; 1 sequence, B=4 + greedy verify"),
+    "c7": ("c7_sink_window", "the c2 drafter with every block reading a sink + window source (64 sink cells + "
+           "a 256-position window over a 12000-cell cache, half the sequences with a valid run starting inside "
+           "the window); 8 sequences, B=4 + greedy verify"),
 }
 
 

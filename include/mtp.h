@@ -16,8 +16,9 @@
  *   [MTP] "MTP decoding (--mtp)": "How it is wired" (greedy acceptance of the
  *         longest argmax-matching prefix; the free token of the first
  *         unverified row; next h_prev from row min(n_accepted, n_rows-1)).
- *   [AUD] "opus-mtp-turbo: Track 1 report": s.4 (exact temperature>0
- *         speculative sampling, sampling chain order).
+ *   [AUD] "opus-mtp-turbo: Track 1 report": findings item 2 (sink +
+ *         window draft attention over the drafter's valid cell run), s.4
+ *         (exact temperature>0 speculative sampling, sampling chain order).
  *
  * Conventions for every entry point
  *   - All tensors are caller-owned DEVICE memory unless marked "host".  The
@@ -60,8 +61,12 @@ typedef enum mtp_status {
 typedef enum mtp_dtype { MTP_F32 = 0, MTP_BF16 = 1, MTP_Q8_0 = 2 } mtp_dtype;
 
 /* KV source kinds ([G4] s.1 twist 2: each drafter block reads the last target
-   layer of its own attention type) */
-typedef enum mtp_src { MTP_SRC_FULL = 0, MTP_SRC_SWA = 1 } mtp_src;
+   layer of its own attention type).  MTP_SRC_SINK_WINDOW is the attention
+   sink + sliding window of [AUD] item 2: the drafter sees
+   the first sw_sink positions and the last sw_window positions of a linear
+   cache, the window starting no earlier than the sequence's valid run. */
+typedef enum mtp_src { MTP_SRC_FULL = 0, MTP_SRC_SWA = 1, MTP_SRC_SINK_WINDOW = 2 } mtp_src;
+#define MTP_N_SRC 3
 
 /* Drafter description ([G4] s.3-4).  d_hprev is the target's backbone width
    (n_embd_backbone); the pre-projection maps [embed_scale*E[tok]; h_prev]
@@ -73,7 +78,7 @@ typedef struct mtp_model_desc {
     int32_t head_dtype;   /* MTP_F32 | MTP_BF16 | MTP_Q8_0: tied LM head = token embedding [n_vocab, d_model] */
     int32_t kv_dtype;     /* MTP_F32 | MTP_BF16: target K and V */
     int32_t swa_window;   /* positions visible through an SWA source (0: no SWA block) */
-    int32_t block_src[MTP_MAX_BLOCKS];   /* MTP_SRC_FULL or MTP_SRC_SWA per block */
+    int32_t block_src[MTP_MAX_BLOCKS];   /* an mtp_src per block */
     float rms_eps;        /* RMSNorm epsilon */
     float rope_theta;     /* RoPE base (half-split pairs (i, i + head_dim/2)) */
     float attn_scale;     /* softmax scale, normally 1/sqrt(head_dim) */
@@ -88,6 +93,10 @@ typedef struct mtp_model_desc {
        min(n_centroids, 64), head_dtype MTP_F32 or MTP_BF16. */
     int32_t n_centroids;
     int32_t centroid_top_k;
+    /* Sink + window source (MTP_SRC_SINK_WINDOW blocks only): window length
+       (> 0) and number of leading sink positions (>= 0). */
+    int32_t sw_window;
+    int32_t sw_sink;
 } mtp_model_desc;
 
 /* Borrowed device pointers; must stay valid and unchanged for the context's
@@ -113,8 +122,8 @@ typedef struct mtp_weights {
 
 /* One KV source of one sequence, read-only.  K and V hold n_cells cells;
    cell c of kv head j starts at element c*cell_stride + j*head_dim.  A full
-   source holds position p at cell p; an SWA ring holds position p at cell
-   p mod n_cells (n_cells >= swa_window). */
+   or sink + window source holds position p at cell p; an SWA ring holds
+   position p at cell p mod n_cells (n_cells >= swa_window). */
 typedef struct mtp_kv_view {
     const void *k, *v;
     int64_t n_cells;
@@ -122,12 +131,18 @@ typedef struct mtp_kv_view {
 } mtp_kv_view;
 
 /* Host-side per-sequence draft descriptor ([G4] s.5): the drafter attends to
-   every position <= attn_pos (full) or the last swa_window of them (SWA);
-   step k runs RoPE at position pos0 + k (pos0 = attn_pos + 1 in [G4] s.6). */
+   every position <= attn_pos (full), the last swa_window of them (SWA), or,
+   through a sink + window source, positions [0, min(sw_sink, first)) and
+   [first, attn_pos] with first = max(attn_pos - sw_window + 1, run_lo, 0)
+   ([AUD] item 2: cells before run_lo hold stale entries of an earlier
+   context and are never read).  Step k runs RoPE at position
+   pos0 + k (pos0 = attn_pos + 1 in [G4] s.6). */
 typedef struct mtp_seq {
-    mtp_kv_view src[2];         /* [MTP_SRC_FULL], [MTP_SRC_SWA]; unused ones may be zero */
+    mtp_kv_view src[MTP_N_SRC];  /* indexed by mtp_src; unused ones may be zero */
     int32_t attn_pos;
     int32_t pos0;
+    int32_t run_lo;             /* first valid position (sink + window source only; <= attn_pos) */
+    int32_t pad;
 } mtp_seq;
 
 /* Sampling chain of the temperature>0 verify ([AUD] s.4): top-k, penalties
@@ -165,8 +180,9 @@ void mtp_ctx_destroy(mtp_ctx *ctx);
      out_h_last fp32 [n_seq, d_hprev] or NULL  (h_{n_steps})
      out_logits fp32 [n_seq, n_steps, n_vocab] or NULL
    Requires 1 <= n_seq <= max_seqs, 1 <= n_steps <= max_steps,
-   0 <= attn_pos < n_cells for each full source read, n_cells >= swa_window
-   for each SWA source read.  The KV must not be rewritten at positions <=
+   0 <= attn_pos < n_cells for each full or sink + window source read,
+   n_cells >= swa_window for each SWA source read, and run_lo <= attn_pos
+   where a sink + window source is read.  The KV must not be rewritten at positions <=
    attn_pos until the work completes; appending past attn_pos is allowed. */
 int mtp_draft_block(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const int32_t *last_tok,
                     const float *h_prev, int32_t n_steps, int32_t *out_drafts, float *out_h_last,

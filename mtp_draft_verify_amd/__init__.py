@@ -43,7 +43,7 @@ class ModelDesc(C.Structure):
                [("block_src", C.c_int32 * MAX_BLOCKS)] + \
                [(n, C.c_float) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")] + \
                [("max_seqs", C.c_int32), ("max_steps", C.c_int32), ("n_centroids", C.c_int32),
-                ("centroid_top_k", C.c_int32)]
+                ("centroid_top_k", C.c_int32), ("sw_window", C.c_int32), ("sw_sink", C.c_int32)]
 
 
 class Weights(C.Structure):
@@ -56,8 +56,12 @@ class KVView(C.Structure):
     _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("n_cells", C.c_int64), ("cell_stride", C.c_int64)]
 
 
+N_SRC = 3     # full, SWA ring, sink + window
+
+
 class Seq(C.Structure):
-    _fields_ = [("src", KVView * 2), ("attn_pos", C.c_int32), ("pos0", C.c_int32)]
+    _fields_ = [("src", KVView * N_SRC), ("attn_pos", C.c_int32), ("pos0", C.c_int32), ("run_lo", C.c_int32),
+                ("pad", C.c_int32)]
 
 
 class Sampler(C.Structure):
@@ -209,12 +213,14 @@ def mtp_profile_read(ctx: int, cls: int):
 # --------------------------------------------------------------------------- struct builders
 def make_desc(*, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab, w_dtype, head_dtype,
               kv_dtype, swa_window=0, block_src=(), rms_eps=1e-6, rope_theta=10000.0, attn_scale=None,
-              embed_scale=None, max_seqs=1, max_steps=4, n_centroids=0, centroid_top_k=0) -> ModelDesc:
+              embed_scale=None, max_seqs=1, max_steps=4, n_centroids=0, centroid_top_k=0, sw_window=0,
+              sw_sink=0) -> ModelDesc:
     d = ModelDesc()
     for k, v in dict(d_model=d_model, d_hprev=d_hprev, n_blocks=n_blocks, n_head_q=n_head_q, n_head_kv=n_head_kv,
                      head_dim=head_dim, d_ff=d_ff, n_vocab=n_vocab, w_dtype=w_dtype, head_dtype=head_dtype,
                      kv_dtype=kv_dtype, swa_window=swa_window, max_seqs=max_seqs, max_steps=max_steps,
-                     n_centroids=n_centroids, centroid_top_k=centroid_top_k).items():
+                     n_centroids=n_centroids, centroid_top_k=centroid_top_k, sw_window=sw_window,
+                     sw_sink=sw_sink).items():
         setattr(d, k, int(v))
     for i in range(MAX_BLOCKS):
         d.block_src[i] = int(block_src[i]) if i < len(block_src) else 0
@@ -238,16 +244,21 @@ def make_weights(t: Dict[str, object], n_blocks: int) -> Weights:
 
 
 def make_seqs(seqs: Sequence[dict]) -> C.Array:
-    """seqs: dicts with attn_pos, pos0 and per source (0 full, 1 swa) a tuple
-    (k_tensor, v_tensor, n_cells, cell_stride) or None."""
+    """seqs: dicts with attn_pos, pos0, optional run_lo, and per source (0 full,
+    1 SWA ring, 2 sink + window) a tuple (k_tensor, v_tensor, n_cells,
+    cell_stride) or None."""
     arr = (Seq * len(seqs))()
     for i, s in enumerate(seqs):
-        for j, src in enumerate(s.get("src", (None, None))):
+        srcs = tuple(s.get("src", ()))
+        if len(srcs) > N_SRC:
+            raise ValueError(f"at most {N_SRC} KV sources per sequence")
+        for j, src in enumerate(srcs):
             if src is not None:
                 k, v, n_cells, stride = src
                 arr[i].src[j].k, arr[i].src[j].v = _ptr(k), _ptr(v)
                 arr[i].src[j].n_cells, arr[i].src[j].cell_stride = int(n_cells), int(stride)
         arr[i].attn_pos, arr[i].pos0 = int(s["attn_pos"]), int(s["pos0"])
+        arr[i].run_lo = int(s.get("run_lo", 0))
     return arr
 
 

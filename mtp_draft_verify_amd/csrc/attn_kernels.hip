@@ -56,9 +56,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         for (int t = 0; t < T; ++t) {
             const int pi = cb + t * 16 + gi;
             ok[t] = pi < npos;
-            int cell = sp.c0 + pbeg + pi;
-            if (cell >= sp.n_cells) cell -= sp.n_cells;
-            const int64_t off = (int64_t)cell * sp.cell_stride;
+            const int64_t off = (int64_t)src_cell(sp, pbeg + pi) * sp.cell_stride;
 #pragma unroll
             for (int v = 0; v < NVL; ++v) {
                 kv[t][v] = ok[t] ? *(const uint4 *)(kbase + off + v * EPV) : make_uint4(0, 0, 0, 0);
@@ -289,10 +287,7 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
 
     const uint16_t *kb = (const uint16_t *)sp.k + (int64_t)kvh * HD;
     const uint16_t *vb = (const uint16_t *)sp.v + (int64_t)kvh * HD;
-    auto cell_of = [&](int pi) {
-        int c = sp.c0 + pbeg + min(pi, npos - 1);
-        return c >= sp.n_cells ? c - sp.n_cells : c;
-    };
+    auto cell_of = [&](int pi) { return src_cell(sp, pbeg + min(pi, npos - 1)); };
     auto load = [&](int i, AttnTile<HD, G> &t) {
         const int p0 = i < nt ? 16 * (wid + 4 * i) : 16 * wid;
         const uint16_t *kp = kb + (int64_t)cell_of(p0 + j16) * sp.cell_stride + 8 * g;

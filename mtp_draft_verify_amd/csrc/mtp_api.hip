@@ -84,7 +84,7 @@ struct mtp_ctx {
     int slot = 0;
     // captured draft chains, one per launch shape
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[6]; hipGraph_t g; hipGraphExec_t exec; };
+    struct Graph { int key[7]; hipGraph_t g; hipGraphExec_t exec; };
     std::vector<Graph> graphs;
     bool graph_failed = false;          // capture unsupported: launch directly
     // optional event timing per kernel class
@@ -137,12 +137,15 @@ extern "C" int mtp_check_desc(const mtp_model_desc *d) {
     if (d->d_model > hmax) return MTP_E_SHAPE;
     if (d->max_seqs > 16 || (int64_t)d->max_seqs * d->d_model > 16384) return MTP_E_SHAPE;
     if (d->max_steps > 64) return MTP_E_SHAPE;
-    bool swa = false;
+    bool swa = false, sw = false;
     for (int l = 0; l < d->n_blocks; ++l) {
-        if (d->block_src[l] != MTP_SRC_FULL && d->block_src[l] != MTP_SRC_SWA) return MTP_E_INVAL;
-        swa |= d->block_src[l] == MTP_SRC_SWA;
+        const int b = d->block_src[l];
+        if (b != MTP_SRC_FULL && b != MTP_SRC_SWA && b != MTP_SRC_SINK_WINDOW) return MTP_E_INVAL;
+        swa |= b == MTP_SRC_SWA;
+        sw |= b == MTP_SRC_SINK_WINDOW;
     }
     if (swa && d->swa_window <= 0) return MTP_E_SHAPE;
+    if (sw && (d->sw_window <= 0 || d->sw_sink < 0)) return MTP_E_SHAPE;
     if (!(d->rms_eps >= 0.f) || !(d->attn_scale > 0.f) || !(d->rope_theta > 0.f) || !std::isfinite(d->embed_scale))
         return MTP_E_INVAL;
     if (d->n_centroids < 0) return MTP_E_SHAPE;
@@ -349,16 +352,24 @@ static int src_geometry(const mtp_model_desc &d, const mtp_seq &sq, int src, Src
     p.v = kv.v;
     p.cell_stride = kv.cell_stride;
     p.n_cells = (int32_t)kv.n_cells;
+    p.n_sink = 0;
     if (src == MTP_SRC_FULL) {
         if (sq.attn_pos >= kv.n_cells) return MTP_E_SHAPE;
-        p.lo = 0;
         p.n_vis = sq.attn_pos + 1;
         p.c0 = 0;
-    } else {
+    } else if (src == MTP_SRC_SWA) {
         if (kv.n_cells < d.swa_window) return MTP_E_SHAPE;
-        p.lo = std::max(0, sq.attn_pos - d.swa_window + 1);
-        p.n_vis = sq.attn_pos - p.lo + 1;
-        p.c0 = (int32_t)(p.lo % kv.n_cells);
+        const int32_t lo = std::max(0, sq.attn_pos - d.swa_window + 1);
+        p.n_vis = sq.attn_pos - lo + 1;
+        p.c0 = (int32_t)(lo % kv.n_cells);
+    } else {
+        // sink + window over a linear cache: [0, min(sink, first)) ++ [first, attn_pos]
+        if (sq.attn_pos >= kv.n_cells) return MTP_E_SHAPE;
+        if (sq.run_lo > sq.attn_pos) return MTP_E_INVAL;
+        const int32_t first = std::max({sq.attn_pos - d.sw_window + 1, sq.run_lo, 0});
+        p.n_sink = std::min(d.sw_sink, first);
+        p.c0 = first;
+        p.n_vis = p.n_sink + (sq.attn_pos - first + 1);
     }
     const int64_t per = (p.n_vis + MTP_MAX_SPLITS - 1) / MTP_MAX_SPLITS;
     p.split_len = (int32_t)std::max<int64_t>(64, pow2ceil(per));
@@ -383,7 +394,7 @@ static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStre
 // Launch shape of one draft call: everything the kernel sequence depends on
 // besides the parameter block.
 struct ChainShape {
-    int S, N, split[2];
+    int S, N, split[MTP_N_SRC];
     int logits;     // the caller asked for draft logits
     int conf;       // the caller asked for per-step confidence / the p_min trim
 };
@@ -512,7 +523,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
 
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
-    const int key[6] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.logits, sh.conf};
+    const int key[7] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf};
     for (auto &g : c->graphs)
         if (std::memcmp(g.key, key, sizeof(key)) == 0) return g.exec;
     if (c->graph_failed) return nullptr;
@@ -566,7 +577,7 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
     if (n_seq < 1 || n_seq > d.max_seqs || n_steps < 1 || n_steps > d.max_steps) return MTP_E_SHAPE;
     if (!seqs || !last_tok || !h_prev || !out_drafts) return MTP_E_INVAL;
     if (!aligned16(h_prev)) return MTP_E_INVAL;
-    bool use_src[2] = {false, false};
+    bool use_src[MTP_N_SRC] = {false, false, false};
     for (int l = 0; l < d.n_blocks; ++l) use_src[d.block_src[l]] = true;
 
     // per-call parameter block into the next pinned slot
@@ -577,14 +588,14 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
     CallIO *hio = (CallIO *)hb;
     SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
     std::memset(hio, 0, sizeof(CallIO));
-    ChainShape sh{n_seq, n_steps, {0, 0}, out_logits != nullptr, out_conf != nullptr};
+    ChainShape sh{n_seq, n_steps, {0, 0, 0}, out_logits != nullptr, out_conf != nullptr};
     for (int s = 0; s < n_seq; ++s) {
         const mtp_seq &sq = seqs[s];
         SeqParams &p = hp[s];
         std::memset(&p, 0, sizeof(p));
         if (sq.attn_pos < 0 || sq.pos0 < 0 || (int64_t)sq.pos0 + n_steps > 0x7FFFFFFF) return MTP_E_INVAL;
         p.pos0 = sq.pos0;
-        for (int src = 0; src < 2; ++src) {
+        for (int src = 0; src < MTP_N_SRC; ++src) {
             if (!use_src[src]) continue;
             int rc = src_geometry(d, sq, src, p.src[src]);
             if (rc) return rc;
@@ -593,7 +604,7 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
     }
     // grids are sized for a power-of-two split count so one captured chain
     // serves a range of context lengths (surplus workgroups exit at once)
-    for (int src = 0; src < 2; ++src)
+    for (int src = 0; src < MTP_N_SRC; ++src)
         if (sh.split[src]) sh.split[src] = (int)std::min<int64_t>(MTP_MAX_SPLITS, pow2ceil(sh.split[src]));
     hio->last_tok = last_tok;
     hio->h_prev = h_prev;

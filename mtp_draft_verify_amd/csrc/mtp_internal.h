@@ -8,14 +8,15 @@
 namespace mtp {
 
 // Per-(sequence, source) attention geometry, computed on the host per call and
-// copied to the device once per call.  Positions lo .. lo+n_vis-1 are visible;
-// position lo + j lives at cell c0 + j (wrapped once at n_cells for a ring).
+// copied to the device once per call.  n_vis cells are visible: visible index
+// j < n_sink reads cell j (the sink), and j >= n_sink reads cell
+// c0 + j - n_sink, wrapped once at n_cells (an SWA ring).
 struct SrcParams {
     const void *k;
     const void *v;
     int64_t cell_stride;
     int32_t n_cells;
-    int32_t lo;
+    int32_t n_sink;
     int32_t n_vis;
     int32_t c0;
     int32_t split_len;
@@ -23,10 +24,16 @@ struct SrcParams {
 };
 
 struct SeqParams {
-    SrcParams src[2];
+    SrcParams src[MTP_N_SRC];
     int32_t pos0;
     int32_t pad[3];
 };
+
+// cell holding visible index j of a source
+__device__ __forceinline__ int src_cell(const SrcParams &sp, int j) {
+    int c = j < sp.n_sink ? j : sp.c0 + (j - sp.n_sink);
+    return c >= sp.n_cells ? c - sp.n_cells : c;
+}
 
 // Caller buffers of one draft call.  They sit in device memory at a fixed
 // address (followed by the SeqParams array), so the kernels of a captured

@@ -448,8 +448,9 @@ def c7_sink_window(seed: int = 1, data_seed: int = 5, **over) -> Workload:
     inside the window (a recent prefill of fewer rows than the window), B=4."""
     shape = dict(C2_SHAPE)
     shape.update({k: v for k, v in over.items() if k in shape})
-    m = make_model(seed, **shape, w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16,
-                   block_src=[KV_SINK_WINDOW] * shape["n_blocks"], head_std=1.0 / math.sqrt(1024))
+    m = make_model(seed, **shape, w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16, swa_window=over.get("swa_window", 0),
+                   block_src=over.get("block_src", [KV_SINK_WINDOW] * shape["n_blocks"]),
+                   head_std=1.0 / math.sqrt(1024))
     m.sw_window, m.sw_sink = over.get("sw_window", 256), over.get("sw_sink", 64)
     S = over.get("n_seq", 8)
     lo, hi = over.get("ctx_range", (2000, 12000))

@@ -29,7 +29,8 @@ def upload_model(m: syn.Model, device, max_seqs: int, max_steps: int):
                          w_dtype=m.w_dtype, head_dtype=m.head_dtype, kv_dtype=m.kv_dtype, swa_window=m.swa_window,
                          block_src=m.block_src, rms_eps=m.rms_eps, rope_theta=m.rope_theta,
                          attn_scale=m.attn_scale, embed_scale=m.embed_scale, max_seqs=max_seqs, max_steps=max_steps,
-                         n_centroids=m.n_centroids, centroid_top_k=m.centroid_top_k)
+                         n_centroids=m.n_centroids, centroid_top_k=m.centroid_top_k, sw_window=m.sw_window,
+                         sw_sink=m.sw_sink)
     w = mtp.make_weights(t, m.n_blocks)
     return desc, w, t
 
@@ -54,7 +55,7 @@ def upload_seqs(m: syn.Model, dr: syn.DraftInputs, device, seq_idx=None):
                 keep.extend(cache[key])
             k, v = cache[key]
             srcs.append((k, v, src.n_cells, stride))
-        seqs.append(dict(src=srcs, attn_pos=s.attn_pos, pos0=s.pos0))
+        seqs.append(dict(src=srcs, attn_pos=s.attn_pos, pos0=s.pos0, run_lo=s.run_lo))
     last_tok = to_dev(dr.last_tok[idx].astype(np.int32), device)
     h_prev = to_dev(dr.h_prev[idx].astype(np.float32), device)
     return seqs, last_tok, h_prev, keep

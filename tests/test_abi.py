@@ -48,6 +48,9 @@ def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
     assert mtp.mtp_check_desc(_c2_desc(mtp)) == mtp.MTP_OK
     assert mtp.mtp_check_desc(_c2_desc(mtp, head_dtype=mtp.MTP_Q8_0, max_seqs=8, max_steps=4)) == mtp.MTP_OK
     assert mtp.mtp_check_desc(_c2_desc(mtp, swa_window=1024, block_src=[1, 1, 1, 0])) == mtp.MTP_OK
+    assert mtp.mtp_check_desc(_c2_desc(mtp, sw_window=256, sw_sink=64, block_src=[2, 2, 2, 2])) == mtp.MTP_OK
+    assert mtp.mtp_check_desc(_c2_desc(mtp, sw_window=256, sw_sink=0, block_src=[2, 1, 2, 0],
+                                       swa_window=512)) == mtp.MTP_OK
     tiny = dict(d_model=256, d_hprev=256, n_blocks=1, n_head_q=4, n_head_kv=1, head_dim=64, d_ff=1024, n_vocab=4096,
                 w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32, max_seqs=1, max_steps=3)
     assert mtp.mtp_check_desc(mtp.make_desc(**tiny)) == mtp.MTP_OK
@@ -59,6 +62,9 @@ def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
         dict(kv_dtype=7),
         dict(max_seqs=17),                        # > 16 sequences
         dict(block_src=[1, 0, 0, 0]),             # SWA block without a window
+        dict(block_src=[2, 0, 0, 0]),             # sink + window block without a window
+        dict(block_src=[2, 0, 0, 0], sw_window=256, sw_sink=-1),
+        dict(block_src=[3, 0, 0, 0]),             # unknown source kind
         dict(head_dim=96),                        # no attention instantiation
         dict(d_ff=8192),                          # GEMV row longer than supported
         dict(max_steps=0),
@@ -81,3 +87,30 @@ def test_entry_points_reject_null_context_without_device_work(mtp):
     assert L.mtp_profile_enable(None, 1) == mtp.MTP_E_INVAL
     assert L.mtp_profile_read(None, 0, None, None) == mtp.MTP_E_INVAL
     L.mtp_ctx_destroy(None)
+
+
+def test_ctypes_structs_match_the_c_layout(mtp, tmp_path):
+    """Every field of the binding's structures sits at the offset gcc gives the
+    header's declaration (a drifted field would pass garbage silently)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("no host C compiler")
+    structs = {"mtp_model_desc": mtp.ModelDesc, "mtp_weights": mtp.Weights, "mtp_kv_view": mtp.KVView,
+               "mtp_seq": mtp.Seq, "mtp_sampler": mtp.Sampler}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mtp.h"', 'int main(void) {']
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f in py._fields_:
+            lines.append(f'printf("{cname} {f[0]} %zu\\n", offsetof({cname}, {f[0]}));')
+    lines += ['return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", str(ROOT / "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == C.sizeof(py), cname
+        for f in py._fields_:
+            assert got[(cname, f[0])] == getattr(py, f[0]).offset, (cname, f[0])

@@ -118,7 +118,7 @@ def test_kv_is_read_only_and_unseen_cells_are_never_read():
     # poison: full cells > attn_pos; SWA ring cells are all visible when ctx >= W,
     # so rebuild each ring with extra capacity and poison the unused cells
     for s in w.draft.seqs:
-        full, swa = s.src
+        full, swa = s.src[syn.KV_FULL], s.src[syn.KV_SWA]
         k, v = full.k.copy(), full.v.copy()
         k[s.attn_pos + 1:] = 0x7FC0
         v[s.attn_pos + 1:] = 0x7FC0
@@ -128,7 +128,7 @@ def test_kv_is_read_only_and_unseen_cells_are_never_read():
         W = w.model.swa_window
         for p in range(s.attn_pos - W + 1, s.attn_pos + 1):
             k2[p % C], v2[p % C] = swa.k[p % swa.n_cells], swa.v[p % swa.n_cells]
-        s.src = [syn.KVSource(k, v), syn.KVSource(k2, v2)]
+        s.src = [syn.KVSource(k, v), syn.KVSource(k2, v2), None]
     seqs, lt, hp, keep = upload_seqs(w.model, w.draft, "cuda")
     before = [torch.cat([t.view(torch.int16).flatten().to(torch.int64) for t in keep]).sum().item()]
     import mtp_draft_verify_amd as mtp
