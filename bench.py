@@ -123,7 +123,7 @@ WORKLOADS = {
     "c6": ("c6_centroid", "the c2 drafter with a centroid LM head: 2048 centroids x 128 token ids, top 32 "
            "centroids (4096 candidate rows) per step; full KV 8192; 1 sequence, B=4 + greedy verify"),
     "c7": ("c7_sink_window", "the c2 drafter with every block reading a sink + window source (64 sink cells + "
-           "a 256-position window over a 12000-cell cache, half the sequences with a valid run starting inside "
+           "a 257-cell window ending at attn_pos over a 12000-cell cache, half the sequences with a valid run starting inside "
            "the window); 8 sequences, B=4 + greedy verify"),
 }
 
@@ -280,8 +280,12 @@ def main():
         head_launch_bytes -= m.n_centroids * m.d_model * (4 if m.w_dtype == syn.F32 else 2)
     head_avg_ms = head_ms / max(head_n, 1)
     achieved = head_launch_bytes / (head_avg_ms * 1e-3) / 1e9
-    kernel_name = ("cand_head_kernel (centroid head candidate rows + argmax + post-proj)" if m.n_centroids
-                   else "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)")
+    if m.n_centroids:
+        kernel_name = "cand_head_kernel (centroid head candidate rows + argmax + post-proj)"
+    elif S >= 2 and m.head_dtype != syn.F32:
+        kernel_name = "mm_head_kernel (final RMSNorm + matrix-core LM head + argmax + post-proj)"
+    else:
+        kernel_name = "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)"
     value = S * N / (ms_per_step * 1e-3)
     acc = n_acc.cpu().numpy()
 
@@ -305,10 +309,11 @@ def main():
         "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_round": round_bytes,
         "roofline": {"bound": "hbm", "kernel": kernel_name,
-                     "note": None if args.workload == "c2" else "traffic counters were taken on the c2 workload",
+                     "note": None if args.workload == "c2" else "HBM counters are taken on the c2 workload only",
                      "timing": f"HIP events around each head launch over {args.steps} steps after the timed region",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": head_traffic_from_counters(), "bytes_per_launch": head_launch_bytes,
+                     "traffic": head_traffic_from_counters() if args.workload == "c2" else None,
+                     "bytes_per_launch": head_launch_bytes,
                      "avg_launch_ms": head_avg_ms,
                      "launches": head_n},
         "roofline_attn": {"bound": "hbm", "kernel": "attn_mm_kernel + merge_kernel (split-K attention, a3)",

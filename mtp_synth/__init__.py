@@ -443,7 +443,8 @@ def c6_centroid(seed: int = 1, **over) -> Workload:
 
 def c7_sink_window(seed: int = 1, data_seed: int = 5, **over) -> Workload:
     """The c2 drafter with every block reading a sink + window source: 64 sink
-    cells plus a 256-position window over a 12000-cell cache; 8 sequences
+    cells plus a 257-cell window [attn_pos - 256, attn_pos] over a 12000-cell
+    cache (at most 321 cells, the report's count); 8 sequences
     with ctx ~ U{2000..12000}, half of them with a valid run that starts
     inside the window (a recent prefill of fewer rows than the window), B=4."""
     shape = dict(C2_SHAPE)
@@ -451,7 +452,7 @@ def c7_sink_window(seed: int = 1, data_seed: int = 5, **over) -> Workload:
     m = make_model(seed, **shape, w_dtype=BF16, head_dtype=BF16, kv_dtype=BF16, swa_window=over.get("swa_window", 0),
                    block_src=over.get("block_src", [KV_SINK_WINDOW] * shape["n_blocks"]),
                    head_std=1.0 / math.sqrt(1024))
-    m.sw_window, m.sw_sink = over.get("sw_window", 256), over.get("sw_sink", 64)
+    m.sw_window, m.sw_sink = over.get("sw_window", 257), over.get("sw_sink", 64)
     S = over.get("n_seq", 8)
     lo, hi = over.get("ctx_range", (2000, 12000))
     r = rng_for(data_seed, "c7.ctx")

@@ -34,7 +34,7 @@ def _edge_workload(**over):
 
 
 def test_sink_window_full_size_sampled_sequences(orc):
-    log("case c7 full: sink 64 + window 256 over 12000 cells, 8 seqs (4 with a stale run), S=8 N=3; "
+    log("case c7 full: sink 64 + window 257 over 12000 cells, 8 seqs (4 with a stale run), S=8 N=3; "
         "oracle on 4 sampled sequences")
     w = syn.c7_sink_window()
     assert any(s.run_lo > s.attn_pos - w.model.sw_window + 1 for s in w.draft.seqs)

@@ -158,6 +158,11 @@ def test_sink_window_visible_cells_hand_cases(orc):
     assert cells(1000, sink=0) == list(range(745, 1001))
     assert cells(1000, run_lo=20, sink=64) == list(range(64)) + list(range(745, 1001))
     assert cells(200, run_lo=150) == list(range(64)) + list(range(150, 201))
+    # the page's own list: window [cell0 - 256, cell0] (W = 257 cells) and
+    # sink 64 give at most 64 + 257 = 321 cells
+    m.sw_window = 257
+    assert cells(1000) == list(range(64)) + list(range(744, 1001))
+    assert len(cells(1000)) == 321
 
 
 def test_sink_window_equal_keys_average_exactly_the_visible_values(orc):
