@@ -350,12 +350,55 @@ C2_SHAPE = dict(d_model=1024, d_hprev=2816, n_blocks=4, n_head_q=8, n_head_kv=2,
 
 
 @dataclass
+class HiddenVerifyInputs:
+    """The target's final hidden rows for a verify from hidden states."""
+    d: int
+    n_vocab: int
+    head_dtype: int
+    head: np.ndarray             # the target's LM head [V, d] in its storage format
+    g: Optional[np.ndarray]      # fp32 [d] final-norm gain, or None (rows already normed)
+    eps: float
+    hidden: np.ndarray           # fp32 [S, N+1, d]
+    drafts: np.ndarray           # int32 [S, N]
+    planted: np.ndarray          # int32 [S, N+1]: token a row was built around, -1 for a pure-noise row
+
+
+def make_hidden_verify(seed: int, S: int, N: int, d: int, V: int, *, head_dtype: int = BF16, p_accept: float = 0.8,
+                       plant_frac: float = 0.9, beta: float = 1.0, gain: bool = True,
+                       eps: float = 1e-6) -> HiddenVerifyInputs:
+    """Head ~ N(0, 1/d); gain 1 + 0.1 N(0,1); hidden rows N(0,1), and with
+    probability plant_frac a row also gets beta * sqrt(d) * W_head[t] added for
+    a random token t (a clear favourite, as a trained target's rows have);
+    draft i equals row i's planted token with probability p_accept, else it is
+    another random token."""
+    head_f = normal(seed, "hv.head", (V, d), std=1.0 / math.sqrt(d))
+    head = store(head_f, head_dtype)
+    g = (1.0 + 0.1 * normal(seed, "hv.gain", (d,))).astype(np.float32) if gain else None
+    r = rng_for(seed, "hv.plant")
+    tok = r.integers(0, V, size=(S, N + 1)).astype(np.int32)
+    is_planted = r.random((S, N + 1)) < plant_frac
+    hidden = normal(seed, "hv.hidden", (S, N + 1, d))
+    for s in range(S):
+        for i in range(N + 1):
+            if is_planted[s, i]:
+                hidden[s, i] += np.float32(beta * math.sqrt(d)) * head_f[tok[s, i]]
+    planted = np.where(is_planted, tok, -1).astype(np.int32)
+    other = r.integers(0, V - 1, size=(S, N)).astype(np.int32)
+    hit = r.random((S, N)) < p_accept
+    drafts = np.where(hit & (planted[:, :N] >= 0), planted[:, :N],
+                      np.where(other >= tok[:, :N], other + 1, other)).astype(np.int32)
+    del head_f
+    return HiddenVerifyInputs(d, V, head_dtype, head, g, eps, hidden, drafts, planted)
+
+
+@dataclass
 class Workload:
     name: str
     model: Optional[Model]
     draft: Optional[DraftInputs]
     greedy: Optional[GreedyVerifyInputs] = None
     sample: Optional[SampleVerifyInputs] = None
+    hidden: Optional[HiddenVerifyInputs] = None
     p_accept: float = 0.0
     plant_mode: str = "max5"
 
@@ -464,8 +507,18 @@ def c7_sink_window(seed: int = 1, data_seed: int = 5, **over) -> Workload:
     return Workload("c7_sink_window", m, dr, gv, p_accept=0.8)
 
 
+def c8_hidden_verify(seed: int = 6, **over) -> Workload:
+    """Verify from the target's hidden rows: Gemma-4-26B-like backbone width
+    2816, bf16 LM head V=262144 with its final-norm gain; 16 sequences x
+    (1 + 3) rows."""
+    hv = make_hidden_verify(seed, over.get("n_seq", 16), over.get("n_draft", 3), over.get("d", 2816),
+                            over.get("n_vocab", 262144), head_dtype=over.get("head_dtype", BF16),
+                            p_accept=over.get("p_accept", 0.8), gain=over.get("gain", True))
+    return Workload("c8_hidden_state_verify", None, None, hidden=hv, p_accept=0.8)
+
+
 CONFIGS = {"c1": c1_tiny, "c2": c2_gemma_bf16, "c3": c3_interleaved, "c4": c4_longctx_q8, "c5": c5_sample,
-           "c6": c6_centroid, "c7": c7_sink_window}
+           "c6": c6_centroid, "c7": c7_sink_window, "c8": c8_hidden_verify}
 
 
 # ----------------------------------------------------------------------------

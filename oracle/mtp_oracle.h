@@ -121,6 +121,13 @@ int orc_pmin_trim(int32_t n_seq, int32_t n_steps, const double *conf, double p_m
 int orc_verify_greedy(int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
                       const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept);
 
+/* greedy verify from the target's final hidden rows [n_seq, n_draft+1, d]
+   through rmsnorm(.; g) (skipped when g is NULL) and the head [n_vocab, d] */
+int orc_verify_greedy_hidden(int32_t n_seq, int32_t n_draft, int32_t n_vocab, int32_t d, const float *hidden,
+                             const void *head, int32_t head_dtype, const float *g, double eps,
+                             const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept,
+                             double *out_margin);
+
 /* processed sampling distribution of one row; returns the number of tokens
    with non-zero probability, or < 0 on error */
 int orc_sample_dist(int32_t n_vocab, const float *z, const int32_t *ctx, int32_t n_ctx,

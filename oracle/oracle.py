@@ -95,6 +95,8 @@ def lib():
         L.orc_confidence.argtypes = [C.c_int64, P]
         L.orc_pmin_trim.argtypes = [C.c_int32, C.c_int32, P, C.c_double, C.c_double, P, P, P]
         L.orc_verify_greedy.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
+        L.orc_verify_greedy_hidden.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_int32, P,
+                                               C.c_double, P, P, P, P]
         L.orc_sample_dist.argtypes = [C.c_int32, P, P, C.c_int32, C.POINTER(OrcSampler), P, P]
         L.orc_verify_sample.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
                                         C.POINTER(OrcSampler), C.c_uint64, P, P, P]
@@ -222,6 +224,27 @@ def verify_greedy(logits: np.ndarray, drafts: np.ndarray):
     if rc != 0:
         raise RuntimeError(f"orc_verify_greedy failed: {rc}")
     return tokens, n_acc
+
+
+def verify_greedy_hidden(hidden: np.ndarray, head: np.ndarray, head_dtype: int, n_vocab: int, g, eps: float,
+                         drafts: np.ndarray):
+    """hidden fp32 [S, N+1, d]; head in its storage format (f32 / bf16 bits
+    [V, d], or Q8_0 blocks); g fp32 [d] or None.  -> (tokens, n_accept,
+    margins [S, N+1])"""
+    hidden = np.ascontiguousarray(hidden, dtype=np.float32)
+    drafts = np.ascontiguousarray(drafts, dtype=np.int32)
+    head = np.ascontiguousarray(head)
+    S, R, d = hidden.shape
+    gp = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+    tokens = np.zeros((S, R), np.int32)
+    n_acc = np.zeros(S, np.int32)
+    margin = np.zeros((S, R), np.float64)
+    rc = lib().orc_verify_greedy_hidden(S, R - 1, int(n_vocab), d, _p(hidden), _p(head), int(head_dtype),
+                                        _p(gp) if gp is not None else None, float(eps), _p(drafts), _p(tokens),
+                                        _p(n_acc), _p(margin))
+    if rc != 0:
+        raise RuntimeError(f"orc_verify_greedy_hidden failed: {rc}")
+    return tokens, n_acc, margin
 
 
 def sampler_struct(sp: syn.Sampler) -> OrcSampler:

@@ -587,6 +587,96 @@ def test_verify_greedy_is_lossless_and_acceptance_follows_closed_form(orc):
     assert abs(np.mean(na + 1) - mean) < 4 * sd, (np.mean(na + 1), mean)
 
 
+# ------------------------------------------------------- hidden-state verify
+def test_hidden_verify_identity_head_hand_case(orc):
+    """Head [I; -I] without a norm: row i's logits are (h, -h), so its token is
+    the coordinate of largest magnitude, offset by d when it is negative; the
+    acceptance is then read off by hand ("MTP decoding", How it is wired)."""
+    d = 8
+    head = np.concatenate([np.eye(d), -np.eye(d)]).astype(np.float32)
+    h = np.zeros((2, 3, d), np.float32)
+    h[0, 0, 2] = 1.5            # token 2
+    h[0, 1, 5] = -2.0           # token 8 + 5 = 13
+    h[0, 2, 0] = 0.5            # token 0
+    h[1, 0, 7] = -0.25          # token 15
+    h[1, 1, 1] = 3.0            # token 1
+    h[1, 2, 4] = -1.0           # token 12
+    h += np.float32(0.01) * np.arange(d, dtype=np.float32)    # small, the favourites stay
+    drafts = np.array([[2, 13], [15, 4]], np.int32)
+    t, n, margin = orc.verify_greedy_hidden(h, head, syn.F32, 2 * d, None, 1e-6, drafts)
+    assert t.tolist() == [[2, 13, 0], [15, 1, -1]]
+    assert n.tolist() == [2, 1]
+    # row (0, 1): -h[5] = 2 - 0.05 leads, the runner-up is h[7] = 0.07
+    assert abs(margin[0, 1] - (1.95 - 0.07)) < 1e-6
+
+
+def test_hidden_verify_norm_scale_invariance_and_margin_scale(orc):
+    """rmsnorm makes the tokens independent of a row's scale, and with unit gain
+    it divides the logits (hence the top-2 margin) by sqrt(mean(h^2) + eps)."""
+    S, N, d, V = 3, 2, 64, 300
+    r = np.random.default_rng(7)
+    head = syn.f32_to_bf16_bits(r.standard_normal((V, d)).astype(np.float32) / 8)
+    h = r.standard_normal((S, N + 1, d)).astype(np.float32)
+    drafts = r.integers(0, V, (S, N)).astype(np.int32)
+    ones = np.ones(d, np.float32)
+    t0, n0, m0 = orc.verify_greedy_hidden(h, head, syn.BF16, V, None, 1e-6, drafts)
+    t1, n1, m1 = orc.verify_greedy_hidden(h, head, syn.BF16, V, ones, 1e-6, drafts)
+    t2, n2, _ = orc.verify_greedy_hidden(h * np.float32(1024), head, syn.BF16, V, ones, 1e-6, drafts)
+    assert (t0 == t1).all() and (t1 == t2).all() and (n0 == n1).all() and (n1 == n2).all()
+    rms = np.sqrt((h.astype(np.float64) ** 2).mean(axis=2) + 1e-6)
+    np.testing.assert_allclose(m1, m0 / rms, rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", [syn.BF16, syn.Q8_0])
+def test_hidden_verify_equals_logit_verify_of_a_library_matmul(orc, dtype):
+    """Tokens equal the logit-row verify applied to numpy's fp64 matmul of the
+    normed rows with the head decoded in numpy; only fp32-level near ties may
+    differ (none at this size)."""
+    S, N, d, V = 4, 3, 96, 2000
+    r = np.random.default_rng(11)
+    wf = r.standard_normal((V, d)).astype(np.float32) / np.float32(math.sqrt(d))
+    head = syn.store(wf, dtype)
+    if dtype == syn.BF16:
+        W = syn.bf16_bits_to_f32(head).astype(np.float64)
+    else:
+        blk = head.reshape(V, d // 32, 34)
+        scale = blk[:, :, 0:2].copy().view(np.float16).astype(np.float64)      # [V, d/32, 1]
+        W = (scale * blk[:, :, 2:].view(np.int8).astype(np.float64)).reshape(V, d)
+    g = (1 + 0.1 * r.standard_normal(d)).astype(np.float32)
+    h = r.standard_normal((S, N + 1, d)).astype(np.float32)
+    drafts = r.integers(0, V, (S, N)).astype(np.int32)
+    x = h.astype(np.float64)
+    f = x / np.sqrt((x ** 2).mean(axis=2, keepdims=True) + 1e-6) * g.astype(np.float64)
+    z = (f @ W.T).astype(np.float32)
+    am = z.argmax(axis=2)
+    drafts[:, 0] = am[:, 0]                   # some accepted prefixes
+    drafts[0, 1] = am[0, 1]
+    t, n, margin = orc.verify_greedy_hidden(h, head, dtype, V, g, 1e-6, drafts)
+    t_ref, n_ref = orc.verify_greedy(z, drafts)
+    assert margin.min() > 1e-4
+    assert (t == t_ref).all() and (n == n_ref).all()
+    assert n.tolist()[0] >= 2
+
+
+def test_hidden_verify_recovers_planted_rows(orc):
+    """Rows built around a token (beta * sqrt(d) * W_head[t] on top of unit
+    noise) verify to that token, and the accepted prefix is the run of drafts
+    equal to the planted tokens."""
+    hv = syn.make_hidden_verify(3, 6, 3, 256, 4096, p_accept=0.7)
+    t, n, margin = orc.verify_greedy_hidden(hv.hidden, hv.head, hv.head_dtype, hv.n_vocab, hv.g, hv.eps, hv.drafts)
+    planted = hv.planted >= 0
+    assert planted.sum() >= 18
+    for s in range(6):
+        for i in range(4):
+            if planted[s, i] and t[s, i] >= 0:
+                assert t[s, i] == hv.planted[s, i]
+        a = 0
+        while a < 3 and planted[s, a] and hv.drafts[s, a] == hv.planted[s, a]:
+            a += 1
+        assert n[s] == a
+    assert 0 < n.sum() < 18
+
+
 # ------------------------------------------------------------ sampling chain
 def _sp(**kw):
     base = dict(temp=1.0, top_p=1.0, min_p=0.0, rep_penalty=1.0, presence_penalty=0.0, freq_penalty=0.0, top_k=0,
