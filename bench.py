@@ -122,6 +122,8 @@ WORKLOADS = {
            "temp 0.6, top-p 0.95, min-p 0.05, repetition 1.08, presence 0.4 over the last 64 tokens"),
     "c6": ("c6_centroid", "the c2 drafter with a centroid LM head: 2048 centroids x 128 token ids, top 32 "
            "centroids (4096 candidate rows) per step; full KV 8192; 1 sequence, B=4 + greedy verify"),
+    "c8": ("c8_hidden_verify", "greedy verify from the target's final hidden rows: Gemma-4-26B-like width 2816, "
+           "bf16 LM head V=262144 with its final-norm gain, 16 sequences x (1 + 3) rows"),
     "c7": ("c7_sink_window", "the c2 drafter with every block reading a sink + window source (64 sink cells + "
            "a 257-cell window ending at attn_pos over a 12000-cell cache, half the sequences with a valid run starting inside "
            "the window); 8 sequences, B=4 + greedy verify"),
@@ -171,6 +173,78 @@ def bench_sample(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def bench_hidden(args, dev):
+    """Extra measurement: the greedy verify from the target's hidden rows on
+    its own (final norm + LM head over the 1 + N rows + argmax + acceptance)."""
+    import numpy as np
+    import torch
+    import mtp_draft_verify_amd as mtp
+    import mtp_synth as syn
+    from mtp_synth.device import to_dev
+    w = syn.c8_hidden_verify()
+    hv = w.hidden
+    S, R, d = hv.hidden.shape
+    V = hv.n_vocab
+    desc = mtp.make_desc(d_model=32, d_hprev=8, n_blocks=1, n_head_q=1, n_head_kv=1, head_dim=64, d_ff=8,
+                         n_vocab=V, w_dtype=0, head_dtype=0, kv_dtype=0, max_seqs=S, max_steps=R - 1)
+    ctx = mtp.Context(desc, None, stream=torch.cuda.current_stream())
+    wt = torch.from_numpy(hv.head.view(np.int16)).to(dev)
+    g = to_dev(hv.g, dev)
+    head = mtp.make_lm_head(wt, g, d, V, mtp.MTP_BF16, hv.eps)
+    hidden, drafts = to_dev(hv.hidden, dev), to_dev(hv.drafts, dev)
+    toks = torch.zeros((S, R), dtype=torch.int32, device=dev)
+    na = torch.zeros((S,), dtype=torch.int32, device=dev)
+
+    def step():
+        ctx.verify_greedy_hidden(head, hidden, drafts, toks, na)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # HIP events around each call on the context's stream, after the timed region
+    n_diag = min(args.steps, 50)
+    ctx.profile(1 << mtp.MTP_PROF_VERIFY)
+    for _ in range(n_diag):
+        step()
+    v_ms, v_n = ctx.profile_read(mtp.MTP_PROF_VERIFY)
+    ctx.profile(0)
+    avg_ms = v_ms / max(v_n, 1)
+    alg_bytes = V * d * 2 + S * R * d * 4         # the head once + the hidden rows
+    achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
+    out = {"metric": "verified rows/s of greedy verify from hidden states (fused target head + argmax)",
+           "value": S * R / (ms * 1e-3), "unit": "rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": WORKLOADS["c8"][1], "n_seq": S, "rows_per_seq": R, "d": d, "n_vocab": V},
+           "roofline": {"bound": "hbm", "kernel": "hv_prep_kernel + hv_head_kernel + verify_prefix_kernel "
+                                                 "(one entry-point call)",
+                        "timing": f"HIP events around each call over {n_diag} calls after the timed region",
+                        "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "bytes_per_launch": alg_bytes,
+                        "avg_launch_ms": avg_ms, "launches": v_n,
+                        "mfma_tflops": 2.0 * S * R * V * d / (avg_ms * 1e-3) / 1e12},
+           "accepted_per_round": float(na.float().mean())}
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        orc.build(force=False)
+        rows, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_budget and rows < 50 * S * R:
+            s = (rows // R) % S
+            orc.verify_greedy_hidden(hv.hidden[s:s + 1], hv.head, hv.head_dtype, V, hv.g, hv.eps, hv.drafts[s:s + 1])
+            rows += R
+        el = time.perf_counter() - t1
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+        out["cpu_baseline"] = {"value": rows / el, "unit": "rows/s", "cores": threads, "kind": "oracle",
+                               "sample": f"{rows // R} sequence(s) x {R} rows of the same workload through the "
+                                         f"oracle, {el:.1f} s wall, OpenMP threads={threads}"}
+    ctx.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,7 +255,7 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 3 times (calibrates rocprofv3 byte counters)")
     ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS),
-                    help="c2 (default, the headline line); c3, c4, c5 are extra measurements")
+                    help="c2 (default, the headline line); the others are extra measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU form (sequences shard with no exchange; "
@@ -208,6 +282,9 @@ def main():
         return
     if args.workload == "c5":
         bench_sample(args, dev)
+        return
+    if args.workload == "c8":
+        bench_hidden(args, dev)
         return
     log(f"bench: generating workload {args.workload}")
     w = getattr(syn, WORKLOADS[args.workload][0])()

@@ -215,6 +215,36 @@ int mtp_draft_block_conf(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const
 int mtp_verify_greedy(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
                       const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept);
 
+/* The target's LM head, for the verify from hidden states: row-major
+   [n_vocab, d] bf16 weights (dtype MTP_BF16; others are MTP_E_DTYPE) and
+   the gain of the target's final RMSNorm. */
+typedef struct mtp_lm_head {
+    const void *w;          /* [n_vocab, d], 16-byte aligned */
+    const float *g_final;   /* [d] fp32, or NULL: the hidden rows are already final-normed */
+    int32_t d;              /* multiple of 256, <= 16384 */
+    int32_t n_vocab;
+    int32_t dtype;
+    float rms_eps;
+} mtp_lm_head;
+
+/* Greedy verify from the target's final hidden rows ([MTP] "Why a wider
+   decode can be faster": the head weights are read once for all 1 + n_draft
+   rows of every sequence; [MTP] "How it is wired" for the acceptance).  Row
+   i of sequence s is hidden[s, i, :]; its logits are z = W rmsnorm(h; g_final)
+   (z = W h when g_final is NULL), t_i = argmax z (lowest id on ties), and
+   the acceptance is that of mtp_verify_greedy.  No logit row is written:
+   the head runs on the matrix cores with an argmax epilogue, 64 rows per
+   pass over the weights (more rows take more passes).
+     head        host pointer; its w and g_final are device pointers
+     hidden      fp32 [n_seq, n_draft+1, head->d], 16-byte aligned
+     drafts      int32 [n_seq, n_draft]
+     out_tokens  int32 [n_seq, n_draft+1] (-1 past the emitted ones); out_n_accept int32 [n_seq]
+   The first call with a given d allocates a scratch buffer of 256 * d bytes
+   that the context keeps. */
+int mtp_verify_greedy_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                             const float *hidden, const int32_t *drafts, int32_t *out_tokens,
+                             int32_t *out_n_accept);
+
 /* Exact temperature>0 verify ([AUD] s.4, after Leviathan et al. 2023 s.2.3).
    Row i's context is the last penalty_last_n tokens of history[s, :history_len[s]]
    ++ drafts[s, :i]; p_i and q_i are the sampling chain applied to p_logits

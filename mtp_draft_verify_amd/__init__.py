@@ -21,11 +21,11 @@ LIB_PATH = PKG / "libmtp.so"
 MTP_OK, MTP_E_INVAL, MTP_E_SHAPE, MTP_E_DTYPE, MTP_E_NOMEM, MTP_E_DEVICE, MTP_E_NOWEIGHTS, MTP_E_BUSY = \
     0, -1, -2, -3, -4, -5, -6, -7
 MTP_F32, MTP_BF16, MTP_Q8_0 = 0, 1, 2
-MTP_SRC_FULL, MTP_SRC_SWA = 0, 1
+MTP_SRC_FULL, MTP_SRC_SWA, MTP_SRC_SINK_WINDOW = 0, 1, 2
 MAX_BLOCKS = 8
 MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
-           "mtp_verify_sample", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
+           "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
            "mtp_last_error")
 MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY = 0, 1, 2, 3
 
@@ -57,6 +57,11 @@ class KVView(C.Structure):
 
 
 N_SRC = 3     # full, SWA ring, sink + window
+
+
+class LmHead(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("g_final", C.c_void_p), ("d", C.c_int32), ("n_vocab", C.c_int32),
+                ("dtype", C.c_int32), ("rms_eps", C.c_float)]
 
 
 class Seq(C.Structure):
@@ -97,6 +102,8 @@ def lib() -> C.CDLL:
         L.mtp_draft_block_conf.restype = C.c_int
         L.mtp_verify_greedy.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.mtp_verify_greedy.restype = C.c_int
+        L.mtp_verify_greedy_hidden.argtypes = [P, C.c_int32, C.c_int32, C.POINTER(LmHead), P, P, P, P]
+        L.mtp_verify_greedy_hidden.restype = C.c_int
         L.mtp_verify_sample.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
                                         C.POINTER(Sampler), C.c_uint64, P, P]
         L.mtp_verify_sample.restype = C.c_int
@@ -182,6 +189,21 @@ def mtp_verify_greedy(ctx: int, n_seq: int, n_draft: int, n_vocab: int, logits, 
                                  _ptr(out_n_accept))
     if rc != MTP_OK:
         raise MTPError(rc, "mtp_verify_greedy")
+
+
+def make_lm_head(w, g_final, d: int, n_vocab: int, dtype: int = MTP_BF16, rms_eps: float = 1e-6) -> LmHead:
+    h = LmHead()
+    h.w, h.g_final = _ptr(w), _ptr(g_final)
+    h.d, h.n_vocab, h.dtype, h.rms_eps = int(d), int(n_vocab), int(dtype), float(rms_eps)
+    return h
+
+
+def mtp_verify_greedy_hidden(ctx: int, n_seq: int, n_draft: int, head: LmHead, hidden, drafts, out_tokens,
+                             out_n_accept) -> None:
+    rc = lib().mtp_verify_greedy_hidden(ctx, n_seq, n_draft, C.byref(head), _ptr(hidden), _ptr(drafts),
+                                        _ptr(out_tokens), _ptr(out_n_accept))
+    if rc != MTP_OK:
+        raise MTPError(rc, "mtp_verify_greedy_hidden")
 
 
 def mtp_verify_sample(ctx: int, n_seq: int, n_draft: int, n_vocab: int, p_logits, q_logits, drafts, history,
@@ -290,6 +312,10 @@ class Context:
     def verify_greedy(self, logits, drafts, out_tokens, out_n_accept):
         S, R, V = logits.shape
         mtp_verify_greedy(self.handle, S, R - 1, V, logits, drafts, out_tokens, out_n_accept)
+
+    def verify_greedy_hidden(self, head: LmHead, hidden, drafts, out_tokens, out_n_accept):
+        S, R, _ = hidden.shape
+        mtp_verify_greedy_hidden(self.handle, S, R - 1, head, hidden, drafts, out_tokens, out_n_accept)
 
     def verify_sample(self, p_logits, q_logits, drafts, history, history_len, sampler, round_, out_tokens,
                       out_n_accept):

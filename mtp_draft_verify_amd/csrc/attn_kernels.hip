@@ -245,13 +245,7 @@ template <> struct VRow<4> { typedef au32x2_t T; };   // 4 bf16 per lane per cel
 template <> struct VRow<2> { typedef uint32_t T; };   // 2 bf16
 
 // KV addresses come from the per-call parameter block, so the compiler
-// cannot see that they are global memory; flat loads would count against
-// the LDS counter too and force full waits.  Load through global pointers.
-template <typename T>
-__device__ __forceinline__ T ld_global(const void *p) {
-    return *(const __attribute__((address_space(1))) T *)p;
-}
-
+// cannot see that they are global memory: the tile loads use ld_global.
 template <int HD, int G>
 struct AttnTile {
     static constexpr int KS = HD / 32, DPL = HD / 64;

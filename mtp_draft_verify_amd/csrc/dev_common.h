@@ -104,6 +104,22 @@ __device__ __forceinline__ float4 ld_nt(const float4 *p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// Loads through an explicitly global pointer: a generic (flat) load would
+// also count against the LDS counter, so every LDS wait would drain it.
+template <typename T>
+__device__ __forceinline__ T ld_global(const void *p) {
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+template <typename T>
+__device__ __forceinline__ T ld_global_nt(const void *p) {
+    return __builtin_nontemporal_load((const __attribute__((address_space(1))) T *)p);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m), hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Raise a kernel's dynamic-LDS limit once (gfx950 has 160 KiB of LDS per CU).
 template <typename K>
 inline hipError_t allow_dynamic_lds(K kernel, size_t bytes) {

@@ -60,11 +60,6 @@ __device__ __forceinline__ u32x4_t q8_to_bf16(const u32x2_t q) {
 __device__ __forceinline__ u32x4_t ld_nt4(const void *p) { return __builtin_nontemporal_load((const u32x4_t *)p); }
 __device__ __forceinline__ u32x2_t ld_nt2(const void *p) { return __builtin_nontemporal_load((const u32x2_t *)p); }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m), hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 // ============================================================================
 // GEMV tile kernel: one 16-row tile per workgroup, the K steps dealt out
 // round-robin to the NW waves (step t = w + NW i), partial tiles summed over

@@ -93,6 +93,8 @@ struct mtp_ctx {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pending[MTP_PROF_N];
     // verify scratch
     uint64_t *vkeys = nullptr;          // [max_seqs][max_steps + 1]
+    void *hv_plane = nullptr;           // verify from hidden states: staged rows (grown on demand)
+    size_t hv_plane_size = 0;
     // temperature>0 verify scratch, per row (target rows then draft rows)
     int32_t s_cap = 0;                  // candidate slots per row
     uint32_t *s_maxkey = nullptr;
@@ -180,7 +182,7 @@ static void free_ctx(mtp_ctx *c) {
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
-                    c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state};
+                    c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_block) (void)hipHostFree(c->h_block);
@@ -647,6 +649,48 @@ extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     hipError_t e = launch_verify_greedy(logits, drafts, n_seq, n_draft, n_vocab, c->vkeys, out_tokens, out_n_accept,
                                         c->stream);
     return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch", e);
+}
+
+extern "C" int mtp_verify_greedy_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                                        const float *hidden, const int32_t *drafts, int32_t *out_tokens,
+                                        int32_t *out_n_accept) {
+    if (!c || !head) return MTP_E_INVAL;
+    if (n_seq < 1 || n_seq > c->desc.max_seqs || n_draft < 0 || n_draft > c->desc.max_steps) return MTP_E_SHAPE;
+    if (head->dtype != MTP_BF16) return MTP_E_DTYPE;
+    if (head->d < 256 || head->d > 16384 || head->d % 256 || head->n_vocab < 1 || head->n_vocab > 0x7FFFFFF0)
+        return MTP_E_SHAPE;
+    if (!head->w || !aligned16(head->w) || (head->g_final && !aligned16(head->g_final)) || !hidden ||
+        !aligned16(hidden) || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept)
+        return MTP_E_INVAL;
+    if (!(head->rms_eps >= 0.f) || !std::isfinite(head->rms_eps)) return MTP_E_INVAL;
+    const size_t need = hv_plane_bytes(head->d);
+    if (c->hv_plane_size < need) {
+        if (c->hv_plane) {
+            if (hipStreamSynchronize(c->stream) != hipSuccess) return hip_fail("stream wait", hipGetLastError());
+            (void)hipFree(c->hv_plane);
+            c->hv_plane = nullptr;
+            c->hv_plane_size = 0;
+        }
+        if (hipMalloc(&c->hv_plane, need) != hipSuccess) {
+            c->hv_plane = nullptr;
+            (void)hipGetLastError();
+            return MTP_E_NOMEM;
+        }
+        c->hv_plane_size = need;
+    }
+    ProfScope ps(c, MTP_PROF_VERIFY);
+    HvArgs a{};
+    a.hidden = hidden;
+    a.g = head->g_final;
+    a.eps = head->rms_eps;
+    a.d = head->d;
+    a.V = head->n_vocab;
+    a.head = head->w;
+    a.plane = c->hv_plane;
+    a.keys = c->vkeys;
+    hipError_t e = launch_verify_hidden(a, n_seq * (n_draft + 1), c->stream);
+    if (e == hipSuccess) e = launch_verify_prefix(drafts, n_seq, n_draft, c->vkeys, out_tokens, out_n_accept, c->stream);
+    return e == hipSuccess ? MTP_OK : hip_fail("hidden-state verify launch", e);
 }
 
 extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,

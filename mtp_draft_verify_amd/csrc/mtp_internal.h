@@ -169,6 +169,22 @@ bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a);
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a, bool logits, hipStream_t st);
 int mm_head_groups(const HeadArgs &a);   // head workgroups (confidence partials) of one launch
 
+// verify from hidden states: the target's final norm + LM head + argmax over
+// rows [row0, row0 + R) of hidden, in passes of up to 64 rows
+struct HvArgs {
+    const float *hidden;    // [rows, d] fp32 final hidden rows
+    const float *g;         // [d] final-norm gain, or null (rows already normed)
+    float eps;
+    int32_t d, V, row0, R;
+    const void *head;       // [V, d] bf16
+    void *plane;            // scratch: hv_plane_bytes(d) bytes
+    uint64_t *keys;         // [rows] argmax keys, zero before; indexed by row
+};
+size_t hv_plane_bytes(int32_t d);
+hipError_t launch_verify_hidden(const HvArgs &a, int32_t rows, hipStream_t st);
+hipError_t launch_verify_prefix(const int32_t *drafts, int32_t S, int32_t N, uint64_t *keys, int32_t *out_tokens,
+                                int32_t *out_n_accept, hipStream_t st);
+
 // verify
 hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,
                                 uint64_t *keys, int32_t *out_tokens, int32_t *out_n_accept, hipStream_t st);

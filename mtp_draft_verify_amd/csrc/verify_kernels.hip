@@ -13,13 +13,6 @@ namespace mtp {
 
 static constexpr int kVerifyChunk = 8192;
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    lo = (uint32_t)__shfl_xor((int)lo, m);
-    hi = (uint32_t)__shfl_xor((int)hi, m);
-    return ((uint64_t)hi << 32) | lo;
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
@@ -89,6 +82,11 @@ hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int3
                        keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_verify_prefix(drafts, S, N, keys, out_tokens, out_n_accept, st);
+}
+
+hipError_t launch_verify_prefix(const int32_t *drafts, int32_t S, int32_t N, uint64_t *keys, int32_t *out_tokens,
+                                int32_t *out_n_accept, hipStream_t st) {
     hipLaunchKernelGGL(verify_prefix_kernel, dim3((S + 63) / 64), dim3(64), 0, st, drafts, S, N, keys, out_tokens,
                        out_n_accept);
     return hipGetLastError();

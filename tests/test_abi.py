@@ -80,6 +80,8 @@ def test_entry_points_reject_null_context_without_device_work(mtp):
     assert L.mtp_draft_block(None, 1, None, None, None, 1, None, None, None) == mtp.MTP_E_INVAL
     assert L.mtp_draft_block_conf(None, 1, None, None, None, 1, None, None, None, None, 0.5, None) == mtp.MTP_E_INVAL
     assert L.mtp_verify_greedy(None, 1, 1, 10, None, None, None, None) == mtp.MTP_E_INVAL
+    head = mtp.make_lm_head(None, None, 2816, 262144)
+    assert L.mtp_verify_greedy_hidden(None, 1, 3, C.byref(head), None, None, None, None) == mtp.MTP_E_INVAL
     sp = mtp.make_sampler(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4)
     assert L.mtp_verify_sample(None, 1, 1, 10, None, None, None, None, 0, None, C.byref(sp), 0, None,
                                None) == mtp.MTP_E_INVAL
@@ -97,7 +99,7 @@ def test_ctypes_structs_match_the_c_layout(mtp, tmp_path):
     if not shutil.which("gcc"):
         pytest.skip("no host C compiler")
     structs = {"mtp_model_desc": mtp.ModelDesc, "mtp_weights": mtp.Weights, "mtp_kv_view": mtp.KVView,
-               "mtp_seq": mtp.Seq, "mtp_sampler": mtp.Sampler}
+               "mtp_seq": mtp.Seq, "mtp_sampler": mtp.Sampler, "mtp_lm_head": mtp.LmHead}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mtp.h"', 'int main(void) {']
     for cname, py in structs.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
