@@ -73,18 +73,20 @@ def kv_bytes(m, seqs):
 
 HEAD_SOURCES = ["head_kernels.hip", "widen.h", "dev_common.h", "mtp_internal.h"]
 COUNTERS_FILE = ROOT / "profiles" / "head_kernel_c2_hbm_counters.txt"
+HV_SOURCES = ["hv_kernels.hip", "widen.h", "dev_common.h", "mtp_internal.h"]
+HV_COUNTERS_FILE = ROOT / "profiles" / "hv_head_kernel_c8_hbm_counters.txt"
 
 
-def head_traffic_from_counters():
-    """HBM bytes per head-kernel launch from the committed rocprofv3 counter
+def head_traffic_from_counters(path=COUNTERS_FILE, sources=HEAD_SOURCES):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
     summary, or None when the kernel's sources changed since it was taken."""
     import hashlib
-    if not COUNTERS_FILE.exists():
+    if not path.exists():
         return None
     h = hashlib.sha256()
-    for f in HEAD_SOURCES:
+    for f in sources:
         h.update((ROOT / "mtp_draft_verify_amd" / "csrc" / f).read_bytes())
-    fields = dict(l.split(":", 1) for l in COUNTERS_FILE.read_text().splitlines() if ":" in l)
+    fields = dict(l.split(":", 1) for l in path.read_text().splitlines() if ":" in l)
     if fields.get("kernel_source_sha256_16", "").strip() != h.hexdigest()[:16]:
         return None
     return float(fields["traffic_bytes_per_launch"])
@@ -224,7 +226,9 @@ def bench_hidden(args, dev):
                                                  "(one entry-point call)",
                         "timing": f"HIP events around each call over {n_diag} calls after the timed region",
                         "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "bytes_per_launch": alg_bytes,
+                        "frac": achieved / PEAK_HBM_GBPS,
+                        "traffic": head_traffic_from_counters(HV_COUNTERS_FILE, HV_SOURCES),
+                        "traffic_kernel": "hv_head_kernel", "bytes_per_launch": alg_bytes,
                         "avg_launch_ms": avg_ms, "launches": v_n,
                         "mfma_tflops": 2.0 * S * R * V * d / (avg_ms * 1e-3) / 1e12},
            "accepted_per_round": float(na.float().mean())}
