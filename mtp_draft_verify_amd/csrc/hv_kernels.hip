@@ -25,7 +25,7 @@ namespace mtp {
 
 typedef __bf16 hv_bf16x8_t __attribute__((ext_vector_type(8)));
 
-static constexpr int kHvTW = 4;        // 16-row vocabulary tiles per wave in a tile group
+static constexpr int kHvTW = 2;        // 16-row vocabulary tiles per wave in a tile group
 static constexpr int kHvChunk = 8;     // K steps of 32 columns per staged chunk (256 columns)
 static constexpr int kHvMaxRG = 4;     // row groups of 16 per pass (64 rows)
 
@@ -88,13 +88,22 @@ __global__ __launch_bounds__(256) void hv_prep_kernel(HvArgs a) {
 // One workgroup owns tile groups [G0, G1) (a group is 4 waves x TW tiles
 // of 16 vocabulary rows) and walks (group, chunk) pairs in order; the
 // accumulators of a wave's tiles live across the chunks of a group, and the
-// group's last chunk folds them into per-row argmax keys.  The weights of a
-// chunk sit in a ring of per-step slots, refilled with the next chunk's
-// steps right after their MFMAs, so every weight load has a whole chunk of
-// work to arrive in.
+// group's last chunk folds them into per-row argmax keys.
+//
+// Weights.  A load instruction that touches 16 rows (the MFMA operand order:
+// lane l holds row l % 16) streams at ~5.2 TB/s on gfx950; one that touches
+// 4 rows x 256 contiguous bytes streams at ~7.0 TB/s.  So a tile's half chunk
+// (16 rows x 4 steps x 32 columns) is loaded as 4 such instructions into a
+// raw register ring, a chunk ahead, then passed through a small wave-private
+// LDS tile into operand order: 4 writes of 4 rows, 4 reads of one step each.
+// Each half chunk of the next chunk is transposed while the MFMAs of this
+// chunk's other half run.
 template <int RG, int TW>
 __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_wg) {
+    static_assert(TW == 2, "the transpose schedule spreads two tiles over a half chunk's four steps");
+    constexpr int TS = 17;                  // transpose tile row stride in 16-byte slots (256 B + 16 B pad)
     extern __shared__ u32x4_t hv_lds[];     // [2][CS]
+    __shared__ u32x4_t hv_tr[4][16 * TS];   // one transpose tile per wave
     __shared__ uint64_t wbest[4][16 * RG];
     constexpr int CS = hv_chunk_slots<RG>();
     constexpr int SPT = CS / 256;           // staged slots per thread per chunk
@@ -107,32 +116,63 @@ __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_w
     const int G0 = blockIdx.x * groups_per_wg, G1 = min(n_groups, G0 + groups_per_wg);
     const uint16_t *W = (const uint16_t *)a.head;
     const u32x4_t *plane = (const u32x4_t *)a.plane;
+    u32x4_t *tr = hv_tr[wid];
 
-    // Row pointers of a (group, chunk)'s tiles (lane row j16, column 8 g of
-    // the chunk).  Past the last group they point at chunk 0 of group G0
-    // (rows clamped into the matrix): those loads are issued, never used.
-    auto wptr = [&](int grp, int c, int i) {
+    // Raw load q of half hf of tile i of (group, chunk): rows 4 q + lane / 16
+    // of the tile, columns 128 hf + 8 (lane % 16) of the chunk.  Past the
+    // last group the loads read chunk 0 of group G0 (rows clamped into the
+    // matrix): issued, never used.
+    auto raw_load = [&](int grp, int c, int i, int hf, u32x4_t (&r)[4]) {
         const bool real = grp < G1;
-        const int row = min(16 * (((real ? grp : G0) * TW + i) * 4 + wid) + j16, a.V - 1);
-        return W + (int64_t)row * d + 256 * (real ? c : 0) + 8 * g;
+        const int row0 = 16 * (((real ? grp : G0) * TW + i) * 4 + wid) + (lane >> 4);
+        const uint16_t *wc = W + 256 * (real ? c : 0) + 128 * hf + 8 * j16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r[q] = ld_global_nt<u32x4_t>(wc + (int64_t)min(row0 + 4 * q, a.V - 1) * d);
+    };
+    auto tr_write = [&](const u32x4_t (&r)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tr[(4 * q + (lane >> 4)) * TS + j16] = r[q];
+    };
+    // operand of step kk of the half: lane (g, j16) takes row j16, columns 32 kk + 8 g
+    auto tr_read = [&](u32x4_t (&m)[4]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) m[kk] = tr[j16 * TS + 4 * kk + g];
+    };
+    // the (group, chunk) after (grp, c)
+    auto next = [&](int &grp, int &c) {
+        if (++c == NC) {
+            c = 0;
+            ++grp;
+        }
     };
 
     uint64_t best[RG][4];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) best[rg][0] = best[rg][1] = best[rg][2] = best[rg][3] = 0ull;
 
-    u32x4_t w[TW][kHvChunk];
+    // ring: raw[i][1] holds half 1 of the current chunk, raw[i][0] half 0 of
+    // the next one; m[0] holds the current chunk's half 0 in operand order
+    u32x4_t raw[TW][2][4], m[2][TW][4];
     u32x4_t st[SPT];
 #pragma unroll
     for (int j = 0; j < SPT; ++j) st[j] = ld_global<u32x4_t>(plane + tid + 256 * j);
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
-        const uint16_t *wr = wptr(G0, 0, i);
-#pragma unroll
-        for (int k = 0; k < kHvChunk; ++k) w[i][k] = ld_global_nt<u32x4_t>(wr + 32 * k);
+        raw_load(G0, 0, i, 0, raw[i][0]);
+        raw_load(G0, 0, i, 1, raw[i][1]);
     }
 #pragma unroll
     for (int j = 0; j < SPT; ++j) hv_lds[tid + 256 * j] = st[j];
+    {
+        int g1 = G0, c1 = 0;
+        next(g1, c1);
+#pragma unroll
+        for (int i = 0; i < TW; ++i) {
+            tr_write(raw[i][0]);
+            tr_read(m[0][i]);
+            raw_load(g1, c1, i, 0, raw[i][0]);
+        }
+    }
     __syncthreads();
 
     int buf = 0;
@@ -144,63 +184,70 @@ __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_w
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) acc[i][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         for (int c = 0; c < NC; ++c) {
-            // step k's A operands are read during step k - 1 (step 0's first
-            // thing after the barrier); each pair of weight slots is refilled
-            // right after its last MFMA.  The scheduling barriers keep the loads
-            // where they are written (left alone, the compiler sinks them all
-            // below the MFMAs).
+            // step k's A operands are read during step k - 1 (step 0's right
+            // after the barrier).  The scheduling barriers keep loads and LDS
+            // traffic where they are written (left alone, the compiler sinks
+            // the loads below the MFMAs).
             const u32x4_t *xb = hv_lds + buf * CS + lane;
             u32x4_t x[2][2][RG];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) x[0][h][rg] = xb[hv_slot<RG>(0, h, rg, 0)];
-            // the next (group, chunk): its activations (from L2, stored
-            // before the barrier), then the weight ring behind the MFMAs
-            const int gn = c + 1 < NC ? grp : grp + 1, cn = c + 1 < NC ? c + 1 : 0;
+            int g1 = grp, c1 = c;
+            next(g1, c1);
+            int g2 = g1, c2 = c1;
+            next(g2, c2);
+            // the next chunk's activations (from L2, stored before the barrier)
+            const int cs = g1 < G1 ? c1 : 0;
 #pragma unroll
-            for (int j = 0; j < SPT; ++j) st[j] = ld_global<u32x4_t>(plane + (int64_t)cn * CS + tid + 256 * j);
-            const uint16_t *wn[TW];
-#pragma unroll
-            for (int i = 0; i < TW; ++i) wn[i] = wptr(gn, cn, i);
+            for (int j = 0; j < SPT; ++j) st[j] = ld_global<u32x4_t>(plane + (int64_t)cs * CS + tid + 256 * j);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int k = 0; k < kHvChunk; ++k) {
+                const int hf = k >> 2, kk = k & 3, ti = kk >> 1;
                 if (k + 1 < kHvChunk)
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
                         for (int rg = 0; rg < RG; ++rg) x[(k + 1) & 1][h][rg] = xb[hv_slot<RG>(k + 1, h, rg, 0)];
+                // transpose work of this step: half 1 of this chunk during
+                // half 0's steps, half 0 of the next chunk during half 1's
+                if ((kk & 1) == 0) {
+                    tr_write(raw[ti][1 - hf]);
+                } else {
+                    tr_read(m[1 - hf][ti]);
+                    if (hf == 0) raw_load(g1, c1, ti, 1, raw[ti][1]);
+                    else raw_load(g2, c2, ti, 0, raw[ti][0]);
+                }
 #pragma unroll
                 for (int i = 0; i < TW; ++i) {
-                    const hv_bf16x8_t wv = __builtin_bit_cast(hv_bf16x8_t, w[i][k]);
+                    const hv_bf16x8_t wv = __builtin_bit_cast(hv_bf16x8_t, m[hf][i][kk]);
 #pragma unroll
                     for (int h = 0; h < 2; ++h)
 #pragma unroll
                         for (int rg = 0; rg < RG; ++rg)
                             acc[i][rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 __builtin_bit_cast(hv_bf16x8_t, x[k & 1][h][rg]), wv, acc[i][rg], 0, 0, 0);
-                    // steps 2m and 2m + 1 of a lane are the two 64-byte halves
-                    // of one 128-byte line per row: refill both together, or
-                    // the line is fetched from HBM twice
-                    if (k & 1) {
-                        w[i][k - 1] = ld_global_nt<u32x4_t>(wn[i] + 32 * (k - 1));
-                        w[i][k] = ld_global_nt<u32x4_t>(wn[i] + 32 * k);
-                    }
                 }
-                // issue order: the next step's LDS reads interleaved with the
-                // first MFMAs, the other MFMAs, then the weight refills
+                // issue order: LDS traffic interleaved with the first MFMAs,
+                // the other MFMAs, then the raw refills
                 if (k + 1 < kHvChunk) {
 #pragma unroll
-                    for (int j = 0; j < 2 * RG; ++j) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // LDS read
+                    for (int j2 = 0; j2 < 2 * RG + 4; ++j2) {
+                        __builtin_amdgcn_sched_group_barrier(0x300, 1, 0);     // LDS read / write
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
                     }
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RG * TW - 2 * RG, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RG * TW - 2 * RG - 4, 0);
                 } else {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RG * TW, 0);
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        __builtin_amdgcn_sched_group_barrier(0x300, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2 * RG * TW - 4, 0);
                 }
-                if (k & 1) __builtin_amdgcn_sched_group_barrier(0x020, 2 * TW, 0);     // global loads
+                if (kk & 1) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);  // global loads
                 __builtin_amdgcn_sched_barrier(0);
             }
             buf ^= 1;
@@ -262,9 +309,9 @@ static hipError_t launch_hv_pass(const HvArgs &a, hipStream_t st) {
     const size_t lds = 2 * sizeof(u32x4_t) * (size_t)hv_chunk_slots<RG>();
     e = allow_dynamic_lds(hv_head_kernel<RG, kHvTW>, lds);
     if (e != hipSuccess) return e;
-    // up to 32 rows the register file and LDS hold two workgroups per
-    // CU, beyond that one
-    const int per_cu = kHvTW == 2 && RG <= 2 ? 2 : 1;
+    // up to 16 rows the register file and LDS hold two workgroups per CU,
+    // beyond that one
+    const int per_cu = RG == 1 ? 2 : 1;
     const int n_groups = ((a.V + 15) / 16 + 4 * kHvTW - 1) / (4 * kHvTW);
     int n_wg = std::min(256 * per_cu, n_groups);
     const int gpw = (n_groups + n_wg - 1) / n_wg;
