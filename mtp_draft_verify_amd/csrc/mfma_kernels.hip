@@ -210,10 +210,10 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in) {
 
 // ============================================================================
 // LM head tile kernel: f = rmsnorm(x; g_final) is staged once per workgroup
-// in LDS as the B operand (hi and lo halves); the four waves then stream
+// in LDS as the A operand (hi and lo halves); the four waves then stream
 // their 16-row head tiles with several 8-step units of weights in flight,
-// store the logits, and keep a per-sequence argmax key.  Workgroups past
-// n_head_wg run the post-projection h' = W_post f over the same staged f.
+// store the logits, and keep a per-sequence argmax key; the post-projection
+// h' = W_post f runs in the same workgroups over the same staged f.
 // ============================================================================
 static constexpr int kHeadUnit = 8;     // K steps per unit: 16 rows x 256 columns
 static constexpr int kHeadDepth = 4;    // units in flight per wave
@@ -233,22 +233,66 @@ template <> struct HeadUnit<int8_t> {
 // conflict-free ds_read_b128 at a compile-time offset from its lane base.
 __device__ __forceinline__ int bslot(int t, int h, int g, int s) { return ((2 * t + h) * 4 + g) * 16 + s; }
 
-// Unit c (steps 8c .. 8c+7) of the 16-row tile at row0.  Rows are clamped
-// into the matrix (rows past the end are computed but never stored).
+// Weights of unit c (steps 8c .. 8c+7, 256 columns) of the 16-row tile at
+// row0, as loaded.  A wave load that touches 16 rows (the operand order, lane
+// l holds row l % 16) streams at ~5.2 TB/s on gfx950, one that touches 4 rows
+// x 256 contiguous bytes at ~7.0 TB/s, so the unit is loaded in that second
+// form and put into operand order through a small LDS tile (transpose_unit).
+// Rows are clamped into the matrix (rows past the end are computed but never
+// stored).
 template <typename HT>
-__device__ __forceinline__ void head_load_unit(const void *W, const uint16_t *qs, int rows, int d, int row0, int c,
-                                               int j16, int g, HeadUnit<HT> &u) {
-    const int KS = d / 32;
-    const int row = min(row0 + j16, rows - 1);
+struct RawUnit;
+template <> struct RawUnit<uint16_t> {
+    u32x4_t r[8];           // load q: rows 4 (q % 4) + lane / 16, columns 128 (q / 4) + 8 (lane % 16)
+};
+template <> struct RawUnit<int8_t> {
+    u32x4_t r[4];           // load q: rows 4 q + lane / 16, columns 16 (lane % 16) .. + 15
+    u32x4_t sc;             // fp16 scales of the lane's row j16 for the unit's 8 blocks
+};
+
+template <typename HT>
+__device__ __forceinline__ void raw_load_unit(const void *W, const uint16_t *qs, int rows, int d, int row0, int c,
+                                              int lane, RawUnit<HT> &u) {
+    const int rq = lane >> 4, col16 = lane & 15;
     if constexpr (sizeof(HT) == 2) {
-        const uint16_t *wr = (const uint16_t *)W + (int64_t)row * d + 8 * g + 32 * kHeadUnit * c;
+        const uint16_t *wc = (const uint16_t *)W + 256 * c + 8 * col16;
 #pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt4(wr + 32 * k);
+        for (int q = 0; q < 8; ++q)
+            u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * (q & 3) + rq, rows - 1) * d + 128 * (q >> 2));
     } else {
-        const int8_t *wr = (const int8_t *)W + (int64_t)row * d + 8 * g + 32 * kHeadUnit * c;
+        const int8_t *wc = (const int8_t *)W + 256 * c + 16 * col16;
 #pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt2(wr + 32 * k);
-        u.sc = ld_nt4(qs + (int64_t)row * KS + c * kHeadUnit);
+        for (int q = 0; q < 4; ++q) u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * q + rq, rows - 1) * d);
+        u.sc = ld_nt4(qs + (int64_t)min(row0 + col16, rows - 1) * (d / 32) + c * kHeadUnit);
+    }
+}
+
+// Transpose tile of one wave: 16 rows of 256 bytes, rows padded to 272
+// bytes so the operand reads (16 rows, one 16- or 8-byte piece each) hit
+// distinct banks.  LDS operations of one wave execute in order, so the tile
+// is reused unit after unit without waits beyond the data dependences.
+static constexpr int kTrStride = 17;        // 16-byte slots per row
+static constexpr int kTrSlots = 16 * kTrStride;
+
+template <typename HT>
+__device__ __forceinline__ void transpose_unit(const RawUnit<HT> &raw, u32x4_t *tr, int lane, HeadUnit<HT> &u) {
+    const int j16 = lane & 15, g = lane >> 4;
+    u32x4_t *wrow = tr + (lane >> 4) * kTrStride + j16;
+    if constexpr (sizeof(HT) == 2) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wrow[4 * q * kTrStride] = raw.r[4 * hf + q];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) u.w[4 * hf + kk] = tr[j16 * kTrStride + 4 * kk + g];
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wrow[4 * q * kTrStride] = raw.r[q];
+        const u32x2_t *rd = (const u32x2_t *)(tr + j16 * kTrStride) + g;
+#pragma unroll
+        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = rd[4 * k];
+        u.sc = raw.sc;
     }
 }
 
@@ -257,18 +301,18 @@ __device__ __forceinline__ float sc_at(const u32x4_t &v, int k) {
     return half_to_f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFF)));
 }
 
-// MFMAs of one unit; acc_h / acc_l carry the tile's running sums.  The
+// MFMAs of one unit with its activation operands xv (hi, lo per step, read
+// from LDS beforehand); acc_h / acc_l carry the tile's running sums.  The
 // activations are the A operand (rows = sequences) and the weights the B
 // operand (columns = vocabulary rows), so a lane's four results share its
 // weight row j16 and one Q8_0 scale per block.
 template <typename HT>
-__device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4_t *bsm, int c, int g, int j16,
+__device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4_t (&xv)[2 * kHeadUnit],
                                               f32x4_t &acc_h, f32x4_t &acc_l) {
-    const u32x4_t *xb = bsm + bslot(c * kHeadUnit, 0, g, j16);
 #pragma unroll
     for (int k = 0; k < kHeadUnit; ++k) {
-        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, xb[128 * k]);
-        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, xb[128 * k + 64]);
+        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, xv[2 * k]);
+        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, xv[2 * k + 1]);
         if constexpr (sizeof(HT) == 2) {
             const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, u.w[k]);
             acc_h = mfma(xh, wv, acc_h);
@@ -294,40 +338,63 @@ __device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4
 }
 
 // The 16-row tiles [T0, T1) of one workgroup: wave w takes T0 + w, T0 + w + 4,
-// ...  UPT units make a tile and kHeadDepth is a multiple of UPT, so a tile's
-// epilogue sits at a fixed ring position; loads and stores are unconditional
-// (tiles past the wave's last one load the matrix's first unit and store to
-// `sink`), which keeps the loop body straight-line and lets the compiler
-// wait for exactly the unit it is about to use.
+// ...  Units go through a ring of kHeadDepth raw units (loaded kHeadDepth
+// units ahead); unit u + 1 is transposed into operand order while unit u's
+// MFMAs run.  UPT units make a tile and kHeadDepth is a multiple of UPT, so
+// a tile's epilogue sits at a fixed ring position; loads and stores are
+// unconditional (tiles past the wave's last one load the matrix's first unit
+// and store to `sink`), which keeps the loop body straight-line and lets the
+// compiler wait for exactly the unit it is about to use.
 //   HEAD: argmax key over valid rows, logits to `out` when LOGITS
 //   else: rows stored to `out` (the post-projection)
-template <typename HT, int UPT, bool HEAD, bool LOGITS>
+// stage() (the workgroup's activation staging, with its barriers) runs once
+// the ring's first loads are issued.
+template <typename HT, int UPT, bool HEAD, bool LOGITS, typename Stage>
 __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs, int rows, int T0, int T1,
-                           const u32x4_t *bsm, float *out, int64_t out_stride, uint64_t (&best)[4],
-                           float (&cm)[4], float (&cs)[4]) {
+                           const u32x4_t *bsm, u32x4_t *tr, float *out, int64_t out_stride, uint64_t (&best)[4],
+                           float (&cm)[4], float (&cs)[4], Stage &&stage) {
     const bool conf = HEAD && a.conf != nullptr;
     constexpr int TPI = kHeadDepth / UPT;   // tiles per loop iteration
     static_assert(kHeadDepth % UPT == 0, "ring must hold whole tiles");
+    static_assert(kHeadDepth % 2 == 0, "operand buffers alternate with the ring position");
     const int d = a.d, S = a.S;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int j16 = lane & 15, g = lane >> 4;
     const int nt = T1 - T0 > wid ? (T1 - T0 - wid + 3) / 4 : 0;
     const int nit = (nt + TPI - 1) / TPI;
-    auto load = [&](int i, int c, HeadUnit<HT> &dst) {
+    auto load = [&](int i, int c, RawUnit<HT> &dst) {
         const bool real = i < nt;
-        head_load_unit<HT>(W, qs, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, j16, g, dst);
+        raw_load_unit<HT>(W, qs, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
     };
-    HeadUnit<HT> buf[kHeadDepth];
+    RawUnit<HT> raw[kHeadDepth];
+    HeadUnit<HT> op[2];
 #pragma unroll
-    for (int p = 0; p < kHeadDepth; ++p) load(p / UPT, p % UPT, buf[p]);
+    for (int p = 0; p < kHeadDepth; ++p) load(p / UPT, p % UPT, raw[p]);
+    stage();                                // the activations, while the first weights arrive
+    transpose_unit<HT>(raw[0], tr, lane, op[0]);
+    load(TPI, 0, raw[0]);
     f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
         for (int p = 0; p < kHeadDepth; ++p) {
             const int i = it * TPI + p / UPT, c = p % UPT;
-            head_unit_mma<HT>(buf[p], bsm, c, g, j16, acc_h, acc_l);
-            load(i + TPI, c, buf[p]);
+            // unit u + 1 into operand order, then its ring slot refills with
+            // unit u + 1 + kHeadDepth
+            const int pn = (p + 1) % kHeadDepth;
+            const int un_i = it * TPI + (p + 1) / UPT + TPI, un_c = pn % UPT;
+            // this unit's activation operands first: they arrive while the
+            // next unit is transposed
+            u32x4_t xv[2 * kHeadUnit];
+            const u32x4_t *xb = bsm + bslot(c * kHeadUnit, 0, g, j16);
+#pragma unroll
+            for (int k = 0; k < kHeadUnit; ++k) {
+                xv[2 * k] = xb[128 * k];
+                xv[2 * k + 1] = xb[128 * k + 64];
+            }
+            transpose_unit<HT>(raw[pn], tr, lane, op[(p + 1) & 1]);
+            load(un_i, un_c, raw[pn]);
+            head_unit_mma<HT>(op[p & 1], xv, acc_h, acc_l);
             if (c == UPT - 1) {
                 // lane (j16, g) holds row 16 tile + j16 for sequences 4g .. 4g+3
                 const int r = 16 * (T0 + wid + 4 * i) + j16;
@@ -346,57 +413,85 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
                 acc_h = f32x4_t{0.f, 0.f, 0.f, 0.f};
                 acc_l = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
-            __builtin_amdgcn_sched_barrier(0);  // keep each unit's LDS reads next to its MFMAs
+            // issue order within the unit: activation reads, the next unit's
+            // transpose, its ring refill, then the MFMAs (left alone, the
+            // compiler reads each activation operand just before its MFMA)
+            constexpr int n_tr = sizeof(HT) == 2 ? 16 : 4 + kHeadUnit;
+            constexpr int n_ld = sizeof(HT) == 2 ? 8 : 5;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kHeadUnit, 0);     // LDS reads: activations
+            __builtin_amdgcn_sched_group_barrier(0x300, n_tr, 0);              // LDS writes / reads: transpose
+            __builtin_amdgcn_sched_group_barrier(0x020, n_ld, 0);              // global loads
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kHeadUnit, 0);     // MFMA
+            __builtin_amdgcn_sched_barrier(0);  // keep each unit's transpose and loads next to its MFMAs
         }
     }
 }
 
+// One workgroup per CU at d = 1024 (the LDS holds one), so the register file
+// may hold one wave per SIMD: the activation operands of a whole unit are
+// read ahead of its MFMAs.
 template <typename HT, int UPT, bool LOGITS>
-__global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_wg) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mm_head_kernel(HeadArgs a,
+                                                                                                 int tiles_per_wg) {
     extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
+    __shared__ u32x4_t mm_tr[4][kTrSlots];  // one weight transpose tile per wave
     __shared__ float rs[kMaxSeqGroup];
     __shared__ uint64_t wbest[4][16];
     __shared__ float wcm[4][16], wcs[4][16];
+    __shared__ f32x4_t post_part[4][64];    // per-wave partial sums of a post-projection tile
     const int d = a.d, S = a.S, KS = d / 32;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const bool head_wg = (int)blockIdx.x < a.n_head_wg;
+    const int hb = blockIdx.x;
 
-    // f = rmsnorm(x; g_final) -> activation halves (sequences >= S stay zero)
-    for (int j = wid; j < S; j += 4) {
-        const float *x = a.x + (int64_t)j * d;
-        float ss = 0.f;
-        for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
-        ss = wave_sum(ss);
-        if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
-    }
-    __syncthreads();
-    for (int it = tid; it < KS * 64; it += 256) {
-        const int s = it & 15, g = (it >> 4) & 3, t = it >> 6;
-        u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
-        if (s < S) {
-            const int col = 32 * t + 8 * g;
-            const float4 *xp = (const float4 *)(a.x + (int64_t)s * d + col);
-            const float4 *gp = (const float4 *)(a.g_final + col);
-            const float4 x0 = xp[0], x1 = xp[1], g0 = gp[0], g1 = gp[1];
-            const float r = rs[s];
-            const float v[8] = {x0.x * r * g0.x, x0.y * r * g0.y, x0.z * r * g0.z, x0.w * r * g0.w,
-                                x1.x * r * g1.x, x1.y * r * g1.y, x1.z * r * g1.z, x1.w * r * g1.w};
-            split_bf16(v, hi, lo);
+    // f = rmsnorm(x; g_final) -> activation halves (sequences >= S stay zero),
+    // run by head_tiles once its first weights are requested
+    auto stage = [&]() {
+        for (int j = wid; j < S; j += 4) {
+            const float *x = a.x + (int64_t)j * d;
+            float ss = 0.f;
+            for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
         }
-        mm_bsm[bslot(t, 0, g, s)] = hi;
-        mm_bsm[bslot(t, 1, g, s)] = lo;
-    }
-    __syncthreads();
+        __syncthreads();
+        for (int it = tid; it < KS * 64; it += 256) {
+            const int s = it & 15, g = (it >> 4) & 3, t = it >> 6;
+            u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
+            if (s < S) {
+                const int col = 32 * t + 8 * g;
+                const float4 *xp = (const float4 *)(a.x + (int64_t)s * d + col);
+                const float4 *gp = (const float4 *)(a.g_final + col);
+                const float4 x0 = xp[0], x1 = xp[1], g0 = gp[0], g1 = gp[1];
+                const float r = rs[s];
+                const float v[8] = {x0.x * r * g0.x, x0.y * r * g0.y, x0.z * r * g0.z, x0.w * r * g0.w,
+                                    x1.x * r * g1.x, x1.y * r * g1.y, x1.z * r * g1.z, x1.w * r * g1.w};
+                split_bf16(v, hi, lo);
+            }
+            mm_bsm[bslot(t, 0, g, s)] = hi;
+            mm_bsm[bslot(t, 1, g, s)] = lo;
+        }
+        __syncthreads();
+    };
 
     uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};   // sequences 4g .. 4g+3 of this lane
     float cm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, cs[4] = {0.f, 0.f, 0.f, 0.f};
-    if (head_wg) {
+    // Post-projection h' = W_post f: one 16-row tile for each of the first
+    // ceil(dh / 16) workgroups, its K chunks (units) dealt out to the waves,
+    // one unit each, the partial sums added in wave order.  The tile's
+    // weights are requested before the head's and used after them, so the
+    // projection costs a unit of streaming per wave and no extra latency.
+    const int n_post_tiles = (a.dh + 15) / 16;
+    const bool post_unit = wid < UPT;
+    RawUnit<uint16_t> praw;
+    if (hb < n_post_tiles && post_unit) raw_load_unit<uint16_t>(a.w_post, nullptr, a.dh, d, 16 * hb, wid, lane, praw);
+    {
         float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : a.sink;
         const int64_t logits_stride = (int64_t)a.n_steps * a.V;
         const int n_tiles = (a.V + 15) / 16;
-        const int T0 = blockIdx.x * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
+        const int T0 = hb * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
         const void *W = sizeof(HT) == 1 ? (const void *)a.head_q : a.head;
-        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, logits, logits_stride, best, cm, cs);
+        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, mm_tr[wid], logits, logits_stride,
+                                          best, cm, cs, stage);
         // best over the 16 rows of each lane group: xor-shuffles within 16 lanes
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -432,14 +527,39 @@ __global__ __launch_bounds__(256) void mm_head_kernel(HeadArgs a, int tiles_per_
             if (conf) {
                 float m = wcm[0][tid], sm = wcs[0][tid];
                 for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w][tid], wcs[w][tid]);
-                a.conf[(int64_t)tid * kConfSlots + blockIdx.x] = ConfPart{m, sm};
+                a.conf[(int64_t)tid * kConfSlots + hb] = ConfPart{m, sm};
             }
         }
-    } else {
-        float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
-        const int n_tiles = (a.dh + 15) / 16;
-        const int T0 = ((int)blockIdx.x - a.n_head_wg) * 4, T1 = min(n_tiles, T0 + 4);
-        head_tiles<uint16_t, UPT, false, false>(a, a.w_post, nullptr, a.dh, T0, T1, mm_bsm, h_out, a.dh, best, cm, cs);
+    }
+    float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
+    const int j16 = lane & 15, g = lane >> 4;
+    for (int tb = hb; tb < n_post_tiles; tb += (int)gridDim.x) {
+        if (tb != hb && post_unit) raw_load_unit<uint16_t>(a.w_post, nullptr, a.dh, d, 16 * tb, wid, lane, praw);
+        f32x4_t ph = {0.f, 0.f, 0.f, 0.f}, pl = {0.f, 0.f, 0.f, 0.f};
+        if (post_unit) {
+            HeadUnit<uint16_t> u;
+            transpose_unit<uint16_t>(praw, mm_tr[wid], lane, u);
+            u32x4_t xv[2 * kHeadUnit];
+            const u32x4_t *xb = mm_bsm + bslot(wid * kHeadUnit, 0, g, j16);
+#pragma unroll
+            for (int k = 0; k < kHeadUnit; ++k) {
+                xv[2 * k] = xb[128 * k];
+                xv[2 * k + 1] = xb[128 * k + 64];
+            }
+            head_unit_mma<uint16_t>(u, xv, ph, pl);
+        }
+        post_part[wid][lane] = ph + pl;
+        __syncthreads();
+        if (wid == 0) {
+            // lane (j16, g) holds row 16 tb + j16 for sequences 4g .. 4g+3
+            f32x4_t z = post_part[0][lane];
+            for (int w = 1; w < UPT; ++w) z += post_part[w][lane];
+            const int r = 16 * tb + j16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (r < a.dh && 4 * g + q < S) h_out[(int64_t)(4 * g + q) * a.dh + r] = z[q];
+        }
+        __syncthreads();
     }
 }
 
@@ -495,7 +615,8 @@ static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 gri
 
 // Head workgroups of a launch and the 16-row tiles each takes.
 static void mm_head_grid(const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
-    const size_t lds = sizeof(u32x4_t) * (size_t)128 * (a.d / 32);
+    // dynamic activation halves + the static transpose tiles and reduction slots
+    const size_t lds = sizeof(u32x4_t) * ((size_t)128 * (a.d / 32) + 4 * kTrSlots + 4 * 64) + 2048;
     const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
     const int n_tiles = (a.V + 15) / 16;
     n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
@@ -517,8 +638,7 @@ hipError_t launch_mm_head(int head_dtype, const HeadArgs &a_in, bool logits, hip
     int n_wg, tiles_per_wg;
     mm_head_grid(a, n_wg, tiles_per_wg);
     a.n_head_wg = n_wg;
-    const int n_post_wg = ((a.dh + 15) / 16 + 3) / 4;
-    const dim3 grid(n_wg + n_post_wg);
+    const dim3 grid(n_wg);
 #define MTP_MMH(HT, U)                                                                                 \
     if (upt == U) return launch_mm_head_t<HT, U>(a, tiles_per_wg, grid, lds, logits, st);
     if (head_dtype == MTP_BF16) {
