@@ -40,6 +40,47 @@ __device__ __forceinline__ float embed_value(const GemvArgs &a, int s, int c) {
     return a.embed_scale * e;
 }
 
+// Token whose embedding row sequence s gathers: the caller's id at step 0,
+// the previous step's argmax afterwards.
+__device__ __forceinline__ int32_t embed_token(const GemvArgs &a, int s) {
+    return a.tok_in ? a.tok_in[s] : key_index(a.key_in[s]);
+}
+
+// embed_scale * E[tok, col .. col + EPV) with vector loads (col < d_embed,
+// a multiple of EPV); the same values embed_value gives element by element.
+template <int EPV>
+__device__ __forceinline__ void load_embed_slice(const GemvArgs &a, int32_t tok, int col, float (&x)[EPV]) {
+    if (tok < 0 || tok >= a.embed_rows) {   // ids outside the vocabulary embed to zero
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) x[e] = 0.f;
+        return;
+    }
+    const int64_t off = (int64_t)tok * a.d_embed + col;
+    if (a.embed_dtype == MTP_F32) {
+        const float4 *p = (const float4 *)((const float *)a.embed + off);
+#pragma unroll
+        for (int e4 = 0; e4 < EPV / 4; ++e4) {
+            const float4 v = p[e4];
+            x[4 * e4 + 0] = v.x; x[4 * e4 + 1] = v.y; x[4 * e4 + 2] = v.z; x[4 * e4 + 3] = v.w;
+        }
+    } else if (a.embed_dtype == MTP_BF16) {
+        const uint32_t *p = (const uint32_t *)((const uint16_t *)a.embed + off);
+#pragma unroll
+        for (int e2 = 0; e2 < EPV / 2; ++e2) {
+            const uint32_t w = p[e2];
+            x[2 * e2] = bf16_lo(w);
+            x[2 * e2 + 1] = bf16_hi(w);
+        }
+    } else {
+        const float sc = half_to_f(a.embed_qs[(int64_t)tok * (a.d_embed / 32) + col / 32]);
+        const int8_t *q = a.embed_q + off;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) x[e] = sc * (float)q[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) x[e] *= a.embed_scale;
+}
+
 // The EPV input values of sequence s at columns [col, col + EPV), loaded with
 // 16-byte vectors (EPV is 4 or 8 and divides d_model, so a slice never
 // straddles the embedding / hidden-state boundary).
@@ -148,9 +189,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a_in) {
         uint4 wv[RU][NV];
         load_rows<WT, NV, RU>(a, rb, row1, lane, wv);
         float xr[NV][EPV], gr[NV][EPV];
+        if (IN == IN_EMBED) {
+            // the hidden-state part first: it does not wait for the token
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int col = v * CPW + lane * EPV;
+                if (col < K && col >= a.d_embed) load_x_slice<IN, EPV>(a, 0, col, xr[v]);
+            }
+            const int32_t tok = embed_token(a, 0);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                const int col = v * CPW + lane * EPV;
+                if (col < a.d_embed) load_embed_slice<EPV>(a, tok, col, xr[v]);
+                else if (col >= K)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) xr[v][e] = 0.f;
+            }
+        }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             const int col = v * CPW + lane * EPV;
+            if (IN == IN_EMBED) continue;
             if (col < K) {
                 load_x_slice<IN, EPV>(a, 0, col, xr[v]);
                 if (IN == IN_NORM) {
