@@ -563,7 +563,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     __syncthreads();
     if (slice == 0 && chunk * DC + dl < hd) {
         for (int k = 1; k < SL; ++k) lse_combine(m, l, acc, sm[k][dl], sl[k][dl], sa[k][dl]);
-        a.o[((int64_t)s * a.Hq + h) * hd + chunk * DC + dl] = acc / l;
+        const float ov = acc / l;
+        a.o[((int64_t)s * a.Hq + h) * hd + chunk * DC + dl] = ov;
+        if (a.o_op) a.o_op[op_index(h * hd + chunk * DC + dl, s)] = ov;
     }
 }
 

@@ -146,7 +146,15 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in) {
         const int t = wid + NW * i;
         const int col = 32 * t + 8 * g;
         if (sok && t < KS) {
-            mm_load_x<IN>(a, j16, col, x[i]);
+            if (IN != IN_EMBED && a.src_op) {
+                // operand order: the 16 lanes of a group read 256 contiguous bytes
+                const float4 u = *(const float4 *)(a.src_op + op_index(col, j16));
+                const float4 v = *(const float4 *)(a.src_op + op_index(col + 4, j16));
+                x[i][0] = u.x; x[i][1] = u.y; x[i][2] = u.z; x[i][3] = u.w;
+                x[i][4] = v.x; x[i][5] = v.y; x[i][6] = v.z; x[i][7] = v.w;
+            } else {
+                mm_load_x<IN>(a, j16, col, x[i]);
+            }
             if (IN == IN_NORM) {
                 const float4 *gp = (const float4 *)(a.gain + col);
                 const float4 u = gp[0], v = gp[1];
@@ -202,9 +210,9 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in) {
         float y = 0.f;
         for (int w = 0; w < NW; ++w) y += red[w][l][q];
         float *dp = a.dst + (int64_t)s * a.dst_stride + row;
-        if (EPI == EPI_STORE) *dp = y;
-        else if (EPI == EPI_ADD) *dp = *dp + y;
-        else *dp = silu_f(y);
+        const float out = EPI == EPI_STORE ? y : EPI == EPI_ADD ? *dp + y : silu_f(y);
+        *dp = out;
+        if (a.dst_op) a.dst_op[op_index(row, s)] = out;
     }
 }
 

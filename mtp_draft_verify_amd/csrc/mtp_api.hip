@@ -66,6 +66,7 @@ struct mtp_ctx {
     hipStream_t stream = nullptr;
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
+    float *o_op = nullptr, *u_op = nullptr, *x_op = nullptr;    // o, u, x in operand order (several sequences)
     float *sink = nullptr;              // [64] stores that carry nothing land here
     ConfPart *conf_part = nullptr;      // [max_steps][max_seqs][kConfSlots] confidence partials
     float *cl = nullptr;                // [max_seqs, n_centroids] centroid logits (centroid head)
@@ -182,7 +183,8 @@ static void free_ctx(mtp_ctx *c) {
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
-                    c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane};
+                    c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane,
+                    c->o_op, c->u_op, c->x_op};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_block) (void)hipHostFree(c->h_block);
@@ -239,6 +241,7 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         const size_t qd = (size_t)d.n_head_q * d.head_dim;
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
+             dalloc(&c->o_op, 16 * qd) && dalloc(&c->u_op, 16 * (size_t)d.d_ff) && dalloc(&c->x_op, 16 * (size_t)d.d_model) &&
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
              dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64) &&
              dalloc(&c->conf_part, (size_t)d.max_steps * S * kConfSlots);
@@ -269,6 +272,13 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
     if (c->has_weights) {
         hipError_t e = hipMemset(c->dkeys, 0, sizeof(uint64_t) * 2 * S);
         if (e != hipSuccess) { free_ctx(c); return hip_fail("hipMemset (draft keys)", e); }
+        // the operand-order slots of sequences >= S are read (their MFMA
+        // columns are discarded) but never written: keep them finite
+        const size_t qd = (size_t)d.n_head_q * d.head_dim;
+        e = hipMemset(c->o_op, 0, sizeof(float) * 16 * qd);
+        if (e == hipSuccess) e = hipMemset(c->u_op, 0, sizeof(float) * 16 * (size_t)d.d_ff);
+        if (e == hipSuccess) e = hipMemset(c->x_op, 0, sizeof(float) * 16 * (size_t)d.d_model);
+        if (e != hipSuccess) { free_ctx(c); return hip_fail("hipMemset (operand buffers)", e); }
         e = launch_rope_init(c->inv_freq, d.head_dim, d.rope_theta, c->stream);
         if (e != hipSuccess) { free_ctx(c); return hip_fail("rope table kernel", e); }
         if (d.head_dtype == MTP_Q8_0) {
@@ -388,6 +398,7 @@ static int gemv_rows_per_wg(int M) {
 static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStream_t st) {
     ProfScope ps(c, MTP_PROF_GEMV);
     if (mm_gemv_supported(c->desc.w_dtype, a)) return launch_mm_gemv(in_mode, epi, a, st);
+    if (a.src_op || a.dst_op) return hipErrorInvalidValue;     // operand order is a matrix-core path layout
     a.rows_per_wg = gemv_rows_per_wg(a.M);
     const int n_wg = (a.M + a.rows_per_wg - 1) / a.rows_per_wg;
     return launch_gemv(c->desc.w_dtype, in_mode, epi, a, n_wg, st);
@@ -412,6 +423,22 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
     const SeqParams *dp = (const SeqParams *)(c->d_block + sizeof(CallIO));
     hipError_t e = hipSuccess;
     int n_part = 0;                     // confidence partials per (step, sequence)
+    // Several sequences: the residual stream x, the attention output and the
+    // MLP hidden units also go to operand-order buffers, read by the GEMVs
+    // that consume them (all of which then take the matrix-core path).
+    bool mm_io;
+    {
+        GemvArgs t{};
+        t.S = S;
+        t.K = QD;
+        mm_io = mm_gemv_supported(d.w_dtype, t);
+        t.K = D;
+        mm_io = mm_io && mm_gemv_supported(d.w_dtype, t);
+        t.K = F;
+        mm_io = mm_io && mm_gemv_supported(d.w_dtype, t);
+        t.K = D + DH;
+        mm_io = mm_io && mm_gemv_supported(d.w_dtype, t);
+    }
     for (int k = 0; k < N && e == hipSuccess; ++k) {
         uint64_t *key_cur = c->dkeys + (size_t)(k & 1) * d.max_seqs;
         uint64_t *key_prev = c->dkeys + (size_t)((k + 1) & 1) * d.max_seqs;
@@ -426,6 +453,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
         ga.key_reset = key_cur;
         ga.drafts_stride = N; ga.drafts_col = k - 1;
         ga.dst = c->x; ga.dst_stride = D;
+        ga.dst_op = mm_io ? c->x_op : nullptr;
         e = run_gemv(c, IN_EMBED, EPI_STORE, ga, st);
         for (int l = 0; l < d.n_blocks && e == hipSuccess; ++l) {
             // a2: q = W_q rmsnorm(x)
@@ -433,6 +461,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             gq.W = c->w.w_q[l]; gq.M = QD; gq.K = D; gq.S = S;
             gq.src = c->x; gq.src_stride = D; gq.gain = c->w.g_attn[l]; gq.eps = d.rms_eps;
             gq.dst = c->q; gq.dst_stride = QD;
+            gq.src_op = mm_io ? c->x_op : nullptr;
             e = run_gemv(c, IN_NORM, EPI_STORE, gq, st);
             // a3: split-K attention + merge
             const int src = d.block_src[l];
@@ -448,7 +477,8 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 }
                 if (e == hipSuccess) {
                     MergeArgs ma{};
-                    ma.part = c->part; ma.o = c->o; ma.Hq = d.n_head_q; ma.Hkv = d.n_head_kv;
+                    ma.part = c->part; ma.o = c->o; ma.o_op = mm_io ? c->o_op : nullptr;
+                    ma.Hq = d.n_head_q; ma.Hkv = d.n_head_kv;
                     ma.hd = d.head_dim; ma.S = S; ma.src = src; ma.seqs = dp;
                     e = launch_merge(ma, st);
                 }
@@ -458,6 +488,8 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 GemvArgs go{};
                 go.W = c->w.w_o[l]; go.M = D; go.K = QD; go.S = S;
                 go.src = c->o; go.src_stride = QD; go.dst = c->x; go.dst_stride = D;
+                go.src_op = mm_io ? c->o_op : nullptr;
+                go.dst_op = mm_io ? c->x_op : nullptr;
                 e = run_gemv(c, IN_PLAIN, EPI_ADD, go, st);
             }
             // a5: u = silu(W_up rmsnorm(x)); x += W_down u
@@ -466,12 +498,16 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 gu.W = c->w.w_up[l]; gu.M = F; gu.K = D; gu.S = S;
                 gu.src = c->x; gu.src_stride = D; gu.gain = c->w.g_mlp[l]; gu.eps = d.rms_eps;
                 gu.dst = c->u; gu.dst_stride = F;
+                gu.dst_op = mm_io ? c->u_op : nullptr;
+                gu.src_op = mm_io ? c->x_op : nullptr;
                 e = run_gemv(c, IN_NORM, EPI_SILU, gu, st);
             }
             if (e == hipSuccess) {
                 GemvArgs gd{};
                 gd.W = c->w.w_down[l]; gd.M = D; gd.K = F; gd.S = S;
                 gd.src = c->u; gd.src_stride = F; gd.dst = c->x; gd.dst_stride = D;
+                gd.src_op = mm_io ? c->u_op : nullptr;
+                gd.dst_op = mm_io ? c->x_op : nullptr;
                 e = run_gemv(c, IN_PLAIN, EPI_ADD, gd, st);
             }
         }
@@ -481,6 +517,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             gc.W = c->w.centroids; gc.M = d.n_centroids; gc.K = D; gc.S = S;
             gc.src = c->x; gc.src_stride = D; gc.gain = c->w.g_final; gc.eps = d.rms_eps;
             gc.dst = c->cl; gc.dst_stride = d.n_centroids;
+            gc.src_op = mm_io && mm_gemv_supported(d.w_dtype, gc) ? c->x_op : nullptr;
             e = run_gemv(c, IN_NORM, EPI_STORE, gc, st);
             if (e == hipSuccess) e = launch_centroid_topk(c->cl, d.n_centroids, d.centroid_top_k, S, c->cand, st);
         }

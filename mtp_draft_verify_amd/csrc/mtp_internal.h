@@ -90,7 +90,15 @@ struct GemvArgs {
     // output
     float *dst;             // [S, dst_stride]
     int32_t dst_stride;
+    // several sequences (matrix-core path): the input / output also in operand
+    // order, [K / 4][16][4] floats (value k of sequence s at (k / 4 * 16 + s) * 4
+    // + k % 4), so a consumer's wave loads read 256 contiguous bytes per lane group
+    const float *src_op;    // read instead of src when set (IN_PLAIN, IN_NORM)
+    float *dst_op;          // written besides dst when set
 };
+
+// index of value k of sequence s in an operand-order buffer
+__host__ __device__ __forceinline__ int64_t op_index(int k, int s) { return ((int64_t)(k >> 2) * 16 + s) * 4 + (k & 3); }
 
 struct HeadArgs {
     // final norm
@@ -134,6 +142,7 @@ struct AttnArgs {
 struct MergeArgs {
     const float *part;
     float *o;               // [S, Hq*hd]
+    float *o_op;            // o in operand order as well (or null)
     int32_t Hq, Hkv, hd, S, src;
     const SeqParams *seqs;
 };
