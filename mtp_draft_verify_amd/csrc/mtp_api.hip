@@ -63,6 +63,7 @@ struct mtp_ctx {
     mtp_weights w{};
     bool has_weights = false;
     int device = 0;
+    int n_cu = 256;                     // compute units of the device
     hipStream_t stream = nullptr;
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
@@ -224,6 +225,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
     {
         const hipError_t e = hipGetDevice(&c->device);
         if (e != hipSuccess) { free_ctx(c); return hip_fail("hipGetDevice", e); }
+        const hipError_t e2 = hipDeviceGetAttribute(&c->n_cu, hipDeviceAttributeMultiprocessorCount, c->device);
+        if (e2 != hipSuccess) { free_ctx(c); return hip_fail("hipDeviceGetAttribute", e2); }
     }
     const mtp_model_desc &d = c->desc;
     const size_t S = d.max_seqs, R = (size_t)d.max_steps + 1;
@@ -526,7 +529,10 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
             HeadArgs ha{};
             ha.x = c->x; ha.g_final = c->w.g_final; ha.eps = d.rms_eps; ha.d = D; ha.S = S; ha.V = V;
             ha.head = c->w.head; ha.head_q = c->head_q; ha.head_qs = c->head_qs;
-            const int n_head_wg = (int)std::min<int64_t>(2048, std::max<int64_t>(1, (V + 15) / 16));
+            // one sequence: one workgroup per compute unit, each streaming a
+            // contiguous block of rows with the next rows always in flight
+            const int64_t wg_cap = S == 1 ? c->n_cu : 2048;
+            const int n_head_wg = (int)std::min<int64_t>(wg_cap, std::max<int64_t>(1, (V + 15) / 16));
             int rpw = (V + n_head_wg - 1) / n_head_wg;
             rpw = ((rpw + 15) / 16) * 16;
             ha.rows_per_wg = rpw;
@@ -549,7 +555,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 const bool mm = mm_head_supported(d.head_dtype, d.w_dtype, ha);
                 n_part = mm ? mm_head_groups(ha) : ha.n_head_wg;
                 e = mm ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
-                       : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, st);
+                       : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, sh.logits, st);
             }
         }
     }

@@ -149,7 +149,7 @@ struct MergeArgs {
 
 // launchers (defined with their kernels; all enqueue on `st`)
 hipError_t launch_gemv(int w_dtype, int in_mode, int epi, const GemvArgs &a, int n_wg, hipStream_t st);
-hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, hipStream_t st);
+hipError_t launch_head(int head_dtype, int w_dtype, const HeadArgs &a, int n_post_wg, bool logits, hipStream_t st);
 hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st);
 hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *io, int32_t stride, int32_t col,
