@@ -262,7 +262,7 @@ template <int HD, int G>
 __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
     constexpr int KS = HD / 32, DPL = HD / 64;
     static_assert(2 * G <= 16, "hi and lo query columns must fit one MFMA tile");
-    __shared__ float qs[G][HD];
+    __shared__ __attribute__((aligned(16))) float qs[G][HD];
     __shared__ float cs[HD / 2], sn[HD / 2];
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][HD];
@@ -345,14 +345,23 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
 
     // B operand: column h < G holds the hi half of query head h, column 8 + h
     // its lo half (scaled by scale * log2(e)); the other columns are zero.
+    // Every lane reads its 8 values of each step with two 16-byte LDS reads
+    // from a clamped head row and zeroes them afterwards: a per-lane guard
+    // on the reads would turn into a branch and a wait around each of them.
     abf16x8_t qb[KS];
     {
         const int h = j16 & 7;
+        const bool live = h < G;
+        const float *qrow = qs[min(h, G - 1)] + 8 * g;
+        const float sc = a.scale * kLog2e;
 #pragma unroll
         for (int u = 0; u < KS; ++u) {
+            const float4 x0 = *(const float4 *)(qrow + 32 * u);
+            const float4 x1 = *(const float4 *)(qrow + 32 * u + 4);
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = (h < G) ? qs[h][32 * u + 8 * g + e] * (a.scale * kLog2e) : 0.f;
+                const float x = live ? xv[e] * sc : 0.f;
                 const __bf16 hb = (__bf16)x;
                 qb[u][e] = j16 < 8 ? hb : (__bf16)(x - (float)hb);
             }
