@@ -212,8 +212,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         const int cl = (c / DPL) * (DPL + 1) + (c % DPL);
 #pragma unroll
         for (int g = 0; g < 16; ++g) av = fmaf(gw[g][j], gacc[g * GS + j * JS + cl], av);
-        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + 2);
-        pp[2 + c] = av;
+        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + kPartHead);
+        pp[kPartHead + c] = av;
         if (c == 0) {
             pp[0] = gM[j];
             pp[1] = gL[j];
@@ -478,8 +478,8 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
             L = fmaf(wl[w][j], wt, L);
             av = fmaf(wacc[w][j][c], wt, av);
         }
-        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + 2);
-        pp[2 + c] = av;
+        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + kPartHead);
+        pp[kPartHead + c] = av;
         if (c == 0) {
             pp[0] = M;
             pp[1] = L;
@@ -533,54 +533,94 @@ hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream
 
 // Log-sum-exp merge of the split partials of one query head, online form:
 // (m, l, acc) <- (M, l*2^(m-M) + l_j*2^(m_j-M), acc*2^(m-M) + acc_j*2^(m_j-M)),
-// M = max(m, m_j).  Workgroup = (16-dim chunk, query head, sequence): 16
-// thread slices take every 16th split (at most 8 each, all loads in flight at
-// once), then 16 threads combine the slices through LDS in a fixed order.
-__device__ __forceinline__ void lse_combine(float &m, float &l, float &acc, float mj, float lj, float aj) {
+// M = max(m, m_j).  Workgroup = (chunk of 16 * DPT dims, query head,
+// sequence): 16 thread slices take every 16th split (at most 8 each, all
+// loads in flight at once); a lane holds DPT consecutive dims and reads
+// (m, l) as one 8-byte load.  Then the 16 lanes of slice 0 combine the slices
+// through LDS in a fixed order.  Every dim sees the same operations in the
+// same order whatever DPT is.  DPT = 4 (one wave load = 4 partial rows x 256
+// contiguous bytes) serves several sequences; one sequence keeps DPT = 1,
+// whose 4x more workgroups finish its few partials sooner.
+template <int DPT>
+__device__ __forceinline__ void lse_combine(float &m, float &l, float (&acc)[DPT], float mj, float lj,
+                                            const float (&aj)[DPT]) {
     const float mn = fmaxf(m, mj);
     if (mn == -INFINITY) return;
     const float c0 = exp2f(m - mn), c1 = exp2f(mj - mn);
     l = l * c0 + lj * c1;
-    acc = acc * c0 + aj * c1;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[e] = acc[e] * c0 + aj[e] * c1;
     m = mn;
 }
 
+template <int DPT>
+__device__ __forceinline__ void ld_dims(const float *p, float (&v)[DPT]) {
+    if constexpr (DPT == 4) {
+        const float4 t = *(const float4 *)p;
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+        v[0] = *p;
+    }
+}
+
+template <int DPT>
+__device__ __forceinline__ void st_dims(float *p, const float (&v)[DPT]) {
+    if constexpr (DPT == 4) *(float4 *)p = make_float4(v[0], v[1], v[2], v[3]);
+    else *p = v[0];
+}
+
+template <int DPT>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    constexpr int DC = 16, SL = 16, U = MTP_MAX_SPLITS / SL;
-    __shared__ float sm[SL][DC], sl[SL][DC], sa[SL][DC];
+    constexpr int DC = 16 * DPT, SL = 16, U = MTP_MAX_SPLITS / SL;
+    __shared__ float sm[SL][16], sl[SL][16];
+    __shared__ float sa[SL][16][DPT];
     const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
-    const int tid = threadIdx.x, dl = tid % DC, slice = tid / DC;
+    const int tid = threadIdx.x, dl = tid % 16, slice = tid / 16;
     const int hd = a.hd;
-    const int dim = min(chunk * DC + dl, hd - 1);
+    const int dim = chunk * DC + DPT * dl;      // hd is a multiple of 64
     const int ns = a.seqs[s].src[a.src].n_split;
-    const float *base = a.part + ((int64_t)s * a.Hq + h) * MTP_MAX_SPLITS * (hd + 2);
-    float mj[U], lj[U], aj[U];
+    const int64_t row = hd + kPartHead;
+    const float *base = a.part + ((int64_t)s * a.Hq + h) * MTP_MAX_SPLITS * row;
+    float2 ml[U];
+    float aj[U][DPT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int j = slice + SL * u;
-        const float *pj = base + (int64_t)min(j, ns - 1) * (hd + 2);
-        mj[u] = (j < ns) ? pj[0] : -INFINITY;
-        lj[u] = pj[1];
-        aj[u] = pj[2 + dim];
+        const float *pj = base + (int64_t)min(slice + SL * u, ns - 1) * row;
+        ml[u] = *(const float2 *)pj;
+        ld_dims<DPT>(pj + kPartHead + dim, aj[u]);
     }
-    float m = -INFINITY, l = 0.f, acc = 0.f;
+    float m = -INFINITY, l = 0.f, acc[DPT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) lse_combine(m, l, acc, mj[u], lj[u], aj[u]);
+    for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) lse_combine<DPT>(m, l, acc, slice + SL * u < ns ? ml[u].x : -INFINITY, ml[u].y, aj[u]);
     sm[slice][dl] = m;
     sl[slice][dl] = l;
-    sa[slice][dl] = acc;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) sa[slice][dl][e] = acc[e];
     __syncthreads();
-    if (slice == 0 && chunk * DC + dl < hd) {
-        for (int k = 1; k < SL; ++k) lse_combine(m, l, acc, sm[k][dl], sl[k][dl], sa[k][dl]);
-        const float ov = acc / l;
-        a.o[((int64_t)s * a.Hq + h) * hd + chunk * DC + dl] = ov;
-        if (a.o_op) a.o_op[op_index(h * hd + chunk * DC + dl, s)] = ov;
+    if (slice == 0) {
+        for (int k = 1; k < SL; ++k) {
+            float ak[DPT];
+#pragma unroll
+            for (int e = 0; e < DPT; ++e) ak[e] = sa[k][dl][e];
+            lse_combine<DPT>(m, l, acc, sm[k][dl], sl[k][dl], ak);
+        }
+        float ov[DPT];
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) ov[e] = acc[e] / l;
+        st_dims<DPT>(a.o + ((int64_t)s * a.Hq + h) * hd + dim, ov);
+        if (a.o_op) st_dims<DPT>(a.o_op + op_index(h * hd + dim, s), ov);   // DPT consecutive k: one run
     }
 }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
-    dim3 grid((a.hd + 15) / 16, a.Hq, a.S);
-    hipLaunchKernelGGL(merge_kernel, grid, dim3(kBlock), 0, st, a);
+    if (a.hd % 64) return hipErrorInvalidValue;
+    if (a.S == 1) {
+        hipLaunchKernelGGL(merge_kernel<1>, dim3(a.hd / 16, a.Hq, a.S), dim3(kBlock), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(merge_kernel<4>, dim3(a.hd / 64, a.Hq, a.S), dim3(kBlock), 0, st, a);
+    }
     return hipGetLastError();
 }
 

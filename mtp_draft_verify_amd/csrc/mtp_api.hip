@@ -245,7 +245,7 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
              dalloc(&c->o_op, 16 * qd) && dalloc(&c->u_op, 16 * (size_t)d.d_ff) && dalloc(&c->x_op, 16 * (size_t)d.d_model) &&
-             dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + 2)) &&
+             dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + kPartHead)) &&
              dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64) &&
              dalloc(&c->conf_part, (size_t)d.max_steps * S * kConfSlots);
         if (ok && d.n_centroids > 0)

@@ -54,6 +54,8 @@ static_assert(sizeof(CallIO) == 64, "the parameter block layout is fixed");
 // Per-workgroup partials of the draft confidence: (max, sum exp(z - max))
 // of the workgroup's logits, per (step, sequence) in slots [kConfSlots].
 static constexpr int kConfSlots = 2048;
+// A split partial row: m, l, two pad floats, then acc[hd] (16-byte aligned).
+static constexpr int kPartHead = 4;
 struct ConfPart {
     float m, s;
 };
@@ -136,7 +138,7 @@ struct AttnArgs {
     float eps, theta, scale;
     int32_t Hq, Hkv, hd, S, src, step;
     const SeqParams *seqs;
-    float *part;            // [S, Hq, MTP_MAX_SPLITS, hd + 2]  (m, l, o[hd])
+    float *part;            // [S, Hq, MTP_MAX_SPLITS, kPartHead + hd]  (m, l, pad, pad, o[hd])
 };
 
 struct MergeArgs {
