@@ -1,0 +1,49 @@
+"""GPU parity of the draft chain for every attention kernel the library
+builds (head dim x query heads per KV head x KV dtype), against the oracle.
+
+Small drafters (d 256, one block, V 4096) over ragged contexts, so that the
+split-K partition has a ragged last split and the cross-attention runs every
+instantiation of the bf16 matrix-core kernel and of the fp32 vector kernel.
+Two sequences take the several-sequence GEMV and head paths, one sequence the
+one-sequence paths.
+"""
+import pytest
+
+import mtp_synth as syn
+from tests.gpu_harness import GpuDrafter, compare_draft, log
+
+pytestmark = pytest.mark.gpu
+
+# (kv dtype, weight dtype, head_dim, n_head_q, n_head_kv): G = n_head_q / n_head_kv
+CASES = [
+    (syn.BF16, syn.BF16, 256, 4, 1),
+    (syn.BF16, syn.BF16, 256, 4, 2),
+    (syn.BF16, syn.BF16, 256, 4, 4),
+    (syn.BF16, syn.BF16, 128, 8, 1),
+    (syn.BF16, syn.BF16, 128, 8, 2),
+    (syn.BF16, syn.BF16, 128, 8, 4),
+    (syn.BF16, syn.BF16, 128, 8, 8),
+    (syn.F32, syn.F32, 64, 4, 1),
+    (syn.F32, syn.F32, 64, 8, 1),
+    (syn.F32, syn.F32, 64, 4, 2),
+    (syn.F32, syn.F32, 64, 4, 4),
+    (syn.F32, syn.F32, 128, 4, 1),
+    (syn.F32, syn.F32, 256, 4, 1),
+]
+
+
+@pytest.mark.parametrize("kv,wd,hd,hq,hkv", CASES,
+                         ids=[f"{'bf16' if c[0] == syn.BF16 else 'f32'}-hd{c[2]}-hq{c[3]}-hkv{c[4]}" for c in CASES])
+@pytest.mark.parametrize("n_seq", [1, 2], ids=["S1", "S2"])
+def test_attention_instantiations_match_oracle(orc, kv, wd, hd, hq, hkv, n_seq):
+    name = f"kv={'bf16' if kv == syn.BF16 else 'f32'} hd={hd} Hq={hq} Hkv={hkv} S={n_seq}"
+    log(f"case attention shapes: {name}")
+    m = syn.make_model(11 + hd + 7 * hq + hkv, d_model=256, d_hprev=256, n_blocks=1, n_head_q=hq, n_head_kv=hkv,
+                       head_dim=hd, d_ff=512, n_vocab=4096, w_dtype=wd, head_dtype=wd, kv_dtype=kv)
+    ctx = [1000, 333][:n_seq]           # 1000 cells: 16 splits of 64, the last one 40 cells long
+    dr = syn.make_draft_inputs(5 + hd, m, ctx, 3)
+    gpu = GpuDrafter(m, n_seq, 3).run(dr)
+    c = compare_draft(m, gpu, orc.draft_block(m, dr))
+    log(f"  {name}: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
+        f"max_h_err={c.max_h_err:.3g}")
+    assert c.near_ties <= 1
