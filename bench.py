@@ -232,6 +232,27 @@ def bench_hidden(args, dev):
                         "avg_launch_ms": avg_ms, "launches": v_n,
                         "mfma_tflops": 2.0 * S * R * V * d / (avg_ms * 1e-3) / 1e12},
            "accepted_per_round": float(na.float().mean())}
+    # the same rows through the exact sampling verify (logit rows to context
+    # scratch, then the sampling chain): one-hot drafts, no penalties
+    sp = mtp.make_sampler(temp=0.8, top_p=0.95, min_p=0.05, rep_penalty=1.0, presence_penalty=0.0,
+                          penalty_last_n=0, seed=11)
+    hist = torch.zeros((S, 1), dtype=torch.int32, device=dev)
+    hlen = torch.zeros((S,), dtype=torch.int32, device=dev)
+
+    def sample_step(k):
+        ctx.verify_sample_hidden(head, hidden, None, drafts, hist, hlen, sp, k, toks, na)
+    for k in range(args.warmup):
+        sample_step(k)
+    torch.cuda.synchronize()
+    n_s = min(args.steps, 50)
+    t0 = time.perf_counter()
+    for k in range(n_s):
+        sample_step(k)
+    torch.cuda.synchronize()
+    s_ms = (time.perf_counter() - t0) * 1e3 / n_s
+    out["sample_hidden"] = {"what": "mtp_verify_sample_hidden on the same rows (temp 0.8, top-p 0.95, min-p 0.05, "
+                                    "one-hot drafts)", "ms_per_call": s_ms, "rows_per_s": S * R / (s_ms * 1e-3),
+                            "calls": n_s, "accepted_per_round": float(na.float().mean())}
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         orc.build(force=False)

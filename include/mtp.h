@@ -263,6 +263,27 @@ int mtp_verify_sample(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vo
                       int32_t history_stride, const int32_t *history_len, const mtp_sampler *sampler,
                       uint64_t round, int32_t *out_tokens, int32_t *out_n_accept);
 
+/* Exact temperature>0 verify from the target's final hidden rows ("MTP
+   decoding", why a wider decode can be faster; [AUD] s.4): the 1 + N rows of
+   every sequence meet the target's LM head in one pass over its weights, as
+   in mtp_verify_greedy_hidden, and the resulting logit rows go through the
+   sampling chain and acceptance rule of mtp_verify_sample (same draws, same
+   outputs as mtp_verify_sample called on those rows).
+     head        host pointer (bf16 head, as for mtp_verify_greedy_hidden);
+                 head->n_vocab must not exceed the context's n_vocab
+     hidden      fp32 [n_seq, n_draft+1, head->d], 16-byte aligned
+     q_logits    fp32 [n_seq, n_draft, head->n_vocab] or NULL (one-hot drafts)
+     drafts, history, history_stride, history_len, sampler, round, out_tokens,
+     out_n_accept: as for mtp_verify_sample
+   The logit rows go to a context-owned buffer of n_seq * (n_draft+1) *
+   n_vocab floats (allocated, or grown, on first need, together with the
+   staging buffer of mtp_verify_greedy_hidden); the caller never sees them. */
+int mtp_verify_sample_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                             const float *hidden, const float *q_logits, const int32_t *drafts,
+                             const int32_t *history, int32_t history_stride, const int32_t *history_len,
+                             const mtp_sampler *sampler, uint64_t round, int32_t *out_tokens,
+                             int32_t *out_n_accept);
+
 /* Optional HIP-event timing of the kernels one context launches, for
    measurement tools.  mtp_profile_enable waits for the stream, clears all
    counters and enables the classes whose bit (1 << class) is set in mask

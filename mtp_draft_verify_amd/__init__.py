@@ -6,7 +6,7 @@ the current HIP stream) and raises on a non-zero status.  It fails loudly when
 the library is missing: there is no fallback path.
 
 The module-level functions carry the C names (mtp_ctx_create, mtp_draft_block, mtp_draft_block_conf,
-mtp_verify_greedy, mtp_verify_sample, mtp_ctx_destroy, mtp_strerror,
+mtp_verify_greedy, mtp_verify_sample, mtp_verify_sample_hidden, mtp_ctx_destroy, mtp_strerror,
 mtp_check_desc); `Context` is a small owner around them.
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ MTP_SRC_FULL, MTP_SRC_SWA, MTP_SRC_SINK_WINDOW = 0, 1, 2
 MAX_BLOCKS = 8
 MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
-           "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
+           "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_verify_sample_hidden", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
            "mtp_last_error")
 MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY = 0, 1, 2, 3
 
@@ -107,6 +107,9 @@ def lib() -> C.CDLL:
         L.mtp_verify_sample.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
                                         C.POINTER(Sampler), C.c_uint64, P, P]
         L.mtp_verify_sample.restype = C.c_int
+        L.mtp_verify_sample_hidden.argtypes = [P, C.c_int32, C.c_int32, C.POINTER(LmHead), P, P, P, P, C.c_int32, P,
+                                               C.POINTER(Sampler), C.c_uint64, P, P]
+        L.mtp_verify_sample_hidden.restype = C.c_int
         L.mtp_strerror.argtypes = [C.c_int]
         L.mtp_strerror.restype = C.c_char_p
         L.mtp_last_error.argtypes = []
@@ -216,6 +219,16 @@ def mtp_verify_sample(ctx: int, n_seq: int, n_draft: int, n_vocab: int, p_logits
         raise MTPError(rc, "mtp_verify_sample")
 
 
+def mtp_verify_sample_hidden(ctx: int, n_seq: int, n_draft: int, head: LmHead, hidden, q_logits, drafts, history,
+                             history_stride: int, history_len, sampler: Sampler, round_: int, out_tokens,
+                             out_n_accept) -> None:
+    rc = lib().mtp_verify_sample_hidden(ctx, n_seq, n_draft, C.byref(head), _ptr(hidden), _ptr(q_logits),
+                                        _ptr(drafts), _ptr(history), history_stride, _ptr(history_len),
+                                        C.byref(sampler), round_, _ptr(out_tokens), _ptr(out_n_accept))
+    if rc != MTP_OK:
+        raise MTPError(rc, "mtp_verify_sample_hidden")
+
+
 def mtp_profile_enable(ctx: int, mask: int) -> None:
     """mask: bit (1 << class) enables event timing of that kernel class; 0 disables."""
     rc = lib().mtp_profile_enable(ctx, int(mask))
@@ -323,6 +336,13 @@ class Context:
         hs = history.shape[1] if history is not None and history.dim() == 2 else 0
         mtp_verify_sample(self.handle, S, R - 1, V, p_logits, q_logits, drafts, history, hs, history_len, sampler,
                           round_, out_tokens, out_n_accept)
+
+    def verify_sample_hidden(self, head: LmHead, hidden, q_logits, drafts, history, history_len, sampler, round_,
+                             out_tokens, out_n_accept):
+        S, R, _ = hidden.shape
+        hs = history.shape[1] if history is not None and history.dim() == 2 else 0
+        mtp_verify_sample_hidden(self.handle, S, R - 1, head, hidden, q_logits, drafts, history, hs, history_len,
+                                 sampler, round_, out_tokens, out_n_accept)
 
     def profile(self, mask: int):
         mtp_profile_enable(self.handle, mask)

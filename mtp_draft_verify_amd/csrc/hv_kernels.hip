@@ -98,7 +98,9 @@ __global__ __launch_bounds__(256) void hv_prep_kernel(HvArgs a) {
 // LDS tile into operand order: 4 writes of 4 rows, 4 reads of one step each.
 // Each half chunk of the next chunk is transposed while the MFMAs of this
 // chunk's other half run.
-template <int RG, int TW>
+// LOGITS: write the logit rows to a.logits instead of argmax keys (for the
+// sampling verify, which needs every row's whole distribution).
+template <int RG, int TW, bool LOGITS>
 __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_wg) {
     static_assert(TW == 2, "the transpose schedule spreads two tiles over a half chunk's four steps");
     constexpr int TS = 17;                  // transpose tile row stride in 16-byte slots (256 B + 16 B pad)
@@ -265,13 +267,19 @@ __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_w
                 const f32x4_t z = acc[i][rg];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const bool ok = v < a.V && 16 * rg + 4 * g + q < a.R;
-                    const uint64_t key = ok ? argmax_key(z[q], (uint32_t)v) : 0ull;
-                    best[rg][q] = key > best[rg][q] ? key : best[rg][q];
+                    const int row = 16 * rg + 4 * g + q;
+                    const bool ok = v < a.V && row < a.R;
+                    if (LOGITS) {
+                        if (ok) a.logits[(int64_t)(a.row0 + row) * a.V + v] = z[q];
+                    } else {
+                        const uint64_t key = ok ? argmax_key(z[q], (uint32_t)v) : 0ull;
+                        best[rg][q] = key > best[rg][q] ? key : best[rg][q];
+                    }
                 }
             }
         }
     }
+    if (LOGITS) return;
 
     // best over the 16 vocabulary lanes of each lane group, then the 4 waves
 #pragma unroll
@@ -301,13 +309,13 @@ __global__ __launch_bounds__(256) void hv_head_kernel(HvArgs a, int groups_per_w
 // ----------------------------------------------------------------------------
 size_t hv_plane_bytes(int32_t d) { return sizeof(u32x4_t) * (size_t)hv_chunk_slots<kHvMaxRG>() * (d / 256); }
 
-template <int RG>
+template <int RG, bool LOGITS>
 static hipError_t launch_hv_pass(const HvArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(hv_prep_kernel<RG>, dim3(16 * RG), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = 2 * sizeof(u32x4_t) * (size_t)hv_chunk_slots<RG>();
-    e = allow_dynamic_lds(hv_head_kernel<RG, kHvTW>, lds);
+    e = allow_dynamic_lds(hv_head_kernel<RG, kHvTW, LOGITS>, lds);
     if (e != hipSuccess) return e;
     // up to 16 rows the register file and LDS hold two workgroups per CU,
     // beyond that one
@@ -316,7 +324,7 @@ static hipError_t launch_hv_pass(const HvArgs &a, hipStream_t st) {
     int n_wg = std::min(256 * per_cu, n_groups);
     const int gpw = (n_groups + n_wg - 1) / n_wg;
     n_wg = (n_groups + gpw - 1) / gpw;
-    hipLaunchKernelGGL((hv_head_kernel<RG, kHvTW>), dim3(n_wg), dim3(256), lds, st, a, gpw);
+    hipLaunchKernelGGL((hv_head_kernel<RG, kHvTW, LOGITS>), dim3(n_wg), dim3(256), lds, st, a, gpw);
     return hipGetLastError();
 }
 
@@ -327,10 +335,17 @@ hipError_t launch_verify_hidden(const HvArgs &a_in, int32_t rows, hipStream_t st
         a.row0 = row0;
         a.R = std::min<int32_t>(16 * kHvMaxRG, rows - row0);
         const int rg = (a.R + 15) / 16;
-        hipError_t e = rg == 1 ? launch_hv_pass<1>(a, st)
-                     : rg == 2 ? launch_hv_pass<2>(a, st)
-                     : rg == 3 ? launch_hv_pass<3>(a, st)
-                               : launch_hv_pass<4>(a, st);
+        hipError_t e;
+        if (a.logits)
+            e = rg == 1 ? launch_hv_pass<1, true>(a, st)
+              : rg == 2 ? launch_hv_pass<2, true>(a, st)
+              : rg == 3 ? launch_hv_pass<3, true>(a, st)
+                        : launch_hv_pass<4, true>(a, st);
+        else
+            e = rg == 1 ? launch_hv_pass<1, false>(a, st)
+              : rg == 2 ? launch_hv_pass<2, false>(a, st)
+              : rg == 3 ? launch_hv_pass<3, false>(a, st)
+                        : launch_hv_pass<4, false>(a, st);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

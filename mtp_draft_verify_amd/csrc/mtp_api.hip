@@ -99,6 +99,8 @@ struct mtp_ctx {
     uint64_t *vkeys = nullptr;          // [max_seqs][max_steps + 1]
     void *hv_plane = nullptr;           // verify from hidden states: staged rows (grown on demand)
     size_t hv_plane_size = 0;
+    float *hv_logits = nullptr;         // sampling verify from hidden states: logit rows (grown on demand)
+    size_t hv_logits_size = 0;
     // temperature>0 verify scratch, per row (target rows then draft rows)
     int32_t s_cap = 0;                  // candidate slots per row
     uint32_t *s_maxkey = nullptr;
@@ -187,7 +189,7 @@ static void free_ctx(mtp_ctx *c) {
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane,
-                    c->o_op, c->u_op, c->x_op, c->kpart};
+                    c->o_op, c->u_op, c->x_op, c->kpart, c->hv_logits};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_block) (void)hipHostFree(c->h_block);
@@ -697,9 +699,30 @@ extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch", e);
 }
 
-extern "C" int mtp_verify_greedy_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
-                                        const float *hidden, const int32_t *drafts, int32_t *out_tokens,
-                                        int32_t *out_n_accept) {
+// Grow a context-owned scratch buffer to at least `need` bytes.  A buffer in
+// use by enqueued work is freed only after the stream has drained it.
+static int grow_scratch(mtp_ctx *c, void **buf, size_t *size, size_t need) {
+    if (*size >= need) return MTP_OK;
+    if (*buf) {
+        if (hipStreamSynchronize(c->stream) != hipSuccess) return hip_fail("stream wait", hipGetLastError());
+        (void)hipFree(*buf);
+        *buf = nullptr;
+        *size = 0;
+    }
+    if (hipMalloc(buf, need) != hipSuccess) {
+        *buf = nullptr;
+        (void)hipGetLastError();
+        return MTP_E_NOMEM;
+    }
+    *size = need;
+    return MTP_OK;
+}
+
+// Checks of a caller's LM head and hidden rows shared by both hidden-state
+// verifies; grows the context's staging plane to the head width.
+static int prepare_hidden_head(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                               const float *hidden, const int32_t *drafts, int32_t *out_tokens,
+                               int32_t *out_n_accept) {
     if (!c || !head) return MTP_E_INVAL;
     if (n_seq < 1 || n_seq > c->desc.max_seqs || n_draft < 0 || n_draft > c->desc.max_steps) return MTP_E_SHAPE;
     if (head->dtype != MTP_BF16) return MTP_E_DTYPE;
@@ -710,21 +733,10 @@ extern "C" int mtp_verify_greedy_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_dra
         return MTP_E_INVAL;
     if (!(head->rms_eps >= 0.f) || !std::isfinite(head->rms_eps)) return MTP_E_INVAL;
     const size_t need = hv_plane_bytes(head->d);
-    if (c->hv_plane_size < need) {
-        if (c->hv_plane) {
-            if (hipStreamSynchronize(c->stream) != hipSuccess) return hip_fail("stream wait", hipGetLastError());
-            (void)hipFree(c->hv_plane);
-            c->hv_plane = nullptr;
-            c->hv_plane_size = 0;
-        }
-        if (hipMalloc(&c->hv_plane, need) != hipSuccess) {
-            c->hv_plane = nullptr;
-            (void)hipGetLastError();
-            return MTP_E_NOMEM;
-        }
-        c->hv_plane_size = need;
-    }
-    ProfScope ps(c, MTP_PROF_VERIFY);
+    return grow_scratch(c, &c->hv_plane, &c->hv_plane_size, need);
+}
+
+static HvArgs hidden_args(mtp_ctx *c, const mtp_lm_head *head, const float *hidden) {
     HvArgs a{};
     a.hidden = hidden;
     a.g = head->g_final;
@@ -734,21 +746,26 @@ extern "C" int mtp_verify_greedy_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_dra
     a.head = head->w;
     a.plane = c->hv_plane;
     a.keys = c->vkeys;
+    return a;
+}
+
+extern "C" int mtp_verify_greedy_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                                        const float *hidden, const int32_t *drafts, int32_t *out_tokens,
+                                        int32_t *out_n_accept) {
+    const int rc = prepare_hidden_head(c, n_seq, n_draft, head, hidden, drafts, out_tokens, out_n_accept);
+    if (rc != MTP_OK) return rc;
+    ProfScope ps(c, MTP_PROF_VERIFY);
+    const HvArgs a = hidden_args(c, head, hidden);
     hipError_t e = launch_verify_hidden(a, n_seq * (n_draft + 1), c->stream);
     if (e == hipSuccess) e = launch_verify_prefix(drafts, n_seq, n_draft, c->vkeys, out_tokens, out_n_accept, c->stream);
     return e == hipSuccess ? MTP_OK : hip_fail("hidden-state verify launch", e);
 }
 
-extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
-                                 const float *q_logits, const int32_t *drafts, const int32_t *history,
-                                 int32_t history_stride, const int32_t *history_len, const mtp_sampler *sp,
-                                 uint64_t round, int32_t *out_tokens, int32_t *out_n_accept) {
-    if (!c || !sp) return MTP_E_INVAL;
-    const mtp_model_desc &d = c->desc;
-    if (n_seq < 1 || n_seq > d.max_seqs || n_draft < 0 || n_draft > d.max_steps || n_vocab < 1 ||
-        n_vocab > d.n_vocab)
-        return MTP_E_SHAPE;
-    if (!p_logits || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept) return MTP_E_INVAL;
+// Sampler checks and the launch arguments of the sampling verify.
+static int sample_args(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
+                       const float *q_logits, const int32_t *drafts, const int32_t *history, int32_t history_stride,
+                       const int32_t *history_len, const mtp_sampler *sp, uint64_t round, int32_t *out_tokens,
+                       int32_t *out_n_accept, SampleArgs *out) {
     if (q_logits && n_draft == 0) q_logits = nullptr;
     if (!(sp->temp > 0.f) || !(sp->top_p > 0.f && sp->top_p <= 1.f) || !(sp->min_p >= 0.f && sp->min_p < 1.f) ||
         !(sp->rep_penalty > 0.f) || !std::isfinite(sp->presence_penalty) || !std::isfinite(sp->freq_penalty) ||
@@ -766,7 +783,51 @@ extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     a.row_maxkey = c->s_maxkey; a.topk_key = c->s_topk; a.cand_n = c->s_cand_n; a.cand_id = c->s_cand_id;
     a.cand_v = c->s_cand_v; a.row_state = c->s_state; a.cap = std::min(c->s_cap, n_vocab);
     a.out_tokens = out_tokens; a.out_n_accept = out_n_accept;
+    *out = a;
+    return MTP_OK;
+}
+
+extern "C" int mtp_verify_sample(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
+                                 const float *q_logits, const int32_t *drafts, const int32_t *history,
+                                 int32_t history_stride, const int32_t *history_len, const mtp_sampler *sp,
+                                 uint64_t round, int32_t *out_tokens, int32_t *out_n_accept) {
+    if (!c || !sp) return MTP_E_INVAL;
+    const mtp_model_desc &d = c->desc;
+    if (n_seq < 1 || n_seq > d.max_seqs || n_draft < 0 || n_draft > d.max_steps || n_vocab < 1 ||
+        n_vocab > d.n_vocab)
+        return MTP_E_SHAPE;
+    if (!p_logits || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept) return MTP_E_INVAL;
+    SampleArgs a;
+    const int rc = sample_args(c, n_seq, n_draft, n_vocab, p_logits, q_logits, drafts, history, history_stride,
+                               history_len, sp, round, out_tokens, out_n_accept, &a);
+    if (rc != MTP_OK) return rc;
     ProfScope ps(c, MTP_PROF_VERIFY);
     const hipError_t e = launch_verify_sample(a, c->stream);
     return e == hipSuccess ? MTP_OK : hip_fail("sampling verify launch", e);
+}
+
+extern "C" int mtp_verify_sample_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
+                                        const float *hidden, const float *q_logits, const int32_t *drafts,
+                                        const int32_t *history, int32_t history_stride, const int32_t *history_len,
+                                        const mtp_sampler *sp, uint64_t round, int32_t *out_tokens,
+                                        int32_t *out_n_accept) {
+    if (!sp) return MTP_E_INVAL;
+    int rc = prepare_hidden_head(c, n_seq, n_draft, head, hidden, drafts, out_tokens, out_n_accept);
+    if (rc != MTP_OK) return rc;
+    if (head->n_vocab > c->desc.n_vocab) return MTP_E_SHAPE;     // the sampling scratch is sized by desc.n_vocab
+    SampleArgs sa;
+    rc = sample_args(c, n_seq, n_draft, head->n_vocab, nullptr, q_logits, drafts, history, history_stride,
+                     history_len, sp, round, out_tokens, out_n_accept, &sa);
+    if (rc != MTP_OK) return rc;
+    const int32_t rows = n_seq * (n_draft + 1);
+    rc = grow_scratch(c, reinterpret_cast<void **>(&c->hv_logits), &c->hv_logits_size,
+                      sizeof(float) * (size_t)rows * head->n_vocab);
+    if (rc != MTP_OK) return rc;
+    sa.p_logits = c->hv_logits;
+    ProfScope ps(c, MTP_PROF_VERIFY);
+    HvArgs a = hidden_args(c, head, hidden);
+    a.logits = c->hv_logits;
+    hipError_t e = launch_verify_hidden(a, rows, c->stream);
+    if (e == hipSuccess) e = launch_verify_sample(sa, c->stream);
+    return e == hipSuccess ? MTP_OK : hip_fail("hidden-state sampling verify launch", e);
 }

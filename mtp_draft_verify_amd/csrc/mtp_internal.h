@@ -195,6 +195,7 @@ struct HvArgs {
     const void *head;       // [V, d] bf16
     void *plane;            // scratch: hv_plane_bytes(d) bytes
     uint64_t *keys;         // [rows] argmax keys, zero before; indexed by row
+    float *logits;          // [rows, V] logit rows instead of keys (or null)
 };
 size_t hv_plane_bytes(int32_t d);
 hipError_t launch_verify_hidden(const HvArgs &a, int32_t rows, hipStream_t st);

@@ -464,12 +464,35 @@ int orc_verify_greedy(int32_t n_seq, int32_t n_draft, int32_t n_vocab, const flo
     return 0;
 }
 
-/* Hidden-state greedy verify ("MTP decoding", "Why a wider decode can be
-   faster": the 1 + N verify rows meet the target's head weights in one pass).
-   Row i of sequence s is the target's final hidden state h; f = rmsnorm(h; g)
+/* The target's logit rows from its final hidden rows ("MTP decoding", "Why
+   a wider decode can be faster": the 1 + N verify rows meet the target's head
+   weights in one pass).  Row r is the final hidden state h; f = rmsnorm(h; g)
    (f = h when g is NULL: the caller already normed it), z = W_head f in fp64,
-   rounded to fp32 as the target's logit row is, then the greedy acceptance of
-   orc_verify_greedy.  out_margin[row] (optional) is the row's top-2 gap. */
+   rounded to fp32 as the target's logit row is.  Returns a malloc'd
+   [rows, n_vocab] array, or NULL when out of memory. */
+static float *hidden_logits(int64_t rows, int32_t n_vocab, int32_t d, const float *hidden, const void *head,
+                            int32_t head_dtype, const float *g, double eps) {
+    double *f = (double *)malloc(sizeof(double) * (size_t)(rows * d));
+    double *z = (double *)malloc(sizeof(double) * (size_t)(rows * n_vocab));
+    float *z32 = (float *)malloc(sizeof(float) * (size_t)(rows * n_vocab));
+    if (!f || !z || !z32) {
+        free(f); free(z); free(z32);
+        return NULL;
+    }
+    for (int64_t r = 0; r < rows; ++r) {
+        double *fr = f + r * d;
+        for (int32_t c = 0; c < d; ++c) fr[c] = (double)hidden[r * d + c];
+        if (g) orc_rmsnorm(d, fr, g, eps, fr);
+    }
+    gemv_batch(head, head_dtype, n_vocab, d, (int32_t)rows, f, d, z, n_vocab);
+    for (int64_t i = 0; i < rows * n_vocab; ++i) z32[i] = (float)z[i];
+    free(f); free(z);
+    return z32;
+}
+
+/* Hidden-state greedy verify: the logit rows of hidden_logits, then the
+   greedy acceptance of orc_verify_greedy.  out_margin[row] (optional) is the
+   row's top-2 gap. */
 int orc_verify_greedy_hidden(int32_t n_seq, int32_t n_draft, int32_t n_vocab, int32_t d, const float *hidden,
                              const void *head, int32_t head_dtype, const float *g, double eps,
                              const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept,
@@ -479,24 +502,12 @@ int orc_verify_greedy_hidden(int32_t n_seq, int32_t n_draft, int32_t n_vocab, in
         return -1;
     if (head_dtype == ORC_Q8_0 && d % 32) return -1;
     const int64_t rows = (int64_t)n_seq * (n_draft + 1);
-    double *f = (double *)malloc(sizeof(double) * (size_t)(rows * d));
-    double *z = (double *)malloc(sizeof(double) * (size_t)(rows * n_vocab));
-    float *z32 = (float *)malloc(sizeof(float) * (size_t)(rows * n_vocab));
-    if (!f || !z || !z32) {
-        free(f); free(z); free(z32);
-        return -4;
-    }
-    for (int64_t r = 0; r < rows; ++r) {
-        double *fr = f + r * d;
-        for (int32_t c = 0; c < d; ++c) fr[c] = (double)hidden[r * d + c];
-        if (g) orc_rmsnorm(d, fr, g, eps, fr);
-    }
-    gemv_batch(head, head_dtype, n_vocab, d, (int32_t)rows, f, d, z, n_vocab);
-    for (int64_t i = 0; i < rows * n_vocab; ++i) z32[i] = (float)z[i];
+    float *z32 = hidden_logits(rows, n_vocab, d, hidden, head, head_dtype, g, eps);
+    if (!z32) return -4;
     if (out_margin)
         for (int64_t r = 0; r < rows; ++r) orc_argmax_f32(n_vocab, z32 + r * n_vocab, &out_margin[r]);
     const int rc = orc_verify_greedy(n_seq, n_draft, n_vocab, z32, drafts, out_tokens, out_n_accept);
-    free(f); free(z); free(z32);
+    free(z32);
     return rc;
 }
 
@@ -739,6 +750,23 @@ int orc_verify_sample(int32_t n_seq, int32_t n_draft, int32_t V, const float *p_
         free(p); free(q); free(r); free(e); free(ctx);
     }
     return err;
+}
+
+/* Hidden-state sampling verify: the logit rows of hidden_logits, then the
+   exact speculative sampling of orc_verify_sample on them. */
+int orc_verify_sample_hidden(int32_t n_seq, int32_t n_draft, int32_t n_vocab, int32_t d, const float *hidden,
+                             const void *head, int32_t head_dtype, const float *g, double eps,
+                             const float *q_logits, const int32_t *drafts, const int32_t *history,
+                             int32_t history_stride, const int32_t *history_len, const orc_sampler *sp,
+                             uint64_t round, int32_t *out_tokens, int32_t *out_n_accept, int32_t *out_flags) {
+    if (n_seq <= 0 || n_draft < 0 || n_vocab <= 0 || d <= 0 || !hidden || !head) return -1;
+    if (head_dtype == ORC_Q8_0 && d % 32) return -1;
+    float *z32 = hidden_logits((int64_t)n_seq * (n_draft + 1), n_vocab, d, hidden, head, head_dtype, g, eps);
+    if (!z32) return -4;
+    const int rc = orc_verify_sample(n_seq, n_draft, n_vocab, z32, q_logits, drafts, history, history_stride,
+                                     history_len, sp, round, out_tokens, out_n_accept, out_flags);
+    free(z32);
+    return rc;
 }
 
 int orc_verify_greedy_match(int32_t n_seq, int32_t n_draft, int32_t V, const float *p_logits, const int32_t *drafts,

@@ -137,6 +137,12 @@ int orc_verify_sample(int32_t n_seq, int32_t n_draft, int32_t n_vocab, const flo
                       const float *q_logits, const int32_t *drafts, const int32_t *history,
                       int32_t history_stride, const int32_t *history_len, const orc_sampler *sp,
                       uint64_t round, int32_t *out_tokens, int32_t *out_n_accept, int32_t *out_flags);
+/* the logit rows of the hidden-state greedy verify, then orc_verify_sample */
+int orc_verify_sample_hidden(int32_t n_seq, int32_t n_draft, int32_t n_vocab, int32_t d, const float *hidden,
+                             const void *head, int32_t head_dtype, const float *g, double eps,
+                             const float *q_logits, const int32_t *drafts, const int32_t *history,
+                             int32_t history_stride, const int32_t *history_len, const orc_sampler *sp,
+                             uint64_t round, int32_t *out_tokens, int32_t *out_n_accept, int32_t *out_flags);
 
 /* the old temperature>0 rule the pages replace: drafts kept while they equal
    the raw argmax, only the first non-matching row sampled (negative control) */

@@ -100,6 +100,9 @@ def lib():
         L.orc_sample_dist.argtypes = [C.c_int32, P, P, C.c_int32, C.POINTER(OrcSampler), P, P]
         L.orc_verify_sample.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
                                         C.POINTER(OrcSampler), C.c_uint64, P, P, P]
+        L.orc_verify_sample_hidden.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int32, P, P, C.c_int32, P,
+                                               C.c_double, P, P, P, C.c_int32, P, C.POINTER(OrcSampler),
+                                               C.c_uint64, P, P, P]
         L.orc_verify_greedy_match.argtypes = [C.c_int32, C.c_int32, C.c_int32, P, P, P, C.c_int32, P,
                                               C.POINTER(OrcSampler), C.c_uint64, P, P]
         L.orc_sample_row.restype = C.c_int32
@@ -283,6 +286,32 @@ def verify_sample(p_logits, q_logits, drafts, history, history_len, sp: syn.Samp
                                  _p(history_len), C.byref(o), round_, _p(tokens), _p(n_acc), _p(flags))
     if rc != 0:
         raise RuntimeError(f"orc_verify_sample failed: {rc}")
+    return tokens, n_acc, flags
+
+
+def verify_sample_hidden(hidden: np.ndarray, head: np.ndarray, head_dtype: int, n_vocab: int, g, eps: float,
+                         q_logits, drafts, history, history_len, sp: syn.Sampler, round_: int = 0):
+    """hidden fp32 [S, N+1, d] and the head as for verify_greedy_hidden; the
+    rest as for verify_sample.  -> (tokens, n_accept, flags)"""
+    hidden = np.ascontiguousarray(hidden, dtype=np.float32)
+    head = np.ascontiguousarray(head)
+    q_logits = None if q_logits is None else np.ascontiguousarray(q_logits, dtype=np.float32)
+    drafts = np.ascontiguousarray(drafts, dtype=np.int32)
+    history = np.ascontiguousarray(history, dtype=np.int32)
+    history_len = np.ascontiguousarray(history_len, dtype=np.int32)
+    gp = None if g is None else np.ascontiguousarray(g, dtype=np.float32)
+    S, R, d = hidden.shape
+    tokens = np.zeros((S, R), np.int32)
+    n_acc = np.zeros(S, np.int32)
+    flags = np.zeros(S, np.int32)
+    o = sampler_struct(sp)
+    rc = lib().orc_verify_sample_hidden(S, R - 1, int(n_vocab), d, _p(hidden), _p(head), int(head_dtype),
+                                        _p(gp) if gp is not None else None, float(eps), _p(q_logits),
+                                        _p(drafts) if drafts.size else None, _p(history) if history.size else None,
+                                        history.shape[1] if history.ndim == 2 else 0, _p(history_len), C.byref(o),
+                                        round_, _p(tokens), _p(n_acc), _p(flags))
+    if rc != 0:
+        raise RuntimeError(f"orc_verify_sample_hidden failed: {rc}")
     return tokens, n_acc, flags
 
 

@@ -85,6 +85,10 @@ def test_entry_points_reject_null_context_without_device_work(mtp):
     sp = mtp.make_sampler(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4)
     assert L.mtp_verify_sample(None, 1, 1, 10, None, None, None, None, 0, None, C.byref(sp), 0, None,
                                None) == mtp.MTP_E_INVAL
+    assert L.mtp_verify_sample_hidden(None, 1, 3, C.byref(head), None, None, None, None, 0, None, C.byref(sp), 0,
+                                      None, None) == mtp.MTP_E_INVAL
+    assert L.mtp_verify_sample_hidden(None, 1, 3, C.byref(head), None, None, None, None, 0, None, None, 0,
+                                      None, None) == mtp.MTP_E_INVAL
     assert L.mtp_ctx_create(None, None, None, None) == mtp.MTP_E_INVAL
     assert L.mtp_profile_enable(None, 1) == mtp.MTP_E_INVAL
     assert L.mtp_profile_read(None, 0, None, None) == mtp.MTP_E_INVAL

@@ -1,12 +1,16 @@
-"""GPU parity of the greedy verify from hidden states (through the C ABI)
-against the oracle: the target's final RMSNorm, its LM head over the 1 + N
-verify rows of every sequence and the argmax, fused ("MTP decoding", why a
-wider decode can be faster).
+"""GPU parity of the verifies from hidden states (through the C ABI) against
+the oracle: the target's final RMSNorm and its LM head over the 1 + N verify
+rows of every sequence in one pass over the weights ("MTP decoding", why a
+wider decode can be faster), then the greedy argmax, or the exact sampling
+verify on the logit rows.
 
-Tokens and accept lengths must match bit for bit, except after a row whose
-oracle top-2 margin is below the bf16 logit tolerance (a near tie, counted and
-reported separately).
+Greedy: tokens and accept lengths must match bit for bit, except after a row
+whose oracle top-2 margin is below the bf16 logit tolerance (a near tie,
+counted and reported separately).  Sampling: sequences whose oracle run
+flagged no near-boundary decision must match bit for bit.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -38,10 +42,10 @@ def _run(ctx, hv, reps=1):
     return outs
 
 
-def _ctx(max_seqs, max_steps):
+def _ctx(max_seqs, max_steps, n_vocab=4096):
     import mtp_draft_verify_amd as mtp
     desc = mtp.make_desc(d_model=256, d_hprev=256, n_blocks=1, n_head_q=4, n_head_kv=1, head_dim=64, d_ff=1024,
-                         n_vocab=4096, w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32,
+                         n_vocab=n_vocab, w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32,
                          max_seqs=max_seqs, max_steps=max_steps)
     return mtp.Context(desc, None)
 
@@ -107,4 +111,96 @@ def test_hidden_verify_scratch_grows_with_the_head_width(orc):
         hv = syn.make_hidden_verify(5 + d, 4, 3, d, 6000)
         (tok, na), = _run(ctx, hv)
         assert _compare(hv, tok, na, orc, list(range(4))) <= 1
+    ctx.close()
+
+
+# ------------------------------------------------- sampling verify from hidden rows
+def _run_sample(ctx, hv, q, history, history_len, sp, round_):
+    import torch
+    import mtp_draft_verify_amd as mtp
+    dev = "cuda"
+    w = torch.from_numpy(hv.head.view(np.int16)).to(dev)
+    g = torch.from_numpy(hv.g).to(dev) if hv.g is not None else None
+    head = mtp.make_lm_head(w, g, hv.d, hv.n_vocab, mtp.MTP_BF16, hv.eps)
+    hidden = torch.from_numpy(hv.hidden).to(dev)
+    drafts = torch.from_numpy(hv.drafts).to(dev)
+    qt = torch.from_numpy(q).to(dev) if q is not None else None
+    ht = torch.from_numpy(history).to(dev)
+    hl = torch.from_numpy(history_len).to(dev)
+    S, R = hv.hidden.shape[:2]
+    tok = torch.full((S, R), -7, dtype=torch.int32, device=dev)
+    na = torch.full((S,), -7, dtype=torch.int32, device=dev)
+    s = mtp.make_sampler(temp=sp.temp, top_p=sp.top_p, min_p=sp.min_p, rep_penalty=sp.rep_penalty,
+                         presence_penalty=sp.presence_penalty, freq_penalty=sp.freq_penalty, top_k=sp.top_k,
+                         penalty_last_n=sp.penalty_last_n, seed=sp.seed)
+    ctx.verify_sample_hidden(head, hidden, qt, drafts, ht, hl, s, round_, tok, na)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), na.cpu().numpy()
+
+
+def _sample_case(seed, S, N, d, V, gain, one_hot):
+    """Broad target rows (a weakly planted token, beta 0.1), drafts mostly the
+    planted tokens, q rows N(0, 3) (or one-hot), 40-token histories of varied
+    length."""
+    hv = syn.make_hidden_verify(seed, S, N, d, V, gain=gain, beta=0.1, p_accept=0.7)
+    r = np.random.default_rng(seed)
+    q = None if one_hot else (math.sqrt(3.0) * r.standard_normal((S, N, V))).astype(np.float32)
+    history = r.integers(0, V, (S, 40)).astype(np.int32)
+    history_len = r.integers(0, 41, S).astype(np.int32)
+    return hv, q, history, history_len
+
+
+SAMPLER = syn.Sampler(temp=0.8, top_p=0.95, min_p=0.05, rep_penalty=1.05, presence_penalty=0.2, freq_penalty=0.0,
+                      top_k=0, penalty_last_n=32, seed=7)
+
+
+def _compare_sample(orc, ctx, hv, q, history, history_len, sp, round_):
+    """Unflagged sequences (no near-boundary decision in the oracle run) must
+    match bit for bit; the logits differ from the oracle's by fp32 rounding,
+    far inside the flags' 1e-5 windows.  Returns the flagged count."""
+    t_o, n_o, fl = orc.verify_sample_hidden(hv.hidden, hv.head, hv.head_dtype, hv.n_vocab, hv.g, hv.eps, q,
+                                            hv.drafts, history, history_len, sp, round_)
+    t_g, n_g = _run_sample(ctx, hv, q, history, history_len, sp, round_)
+    clean = fl == 0
+    bad = np.nonzero(clean & ((n_g != n_o) | np.any(t_g != t_o, axis=1)))[0]
+    log(f"  S={len(fl)} flagged={int((~clean).sum())} accept_mean={n_o.mean():.3f} mismatches_on_clean={len(bad)}")
+    assert len(bad) == 0, (bad[:5], t_g[bad[:3]], t_o[bad[:3]], n_g[bad[:3]], n_o[bad[:3]])
+    assert (t_g[:, 0] >= 0).all() and (n_g >= 0).all()
+    return int((~clean).sum())
+
+
+@pytest.mark.parametrize("S,N,d,V,gain,one_hot", [
+    (6, 3, 256, 20000 - 123, True, False),      # 24 rows, ragged vocabulary, q rows
+    (8, 4, 512, 9000, False, True),             # 40 rows, no norm, one-hot drafts
+    (16, 4, 768, 16387, True, False),           # 80 rows: a 64-row pass and a 16-row pass
+    (5, 0, 256, 5000, True, True),              # no drafts: only the bonus token
+])
+def test_hidden_sampling_verify_shapes(orc, S, N, d, V, gain, one_hot):
+    log(f"case hidden sampling verify: S={S} N={N} d={d} V={V} gain={gain} one_hot={one_hot}")
+    hv, q, history, history_len = _sample_case(31 + d, S, N, d, V, gain, one_hot)
+    ctx = _ctx(16, 4, V)
+    flagged = sum(_compare_sample(orc, ctx, hv, q, history, history_len, SAMPLER, rd) for rd in (0, 5))
+    assert flagged <= S
+    ctx.close()
+
+
+def test_hidden_sampling_verify_full_width(orc):
+    """The c8 head shape (d 2816, V 262144, bf16, gain) on 4 sequences x 4 rows."""
+    log("case hidden sampling verify full width: d 2816, V 262144, 4 seqs x 4 rows")
+    hv, q, history, history_len = _sample_case(77, 4, 3, 2816, 262144, True, False)
+    ctx = _ctx(4, 3, 262144)
+    _compare_sample(orc, ctx, hv, q, history, history_len, SAMPLER, 2)
+    ctx.close()
+
+
+def test_hidden_sampling_then_greedy_reuses_the_context(orc):
+    """A sampling verify from hidden rows leaves no state behind: a greedy one
+    on the same context right after still matches the oracle."""
+    log("case hidden sampling then greedy on one context")
+    ctx = _ctx(8, 3, 7000)
+    hv, q, history, history_len = _sample_case(5, 8, 3, 512, 7000, True, False)
+    _compare_sample(orc, ctx, hv, q, history, history_len, SAMPLER, 0)
+    hv2 = syn.make_hidden_verify(9, 8, 3, 512, 7000, p_accept=0.7)
+    (tok, na), = _run(ctx, hv2)
+    assert _compare(hv2, tok, na, orc, list(range(8))) <= 1
     ctx.close()

@@ -677,6 +677,32 @@ def test_hidden_verify_recovers_planted_rows(orc):
     assert 0 < n.sum() < 18
 
 
+def test_sample_hidden_with_signed_identity_head_is_the_logit_row_sampling_verify(orc):
+    """Head [I; -I] without a norm makes row i's logits exactly (h_i, -h_i), so
+    the hidden-state sampling verify must return what the logit-row sampling
+    verify returns on those rows: same tokens, accept lengths and near-boundary
+    flags, with q rows, history penalties, min-p and top-p in play."""
+    S, N, d = 8, 3, 64
+    V = 2 * d
+    r = np.random.default_rng(23)
+    head = np.concatenate([np.eye(d), -np.eye(d)]).astype(np.float32)
+    h = (1.5 * r.standard_normal((S, N + 1, d))).astype(np.float32)
+    z = np.concatenate([h, -h], axis=2)
+    q = (z[:, :N] + r.standard_normal((S, N, V))).astype(np.float32)
+    drafts = np.stack([[r.choice(V, p=np.exp(q[s, i]) / np.exp(q[s, i]).sum()) for i in range(N)]
+                       for s in range(S)]).astype(np.int32)
+    drafts[:, 0] = z[:, 0].argmax(axis=1)        # some accepted first drafts
+    history = r.integers(0, V, (S, 16)).astype(np.int32)
+    history_len = np.full(S, 16, np.int32)
+    sp = _sp(temp=0.7, top_p=0.9, min_p=0.02, rep_penalty=1.1, presence_penalty=0.2, penalty_last_n=8, seed=5)
+    for q_rows in (q, None):
+        t_h, n_h, f_h = orc.verify_sample_hidden(h, head, syn.F32, V, None, 1e-6, q_rows, drafts, history,
+                                                 history_len, sp, 3)
+        t_z, n_z, f_z = orc.verify_sample(z, q_rows, drafts, history, history_len, sp, 3)
+        assert (t_h == t_z).all() and (n_h == n_z).all() and (f_h == f_z).all()
+        assert (t_h[:, 0] >= 0).all()
+
+
 # ------------------------------------------------------------ sampling chain
 def _sp(**kw):
     base = dict(temp=1.0, top_p=1.0, min_p=0.0, rep_penalty=1.0, presence_penalty=0.0, freq_penalty=0.0, top_k=0,
