@@ -115,22 +115,31 @@ __device__ __forceinline__ float chain_value(const SampleArgs &a, float z, int c
     return z / a.temp;
 }
 
-// block-wide helpers (256 threads)
+// block-wide helpers (NT threads, NT / 64 waves; red holds NT / 64 floats)
+template <int NT = kBlock>
 __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max(v);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+    return m;
 }
+template <int NT = kBlock>
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) red[wid] = v;
     __syncthreads();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    // pairwise in a fixed order: (0 + 1) + (2 + 3), then those sums in order
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w += 4) tot += (red[w] + red[w + 1]) + (red[w + 2] + red[w + 3]);
+    return tot;
 }
 
 // Context of one row in LDS: token list, and a bitmap over [c0, c0 + nbits).
@@ -152,14 +161,15 @@ __device__ void load_ctx(const SampleArgs &a, int s, int i, int c0, int nbits, C
 }
 
 // sort a context list of n <= kMaxCtx tokens ascending in place (LDS, bitonic)
+template <int NT>
 __device__ void sort_ctx(int32_t *tok, int n) {
     int np2 = 1;
     while (np2 < n) np2 <<= 1;
-    for (int j = n + threadIdx.x; j < np2; j += kBlock) tok[j] = 0x7FFFFFFF;
+    for (int j = n + threadIdx.x; j < np2; j += NT) tok[j] = 0x7FFFFFFF;
     __syncthreads();
     for (int k = 2; k <= np2; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int x = threadIdx.x; x < np2; x += kBlock) {
+            for (int x = threadIdx.x; x < np2; x += NT) {
                 const int y = x ^ j;
                 if (y > x) {
                     const bool up = (x & k) == 0;
@@ -197,15 +207,15 @@ __device__ __forceinline__ float token_value(const SampleArgs &a, const float *z
 // radix select over one row: the largest 64-bit key K with W(key >= K) >= target,
 // where W sums weight(t) over the row's eligible tokens.  8 passes of 8 bits.
 // ---------------------------------------------------------------------------
-template <typename KeyW>
+template <int NT, typename KeyW>
 __device__ uint64_t radix_select(int V, uint64_t target, KeyW key_weight, uint64_t *hist /* [256] LDS */,
                                  uint64_t *scal /* [4] LDS */) {
     uint64_t prefix = 0, mask = 0;
     for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
-        for (int b = threadIdx.x; b < 256; b += kBlock) hist[b] = 0;
+        for (int b = threadIdx.x; b < 256; b += NT) hist[b] = 0;
         __syncthreads();
-        for (int t = threadIdx.x; t < V; t += kBlock) {
+        for (int t = threadIdx.x; t < V; t += NT) {
             uint64_t k, wgt;
             if (!key_weight(t, k, wgt)) continue;
             if ((k & mask) != prefix) continue;
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
         w = 1;
         return true;
     };
-    const uint64_t K = radix_select(a.V, (uint64_t)a.top_k, kw, hist, scal);
+    const uint64_t K = radix_select<kBlock>(a.V, (uint64_t)a.top_k, kw, hist, scal);
     if (threadIdx.x == 0) a.topk_key[row] = K;
 }
 
@@ -298,11 +308,17 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
 // row finalisation
 // ---------------------------------------------------------------------------
 static constexpr int kSortMax = 4096;
+// The row and sequence kernels run one workgroup per row / sequence; a
+// broad row (more candidates than kSortMax) makes them walk the whole
+// vocabulary several times, so they take 16 waves.
+static constexpr int kRowThreads = 1024;
+static constexpr int kPrefixBlocks = 256;   // blocks of the sorted candidates' prefix sums
 
-__global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
+    constexpr int NT = kRowThreads;
     __shared__ uint64_t keys[kSortMax];
-    __shared__ float part[kBlock];
-    __shared__ float red[4];
+    __shared__ float part[kPrefixBlocks];
+    __shared__ float red[NT / 64];
     __shared__ int cut_sh;
     __shared__ uint64_t hist[256], scal[4];
     const int row = blockIdx.x;
@@ -317,12 +333,12 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
         const int n = n_all;
         int np2 = 1;
         while (np2 < n) np2 <<= 1;
-        for (int j = tid; j < np2; j += kBlock)
+        for (int j = tid; j < np2; j += NT)
             keys[j] = j < n ? tok_key(a.cand_v[(int64_t)row * a.cap + j], a.cand_id[(int64_t)row * a.cap + j]) : 0ull;
         __syncthreads();
         for (int k = 2; k <= np2; k <<= 1) {           // bitonic sort, descending
             for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int x = tid; x < np2; x += kBlock) {
+                for (int x = tid; x < np2; x += NT) {
                     const int y = x ^ j;
                     if (y > x) {
                         const bool desc = (x & k) == 0;
@@ -335,21 +351,23 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
         }
         // inclusive prefix sums of e in sorted order: contiguous per-thread
         // blocks, then a serial scan of the block totals (fixed order)
-        const int per = (n + kBlock - 1) / kBlock;
-        const int b0 = tid * per, b1 = min(n, b0 + per);
+        // (kPrefixBlocks contiguous blocks, whatever the workgroup size)
+        constexpr int PB = kPrefixBlocks;
+        const int per = (n + PB - 1) / PB;
+        const int b0 = tid < PB ? tid * per : n, b1 = min(n, b0 + per);
         float run = 0.f;
         for (int j = b0; j < b1; ++j) run += fkey_inv((uint32_t)(keys[j] >> 32));
-        part[tid] = run;
+        if (tid < PB) part[tid] = run;
         if (tid == 0) cut_sh = n - 1;
         __syncthreads();
         if (tid == 0) {
             float acc = 0.f;
-            for (int b = 0; b < kBlock; ++b) { const float t = part[b]; part[b] = acc; acc += t; }
+            for (int b = 0; b < PB; ++b) { const float t = part[b]; part[b] = acc; acc += t; }
             red[0] = acc;
         }
         __syncthreads();
         const float Z2 = red[0];
-        if (a.top_p < 1.f) {
+        if (a.top_p < 1.f && tid < PB) {
             float cum = part[tid];
             for (int j = b0; j < b1; ++j) {
                 cum += fkey_inv((uint32_t)(keys[j] >> 32));
@@ -368,7 +386,7 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
             st.n_keep = cut + 1;
             ((RowState *)a.row_state)[row] = st;
         }
-        for (int j = tid; j <= cut; j += kBlock) {
+        for (int j = tid; j <= cut; j += NT) {
             a.cand_id[(int64_t)row * a.cap + j] = (int32_t)(0xFFFFFFFFu - (uint32_t)keys[j]);
             a.cand_v[(int64_t)row * a.cap + j] = fkey_inv((uint32_t)(keys[j] >> 32));
         }
@@ -378,9 +396,9 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
     const RowRef rr = row_ref(a, row);
     __shared__ int32_t ctx_tok[kMaxCtx];
     const int n_ctx = ctx_len(a, rr.s, rr.i);
-    for (int j = tid; j < n_ctx; j += kBlock) ctx_tok[j] = ctx_token(a, rr.s, rr.i, n_ctx, j);
+    for (int j = tid; j < n_ctx; j += NT) ctx_tok[j] = ctx_token(a, rr.s, rr.i, n_ctx, j);
     __syncthreads();
-    sort_ctx(ctx_tok, n_ctx);
+    sort_ctx<NT>(ctx_tok, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     auto e_of = [&](int t, float &e) {
         const float raw = rr.z[t];
@@ -389,11 +407,11 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
         return e >= a.min_p;
     };
     float z2 = 0.f;
-    for (int t = tid; t < a.V; t += kBlock) {
+    for (int t = tid; t < a.V; t += NT) {
         float e;
         if (e_of(t, e)) z2 += e;
     }
-    const float Z2 = block_sum(z2, red);
+    const float Z2 = block_sum<NT>(z2, red);
     uint64_t tau = 0;
     if (a.top_p < 1.f) {
         // fixed-point weights (2^40 per unit) keep the histogram sums exact
@@ -406,14 +424,14 @@ __global__ __launch_bounds__(256) void sample_row_kernel(SampleArgs a) {
             w = (uint64_t)((double)e * scale);
             return true;
         };
-        tau = radix_select(a.V, target, kw, hist, scal);
+        tau = radix_select<NT>(a.V, target, kw, hist, scal);
     }
     float z3 = 0.f;
-    for (int t = tid; t < a.V; t += kBlock) {
+    for (int t = tid; t < a.V; t += NT) {
         float e;
         if (e_of(t, e) && tok_key(e, t) >= tau) z3 += e;
     }
-    const float Z3 = block_sum(z3, red);
+    const float Z3 = block_sum<NT>(z3, red);
     if (tid == 0) {
         st.Z = Z3;
         st.tau = tau;
@@ -438,9 +456,10 @@ __device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t
     return e / st.Z;
 }
 
-__global__ __launch_bounds__(256) void sample_seq_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
+    constexpr int NT = kRowThreads;
     __shared__ int32_t ctx_tok[kMaxCtx];
-    __shared__ uint64_t best_w[4];
+    __shared__ uint64_t best_w[NT / 64];
     __shared__ int decision;
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int N = a.N, R = N + 1;
@@ -449,9 +468,9 @@ __global__ __launch_bounds__(256) void sample_seq_kernel(SampleArgs a) {
         const int prow = s * R + i;
         const int n_ctx = ctx_len(a, s, i);
         __syncthreads();
-        for (int j = tid; j < n_ctx; j += kBlock) ctx_tok[j] = ctx_token(a, s, i, n_ctx, j);
+        for (int j = tid; j < n_ctx; j += NT) ctx_tok[j] = ctx_token(a, s, i, n_ctx, j);
         __syncthreads();
-        sort_ctx(ctx_tok, n_ctx);
+        sort_ctx<NT>(ctx_tok, n_ctx);
         const int32_t d = i < N ? a.drafts[(int64_t)s * N + i] : -1;
         const int qrow = a.q_logits ? a.S * R + s * N + i : -1;
         if (i < N) {
@@ -481,10 +500,10 @@ __global__ __launch_bounds__(256) void sample_seq_kernel(SampleArgs a) {
             best = k > best ? k : best;
         };
         if (st.n_keep >= 0) {
-            for (int j = tid; j < st.n_keep; j += kBlock)
+            for (int j = tid; j < st.n_keep; j += NT)
                 consider(a.cand_id[(int64_t)prow * a.cap + j], a.cand_v[(int64_t)prow * a.cap + j] / st.Z);
         } else {
-            for (int t = tid; t < a.V; t += kBlock) {
+            for (int t = tid; t < a.V; t += NT) {
                 const float pt = row_prob(a, prow, t, ctx_tok, n_ctx);
                 if (pt > 0.f) consider(t, pt);
             }
@@ -499,23 +518,23 @@ __global__ __launch_bounds__(256) void sample_seq_kernel(SampleArgs a) {
         __syncthreads();
         if (tid == 0) {
             uint64_t b = best_w[0];
-            for (int w = 1; w < 4; ++w) b = best_w[w] > b ? best_w[w] : b;
+            for (int w = 1; w < NT / 64; ++w) b = best_w[w] > b ? best_w[w] : b;
             a.out_tokens[(int64_t)s * R + i] = b ? (int32_t)(0xFFFFFFFFu - (uint32_t)b) : -1;
         }
         n_acc = i < N ? i : N;
         if (i < N) {
-            for (int j = i + 1 + tid; j < R; j += kBlock) a.out_tokens[(int64_t)s * R + j] = -1;
+            for (int j = i + 1 + tid; j < R; j += NT) a.out_tokens[(int64_t)s * R + j] = -1;
         }
         break;
     }
     if (tid == 0) a.out_n_accept[s] = n_acc;
     // clear this sequence's row scratch for the next call
-    for (int i = tid; i < R; i += kBlock) {
+    for (int i = tid; i < R; i += NT) {
         a.row_maxkey[s * R + i] = 0u;
         a.cand_n[s * R + i] = 0;
     }
     if (a.q_logits)
-        for (int i = tid; i < N; i += kBlock) {
+        for (int i = tid; i < N; i += NT) {
             a.row_maxkey[a.S * R + s * N + i] = 0u;
             a.cand_n[a.S * R + s * N + i] = 0;
         }
@@ -531,8 +550,8 @@ hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st) {
     }
     hipLaunchKernelGGL(sample_max_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
     hipLaunchKernelGGL(sample_cand_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kBlock), 0, st, a);
-    hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kRowThreads), 0, st, a);
+    hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();
 }
 
