@@ -469,37 +469,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                                                  int tiles_per_wg) {
     extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
     __shared__ u32x4_t mm_tr[4][kTrSlots];  // one weight transpose tile per wave
-    __shared__ float rs[kMaxSeqGroup];
+    __shared__ float rsw[4][16];            // per-wave partial sums of squares of each sequence
     __shared__ uint64_t wbest[4][16];
     __shared__ float wcm[4][16], wcs[4][16];
     __shared__ f32x4_t post_part[4][64];    // per-wave partial sums of a post-projection tile
-    const int d = a.d, S = a.S, KS = d / 32;
+    const int d = a.d, S = a.S;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int hb = blockIdx.x;
 
     // f = rmsnorm(x; g_final) -> activation halves (sequences >= S stay zero),
-    // run by head_tiles once its first weights are requested
+    // run by head_tiles once its first weights are requested.  Thread tid
+    // stages the slots tid + 256 k, all of sequence s = tid % 16: it loads
+    // its 16 * UPT column groups of x and of the gain at once, sums its
+    // squares, and the 16 threads of a sequence (4 lanes of each wave) add
+    // theirs in a fixed order, so the stage costs one memory round trip.
     auto stage = [&]() {
-        for (int j = wid; j < S; j += 4) {
-            const float *x = a.x + (int64_t)j * d;
-            float ss = 0.f;
-            for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
-            ss = wave_sum(ss);
-            if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
+        constexpr int NIT = 2 * UPT;        // KS * 64 / 256 slots per thread
+        const int s = tid & 15;
+        const float *xs = a.x + (int64_t)min(s, S - 1) * d;
+        float v[NIT][8], gv[NIT][8];
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) {
+            const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
+            const int col = 32 * t + 8 * g;
+            const float4 x0 = *(const float4 *)(xs + col), x1 = *(const float4 *)(xs + col + 4);
+            const float4 g0 = *(const float4 *)(a.g_final + col), g1 = *(const float4 *)(a.g_final + col + 4);
+            v[k][0] = x0.x; v[k][1] = x0.y; v[k][2] = x0.z; v[k][3] = x0.w;
+            v[k][4] = x1.x; v[k][5] = x1.y; v[k][6] = x1.z; v[k][7] = x1.w;
+            gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
+            gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
         }
+        float ss = 0.f;
+#pragma unroll
+        for (int k = 0; k < NIT; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(v[k][e], v[k][e], ss);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (lane < 16) rsw[wid][lane] = ss;
         __syncthreads();
-        for (int it = tid; it < KS * 64; it += 256) {
-            const int s = it & 15, g = (it >> 4) & 3, t = it >> 6;
+        const float r = 1.0f / sqrtf(((rsw[0][s] + rsw[1][s]) + (rsw[2][s] + rsw[3][s])) / (float)d + a.eps);
+#pragma unroll
+        for (int k = 0; k < NIT; ++k) {
+            const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
             u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
             if (s < S) {
-                const int col = 32 * t + 8 * g;
-                const float4 *xp = (const float4 *)(a.x + (int64_t)s * d + col);
-                const float4 *gp = (const float4 *)(a.g_final + col);
-                const float4 x0 = xp[0], x1 = xp[1], g0 = gp[0], g1 = gp[1];
-                const float r = rs[s];
-                const float v[8] = {x0.x * r * g0.x, x0.y * r * g0.y, x0.z * r * g0.z, x0.w * r * g0.w,
-                                    x1.x * r * g1.x, x1.y * r * g1.y, x1.z * r * g1.z, x1.w * r * g1.w};
-                split_bf16(v, hi, lo);
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = v[k][e] * r * gv[k][e];
+                split_bf16(f, hi, lo);
             }
             mm_bsm[bslot(t, 0, g, s)] = hi;
             mm_bsm[bslot(t, 1, g, s)] = lo;
