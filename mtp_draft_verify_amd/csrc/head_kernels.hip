@@ -87,44 +87,67 @@ __global__ __launch_bounds__(256) void head_kernel(HeadArgs a, int w_dtype) {
     const bool head_wg = (int)blockIdx.x < a.n_head_wg;
     if (head_wg) load_head_rows(r0 + wid * RU, wv, sc);
 
-    // f = rmsnorm(x; g_final)
-    for (int j = wid; j < S; j += 4) {
-        const float *x = a.x + (int64_t)j * d;
+    float fr[ONE ? NV : 1][EPV];
+    if (ONE && head_wg) {
+        // f = rmsnorm(x; g_final) for the one sequence, in registers: every
+        // wave loads its lanes' slices of x and of the gain at once and
+        // reduces the sum of squares itself (no LDS, no barrier)
+        float xr[NV][EPV], gr[NV][EPV];
+#pragma unroll
+        for (int v = 0; v < (ONE ? NV : 1); ++v) {
+            const int col = min(v * CPW + lane * EPV, d - EPV);     // clamped; tail columns zeroed by mask
+            const uint32_t m = v * CPW + lane * EPV < d ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+            for (int e4 = 0; e4 < EPV / 4; ++e4) {
+                const float4 x4 = *(const float4 *)(a.x + col + 4 * e4);
+                const float4 g4 = *(const float4 *)(a.g_final + col + 4 * e4);
+                xr[v][4 * e4 + 0] = __uint_as_float(__float_as_uint(x4.x) & m);
+                xr[v][4 * e4 + 1] = __uint_as_float(__float_as_uint(x4.y) & m);
+                xr[v][4 * e4 + 2] = __uint_as_float(__float_as_uint(x4.z) & m);
+                xr[v][4 * e4 + 3] = __uint_as_float(__float_as_uint(x4.w) & m);
+                gr[v][4 * e4 + 0] = g4.x; gr[v][4 * e4 + 1] = g4.y; gr[v][4 * e4 + 2] = g4.z; gr[v][4 * e4 + 3] = g4.w;
+            }
+        }
         float ss = 0.f;
-        for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
-        ss = wave_sum(ss);
-        if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
-    }
-    if (tid < 4 * kMaxSeqGroup) {
-        wbest[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0ull;
-        wcm[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = -INFINITY;
-        wcs[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0.f;
-    }
-    __syncthreads();
-    for (int i = tid; i < S * d; i += kBlock) {
-        const int j = i / d, c = i - j * d;
-        fs[i] = a.x[i] * rs[j] * a.g_final[c];
-    }
-    __syncthreads();
-
-    if ((int)blockIdx.x >= a.n_head_wg) {
-        float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
-        if (w_dtype == MTP_BF16) post_rows<uint16_t>(a, fs, h_out);
-        else post_rows<float>(a, fs, h_out);
-        return;
+#pragma unroll
+        for (int v = 0; v < (ONE ? NV : 1); ++v)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) ss = fmaf(xr[v][e], xr[v][e], ss);
+        const float r = 1.0f / sqrtf(wave_sum(ss) / (float)d + a.eps);
+#pragma unroll
+        for (int v = 0; v < (ONE ? NV : 1); ++v)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) fr[ONE ? v : 0][e] = xr[v][e] * r * gr[v][e];
+    } else {
+        // f = rmsnorm(x; g_final) staged in LDS for every sequence
+        for (int j = wid; j < S; j += 4) {
+            const float *x = a.x + (int64_t)j * d;
+            float ss = 0.f;
+            for (int c = lane; c < d; c += 64) ss = fmaf(x[c], x[c], ss);
+            ss = wave_sum(ss);
+            if (lane == 0) rs[j] = 1.0f / sqrtf(ss / (float)d + a.eps);
+        }
+        if (tid < 4 * kMaxSeqGroup) {
+            wbest[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0ull;
+            wcm[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = -INFINITY;
+            wcs[tid / kMaxSeqGroup][tid % kMaxSeqGroup] = 0.f;
+        }
+        __syncthreads();
+        for (int i = tid; i < S * d; i += kBlock) {
+            const int j = i / d, c = i - j * d;
+            fs[i] = a.x[i] * rs[j] * a.g_final[c];
+        }
+        __syncthreads();
+        if (!head_wg) {
+            float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
+            if (w_dtype == MTP_BF16) post_rows<uint16_t>(a, fs, h_out);
+            else post_rows<float>(a, fs, h_out);
+            return;
+        }
     }
     float *logits = LOGITS && a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : nullptr;
     const int64_t logits_stride = (int64_t)a.n_steps * a.V;
 
-    float fr[ONE ? NV : 1][EPV];
-    if (ONE) {
-#pragma unroll
-        for (int v = 0; v < (ONE ? NV : 1); ++v) {
-            const int col = v * CPW + lane * EPV;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) fr[v][e] = (col < d) ? fs[col + e] : 0.f;
-        }
-    }
     uint64_t best1 = 0ull;                  // one-sequence path keeps its best in a register
     float cm1 = -INFINITY, cs1 = 0.f;       // and its confidence partial
     constexpr bool conf = CONF;             // confidence partials requested
