@@ -237,7 +237,12 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
     bool ok = dalloc(&c->vkeys, S * R);
     {
         const size_t rows = S * (2 * (size_t)d.max_steps + 1);
-        c->s_cap = std::min(4096, d.n_vocab);
+        // candidate slots per row: a row's min-p survivors up to this many are
+        // kept as a list (sorted when there are at most 4096); at least 4096,
+        // at most 65536, within 64 MiB of lists for all rows
+        const size_t fit = ((size_t)8 << 20) / rows;
+        const size_t cap = std::max<size_t>(4096, std::min<size_t>(65536, fit)) & ~(size_t)255;
+        c->s_cap = (int32_t)std::min<size_t>(cap, (size_t)d.n_vocab);
         ok = ok && dalloc(&c->s_maxkey, rows) && dalloc(&c->s_topk, rows) && dalloc(&c->s_cand_n, rows) &&
              dalloc(&c->s_cand_id, rows * c->s_cap) && dalloc(&c->s_cand_v, rows * c->s_cap) &&
              dalloc((uint8_t **)&c->s_state, rows * sample_row_state_bytes());

@@ -14,11 +14,13 @@
 //   max    per (row, 8192-token chunk): max of the penalised, tempered logit
 //   cand   per (row, chunk): tokens with exp(v - M) >= min_p join the row's
 //          candidate list (order fixed later by sorting)
-//   row    one workgroup per row: sort candidates by (prob desc, id asc),
-//          cumulative sums in a fixed tree order, top-p cut, normaliser; when
-//          the candidates overflow their slots the row switches to an implicit
-//          form (a 64-bit threshold key found by radix select over the whole
-//          row, exact for any distribution)
+//   row    one workgroup per row: up to 4096 candidates are sorted by (prob
+//          desc, id asc), with cumulative sums in a fixed tree order, top-p
+//          cut and normaliser; more candidates that still fit the row's list
+//          keep it unsorted (list form: the top-p threshold key by radix
+//          select over the list, fixed-point sums); beyond the list the row
+//          switches to an implicit form (radix select over the whole row).
+//          Every form is exact for any distribution
 //   seq    one workgroup per sequence: accept tests, residual or bonus draw by
 //          Gumbel-max over counter-based SplitMix64 uniforms, outputs, and the
 //          reset of the per-row scratch for the next call
@@ -29,13 +31,15 @@
 namespace mtp {
 
 static constexpr int kChunk = 8192;
+static constexpr int32_t kImplicitForm = -1, kListForm = -2;
 static constexpr int kMaxCtx = 1024;
 
 struct RowState {
     float M;          // max of the penalised, tempered logits (kept set)
     float Z;          // normaliser of the final kept set
     uint64_t tau;     // kept iff key(e, id) >= tau (after the min-p test)
-    int32_t n_keep;   // compact form: number of kept entries in the row's list; -1: implicit form
+    int32_t n_keep;   // compact form: number of kept entries in the sorted list; kListForm: the
+                      // unsorted list of cand_n entries, kept iff key >= tau; kImplicitForm: the whole row
     int32_t pad;
 };
 
@@ -140,6 +144,20 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 #pragma unroll
     for (int w = 0; w < NT / 64; w += 4) tot += (red[w] + red[w + 1]) + (red[w + 2] + red[w + 3]);
     return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *red) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    uint64_t t = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t += red[w];
+    return t;
 }
 
 // Context of one row in LDS: token list, and a bitmap over [c0, c0 + nbits).
@@ -320,7 +338,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     __shared__ float part[kPrefixBlocks];
     __shared__ float red[NT / 64];
     __shared__ int cut_sh;
-    __shared__ uint64_t hist[256], scal[4];
+    __shared__ uint64_t hist[256], scal[4], red64[NT / 64];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int n_all = a.cand_n[row];
@@ -328,7 +346,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     RowState st;
     st.M = M;
     st.pad = 0;
-    if (n_all <= a.cap) {
+    if (n_all <= min(kSortMax, a.cap)) {
         // ---- compact form: sort the candidates ----
         const int n = n_all;
         int np2 = 1;
@@ -392,6 +410,40 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
         }
         return;
     }
+    const double scale = 1099511627776.0;   // 2^40: fixed-point weights (e <= 1), exact sums in any order
+    if (n_all <= a.cap) {
+        // ---- list form: every min-p survivor is in the row's (unordered)
+        // list; the top-p threshold is a radix select over the list, and
+        // the sums are fixed-point so that they do not depend on its order
+        const int n = n_all;
+        const int32_t *lid = a.cand_id + (int64_t)row * a.cap;
+        const float *lv = a.cand_v + (int64_t)row * a.cap;
+        uint64_t z2 = 0;
+        for (int j = tid; j < n; j += NT) z2 += (uint64_t)((double)lv[j] * scale);
+        const uint64_t Z2 = block_sum_u64<NT>(z2, red64);
+        uint64_t tau = 0;
+        if (a.top_p < 1.f) {
+            const uint64_t target = (uint64_t)ceil((double)a.top_p * (double)Z2);
+            auto kw = [&](int j, uint64_t &k, uint64_t &w) {
+                const float e = lv[j];
+                k = tok_key(e, lid[j]);
+                w = (uint64_t)((double)e * scale);
+                return true;
+            };
+            tau = radix_select<NT>(n, target, kw, hist, scal);
+        }
+        uint64_t z3 = 0;
+        for (int j = tid; j < n; j += NT)
+            if (tok_key(lv[j], lid[j]) >= tau) z3 += (uint64_t)((double)lv[j] * scale);
+        const uint64_t Z3 = block_sum_u64<NT>(z3, red64);
+        if (tid == 0) {
+            st.Z = (float)((double)Z3 / scale);
+            st.tau = tau;
+            st.n_keep = kListForm;
+            ((RowState *)a.row_state)[row] = st;
+        }
+        return;
+    }
     // ---- implicit form: thresholds over the whole row ----
     const RowRef rr = row_ref(a, row);
     __shared__ int32_t ctx_tok[kMaxCtx];
@@ -414,8 +466,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     const float Z2 = block_sum<NT>(z2, red);
     uint64_t tau = 0;
     if (a.top_p < 1.f) {
-        // fixed-point weights (2^40 per unit) keep the histogram sums exact
-        const double scale = 1099511627776.0;
+        // fixed-point weights (scale = 2^40 per unit) keep the histogram sums exact
         const uint64_t target = (uint64_t)ceil((double)a.top_p * (double)Z2 * scale);
         auto kw = [&](int t, uint64_t &k, uint64_t &w) {
             float e;
@@ -435,7 +486,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     if (tid == 0) {
         st.Z = Z3;
         st.tau = tau;
-        st.n_keep = -1;
+        st.n_keep = kImplicitForm;
         ((RowState *)a.row_state)[row] = st;
     }
 }
@@ -502,6 +553,13 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
         if (st.n_keep >= 0) {
             for (int j = tid; j < st.n_keep; j += NT)
                 consider(a.cand_id[(int64_t)prow * a.cap + j], a.cand_v[(int64_t)prow * a.cap + j] / st.Z);
+        } else if (st.n_keep == kListForm) {
+            const int n = a.cand_n[prow];
+            for (int j = tid; j < n; j += NT) {
+                const int32_t t = a.cand_id[(int64_t)prow * a.cap + j];
+                const float e = a.cand_v[(int64_t)prow * a.cap + j];
+                if (tok_key(e, t) >= st.tau) consider(t, e / st.Z);
+            }
         } else {
             for (int t = tid; t < a.V; t += NT) {
                 const float pt = row_prob(a, prow, t, ctx_tok, n_ctx);

@@ -95,6 +95,29 @@ def test_sampling_chain_variants_match_oracle(orc, name, over):
     _compare(orc, g, sv, sp, max_flag_frac=0.5)
 
 
+@pytest.mark.parametrize("name,V,over", [
+    # (a top-p cut deep in a broad row's tail lands within the oracle's 1e-5
+    # window almost always, so the cuts here sit in the head of the rows)
+    ("list form: 30000 survivors per row, top-p over the unsorted list", 30000, dict(min_p=0.0, top_p=0.7)),
+    ("implicit form: 100000 survivors, more than the list holds", 100000, dict(min_p=0.0, top_p=0.5)),
+    ("list form without top-p, flat rows", 20000, dict(min_p=0.0, top_p=1.0, temp=1.5)),
+])
+def test_broad_rows_in_every_candidate_form_match_oracle(orc, name, V, over):
+    """Rows whose min-p survivors overflow the 4096-slot sort go to the list
+    form (all survivors kept unsorted, fixed-point sums) or, beyond the list's
+    slots, to the implicit form over the whole row; both must decide exactly
+    as the oracle does."""
+    log(f"case broad rows: {name}")
+    base = dict(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4, freq_penalty=0.0,
+                top_k=0, penalty_last_n=64, seed=41)
+    base.update(over)
+    sp = syn.Sampler(**base)
+    sv = syn.make_sample_verify(23, 6, 3, V, sampler=sp, hist=64)
+    g = GpuSampler(6, 3, V)
+    _compare(orc, g, sv, sp, max_flag_frac=0.5)
+    _compare(orc, g, sv, sp, round_=3, max_flag_frac=0.5)
+
+
 def test_drafts_outside_vocabulary_are_rejected(orc):
     log("case out-of-range drafts")
     sp = syn.Sampler(temp=1.0, top_p=1.0, min_p=0.0, rep_penalty=1.0, presence_penalty=0.0, seed=3)
