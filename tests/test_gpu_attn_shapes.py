@@ -47,3 +47,28 @@ def test_attention_instantiations_match_oracle(orc, kv, wd, hd, hq, hkv, n_seq):
     log(f"  {name}: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
         f"max_h_err={c.max_h_err:.3g}")
     assert c.near_ties <= 1
+
+
+@pytest.mark.parametrize("kv,wd,hd,hq,hkv", [
+    (syn.BF16, syn.BF16, 256, 4, 1),
+    (syn.F32, syn.F32, 64, 4, 1),
+], ids=["bf16-hd256", "f32-hd64"])
+def test_degenerate_and_boundary_contexts_match_oracle(orc, kv, wd, hd, hq, hkv):
+    """One visible cell (attention is then that cell's V), one and two tiles,
+    a split boundary, and 8193 cells (129 splits of 64 would exceed the 128
+    partial slots, so the split doubles to 128 cells and the last split holds
+    one cell), in one batch and each alone."""
+    name = f"kv={'bf16' if kv == syn.BF16 else 'f32'} hd={hd}"
+    ctx = [1, 2, 16, 17, 64, 65, 8193]
+    log(f"case boundary contexts {name}: ctx {ctx}")
+    m = syn.make_model(41 + hd, d_model=256, d_hprev=256, n_blocks=1, n_head_q=hq, n_head_kv=hkv, head_dim=hd,
+                       d_ff=512, n_vocab=4096, w_dtype=wd, head_dtype=wd, kv_dtype=kv)
+    dr = syn.make_draft_inputs(9 + hd, m, ctx, 3)
+    g = GpuDrafter(m, len(ctx), 3)
+    c = compare_draft(m, g.run(dr), orc.draft_block(m, dr))
+    log(f"  batch: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g}")
+    assert c.near_ties <= 1
+    for s in (0, 6):
+        one = g.run(dr, seq_idx=[s])
+        c1 = compare_draft(m, one, orc.draft_block(m, dr, seq_idx=[s]), [0])
+        assert c1.near_ties == 0
