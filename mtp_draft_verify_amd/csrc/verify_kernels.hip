@@ -33,14 +33,21 @@ __global__ __launch_bounds__(256) void verify_argmax_kernel(const float *logits,
     const int c1 = min(V, c0 + kVerifyChunk);
     uint64_t best = 0ull;
     if ((V & 3) == 0 && ((uintptr_t)logits & 15) == 0) {
-        for (int c = c0 + tid * 4; c < c1; c += kBlock * 4) {
-            const float4 v = ld_nt((const float4 *)(row + c));
-            uint64_t k0 = argmax_key(v.x, c), k1 = argmax_key(v.y, c + 1);
-            uint64_t k2 = argmax_key(v.z, c + 2), k3 = argmax_key(v.w, c + 3);
+        // all 8 vectors of the thread are requested at once (clamped into the
+        // chunk; those past its end are dropped), then folded
+        constexpr int NI = kVerifyChunk / (kBlock * 4);
+        float4 v[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) v[i] = ld_nt((const float4 *)(row + min(c0 + tid * 4 + kBlock * 4 * i, c1 - 4)));
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int c = c0 + tid * 4 + kBlock * 4 * i;
+            uint64_t k0 = argmax_key(v[i].x, c), k1 = argmax_key(v[i].y, c + 1);
+            uint64_t k2 = argmax_key(v[i].z, c + 2), k3 = argmax_key(v[i].w, c + 3);
             k0 = k1 > k0 ? k1 : k0;
             k2 = k3 > k2 ? k3 : k2;
             k0 = k2 > k0 ? k2 : k0;
-            best = k0 > best ? k0 : best;
+            best = (c < c1 && k0 > best) ? k0 : best;
         }
     } else {
         for (int c = c0 + tid; c < c1; c += kBlock) {
