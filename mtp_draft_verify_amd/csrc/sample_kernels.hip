@@ -213,12 +213,21 @@ __device__ __forceinline__ int ctx_count(const CtxLds &cl, int n_ctx, int32_t t)
     return c;
 }
 
-// value of token t of a row after top-k and penalties (NaN when top-k drops it)
-__device__ __forceinline__ float token_value(const SampleArgs &a, const float *z, int32_t t, bool member,
-                                             const CtxLds &cl, int n_ctx, uint64_t topk_key) {
-    const float raw = z[t];
+// value of token t of a row (raw logit `raw`) after top-k and penalties (NaN
+// when top-k drops it)
+__device__ __forceinline__ float raw_value(const SampleArgs &a, float raw, int32_t t, bool member, const CtxLds &cl,
+                                           int n_ctx, uint64_t topk_key) {
     if (a.top_k > 0 && tok_key(raw, t) < topk_key) return __int_as_float(0x7FC00000);
     return chain_value(a, raw, member ? ctx_count(cl, n_ctx, t) : 0);
+}
+
+// The chunk passes walk their 8192 tokens in batches of kBatch per thread:
+// all of a batch's logits are requested at once (clamped into the chunk),
+// then used.
+static constexpr int kBatch = 8;
+__device__ __forceinline__ void load_batch(const float *z, int b0, int c1, float (&raw)[kBatch]) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) raw[k] = z[min(b0 + (int)threadIdx.x + kBlock * k, c1 - 1)];
 }
 
 // ---------------------------------------------------------------------------
@@ -288,10 +297,17 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     float mx = -INFINITY;
-    for (int t = c0 + threadIdx.x; t < c1; t += kBlock) {
-        const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-        const float v = token_value(a, rr.z, t, member, cl, n_ctx, tk);
-        if (v == v) mx = fmaxf(mx, v);
+    for (int b0 = c0; b0 < c1; b0 += kBlock * kBatch) {
+        float raw[kBatch];
+        load_batch(rr.z, b0, c1, raw);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int t = b0 + (int)threadIdx.x + kBlock * k;
+            if (t >= c1) break;
+            const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+            const float v = raw_value(a, raw[k], t, member, cl, n_ctx, tk);
+            if (v == v) mx = fmaxf(mx, v);
+        }
     }
     mx = block_max(mx, red);
     if (threadIdx.x == 0 && mx > -INFINITY) atomicMax(&a.row_maxkey[row], fkey(mx));
@@ -307,14 +323,32 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     const float M = fkey_inv(a.row_maxkey[row]);
-    for (int t = c0 + threadIdx.x; t < c1; t += kBlock) {
-        const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-        const float v = token_value(a, rr.z, t, member, cl, n_ctx, tk);
-        if (!(v == v)) continue;
-        const float e = expf(v - M);
-        if (e >= a.min_p) {
-            const int slot = atomicAdd(&a.cand_n[row], 1);
-            if (slot < a.cap) {
+    const int lane = threadIdx.x & 63;
+    for (int b0 = c0; b0 < c1; b0 += kBlock * kBatch) {
+        float raw[kBatch];
+        load_batch(rr.z, b0, c1, raw);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int t = b0 + (int)threadIdx.x + kBlock * k;
+            bool keep = false;
+            float e = 0.f;
+            if (t < c1) {
+                const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                const float v = raw_value(a, raw[k], t, member, cl, n_ctx, tk);
+                if (v == v) {
+                    e = expf(v - M);
+                    keep = e >= a.min_p;
+                }
+            }
+            // one slot reservation per wave: the survivors of the wave take
+            // consecutive slots in lane order
+            const uint64_t mask = __ballot(keep);
+            if (mask == 0ull) continue;             // wave-uniform
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&a.cand_n[row], __popcll(mask));
+            base = __shfl(base, 0);
+            const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+            if (keep && slot < a.cap) {
                 a.cand_id[(int64_t)row * a.cap + slot] = t;
                 a.cand_v[(int64_t)row * a.cap + slot] = e;
             }
