@@ -283,8 +283,9 @@ def main():
                     help="c2 (default, the headline line); the others are extra measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this path has no multi-GPU form (sequences shard with no exchange; "
-              "see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: this path has no multi-GPU form (sequences would shard across GPUs "
+              "with no exchange, each GPU running this same path on its own sequences). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
