@@ -425,9 +425,10 @@ def main():
                           "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                           "frac": N * kvb / (breakdown["attn"]["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                           "bytes_per_round": N * kvb,
-                          "note": "per-launch latency dominates when a block's KV is small (16 MiB over 256 "
-                                  "workgroups at 8192 cells, one tile per wave); the same kernel streams 256 MiB "
-                                  "(131072 cells, one sequence) at ~5.9 TB/s"},
+                          "note": "with little KV per block per step, per-launch latency dominates (one "
+                                  "sequence at 8192 cells: 16 MiB per block over 256 workgroups, one tile per "
+                                  "wave); with long KV the same kernel streams at ~5.9 TB/s (one sequence at "
+                                  "131072 cells: 256 MiB in 45 us)"},
         "breakdown": breakdown,
         "accepted_per_round": float(acc.mean()),
     }
