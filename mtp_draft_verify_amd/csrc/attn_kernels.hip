@@ -263,9 +263,10 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
     constexpr int KS = HD / 32, DPL = HD / 64;
     static_assert(2 * G <= 16, "hi and lo query columns must fit one MFMA tile");
     __shared__ __attribute__((aligned(16))) float qs[G][HD];
-    __shared__ float cs[HD / 2], sn[HD / 2];
+    __shared__ __attribute__((aligned(16))) float cs[HD / 2], sn[HD / 2];
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][HD];
+    __shared__ abf16x8_t qbs[KS][64];
 
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const SeqParams &sqp = a.seqs[s];
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
     if (nt > 0) load(0, buf[0]);
     if (nt > 1) load(1, buf[1]);
 
-    // --- prologue: per-head q RMSNorm and RoPE, as in attn_kernel ----------
+    // --- prologue: per-head q RMSNorm; RoPE follows in the operand build ---
     constexpr int QPL = (HD + 63) / 64;
     constexpr int GW = (G + 3) / 4;
     float qv[GW][QPL], gq[QPL];
@@ -335,38 +336,51 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * (HD / 2); i += kBlock) {
-        const int j = i / (HD / 2), c = i - j * (HD / 2);
-        const float x0 = qs[j][c], x1 = qs[j][c + HD / 2];
-        qs[j][c] = x0 * cs[c] - x1 * sn[c];
-        qs[j][c + HD / 2] = x0 * sn[c] + x1 * cs[c];
-    }
-    __syncthreads();
 
-    // B operand: column h < G holds the hi half of query head h, column 8 + h
-    // its lo half (scaled by scale * log2(e)); the other columns are zero.
-    // Every lane reads its 8 values of each step with two 16-byte LDS reads
-    // from a clamped head row and zeroes them afterwards: a per-lane guard
-    // on the reads would turn into a branch and a wait around each of them.
-    abf16x8_t qb[KS];
+    // B operand: column h < G holds the hi half of query head h after RoPE,
+    // column 8 + h its lo half (scaled by scale * log2(e)); the other
+    // columns are zero.  Each wave builds KS / 4 of the KS steps and puts
+    // them in LDS, where every wave reads the whole operand back.  A lane's
+    // 8 values of a step are 8 consecutive dims inside one rotation half
+    // (which half depends on the step only); it reads them and their
+    // partners from a clamped head row with 16-byte LDS reads and zeroes
+    // dead columns afterwards: a per-lane guard on the reads would turn into
+    // a branch and a wait around each of them.
     {
         const int h = j16 & 7;
         const bool live = h < G;
-        const float *qrow = qs[min(h, G - 1)] + 8 * g;
+        const float *qrow = qs[min(h, G - 1)];
         const float sc = a.scale * kLog2e;
 #pragma unroll
-        for (int u = 0; u < KS; ++u) {
-            const float4 x0 = *(const float4 *)(qrow + 32 * u);
-            const float4 x1 = *(const float4 *)(qrow + 32 * u + 4);
-            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        for (int uu = 0; uu < KS / 4; ++uu) {
+            const int u = wid * (KS / 4) + uu;
+            const bool first = 32 * u < HD / 2;             // rotation half, uniform per step
+            const int c0 = (32 * u + 8 * g) % (HD / 2);
+            float x0[8], x1[8], cv[8], sv[8];
+            auto rd8 = [](const float *src, float (&d)[8]) {
+                const float4 lo = *(const float4 *)src, hi = *(const float4 *)(src + 4);
+                d[0] = lo.x; d[1] = lo.y; d[2] = lo.z; d[3] = lo.w;
+                d[4] = hi.x; d[5] = hi.y; d[6] = hi.z; d[7] = hi.w;
+            };
+            rd8(qrow + c0, x0);
+            rd8(qrow + c0 + HD / 2, x1);
+            rd8(cs + c0, cv);
+            rd8(sn + c0, sv);
+            abf16x8_t qv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float x = live ? xv[e] * sc : 0.f;
+                const float r0 = x0[e] * cv[e] - x1[e] * sv[e], r1 = x0[e] * sv[e] + x1[e] * cv[e];
+                const float x = live ? (first ? r0 : r1) * sc : 0.f;
                 const __bf16 hb = (__bf16)x;
-                qb[u][e] = j16 < 8 ? hb : (__bf16)(x - (float)hb);
+                qv[e] = j16 < 8 ? hb : (__bf16)(x - (float)hb);
             }
+            qbs[u][lane] = qv;
         }
     }
+    __syncthreads();
+    abf16x8_t qb[KS];
+#pragma unroll
+    for (int u = 0; u < KS; ++u) qb[u] = qbs[u][lane];
 
     float m = -INFINITY, l = 0.f;           // head j16 (lanes j16 < G)
     float acc[G][DPL];

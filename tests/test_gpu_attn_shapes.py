@@ -19,6 +19,7 @@ CASES = [
     (syn.BF16, syn.BF16, 256, 4, 1),
     (syn.BF16, syn.BF16, 256, 4, 2),
     (syn.BF16, syn.BF16, 256, 4, 4),
+    (syn.BF16, syn.BF16, 256, 8, 1),
     (syn.BF16, syn.BF16, 128, 8, 1),
     (syn.BF16, syn.BF16, 128, 8, 2),
     (syn.BF16, syn.BF16, 128, 8, 4),
@@ -40,7 +41,8 @@ def test_attention_instantiations_match_oracle(orc, kv, wd, hd, hq, hkv, n_seq):
     log(f"case attention shapes: {name}")
     m = syn.make_model(11 + hd + 7 * hq + hkv, d_model=256, d_hprev=256, n_blocks=1, n_head_q=hq, n_head_kv=hkv,
                        head_dim=hd, d_ff=512, n_vocab=4096, w_dtype=wd, head_dtype=wd, kv_dtype=kv)
-    ctx = [1000, 333][:n_seq]           # 1000 cells: 16 splits of 64, the last one 40 cells long
+    # 1000 cells: 16 splits of 64, the last one 40 cells long; 333: 6, the last 13
+    ctx = [1000, 333][:n_seq]
     dr = syn.make_draft_inputs(5 + hd, m, ctx, 3)
     gpu = GpuDrafter(m, n_seq, 3).run(dr)
     c = compare_draft(m, gpu, orc.draft_block(m, dr))
@@ -55,11 +57,13 @@ def test_attention_instantiations_match_oracle(orc, kv, wd, hd, hq, hkv, n_seq):
 ], ids=["bf16-hd256", "f32-hd64"])
 def test_degenerate_and_boundary_contexts_match_oracle(orc, kv, wd, hd, hq, hkv):
     """One visible cell (attention is then that cell's V), one and two tiles,
-    a split boundary, and 8193 cells (129 splits of 64 would exceed the 128
-    partial slots, so the split doubles to 128 cells and the last split holds
-    one cell), in one batch and each alone."""
+    both sides of a 64-cell split, 2047 cells (32 splits of 64) and 2049
+    (in a batch, 17 splits of 128, the last holding one cell; alone, 33 of
+    64), and 8193 cells (129 splits of 64 would exceed the 128 partial slots,
+    so the split doubles to 128 cells and the last split holds one cell), in
+    one batch and the 1-, 2049- and 8193-cell ones alone."""
     name = f"kv={'bf16' if kv == syn.BF16 else 'f32'} hd={hd}"
-    ctx = [1, 2, 16, 17, 64, 65, 8193]
+    ctx = [1, 2, 16, 17, 64, 65, 2047, 2049, 8193]
     log(f"case boundary contexts {name}: ctx {ctx}")
     m = syn.make_model(41 + hd, d_model=256, d_hprev=256, n_blocks=1, n_head_q=hq, n_head_kv=hkv, head_dim=hd,
                        d_ff=512, n_vocab=4096, w_dtype=wd, head_dtype=wd, kv_dtype=kv)
@@ -68,7 +72,7 @@ def test_degenerate_and_boundary_contexts_match_oracle(orc, kv, wd, hd, hq, hkv)
     c = compare_draft(m, g.run(dr), orc.draft_block(m, dr))
     log(f"  batch: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g}")
     assert c.near_ties <= 1
-    for s in (0, 6):
+    for s in (0, 7, 8):
         one = g.run(dr, seq_idx=[s])
         c1 = compare_draft(m, one, orc.draft_block(m, dr, seq_idx=[s]), [0])
         assert c1.near_ties == 0
