@@ -11,7 +11,7 @@
 // Kernels (rows = S*(N+1) target rows followed by S*N draft rows):
 //   topk   (only when top_k > 0) one workgroup per row: radix select of the
 //          k-th largest raw (logit, -id) key
-//   max    per (row, 8192-token chunk): max of the penalised, tempered logit
+//   max    per (row, 16384-token chunk): max of the penalised, tempered logit
 //   cand   per (row, chunk): tokens with exp(v - M) >= min_p join the row's
 //          candidate list (order fixed later by sorting)
 //   row    one workgroup per row: up to 4096 candidates are sorted by (prob
@@ -30,7 +30,7 @@
 
 namespace mtp {
 
-static constexpr int kChunk = 8192;
+static constexpr int kChunk = 16384;
 static constexpr int32_t kImplicitForm = -1, kListForm = -2;
 static constexpr int kMaxCtx = 1024;
 
@@ -221,10 +221,12 @@ __device__ __forceinline__ float raw_value(const SampleArgs &a, float raw, int32
     return chain_value(a, raw, member ? ctx_count(cl, n_ctx, t) : 0);
 }
 
-// The chunk passes walk their 8192 tokens in batches of kBatch per thread:
-// all of a batch's logits are requested at once (clamped into the chunk),
-// then used.
+// The chunk passes walk their kChunk tokens in kNBatch batches of kBatch per
+// thread: all of a batch's logits are requested at once (clamped into the
+// chunk), the first batch before the context is read, each next one before
+// the current one is used.
 static constexpr int kBatch = 8;
+static constexpr int kNBatch = kChunk / (kBlock * kBatch);
 __device__ __forceinline__ void load_batch(const float *z, int b0, int c1, float (&raw)[kBatch]) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) raw[k] = z[min(b0 + (int)threadIdx.x + kBlock * k, c1 - 1)];
@@ -293,19 +295,23 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
+    // the first batch does not depend on the context: request it first
+    float raw[2][kBatch];
+    load_batch(rr.z, c0, c1, raw[0]);
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     float mx = -INFINITY;
-    for (int b0 = c0; b0 < c1; b0 += kBlock * kBatch) {
-        float raw[kBatch];
-        load_batch(rr.z, b0, c1, raw);
+#pragma unroll
+    for (int b = 0; b < kNBatch; ++b) {
+        const int b0 = c0 + b * kBlock * kBatch;
+        if (b + 1 < kNBatch) load_batch(rr.z, b0 + kBlock * kBatch, c1, raw[(b + 1) & 1]);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int t = b0 + (int)threadIdx.x + kBlock * k;
             if (t >= c1) break;
             const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-            const float v = raw_value(a, raw[k], t, member, cl, n_ctx, tk);
+            const float v = raw_value(a, raw[b & 1][k], t, member, cl, n_ctx, tk);
             if (v == v) mx = fmaxf(mx, v);
         }
     }
@@ -319,14 +325,17 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
+    float raw[2][kBatch];
+    load_batch(rr.z, c0, c1, raw[0]);
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     const float M = fkey_inv(a.row_maxkey[row]);
     const int lane = threadIdx.x & 63;
-    for (int b0 = c0; b0 < c1; b0 += kBlock * kBatch) {
-        float raw[kBatch];
-        load_batch(rr.z, b0, c1, raw);
+#pragma unroll
+    for (int b = 0; b < kNBatch; ++b) {
+        const int b0 = c0 + b * kBlock * kBatch;
+        if (b + 1 < kNBatch) load_batch(rr.z, b0 + kBlock * kBatch, c1, raw[(b + 1) & 1]);
 #pragma unroll
         for (int k = 0; k < kBatch; ++k) {
             const int t = b0 + (int)threadIdx.x + kBlock * k;
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
             float e = 0.f;
             if (t < c1) {
                 const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-                const float v = raw_value(a, raw[k], t, member, cl, n_ctx, tk);
+                const float v = raw_value(a, raw[b & 1][k], t, member, cl, n_ctx, tk);
                 if (v == v) {
                     e = expf(v - M);
                     keep = e >= a.min_p;
