@@ -221,15 +221,28 @@ __device__ __forceinline__ float raw_value(const SampleArgs &a, float raw, int32
     return chain_value(a, raw, member ? ctx_count(cl, n_ctx, t) : 0);
 }
 
-// The chunk passes walk their kChunk tokens in kNBatch batches of kBatch per
-// thread: all of a batch's logits are requested at once (clamped into the
-// chunk), the first batch before the context is read, each next one before
-// the current one is used.
-static constexpr int kBatch = 8;
-static constexpr int kNBatch = kChunk / (kBlock * kBatch);
-__device__ __forceinline__ void load_batch(const float *z, int b0, int c1, float (&raw)[kBatch]) {
+// The chunk passes walk their kChunk tokens in batches of KB = 32 / E loads
+// per thread, each load E consecutive logits (E = 4 when rows are 16-byte
+// aligned: one wave load then moves 1 KiB): all of a batch's logits are
+// requested at once (clamped into the chunk), the first batch before the
+// context is read, each next one before the current one is used.
+template <int E> struct ChunkShape {
+    static constexpr int KB = E == 4 ? 4 : 8;           // loads per thread per batch
+    static constexpr int BT = E * kBlock * KB;          // tokens per batch
+    static constexpr int NB = kChunk / BT;              // batches per chunk
+};
+template <int E, int KB>
+__device__ __forceinline__ void load_batch(const float *z, int b0, int c1, float (&raw)[KB][E]) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) raw[k] = z[min(b0 + (int)threadIdx.x + kBlock * k, c1 - 1)];
+    for (int k = 0; k < KB; ++k) {
+        const int t = min(b0 + E * ((int)threadIdx.x + kBlock * k), c1 - E);
+        if constexpr (E == 4) {
+            const float4 v = *(const float4 *)(z + t);
+            raw[k][0] = v.x; raw[k][1] = v.y; raw[k][2] = v.z; raw[k][3] = v.w;
+        } else {
+            raw[k][0] = z[t];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -289,79 +302,88 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
 }
 
 // pass 1: row max of the chain values
+template <int E>
 __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chunk) {
+    constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     __shared__ float red[4];
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
     // the first batch does not depend on the context: request it first
-    float raw[2][kBatch];
-    load_batch(rr.z, c0, c1, raw[0]);
+    float raw[2][KB][E];
+    load_batch<E, KB>(rr.z, c0, c1, raw[0]);
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < kNBatch; ++b) {
-        const int b0 = c0 + b * kBlock * kBatch;
-        if (b + 1 < kNBatch) load_batch(rr.z, b0 + kBlock * kBatch, c1, raw[(b + 1) & 1]);
+    for (int b = 0; b < NB; ++b) {
+        const int b0 = c0 + b * BT;
+        if (b + 1 < NB) load_batch<E, KB>(rr.z, b0 + BT, c1, raw[(b + 1) & 1]);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int t = b0 + (int)threadIdx.x + kBlock * k;
-            if (t >= c1) break;
-            const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-            const float v = raw_value(a, raw[b & 1][k], t, member, cl, n_ctx, tk);
-            if (v == v) mx = fmaxf(mx, v);
-        }
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int t = b0 + E * ((int)threadIdx.x + kBlock * k) + e;
+                if (t < c1) {
+                    const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                    const float v = raw_value(a, raw[b & 1][k][e], t, member, cl, n_ctx, tk);
+                    if (v == v) mx = fmaxf(mx, v);
+                }
+            }
     }
     mx = block_max(mx, red);
     if (threadIdx.x == 0 && mx > -INFINITY) atomicMax(&a.row_maxkey[row], fkey(mx));
 }
 
 // pass 2: min-p survivors join the candidate list
+template <int E>
 __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_chunk) {
+    constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
-    float raw[2][kBatch];
-    load_batch(rr.z, c0, c1, raw[0]);
+    float raw[2][KB][E];
+    load_batch<E, KB>(rr.z, c0, c1, raw[0]);
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     const float M = fkey_inv(a.row_maxkey[row]);
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int b = 0; b < kNBatch; ++b) {
-        const int b0 = c0 + b * kBlock * kBatch;
-        if (b + 1 < kNBatch) load_batch(rr.z, b0 + kBlock * kBatch, c1, raw[(b + 1) & 1]);
+    for (int b = 0; b < NB; ++b) {
+        const int b0 = c0 + b * BT;
+        if (b + 1 < NB) load_batch<E, KB>(rr.z, b0 + BT, c1, raw[(b + 1) & 1]);
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) {
-            const int t = b0 + (int)threadIdx.x + kBlock * k;
-            bool keep = false;
-            float e = 0.f;
-            if (t < c1) {
-                const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-                const float v = raw_value(a, raw[b & 1][k], t, member, cl, n_ctx, tk);
-                if (v == v) {
-                    e = expf(v - M);
-                    keep = e >= a.min_p;
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int t = b0 + E * ((int)threadIdx.x + kBlock * k) + e;
+                bool keep = false;
+                float ev = 0.f;
+                if (t < c1) {
+                    const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                    const float v = raw_value(a, raw[b & 1][k][e], t, member, cl, n_ctx, tk);
+                    if (v == v) {
+                        ev = expf(v - M);
+                        keep = ev >= a.min_p;
+                    }
+                }
+                // one slot reservation per wave: the survivors of the wave
+                // take consecutive slots in lane order
+                const uint64_t mask = __ballot(keep);
+                if (mask == 0ull) continue;             // wave-uniform
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&a.cand_n[row], __popcll(mask));
+                base = __shfl(base, 0);
+                const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+                if (keep && slot < a.cap) {
+                    a.cand_id[(int64_t)row * a.cap + slot] = t;
+                    a.cand_v[(int64_t)row * a.cap + slot] = ev;
                 }
             }
-            // one slot reservation per wave: the survivors of the wave take
-            // consecutive slots in lane order
-            const uint64_t mask = __ballot(keep);
-            if (mask == 0ull) continue;             // wave-uniform
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&a.cand_n[row], __popcll(mask));
-            base = __shfl(base, 0);
-            const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-            if (keep && slot < a.cap) {
-                a.cand_id[(int64_t)row * a.cap + slot] = t;
-                a.cand_v[(int64_t)row * a.cap + slot] = e;
-            }
-        }
     }
 }
 
@@ -649,8 +671,15 @@ hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st) {
         hipLaunchKernelGGL(sample_topk_kernel, dim3(rows), dim3(kBlock), 0, st, a);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    hipLaunchKernelGGL(sample_max_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    hipLaunchKernelGGL(sample_cand_kernel, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    // 4 logits per load when every row starts on a 16-byte boundary
+    const bool v4 = a.V % 4 == 0 && ((uintptr_t)a.p_logits & 15) == 0 && ((uintptr_t)a.q_logits & 15) == 0;
+    if (v4) {
+        hipLaunchKernelGGL(sample_max_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+        hipLaunchKernelGGL(sample_cand_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    } else {
+        hipLaunchKernelGGL(sample_max_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+        hipLaunchKernelGGL(sample_cand_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    }
     hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kRowThreads), 0, st, a);
     hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();

@@ -118,6 +118,17 @@ def test_broad_rows_in_every_candidate_form_match_oracle(orc, name, V, over):
     _compare(orc, g, sv, sp, round_=3, max_flag_frac=0.5)
 
 
+def test_vocabulary_not_a_multiple_of_four_matches_oracle(orc):
+    """V = 20001: rows do not start on 16-byte boundaries, so the chunk
+    passes read one logit per load; two chunks, the second 3617 tokens."""
+    log("case V=20001 (scalar chunk loads)")
+    sp = syn.Sampler(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4, freq_penalty=0.0,
+                     top_k=0, penalty_last_n=64, seed=77)
+    sv = syn.make_sample_verify(29, 6, 3, 20001, sampler=sp, hist=64)
+    g = GpuSampler(6, 3, 20001)
+    _compare(orc, g, sv, sp, max_flag_frac=0.5)
+
+
 def test_drafts_outside_vocabulary_are_rejected(orc):
     log("case out-of-range drafts")
     sp = syn.Sampler(temp=1.0, top_p=1.0, min_p=0.0, rep_penalty=1.0, presence_penalty=0.0, seed=3)
