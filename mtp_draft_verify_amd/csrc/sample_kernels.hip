@@ -316,7 +316,11 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
-    float mx = -INFINITY;
+    // Context tokens take the full chain; every other token's value is
+    // fl(z / temp), which does not decrease as z grows, so the largest of
+    // them is the value of the largest raw logit: those tokens only need a
+    // running max of z (after the top-k test).
+    float mx = -INFINITY, mz = -INFINITY;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int b0 = c0 + b * BT;
@@ -327,12 +331,18 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
             for (int e = 0; e < E; ++e) {
                 const int t = b0 + E * ((int)threadIdx.x + kBlock * k) + e;
                 if (t < c1) {
+                    const float z = raw[b & 1][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-                    const float v = raw_value(a, raw[b & 1][k][e], t, member, cl, n_ctx, tk);
-                    if (v == v) mx = fmaxf(mx, v);
+                    if (member) {
+                        const float v = raw_value(a, z, t, true, cl, n_ctx, tk);
+                        if (v == v) mx = fmaxf(mx, v);
+                    } else if (!(a.top_k > 0 && tok_key(z, t) < tk)) {
+                        mz = fmaxf(mz, z);
+                    }
                 }
             }
     }
+    if (mz > -INFINITY) mx = fmaxf(mx, chain_value(a, mz, 0));
     mx = block_max(mx, red);
     if (threadIdx.x == 0 && mx > -INFINITY) atomicMax(&a.row_maxkey[row], fkey(mx));
 }
@@ -351,6 +361,16 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     const float M = fkey_inv(a.row_maxkey[row]);
+    // A token outside the context keeps when expf(fl(z / temp) - M) >=
+    // min_p.  With fp32 rounding and expf's error that needs z / temp >=
+    // M + ln(min_p) - 1e-5 (1 + |M|) at the least, so a raw logit below
+    // zlo = temp * (M + ln(min_p) - 0.01 - 1e-5 |M|) (rounded down) cannot
+    // keep and skips the exact test; every other token takes it unchanged.
+    float zlo = -INFINITY;
+    if (a.min_p > 0.f && M > -INFINITY) {
+        const double zl = (double)a.temp * ((double)M + log((double)a.min_p) - 0.01 - 1e-5 * fabs((double)M));
+        zlo = nextafterf((float)zl, -INFINITY);
+    }
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -364,11 +384,14 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
                 bool keep = false;
                 float ev = 0.f;
                 if (t < c1) {
+                    const float z = raw[b & 1][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
-                    const float v = raw_value(a, raw[b & 1][k][e], t, member, cl, n_ctx, tk);
-                    if (v == v) {
-                        ev = expf(v - M);
-                        keep = ev >= a.min_p;
+                    if (member || z >= zlo) {
+                        const float v = raw_value(a, z, t, member, cl, n_ctx, tk);
+                        if (v == v) {
+                            ev = expf(v - M);
+                            keep = ev >= a.min_p;
+                        }
                     }
                 }
                 // one slot reservation per wave: the survivors of the wave
