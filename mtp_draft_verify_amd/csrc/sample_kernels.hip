@@ -21,9 +21,10 @@
 //          select over the list, fixed-point sums); beyond the list the row
 //          switches to an implicit form (radix select over the whole row).
 //          Every form is exact for any distribution
-//   seq    one workgroup per sequence: accept tests, residual or bonus draw by
-//          Gumbel-max over counter-based SplitMix64 uniforms, outputs, and the
-//          reset of the per-row scratch for the next call
+//   seq    one workgroup per sequence: accept tests (all drafts at once),
+//          residual or bonus draw by Gumbel-max over counter-based SplitMix64
+//          uniforms, outputs, and the reset of the per-row scratch for the
+//          next call
 // All floating point is fp32; every sum runs in a fixed order, so a call is
 // deterministic.
 #include "dev_common.h"
@@ -33,6 +34,7 @@ namespace mtp {
 static constexpr int kChunk = 16384;
 static constexpr int32_t kImplicitForm = -1, kListForm = -2;
 static constexpr int kMaxCtx = 1024;
+static constexpr int kMaxDrafts = 64;     // drafts per sequence (the context's max_steps bound)
 
 struct RowState {
     float M;          // max of the penalised, tempered logits (kept set)
@@ -582,49 +584,62 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
 // ---------------------------------------------------------------------------
 // per-sequence accept / resample
 // ---------------------------------------------------------------------------
-// probability of token t under row `row` (its RowState already final);
-// ctx_tok is the row's context, sorted
-__device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t *ctx_tok, int n_ctx) {
+// probability of token t under row `row` (its RowState already final), t
+// occurring cnt times in the row's context
+__device__ float row_prob_cnt(const SampleArgs &a, int row, int32_t t, int cnt) {
     if (t < 0 || t >= a.V) return 0.f;
     const RowRef rr = row_ref(a, row);
     const RowState st = ((const RowState *)a.row_state)[row];
     const float raw = rr.z[t];
     if (a.top_k > 0 && tok_key(raw, t) < a.topk_key[row]) return 0.f;
-    const float e = expf(chain_value(a, raw, sorted_count(ctx_tok, n_ctx, t)) - st.M);
+    const float e = expf(chain_value(a, raw, cnt) - st.M);
     if (!(e >= a.min_p) || tok_key(e, t) < st.tau) return 0.f;
     return e / st.Z;
+}
+// the same with the row's context as a sorted list
+__device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t *ctx_tok, int n_ctx) {
+    if (t < 0 || t >= a.V) return 0.f;
+    return row_prob_cnt(a, row, t, sorted_count(ctx_tok, n_ctx, t));
 }
 
 __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
     constexpr int NT = kRowThreads;
     __shared__ int32_t ctx_tok[kMaxCtx];
     __shared__ uint64_t best_w[NT / 64];
-    __shared__ int decision;
+    __shared__ int accept[kMaxDrafts];
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int N = a.N, R = N + 1;
-    int n_acc = N;
-    for (int i = 0; i <= N; ++i) {
+    // The accept test of draft i needs only the final states of its p and q
+    // rows, the draft's count in row i's context and its own uniform, none
+    // of the earlier outcomes: all the tests run at once, one wave per draft.
+    for (int i = wid; i < N; i += NT / 64) {
+        const int32_t d = a.drafts[(int64_t)s * N + i];
+        const int n_ctx = ctx_len(a, s, i);
+        float c = 0.f;
+        if (d >= 0 && d < a.V)
+            for (int j = lane; j < n_ctx; j += 64) c += ctx_token(a, s, i, n_ctx, j) == d ? 1.f : 0.f;
+        const int cnt = (int)wave_sum(c);         // exact: at most kMaxCtx ones
+        if (lane == 0) {
+            const float pd = row_prob_cnt(a, s * R + i, d, cnt);
+            const float qd = a.q_logits ? row_prob_cnt(a, a.S * R + s * N + i, d, cnt)
+                                        : ((d >= 0 && d < a.V) ? 1.f : 0.f);
+            const float u = counter_uniform(a.seed, s, a.round, i, 0, 0);
+            accept[i] = (u * qd < pd) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    int i = 0;
+    while (i < N && accept[i]) ++i;              // first rejection, or N
+    const int n_acc = i;
+    for (int j = tid; j < n_acc; j += NT) a.out_tokens[(int64_t)s * R + j] = a.drafts[(int64_t)s * N + j];
+    {
         const int prow = s * R + i;
         const int n_ctx = ctx_len(a, s, i);
-        __syncthreads();
         for (int j = tid; j < n_ctx; j += NT) ctx_tok[j] = ctx_token(a, s, i, n_ctx, j);
         __syncthreads();
         sort_ctx<NT>(ctx_tok, n_ctx);
         const int32_t d = i < N ? a.drafts[(int64_t)s * N + i] : -1;
         const int qrow = a.q_logits ? a.S * R + s * N + i : -1;
-        if (i < N) {
-            if (tid == 0) {
-                const float pd = row_prob(a, prow, d, ctx_tok, n_ctx);
-                const float qd = a.q_logits ? row_prob(a, qrow, d, ctx_tok, n_ctx) : ((d >= 0 && d < a.V) ? 1.f : 0.f);
-                const float u = counter_uniform(a.seed, s, a.round, i, 0, 0);
-                decision = (u * qd < pd) ? 1 : 0;
-            }
-            __syncthreads();
-            if (decision) {
-                if (tid == 0) a.out_tokens[(int64_t)s * R + i] = d;
-                continue;
-            }
-        }
         // draw from max(p - q, 0) (rejection at row i) or from p_N (bonus)
         const uint64_t stream = i < N ? 1 : 2;
         const RowState st = ((const RowState *)a.row_state)[prow];
@@ -667,11 +682,9 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
             for (int w = 1; w < NT / 64; ++w) b = best_w[w] > b ? best_w[w] : b;
             a.out_tokens[(int64_t)s * R + i] = b ? (int32_t)(0xFFFFFFFFu - (uint32_t)b) : -1;
         }
-        n_acc = i < N ? i : N;
         if (i < N) {
             for (int j = i + 1 + tid; j < R; j += NT) a.out_tokens[(int64_t)s * R + j] = -1;
         }
-        break;
     }
     if (tid == 0) a.out_n_accept[s] = n_acc;
     // clear this sequence's row scratch for the next call
