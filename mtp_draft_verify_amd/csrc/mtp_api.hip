@@ -794,6 +794,7 @@ static int sample_args(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int32_t n_voc
     a.history = history; a.history_len = sp->penalty_last_n > 0 ? history_len : nullptr;
     a.hstride = history_stride; a.S = n_seq; a.N = n_draft; a.V = n_vocab;
     a.temp = sp->temp; a.top_p = sp->top_p; a.min_p = sp->min_p;
+    a.ln_min_p = std::log((double)a.min_p);
     a.rep = sp->rep_penalty; a.presence = sp->presence_penalty; a.freq = sp->freq_penalty;
     a.top_k = sp->top_k; a.last_n = sp->penalty_last_n; a.seed = sp->seed; a.round = round;
     a.row_maxkey = c->s_maxkey; a.topk_key = c->s_topk; a.cand_n = c->s_cand_n; a.cand_id = c->s_cand_id;

@@ -214,6 +214,7 @@ struct SampleArgs {
     const int32_t *history_len;
     int32_t hstride, S, N, V;
     float temp, top_p, min_p, rep, presence, freq;
+    double ln_min_p;        // log(min_p) (-inf for min_p = 0), once per call on the host
     int32_t top_k, last_n;
     uint64_t seed, round;
     // scratch, per row (S*(N+1) target rows, then S*N draft rows)

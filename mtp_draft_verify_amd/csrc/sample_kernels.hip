@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_ch
     // keep and skips the exact test; every other token takes it unchanged.
     float zlo = -INFINITY;
     if (a.min_p > 0.f && M > -INFINITY) {
-        const double zl = (double)a.temp * ((double)M + log((double)a.min_p) - 0.01 - 1e-5 * fabs((double)M));
+        const double zl = (double)a.temp * ((double)M + a.ln_min_p - 0.01 - 1e-5 * fabs((double)M));
         zlo = nextafterf((float)zl, -INFINITY);
     }
     const int lane = threadIdx.x & 63;
