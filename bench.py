@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Throughput of the fused MTP draft chain + greedy verify on one MI355X.
 
-One step = one round of the hot path on the Gemma-4-26B-like workload: a
-draft block of B-1 = 3 chained steps (embed + pre-projection, 4 blocks of
-RMSNorm/Q/split-K cross-attention into an 8192-position bf16 KV/O/MLP, final
-norm + 262144-row bf16 LM head + argmax, post-projection) for one sequence,
-then the greedy verify over the target's [1, 4, 262144] fp32 logits.  Inputs
-are synthetic, seeded, and resident in HBM before timing starts.
+One step = one round of the hot path.  The default (headline) workload is the
+largest configuration: 8 sequences, each with a full-attention bf16 KV of
+131072 positions, a draft block of B-1 = 4 chained steps (embed +
+pre-projection; 4 blocks of RMSNorm/Q/split-K GQA cross-attention/O/SiLU MLP;
+final norm + 262144-row Q8_0 LM head + argmax; post-projection), then the
+greedy verify over the target's [8, 5, 262144] fp32 logits.  Inputs are
+synthetic, seeded, and resident in HBM before timing starts; --workload
+selects the other configurations (extra measurements).
 
 Prints one JSON line: draft tokens/s (= S * N / time per round), the
-whole-round algorithmic HBM GB/s, the LM-head kernel's roofline (algorithmic
-bytes per launch / its average launch time, measured with HIP events on the
-library's stream during the timed region) and the CPU oracle's throughput on
-a bounded sample of the same workload.
+whole-round algorithmic HBM GB/s, the roofline of the round's dominant kernel
+(algorithmic bytes per launch / its average launch time, measured with HIP
+events on the library's stream after the timed region; the other of the two
+large kernels in roofline_other) and the CPU oracle's throughput on a bounded
+sample of the same workload.
 """
 from __future__ import annotations
 
@@ -92,24 +95,60 @@ def head_traffic_from_counters(path=COUNTERS_FILE, sources=HEAD_SOURCES):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w, budget_s):
-    """The oracle as it stands on the same workload: whole rounds (draft block
-    + greedy verify) until about budget_s seconds of host time."""
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, reps=3):
+    """The oracle as it stands (plain fp64 C, OpenMP across sequences and kv
+    heads) on a bounded sample of the same workload: one draft step over all
+    sequences (1 warm-up, then the median of `reps` timed runs) and one
+    greedy verify over all sequences' rows, scaled to a whole round as
+    N * t_step + t_verify (every step reads the same weights and KV, so each
+    costs the same); then the same for one sequence on one thread."""
+    import ctypes
+    import statistics
+    import mtp_synth as syn
     from oracle import oracle as orc
     orc.build(force=False)
-    S, N = len(w.draft.seqs), w.draft.n_steps
-    rounds, t0 = 0, time.perf_counter()
-    while True:
-        out = orc.draft_block(w.model, w.draft, want_logits=False)
-        orc.verify_greedy(w.greedy.logits, out["drafts"])
-        rounds += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or rounds >= 50:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
-    return {"value": rounds * S * N / el, "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rounds} full rounds of the same workload (draft block of {N} steps for {S} sequence(s) "
-                      f"+ greedy verify), {el:.1f} s wall on the host, OpenMP threads={threads}"}
+    S, N, V = len(w.draft.seqs), w.draft.n_steps, w.model.n_vocab
+    # verify rows from the input generator alone (the oracle's verify costs
+    # the same whatever the drafts are)
+    gv = syn.make_greedy_verify(7, S, N, V, w.p_accept, "max5")
+    gomp = ctypes.CDLL("libgomp.so.1")
+    threads = int(gomp.omp_get_max_threads())
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+    step_all = lambda: orc.draft_block(w.model, w.draft, want_logits=False, n_steps=1)
+    timed(step_all)
+    t_step = statistics.median(timed(step_all) for _ in range(reps))
+    t_ver = timed(lambda: orc.verify_greedy(gv.logits, gv.drafts))
+    value = S * N / (N * t_step + t_ver)
+    # one sequence on one thread
+    gomp.omp_set_num_threads(1)
+    try:
+        t1 = timed(lambda: orc.draft_block(w.model, w.draft, want_logits=False, n_steps=1, seq_idx=[0]))
+        t1v = timed(lambda: orc.verify_greedy(gv.logits[:1], gv.drafts[:1]))
+    finally:
+        gomp.omp_set_num_threads(threads)
+    single = N / (N * t1 + t1v)
+    return {"value": value, "unit": "draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one draft step over all {S} sequence(s) (1 warm-up + median of {reps} timed runs: "
+                      f"{t_step:.2f} s) and one greedy verify over all {S}x{N + 1} rows ({t_ver:.2f} s), scaled to "
+                      f"a round of {N} steps as {N}*t_step + t_verify; {threads} OpenMP threads on "
+                      f"'{_cpu_model()}' ({os.cpu_count()} logical CPUs visible)",
+            "single_thread": {"value": single, "unit": "draft tokens/s",
+                              "sample": f"one draft step of sequence 0 ({t1:.2f} s) + its verify rows ({t1v:.3f} s) "
+                                        f"on one thread, scaled to {N} steps"}}
 
 
 WORKLOADS = {
@@ -188,7 +227,8 @@ def bench_hidden(args, dev):
     S, R, d = hv.hidden.shape
     V = hv.n_vocab
     desc = mtp.make_desc(d_model=32, d_hprev=8, n_blocks=1, n_head_q=1, n_head_kv=1, head_dim=64, d_ff=8,
-                         n_vocab=V, w_dtype=0, head_dtype=0, kv_dtype=0, max_seqs=S, max_steps=R - 1)
+                         n_vocab=V, w_dtype=0, head_dtype=0, kv_dtype=0, max_seqs=S, max_steps=R - 1,
+                         hidden_d_max=d, hidden_sample=1)
     ctx = mtp.Context(desc, None, stream=torch.cuda.current_stream())
     wt = torch.from_numpy(hv.head.view(np.int16)).to(dev)
     g = to_dev(hv.g, dev)
@@ -270,17 +310,163 @@ def bench_hidden(args, dev):
     print(json.dumps(out), flush=True)
 
 
+ATTN_SOURCES = ["attn_kernels.hip", "dev_common.h", "mtp_internal.h"]
+
+
+def counters_file(kernel, workload):
+    return ROOT / "profiles" / f"{kernel}_{workload}_hbm_counters.txt"
+
+
+def bench_draft(args, dev):
+    """The headline line: rounds of draft block + greedy verify."""
+    import torch
+    import mtp_draft_verify_amd as mtp
+    import mtp_synth as syn
+    from mtp_synth.device import to_dev, upload_model, upload_seqs
+    log(f"bench: generating workload {args.workload}")
+    w = getattr(syn, WORKLOADS[args.workload][0])()
+    m, dr = w.model, w.draft
+    S, N, V = len(dr.seqs), dr.n_steps, m.n_vocab
+    desc, wts, keep_w = upload_model(m, dev, S, N)
+    seqs, last_tok, h_prev, keep_kv = upload_seqs(m, dr, dev)
+    stream = torch.cuda.current_stream()
+    ctx = mtp.Context(desc, wts, stream=stream, keepalive=keep_w)
+    seq_arr = mtp.make_seqs(seqs)
+    drafts = torch.zeros((S, N), dtype=torch.int32, device=dev)
+    h_last = torch.zeros((S, m.d_hprev), dtype=torch.float32, device=dev)
+    toks = torch.zeros((S, N + 1), dtype=torch.int32, device=dev)
+    n_acc = torch.zeros((S,), dtype=torch.int32, device=dev)
+
+    # target logits with the drafter's own drafts planted (p_accept of the
+    # workload), so that the verify accepts what a real target would
+    ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
+    torch.cuda.synchronize()
+    gv = syn.make_greedy_verify(1, S, N, V, w.p_accept, "max5", drafts=drafts.cpu().numpy())
+    logits = to_dev(gv.logits, dev)
+
+    def step():
+        ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
+        ctx.verify_greedy(logits, drafts, toks, n_acc)
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # Kernel timing: the same steps again with HIP events around every launch
+    # of one kernel class on the library's stream (events make the library
+    # launch the chain kernel by kernel instead of replaying its captured
+    # graph; the kernels themselves are the same).
+    def class_time(cls, n):
+        ctx.profile(1 << cls)
+        for _ in range(n):
+            step()
+        t, k = ctx.profile_read(cls)
+        ctx.profile(0)
+        return t, k
+    head_ms, head_n = class_time(mtp.MTP_PROF_HEAD, args.steps)
+    attn_ms, attn_n = class_time(mtp.MTP_PROF_ATTN, args.steps)
+
+    # per-class breakdown over a separately profiled pass (diagnostic)
+    ctx.profile((1 << mtp.MTP_PROF_N) - 1)
+    n_diag = min(args.steps, 20)
+    for _ in range(n_diag):
+        step()
+    torch.cuda.synchronize()
+    breakdown = {}
+    for name, cls in (("head", mtp.MTP_PROF_HEAD), ("attn", mtp.MTP_PROF_ATTN), ("merge", mtp.MTP_PROF_MERGE),
+                      ("gemv", mtp.MTP_PROF_GEMV), ("verify", mtp.MTP_PROF_VERIFY)):
+        t, n = ctx.profile_read(cls)
+        breakdown[name] = {"ms_per_step": t / n_diag, "launches_per_step": n / n_diag}
+    ctx.profile(0)
+    log(f"bench: breakdown {breakdown}")
+
+    wb, hb, gb = weight_bytes(m, S)
+    kvb = kv_bytes(m, dr.seqs)
+    step_bytes = wb + hb + gb + kvb + S * m.d_model * 2
+    round_bytes = N * step_bytes + S * (N + 1) * V * 4
+    head_launch_bytes = hb + m.d_hprev * m.d_model * 2 + 2 * S * m.d_model * 4
+    if m.n_centroids:   # the head class times only the candidate-row kernel
+        head_launch_bytes -= m.n_centroids * m.d_model * (4 if m.w_dtype == syn.F32 else 2)
+    if m.n_centroids:
+        head_name = "cand_head_kernel (centroid head candidate rows + argmax + post-proj)"
+    elif S >= 2 and m.head_dtype != syn.F32:
+        head_name = "mm_head_kernel (final RMSNorm + matrix-core LM head + argmax + post-proj)"
+    else:
+        head_name = "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)"
+    attn_name = "attn_mm_kernel (split-K GQA cross-attention, partials per split)" if m.kv_dtype != syn.F32 \
+        else "attn_kernel (split-K GQA cross-attention, partials per split)"
+
+    def roofline(name, key, total_ms, n, bytes_per_launch, sources):
+        avg = total_ms / max(n, 1)
+        ach = bytes_per_launch / (avg * 1e-3) / 1e9
+        cf = counters_file(key, args.workload)
+        return {"bound": "hbm", "kernel": name, "timing": f"HIP events around each launch over {args.steps} "
+                "steps after the timed region, on the library's stream",
+                "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
+                "traffic": head_traffic_from_counters(cf, sources), "traffic_source": cf.name,
+                "bytes_per_launch": bytes_per_launch, "avg_launch_ms": avg, "launches": n}
+    r_head = roofline(head_name, "head_kernel" if "head_kernel (" in head_name else head_name.split()[0],
+                      head_ms, head_n, head_launch_bytes, HEAD_SOURCES)
+    # one attention launch reads one block's visible K and V of every sequence
+    r_attn = roofline(attn_name, attn_name.split()[0], attn_ms, attn_n, kvb // m.n_blocks, ATTN_SOURCES)
+    if attn_ms > head_ms:
+        dominant, other = r_attn, r_head
+    else:
+        dominant, other = r_head, r_attn
+    value = S * N / (ms_per_step * 1e-3)
+    acc = n_acc.cpu().numpy()
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOADS[args.workload][1],
+                   "n_seq": S, "draft_steps": N, "n_vocab": V,
+                   "kv_positions": [s_.attn_pos + 1 for s_ in dr.seqs][:16]},
+        "hbm_gbps_round": round_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "bytes_per_round": round_bytes,
+        "roofline": dominant,
+        "roofline_other": other,
+        "breakdown": breakdown,
+        "accepted_per_round": float(acc.mean()),
+    }
+    ctx.close()
+    del keep_kv, keep_w
+    if not args.no_cpu_baseline:
+        log(f"bench: cpu baseline (oracle, {args.cpu_reps} timed runs of one draft step)")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_reps)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-reps", type=int, default=3, help="timed oracle runs (median) for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time (c8 cpu_baseline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only copy a buffer of this many MiB 3 times (calibrates rocprofv3 byte counters)")
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS),
-                    help="c2 (default, the headline line); the others are extra measurements")
+    ap.add_argument("--workload", default="c4", choices=sorted(WORKLOADS),
+                    help="c4 (default, the headline line: the largest configuration); the others are extra "
+                         "measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU form (sequences would shard across GPUs "
@@ -312,133 +498,7 @@ def main():
     if args.workload == "c8":
         bench_hidden(args, dev)
         return
-    log(f"bench: generating workload {args.workload}")
-    w = getattr(syn, WORKLOADS[args.workload][0])()
-    m, dr = w.model, w.draft
-    S, N, V = len(dr.seqs), dr.n_steps, m.n_vocab
-    desc, wts, keep_w = upload_model(m, dev, S, N)
-    seqs, last_tok, h_prev, keep_kv = upload_seqs(m, dr, dev)
-    stream = torch.cuda.current_stream()
-    ctx = mtp.Context(desc, wts, stream=stream, keepalive=keep_w)
-    seq_arr = mtp.make_seqs(seqs)
-    drafts = torch.zeros((S, N), dtype=torch.int32, device=dev)
-    h_last = torch.zeros((S, m.d_hprev), dtype=torch.float32, device=dev)
-    toks = torch.zeros((S, N + 1), dtype=torch.int32, device=dev)
-    n_acc = torch.zeros((S,), dtype=torch.int32, device=dev)
-
-    # target logits with the drafter's own drafts planted (p_accept 0.8)
-    ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
-    torch.cuda.synchronize()
-    gv = syn.make_greedy_verify(1, S, N, V, w.p_accept, "max5", drafts=drafts.cpu().numpy())
-    w.greedy = gv
-    logits = to_dev(gv.logits, dev)
-
-    def step():
-        ctx.draft_block(seq_arr, last_tok, h_prev, N, drafts, h_last)
-        ctx.verify_greedy(logits, drafts, toks, n_acc)
-
-    log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # Kernel timing: the same steps again with HIP events around every LM-head
-    # launch on the library's stream.  Event timing makes the library launch
-    # the chain kernel by kernel instead of replaying its captured graph; the
-    # head kernel itself is identical in both modes.
-    ctx.profile(1 << mtp.MTP_PROF_HEAD)
-    for _ in range(args.steps):
-        step()
-    head_ms, head_n = ctx.profile_read(mtp.MTP_PROF_HEAD)
-    ctx.profile(0)
-
-    # per-class breakdown over a second, separately profiled pass (diagnostic)
-    ctx.profile(0xF)
-    n_diag = min(args.steps, 20)
-    for _ in range(n_diag):
-        step()
-    torch.cuda.synchronize()
-    breakdown = {}
-    for name, cls in (("head", mtp.MTP_PROF_HEAD), ("attn", mtp.MTP_PROF_ATTN), ("gemv", mtp.MTP_PROF_GEMV),
-                      ("verify", mtp.MTP_PROF_VERIFY)):
-        t, n = ctx.profile_read(cls)
-        breakdown[name] = {"ms_per_step": t / n_diag, "launches_per_step": n / n_diag}
-    ctx.profile(0)
-    log(f"bench: breakdown {breakdown}")
-
-    wb, hb, gb = weight_bytes(m, S)
-    kvb = kv_bytes(m, dr.seqs)
-    step_bytes = wb + hb + gb + kvb + S * m.d_model * 2
-    round_bytes = N * step_bytes + S * (N + 1) * V * 4
-    head_launch_bytes = hb + m.d_hprev * m.d_model * 2 + 2 * S * m.d_model * 4
-    if m.n_centroids:   # the head class times only the candidate-row kernel
-        head_launch_bytes -= m.n_centroids * m.d_model * (4 if m.w_dtype == syn.F32 else 2)
-    head_avg_ms = head_ms / max(head_n, 1)
-    achieved = head_launch_bytes / (head_avg_ms * 1e-3) / 1e9
-    if m.n_centroids:
-        kernel_name = "cand_head_kernel (centroid head candidate rows + argmax + post-proj)"
-    elif S >= 2 and m.head_dtype != syn.F32:
-        kernel_name = "mm_head_kernel (final RMSNorm + matrix-core LM head + argmax + post-proj)"
-    else:
-        kernel_name = "head_kernel (final RMSNorm + LM head GEMV + argmax + post-proj)"
-    value = S * N / (ms_per_step * 1e-3)
-    acc = n_acc.cpu().numpy()
-
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "draft tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload][1],
-                   "n_seq": S, "draft_steps": N, "n_vocab": V,
-                   "kv_positions": [s_.attn_pos + 1 for s_ in dr.seqs][:16]},
-        "hbm_gbps_round": round_bytes / (ms_per_step * 1e-3) / 1e9,
-        "hbm_frac_round": round_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "bytes_per_round": round_bytes,
-        "roofline": {"bound": "hbm", "kernel": kernel_name,
-                     "note": None if args.workload == "c2" else "HBM counters are taken on the c2 workload only",
-                     "timing": f"HIP events around each head launch over {args.steps} steps after the timed region",
-                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": head_traffic_from_counters() if args.workload == "c2" else None,
-                     "bytes_per_launch": head_launch_bytes,
-                     "avg_launch_ms": head_avg_ms,
-                     "launches": head_n},
-        "roofline_attn": {"bound": "hbm", "kernel": "attn_mm_kernel + merge_kernel (split-K attention, a3)",
-                          "timing": f"HIP events around each attention + merge pair over {n_diag} steps",
-                          "achieved": N * kvb / (breakdown["attn"]["ms_per_step"] * 1e-3) / 1e9,
-                          "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                          "frac": N * kvb / (breakdown["attn"]["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                          "bytes_per_round": N * kvb,
-                          "note": "with little KV per block per step, per-launch latency dominates (one "
-                                  "sequence at 8192 cells: 16 MiB per block over 256 workgroups, one tile per "
-                                  "wave); with long KV the same kernel streams at ~5.9 TB/s (one sequence at "
-                                  "131072 cells: 256 MiB in 45 us)"},
-        "breakdown": breakdown,
-        "accepted_per_round": float(acc.mean()),
-    }
-    ctx.close()
-    if args.workload != "c2":
-        out["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline and args.workload == "c2":
-        log(f"bench: cpu baseline (~{args.cpu_budget:.0f} s of oracle time)")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    print(json.dumps(out), flush=True)
+    bench_draft(args, dev)
 
 
 if __name__ == "__main__":

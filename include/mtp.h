@@ -97,6 +97,15 @@ typedef struct mtp_model_desc {
        (> 0) and number of leading sink positions (>= 0). */
     int32_t sw_window;
     int32_t sw_sink;
+    /* Verifies from the target's hidden rows (mtp_verify_greedy_hidden,
+       mtp_verify_sample_hidden): the widest target head width d of any later
+       such call (0: those calls are refused with MTP_E_SHAPE; otherwise a
+       multiple of 256, <= 16384), and whether mtp_verify_sample_hidden will be
+       called (nonzero: its logit rows, max_seqs * (max_steps + 1) * n_vocab
+       floats, are allocated at create).  Both apply to verify-only contexts
+       too. */
+    int32_t hidden_d_max;
+    int32_t hidden_sample;
 } mtp_model_desc;
 
 /* Borrowed device pointers; must stay valid and unchanged for the context's
@@ -157,8 +166,9 @@ typedef struct mtp_sampler {
 
 /* Create a context on the current HIP device, bound to hip_stream (a
    hipStream_t; NULL = the null stream).  Allocates all scratch once
-   (vocabulary-sized buffers included).  weights == NULL makes a verify-only
-   context (then only n_vocab, max_seqs and max_steps of desc are used).
+   (vocabulary-sized buffers included); no later call allocates device
+   memory.  weights == NULL makes a verify-only context (then only n_vocab,
+   max_seqs, max_steps, hidden_d_max and hidden_sample of desc are used).
    A Q8_0 head is re-laid out once into a context-owned copy (int8 plane plus
    fp16 scale plane, the same bytes per weight).  Returns MTP_OK and *out. */
 int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *weights, void *hip_stream, mtp_ctx **out);
@@ -239,8 +249,9 @@ typedef struct mtp_lm_head {
      hidden      fp32 [n_seq, n_draft+1, head->d], 16-byte aligned
      drafts      int32 [n_seq, n_draft]
      out_tokens  int32 [n_seq, n_draft+1] (-1 past the emitted ones); out_n_accept int32 [n_seq]
-   The first call with a given d allocates a scratch buffer of 256 * d bytes
-   that the context keeps. */
+   head->d must not exceed the context's hidden_d_max (else MTP_E_SHAPE,
+   nothing enqueued); the staging scratch (256 * hidden_d_max bytes) was
+   allocated at create. */
 int mtp_verify_greedy_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
                              const float *hidden, const int32_t *drafts, int32_t *out_tokens,
                              int32_t *out_n_accept);
@@ -255,8 +266,14 @@ int mtp_verify_greedy_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const
    drawn from p_n_draft.  Draws use Gumbel-max over SplitMix64 counters
    (stream 1 residual, 2 bonus).
      p_logits fp32 [n_seq, n_draft+1, n_vocab]; q_logits fp32 [n_seq, n_draft, n_vocab]
-     history int32 [n_seq, history_stride]; history_len int32 [n_seq]
+     history int32 [n_seq, history_stride]; history_len int32 [n_seq], each
+             read as clamped to [0, history_stride] (history may be NULL when
+             history_stride is 0; history_len may be NULL when
+             penalty_last_n is 0)
      sampler host pointer
+   Logit rows are expected finite.  A row none of whose tokens survives the
+   chain (no finite maximum) has an empty distribution: its draft is
+   rejected and a draw from it emits -1.
      out_tokens int32 [n_seq, n_draft+1] (-1 past the emitted ones); out_n_accept int32 [n_seq] */
 int mtp_verify_sample(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *p_logits,
                       const float *q_logits, const int32_t *drafts, const int32_t *history,
@@ -275,9 +292,9 @@ int mtp_verify_sample(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vo
      q_logits    fp32 [n_seq, n_draft, head->n_vocab] or NULL (one-hot drafts)
      drafts, history, history_stride, history_len, sampler, round, out_tokens,
      out_n_accept: as for mtp_verify_sample
-   The logit rows go to a context-owned buffer of n_seq * (n_draft+1) *
-   n_vocab floats (allocated, or grown, on first need, together with the
-   staging buffer of mtp_verify_greedy_hidden); the caller never sees them. */
+   The logit rows go to a context-owned buffer allocated at create (requires
+   hidden_sample nonzero and head->d <= hidden_d_max, else MTP_E_SHAPE with
+   nothing enqueued); the caller never sees them. */
 int mtp_verify_sample_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
                              const float *hidden, const float *q_logits, const int32_t *drafts,
                              const int32_t *history, int32_t history_stride, const int32_t *history_len,
@@ -293,10 +310,11 @@ int mtp_verify_sample_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const
    class since the last enable/read, and resets that class. */
 typedef enum mtp_prof_class {
     MTP_PROF_HEAD = 0,      /* final norm + LM head + argmax + post-projection */
-    MTP_PROF_ATTN = 1,      /* split-K attention + merge */
+    MTP_PROF_ATTN = 1,      /* split-K attention (partials per split) */
     MTP_PROF_GEMV = 2,      /* pre-projection, Q, O, up, down GEMVs */
     MTP_PROF_VERIFY = 3,    /* greedy or sampling verify */
-    MTP_PROF_N = 4
+    MTP_PROF_MERGE = 4,     /* log-sum-exp merge of the attention splits */
+    MTP_PROF_N = 5
 } mtp_prof_class;
 int mtp_profile_enable(mtp_ctx *ctx, int mask);
 int mtp_profile_read(mtp_ctx *ctx, int cls, double *total_ms, int64_t *count);

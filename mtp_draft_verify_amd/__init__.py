@@ -27,7 +27,7 @@ MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
            "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_verify_sample_hidden", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
            "mtp_last_error")
-MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY = 0, 1, 2, 3
+MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY, MTP_PROF_MERGE = 0, 1, 2, 3, 4
 
 
 class MTPError(RuntimeError):
@@ -43,7 +43,8 @@ class ModelDesc(C.Structure):
                [("block_src", C.c_int32 * MAX_BLOCKS)] + \
                [(n, C.c_float) for n in ("rms_eps", "rope_theta", "attn_scale", "embed_scale")] + \
                [("max_seqs", C.c_int32), ("max_steps", C.c_int32), ("n_centroids", C.c_int32),
-                ("centroid_top_k", C.c_int32), ("sw_window", C.c_int32), ("sw_sink", C.c_int32)]
+                ("centroid_top_k", C.c_int32), ("sw_window", C.c_int32), ("sw_sink", C.c_int32),
+                ("hidden_d_max", C.c_int32), ("hidden_sample", C.c_int32)]
 
 
 class Weights(C.Structure):
@@ -249,13 +250,13 @@ def mtp_profile_read(ctx: int, cls: int):
 def make_desc(*, d_model, d_hprev, n_blocks, n_head_q, n_head_kv, head_dim, d_ff, n_vocab, w_dtype, head_dtype,
               kv_dtype, swa_window=0, block_src=(), rms_eps=1e-6, rope_theta=10000.0, attn_scale=None,
               embed_scale=None, max_seqs=1, max_steps=4, n_centroids=0, centroid_top_k=0, sw_window=0,
-              sw_sink=0) -> ModelDesc:
+              sw_sink=0, hidden_d_max=0, hidden_sample=0) -> ModelDesc:
     d = ModelDesc()
     for k, v in dict(d_model=d_model, d_hprev=d_hprev, n_blocks=n_blocks, n_head_q=n_head_q, n_head_kv=n_head_kv,
                      head_dim=head_dim, d_ff=d_ff, n_vocab=n_vocab, w_dtype=w_dtype, head_dtype=head_dtype,
                      kv_dtype=kv_dtype, swa_window=swa_window, max_seqs=max_seqs, max_steps=max_steps,
                      n_centroids=n_centroids, centroid_top_k=centroid_top_k, sw_window=sw_window,
-                     sw_sink=sw_sink).items():
+                     sw_sink=sw_sink, hidden_d_max=hidden_d_max, hidden_sample=hidden_sample).items():
         setattr(d, k, int(v))
     for i in range(MAX_BLOCKS):
         d.block_src[i] = int(block_src[i]) if i < len(block_src) else 0

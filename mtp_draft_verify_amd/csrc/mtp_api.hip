@@ -22,6 +22,7 @@ using namespace mtp;
 namespace {
 
 constexpr int kParamSlots = 8;
+constexpr size_t kMaxGraphs = 16;       // captured chains kept per context
 
 thread_local char g_last_error[256] = "";
 
@@ -86,10 +87,15 @@ struct mtp_ctx {
     hipEvent_t ev[kParamSlots]{};
     bool ev_pending[kParamSlots]{};
     int slot = 0;
-    // captured draft chains, one per launch shape
+    // captured draft chains, one per launch shape, least recently used evicted
+    // past kMaxGraphs; an evicted graph may still be queued on the stream, so
+    // it is destroyed only once an event recorded behind it has completed
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[7]; hipGraph_t g; hipGraphExec_t exec; };
+    struct Graph { int key[7]; hipGraph_t g; hipGraphExec_t exec; uint64_t last_use; };
     std::vector<Graph> graphs;
+    uint64_t use_clock = 0;
+    struct Retired { hipGraph_t g; hipGraphExec_t exec; hipEvent_t done; };
+    std::vector<Retired> retired;
     bool graph_failed = false;          // capture unsupported: launch directly
     // optional event timing per kernel class
     int prof_mask = 0;
@@ -97,9 +103,9 @@ struct mtp_ctx {
     std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_pending[MTP_PROF_N];
     // verify scratch
     uint64_t *vkeys = nullptr;          // [max_seqs][max_steps + 1]
-    void *hv_plane = nullptr;           // verify from hidden states: staged rows (grown on demand)
+    void *hv_plane = nullptr;           // verify from hidden states: staged rows (hidden_d_max wide)
     size_t hv_plane_size = 0;
-    float *hv_logits = nullptr;         // sampling verify from hidden states: logit rows (grown on demand)
+    float *hv_logits = nullptr;         // sampling verify from hidden states: logit rows (hidden_sample)
     size_t hv_logits_size = 0;
     // temperature>0 verify scratch, per row (target rows then draft rows)
     int32_t s_cap = 0;                  // candidate slots per row
@@ -126,8 +132,16 @@ extern "C" const char *mtp_strerror(int code) {
     }
 }
 
+// Limits of the hidden-state verifies' scratch, sized at create.
+static int check_hidden_desc(const mtp_model_desc *d) {
+    if (d->hidden_d_max < 0 || d->hidden_d_max > 16384 || d->hidden_d_max % 256) return MTP_E_SHAPE;
+    if (d->hidden_sample && d->hidden_d_max == 0) return MTP_E_SHAPE;
+    return MTP_OK;
+}
+
 extern "C" int mtp_check_desc(const mtp_model_desc *d) {
     if (!d) return MTP_E_INVAL;
+    if (check_hidden_desc(d) != MTP_OK) return MTP_E_SHAPE;
     if (d->d_model <= 0 || d->d_hprev <= 0 || d->n_blocks <= 0 || d->n_head_q <= 0 || d->n_head_kv <= 0 ||
         d->head_dim <= 0 || d->d_ff <= 0 || d->n_vocab <= 0 || d->max_seqs <= 0 || d->max_steps <= 0)
         return MTP_E_SHAPE;
@@ -180,8 +194,27 @@ static int check_weights(const mtp_model_desc *d, const mtp_weights *w) {
     return MTP_OK;
 }
 
+// Destroy the evicted graphs whose last launch has completed (all of them
+// when `all`, after the stream has been drained).
+static void reap_graphs(mtp_ctx *c, bool all) {
+    size_t keep = 0;
+    for (size_t i = 0; i < c->retired.size(); ++i) {
+        mtp_ctx::Retired &r = c->retired[i];
+        if (all || hipEventQuery(r.done) == hipSuccess) {
+            (void)hipGraphExecDestroy(r.exec);
+            (void)hipGraphDestroy(r.g);
+            (void)hipEventDestroy(r.done);
+        } else {
+            c->retired[keep++] = r;
+        }
+    }
+    c->retired.resize(keep);
+    (void)hipGetLastError();            // a pending query is not an error
+}
+
 static void free_ctx(mtp_ctx *c) {
     if (!c) return;
+    reap_graphs(c, true);
     for (auto &g : c->graphs) {
         (void)hipGraphExecDestroy(g.exec);
         (void)hipGraphDestroy(g.g);
@@ -218,7 +251,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         if (rc) return rc;
         rc = check_weights(desc, weights);
         if (rc) return rc;
-    } else if (desc->n_vocab <= 0 || desc->max_seqs <= 0 || desc->max_steps <= 0 || desc->max_steps > 64) {
+    } else if (desc->n_vocab <= 0 || desc->max_seqs <= 0 || desc->max_steps <= 0 || desc->max_steps > 64 ||
+               check_hidden_desc(desc) != MTP_OK) {
         return MTP_E_SHAPE;
     }
     mtp_ctx *c = new (std::nothrow) mtp_ctx();
@@ -246,6 +280,16 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->s_maxkey, rows) && dalloc(&c->s_topk, rows) && dalloc(&c->s_cand_n, rows) &&
              dalloc(&c->s_cand_id, rows * c->s_cap) && dalloc(&c->s_cand_v, rows * c->s_cap) &&
              dalloc((uint8_t **)&c->s_state, rows * sample_row_state_bytes());
+    }
+    // verifies from hidden rows: the staging plane for the widest head, and
+    // the logit rows of the sampling form (every row of a largest call)
+    if (ok && d.hidden_d_max > 0) {
+        c->hv_plane_size = hv_plane_bytes(d.hidden_d_max);
+        ok = dalloc((uint8_t **)&c->hv_plane, c->hv_plane_size);
+    }
+    if (ok && d.hidden_sample) {
+        c->hv_logits_size = sizeof(float) * S * R * (size_t)d.n_vocab;
+        ok = dalloc(&c->hv_logits, S * R * (size_t)d.n_vocab);
     }
     if (weights) {
         c->w = *weights;
@@ -499,6 +543,9 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                     aa.S = S; aa.src = src; aa.step = k; aa.seqs = dp; aa.part = c->part;
                     e = launch_attn(d.kv_dtype, aa, sh.split[src], st);
                 }
+            }
+            {
+                ProfScope ps_merge(c, MTP_PROF_MERGE);
                 if (e == hipSuccess) {
                     MergeArgs ma{};
                     ma.part = c->part; ma.o = c->o; ma.o_op = mm_io ? c->o_op : nullptr;
@@ -590,8 +637,13 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
     const int key[7] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf};
+    ++c->use_clock;
+    reap_graphs(c, false);
     for (auto &g : c->graphs)
-        if (std::memcmp(g.key, key, sizeof(key)) == 0) return g.exec;
+        if (std::memcmp(g.key, key, sizeof(key)) == 0) {
+            g.last_use = c->use_clock;
+            return g.exec;
+        }
     if (c->graph_failed) return nullptr;
     if (hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeRelaxed) != hipSuccess) {
         c->graph_failed = true;
@@ -613,15 +665,31 @@ static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
         c->graph_failed = true;
         return nullptr;
     }
-    if (c->graphs.size() >= 16) {       // keep the cache bounded
-        (void)hipGraphExecDestroy(c->graphs.front().exec);
-        (void)hipGraphDestroy(c->graphs.front().g);
-        c->graphs.erase(c->graphs.begin());
+    if (c->graphs.size() >= kMaxGraphs) {
+        // evict the least recently used chain; everything enqueued so far on
+        // the stream (its launches included) precedes the event
+        size_t lru = 0;
+        for (size_t i = 1; i < c->graphs.size(); ++i)
+            if (c->graphs[i].last_use < c->graphs[lru].last_use) lru = i;
+        hipEvent_t done = nullptr;
+        if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess ||
+            hipEventRecord(done, c->stream) != hipSuccess) {
+            // cannot tell when the old chain is idle: keep it, and drop the
+            // new one (never launched); this call launches kernel by kernel
+            if (done) (void)hipEventDestroy(done);
+            (void)hipGetLastError();
+            (void)hipGraphExecDestroy(exec);
+            (void)hipGraphDestroy(g);
+            return nullptr;
+        }
+        c->retired.push_back({c->graphs[lru].g, c->graphs[lru].exec, done});
+        c->graphs.erase(c->graphs.begin() + (long)lru);
     }
     mtp_ctx::Graph ent;
     std::memcpy(ent.key, key, sizeof(key));
     ent.g = g;
     ent.exec = exec;
+    ent.last_use = c->use_clock;
     c->graphs.push_back(ent);
     return exec;
 }
@@ -715,27 +783,8 @@ extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch", e);
 }
 
-// Grow a context-owned scratch buffer to at least `need` bytes.  A buffer in
-// use by enqueued work is freed only after the stream has drained it.
-static int grow_scratch(mtp_ctx *c, void **buf, size_t *size, size_t need) {
-    if (*size >= need) return MTP_OK;
-    if (*buf) {
-        if (hipStreamSynchronize(c->stream) != hipSuccess) return hip_fail("stream wait", hipGetLastError());
-        (void)hipFree(*buf);
-        *buf = nullptr;
-        *size = 0;
-    }
-    if (hipMalloc(buf, need) != hipSuccess) {
-        *buf = nullptr;
-        (void)hipGetLastError();
-        return MTP_E_NOMEM;
-    }
-    *size = need;
-    return MTP_OK;
-}
-
 // Checks of a caller's LM head and hidden rows shared by both hidden-state
-// verifies; grows the context's staging plane to the head width.
+// verifies; the head must fit the staging plane allocated at create.
 static int prepare_hidden_head(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,
                                const float *hidden, const int32_t *drafts, int32_t *out_tokens,
                                int32_t *out_n_accept) {
@@ -748,8 +797,8 @@ static int prepare_hidden_head(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const
         !aligned16(hidden) || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept)
         return MTP_E_INVAL;
     if (!(head->rms_eps >= 0.f) || !std::isfinite(head->rms_eps)) return MTP_E_INVAL;
-    const size_t need = hv_plane_bytes(head->d);
-    return grow_scratch(c, &c->hv_plane, &c->hv_plane_size, need);
+    if (!c->hv_plane || hv_plane_bytes(head->d) > c->hv_plane_size) return MTP_E_SHAPE;
+    return MTP_OK;
 }
 
 static HvArgs hidden_args(mtp_ctx *c, const mtp_lm_head *head, const float *hidden) {
@@ -831,15 +880,14 @@ extern "C" int mtp_verify_sample_hidden(mtp_ctx *c, int32_t n_seq, int32_t n_dra
     if (!sp) return MTP_E_INVAL;
     int rc = prepare_hidden_head(c, n_seq, n_draft, head, hidden, drafts, out_tokens, out_n_accept);
     if (rc != MTP_OK) return rc;
-    if (head->n_vocab > c->desc.n_vocab) return MTP_E_SHAPE;     // the sampling scratch is sized by desc.n_vocab
+    // the sampling scratch and the logit rows are sized by desc.n_vocab
+    if (head->n_vocab > c->desc.n_vocab || !c->hv_logits) return MTP_E_SHAPE;
     SampleArgs sa;
     rc = sample_args(c, n_seq, n_draft, head->n_vocab, nullptr, q_logits, drafts, history, history_stride,
                      history_len, sp, round, out_tokens, out_n_accept, &sa);
     if (rc != MTP_OK) return rc;
     const int32_t rows = n_seq * (n_draft + 1);
-    rc = grow_scratch(c, reinterpret_cast<void **>(&c->hv_logits), &c->hv_logits_size,
-                      sizeof(float) * (size_t)rows * head->n_vocab);
-    if (rc != MTP_OK) return rc;
+    if (sizeof(float) * (size_t)rows * head->n_vocab > c->hv_logits_size) return MTP_E_SHAPE;
     sa.p_logits = c->hv_logits;
     ProfScope ps(c, MTP_PROF_VERIFY);
     HvArgs a = hidden_args(c, head, hidden);

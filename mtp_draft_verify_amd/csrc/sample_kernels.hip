@@ -103,12 +103,16 @@ __device__ __forceinline__ RowRef row_ref(const SampleArgs &a, int row) {
 }
 
 // context of row (s, i): the last last_n tokens of history[s] ++ drafts[s][0..i)
+// (a history length outside [0, hstride] reads as clamped into it)
+__device__ __forceinline__ int hist_len(const SampleArgs &a, int s) {
+    return a.history_len ? min(max(a.history_len[s], 0), a.hstride) : 0;
+}
 __device__ __forceinline__ int ctx_len(const SampleArgs &a, int s, int i) {
-    const int total = (a.history_len ? a.history_len[s] : 0) + i;
+    const int total = hist_len(a, s) + i;
     return a.last_n <= 0 ? 0 : min(a.last_n, total);
 }
 __device__ __forceinline__ int32_t ctx_token(const SampleArgs &a, int s, int i, int n_ctx, int j) {
-    const int hlen = a.history_len ? a.history_len[s] : 0;
+    const int hlen = hist_len(a, s);
     const int pos = hlen + i - n_ctx + j;
     return pos < hlen ? a.history[(int64_t)s * a.hstride + pos] : a.drafts[(int64_t)s * a.N + (pos - hlen)];
 }
@@ -436,6 +440,18 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     RowState st;
     st.M = M;
     st.pad = 0;
+    if (n_all == 0) {
+        // no token survives (a row without a finite maximum): the row's
+        // distribution is empty, every probability reads 0 and a draw from it
+        // emits -1
+        if (tid == 0) {
+            st.Z = 1.f;
+            st.tau = ~0ull;
+            st.n_keep = 0;
+            ((RowState *)a.row_state)[row] = st;
+        }
+        return;
+    }
     if (n_all <= min(kSortMax, a.cap)) {
         // ---- compact form: sort the candidates ----
         const int n = n_all;

@@ -311,7 +311,8 @@ class SampleVerifyInputs:
 
 
 def make_sample_verify(seed: int, S: int, N: int, V: int, *, logit_var: float = 3.0, hist: int = 64,
-                       one_hot: bool = False, sampler: Optional[Sampler] = None) -> SampleVerifyInputs:
+                       one_hot: bool = False, sampler: Optional[Sampler] = None,
+                       draft_mode: str = "sample") -> SampleVerifyInputs:
     """Temperature>0 verify inputs shaped like the exact-sampling workload.
 
     p logits ~ N(0, var logit_var); q logits = p[:, :N] + N(0,1) (an
@@ -321,6 +322,8 @@ def make_sample_verify(seed: int, S: int, N: int, V: int, *, logit_var: float = 
     by the Gumbel trick on this module's own stream (a stand-in drafter; the
     verify rule is exact for whatever drafts it is given only when the drafts
     follow the processed q, which the statistical tests arrange separately).
+    draft_mode "argmax": each draft is instead the highest raw logit of its q
+    row (of its p row when one_hot), as a greedy drafter would propose.
     """
     sampler = sampler or Sampler()
     p = normal(seed, "sample.p", (S, N + 1, V), std=math.sqrt(logit_var))
@@ -337,8 +340,11 @@ def make_sample_verify(seed: int, S: int, N: int, V: int, *, logit_var: float = 
         history[s] = hs
     history_len = np.full(S, hist, dtype=np.int32)
     src = q if q is not None else p[:, :N]
-    g = rng_for(seed, "sample.drafts").gumbel(size=(S, N, V)).astype(np.float32)
-    drafts = np.argmax(src / np.float32(sampler.temp) + g, axis=2).astype(np.int32)
+    if draft_mode == "argmax":
+        drafts = np.argmax(src, axis=2).astype(np.int32)
+    else:
+        g = rng_for(seed, "sample.drafts").gumbel(size=(S, N, V)).astype(np.float32)
+        drafts = np.argmax(src / np.float32(sampler.temp) + g, axis=2).astype(np.int32)
     return SampleVerifyInputs(p, q, drafts, history, history_len, sampler)
 
 
@@ -464,7 +470,8 @@ def c5_sample(seed: int = 4, **over) -> Workload:
     S = over.get("n_seq", 32)
     N = over.get("n_draft", 4)
     V = over.get("n_vocab", 248320)
-    sv = make_sample_verify(seed, S, N, V, one_hot=over.get("one_hot", False))
+    sv = make_sample_verify(seed, S, N, V, one_hot=over.get("one_hot", False),
+                            draft_mode=over.get("draft_mode", "sample"))
     return Workload("c5_exact_sampling_verify", None, None, sample=sv)
 
 

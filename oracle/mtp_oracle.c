@@ -698,7 +698,10 @@ int orc_verify_sample(int32_t n_seq, int32_t n_draft, int32_t V, const float *p_
         for (int32_t s = 0; s < n_seq; ++s) {
             if (err) continue;
             const int32_t *hist = history ? history + (int64_t)s * history_stride : NULL;
-            const int32_t hlen = history_len ? history_len[s] : 0;
+            /* the boundary's contract: a history length reads as clamped to
+               [0, history_stride] */
+            int32_t hlen = history_len ? history_len[s] : 0;
+            hlen = hlen < 0 ? 0 : (hlen > history_stride ? history_stride : hlen);
             const int32_t *dr = drafts ? drafts + (int64_t)s * N : NULL;
             int32_t fl = 0, a = N;
             for (int32_t j = 0; j < R; ++j) out_tokens[(int64_t)s * R + j] = -1;

@@ -19,3 +19,30 @@ def orc():
     from oracle import oracle as O
     O.build(force=False)
     return O
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """The parity counts the GPU tests recorded (near ties, flagged
+    sequences, largest errors), one JSON line per case, and their totals;
+    also written to $MTP_PARITY_RECORD when that names a file."""
+    import json
+    import os
+    try:
+        from tests.gpu_harness import RECORDS
+    except Exception:
+        return
+    if not RECORDS:
+        return
+    tot = {"cases": len(RECORDS)}
+    for r in RECORDS:
+        for k in ("near_ties", "flagged", "compared", "mismatches_on_clean"):
+            if k in r:
+                tot[k] = tot.get(k, 0) + r[k]
+    terminalreporter.write_sep("-", "parity records")
+    for r in RECORDS:
+        terminalreporter.write_line("PARITY " + json.dumps(r, separators=(",", ":")))
+    terminalreporter.write_line("PARITY_TOTAL " + json.dumps(tot, separators=(",", ":")))
+    path = os.environ.get("MTP_PARITY_RECORD")
+    if path:
+        with open(path, "w") as f:
+            json.dump({"total": tot, "cases": RECORDS}, f, indent=1)

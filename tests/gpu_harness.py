@@ -23,6 +23,21 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+# Per-case parity counts (near ties, flagged sequences, errors), printed as
+# one JSON line per case at the end of the session by tests/conftest.py, so
+# that they reach the end of the pytest output whatever its verbosity.
+RECORDS = []
+
+
+def record(case: str, **counts) -> None:
+    import os
+    r = {"case": case}
+    for k, v in counts.items():
+        r[k] = float(v) if isinstance(v, (float, np.floating)) else int(v)
+    r["test"] = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    RECORDS.append(r)
+
+
 def tol_for(m: syn.Model):
     if m.w_dtype == syn.F32 and m.head_dtype == syn.F32 and m.kv_dtype == syn.F32:
         return "rel", 1e-4

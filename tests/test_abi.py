@@ -54,6 +54,7 @@ def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
     tiny = dict(d_model=256, d_hprev=256, n_blocks=1, n_head_q=4, n_head_kv=1, head_dim=64, d_ff=1024, n_vocab=4096,
                 w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32, max_seqs=1, max_steps=3)
     assert mtp.mtp_check_desc(mtp.make_desc(**tiny)) == mtp.MTP_OK
+    assert mtp.mtp_check_desc(_c2_desc(mtp, hidden_d_max=2816, hidden_sample=1)) == mtp.MTP_OK
     bad = [
         dict(n_head_kv=3),                        # Hq % Hkv
         dict(n_blocks=9),                         # > MTP_MAX_BLOCKS
@@ -68,6 +69,10 @@ def test_check_desc_accepts_the_configs_and_rejects_bad_shapes(mtp):
         dict(head_dim=96),                        # no attention instantiation
         dict(d_ff=8192),                          # GEMV row longer than supported
         dict(max_steps=0),
+        dict(hidden_d_max=300),                   # hidden-verify width not a multiple of 256
+        dict(hidden_d_max=16640),                 # wider than the hidden-verify kernels take
+        dict(hidden_d_max=-256),
+        dict(hidden_sample=1),                    # logit rows without a head width
     ]
     for b in bad:
         rc = mtp.mtp_check_desc(_c2_desc(mtp, **b))

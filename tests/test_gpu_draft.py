@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import mtp_synth as syn
-from tests.gpu_harness import GpuDrafter, compare_draft, log
+from tests.gpu_harness import GpuDrafter, compare_draft, log, record
 
 pytestmark = pytest.mark.gpu
 
@@ -12,6 +12,8 @@ def _check(w, gpu_out, orc_out, idx=None, max_near=1):
     c = compare_draft(w.model, gpu_out, orc_out, idx)
     log(f"  {w.name}: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
         f"max_h_err={c.max_h_err:.3g}")
+    record(w.name, compared_steps=c.compared_steps, near_ties=c.near_ties, max_logit_err=c.max_logit_err,
+           max_h_err=c.max_h_err)
     assert c.near_ties <= max_near
     return c
 

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import mtp_synth as syn
-from tests.gpu_harness import log
+from tests.gpu_harness import log, record
 
 pytestmark = pytest.mark.gpu
 
@@ -42,11 +42,12 @@ def _run(ctx, hv, reps=1):
     return outs
 
 
-def _ctx(max_seqs, max_steps, n_vocab=4096):
+def _ctx(max_seqs, max_steps, n_vocab=4096, d_max=2816, sample=True):
     import mtp_draft_verify_amd as mtp
     desc = mtp.make_desc(d_model=256, d_hprev=256, n_blocks=1, n_head_q=4, n_head_kv=1, head_dim=64, d_ff=1024,
                          n_vocab=n_vocab, w_dtype=mtp.MTP_F32, head_dtype=mtp.MTP_F32, kv_dtype=mtp.MTP_F32,
-                         max_seqs=max_seqs, max_steps=max_steps)
+                         max_seqs=max_seqs, max_steps=max_steps, hidden_d_max=((d_max + 255) // 256) * 256,
+                         hidden_sample=int(sample))
     return mtp.Context(desc, None)
 
 
@@ -65,6 +66,7 @@ def _compare(hv, tok, na, orc, idx):
             continue
         assert na[s] == a, (s, na[s], a)
         assert tok[s].tolist() == ot[j].tolist(), (s, tok[s], ot[j])
+    record("hidden greedy verify", compared=len(idx) - near, near_ties=near)
     return near
 
 
@@ -102,15 +104,39 @@ def test_hidden_verify_shapes(orc, S, N, d, V, gain):
     ctx.close()
 
 
-def test_hidden_verify_scratch_grows_with_the_head_width(orc):
-    """One context, a narrow head then a wider one (the staging buffer is
-    reallocated) then the narrow one again: every call matches the oracle."""
-    log("case hidden verify scratch regrowth: d 256 -> 1024 -> 256")
-    ctx = _ctx(4, 3)
+def test_hidden_verify_scratch_sized_at_create_serves_every_width(orc):
+    """One context sized for heads up to 1024 wide: a narrow head, the widest
+    one, then the narrow one again all match the oracle (the staging scratch
+    is allocated once at create).  A wider head, more sequences or rows than
+    the context was sized for, and a sampling call on a context created
+    without its logit rows are refused before anything is enqueued: the
+    outputs keep their fill."""
+    import torch
+    import mtp_draft_verify_amd as mtp
+    log("case hidden verify scratch sized at create: d 256 -> 1024 -> 256, then refusals")
+    ctx = _ctx(4, 3, 6000, d_max=1024, sample=False)
     for d in (256, 1024, 256):
         hv = syn.make_hidden_verify(5 + d, 4, 3, d, 6000)
         (tok, na), = _run(ctx, hv)
         assert _compare(hv, tok, na, orc, list(range(4))) <= 1
+    dev = "cuda"
+    sp = mtp.make_sampler(temp=0.8, top_p=0.95, min_p=0.05, rep_penalty=1.0, presence_penalty=0.0,
+                          penalty_last_n=0, seed=1)
+    for d, S, N, sample in ((1280, 4, 3, False), (256, 5, 3, False), (256, 4, 4, False), (256, 4, 3, True)):
+        hv = syn.make_hidden_verify(3, S, N, d, 6000)
+        w = torch.from_numpy(hv.head.view(np.int16)).to(dev)
+        head = mtp.make_lm_head(w, torch.from_numpy(hv.g).to(dev), d, 6000, mtp.MTP_BF16, hv.eps)
+        hidden, drafts = torch.from_numpy(hv.hidden).to(dev), torch.from_numpy(hv.drafts).to(dev)
+        tok = torch.full((S, N + 1), -7, dtype=torch.int32, device=dev)
+        na = torch.full((S,), -7, dtype=torch.int32, device=dev)
+        with pytest.raises(mtp.MTPError) as ei:
+            if sample:
+                ctx.verify_sample_hidden(head, hidden, None, drafts, None, None, sp, 0, tok, na)
+            else:
+                ctx.verify_greedy_hidden(head, hidden, drafts, tok, na)
+        assert ei.value.code == mtp.MTP_E_SHAPE, (d, S, N, sample)
+        torch.cuda.synchronize()
+        assert (tok.cpu().numpy() == -7).all() and (na.cpu().numpy() == -7).all()
     ctx.close()
 
 
@@ -139,12 +165,15 @@ def _run_sample(ctx, hv, q, history, history_len, sp, round_):
 
 
 def _sample_case(seed, S, N, d, V, gain, one_hot):
-    """Broad target rows (a weakly planted token, beta 0.1), drafts mostly the
-    planted tokens, q rows N(0, 3) (or one-hot), 40-token histories of varied
-    length."""
-    hv = syn.make_hidden_verify(seed, S, N, d, V, gain=gain, beta=0.1, p_accept=0.7)
+    """Target rows with a moderately planted token (beta 0.25), drafts mostly
+    the planted tokens, q rows N(0, 6) (or one-hot), 40-token histories of
+    varied length.  (Broader rows put the top-p cut deep in the tail, where
+    the oracle flags a near-boundary decision for a large share of the
+    sequences; the candidate forms of broad rows are covered by the logit-row
+    sampling tests.)"""
+    hv = syn.make_hidden_verify(seed, S, N, d, V, gain=gain, beta=0.25, p_accept=0.7)
     r = np.random.default_rng(seed)
-    q = None if one_hot else (math.sqrt(3.0) * r.standard_normal((S, N, V))).astype(np.float32)
+    q = None if one_hot else (math.sqrt(6.0) * r.standard_normal((S, N, V))).astype(np.float32)
     history = r.integers(0, V, (S, 40)).astype(np.int32)
     history_len = r.integers(0, 41, S).astype(np.int32)
     return hv, q, history, history_len
@@ -156,16 +185,20 @@ SAMPLER = syn.Sampler(temp=0.8, top_p=0.95, min_p=0.05, rep_penalty=1.05, presen
 
 def _compare_sample(orc, ctx, hv, q, history, history_len, sp, round_):
     """Unflagged sequences (no near-boundary decision in the oracle run) must
-    match bit for bit; the logits differ from the oracle's by fp32 rounding,
-    far inside the flags' 1e-5 windows.  Returns the flagged count."""
+    match bit for bit, and at most 10% may be flagged; the logits differ from
+    the oracle's by fp32 rounding, far inside the flags' 1e-5 windows.
+    Returns the flagged count."""
     t_o, n_o, fl = orc.verify_sample_hidden(hv.hidden, hv.head, hv.head_dtype, hv.n_vocab, hv.g, hv.eps, q,
                                             hv.drafts, history, history_len, sp, round_)
     t_g, n_g = _run_sample(ctx, hv, q, history, history_len, sp, round_)
     clean = fl == 0
     bad = np.nonzero(clean & ((n_g != n_o) | np.any(t_g != t_o, axis=1)))[0]
     log(f"  S={len(fl)} flagged={int((~clean).sum())} accept_mean={n_o.mean():.3f} mismatches_on_clean={len(bad)}")
+    record(f"hidden sampling verify round {round_}", compared=int(clean.sum()), flagged=int((~clean).sum()),
+           mismatches_on_clean=len(bad))
     assert len(bad) == 0, (bad[:5], t_g[bad[:3]], t_o[bad[:3]], n_g[bad[:3]], n_o[bad[:3]])
     assert (t_g[:, 0] >= 0).all() and (n_g >= 0).all()
+    assert (~clean).mean() <= 0.1
     return int((~clean).sum())
 
 
@@ -179,8 +212,8 @@ def test_hidden_sampling_verify_shapes(orc, S, N, d, V, gain, one_hot):
     log(f"case hidden sampling verify: S={S} N={N} d={d} V={V} gain={gain} one_hot={one_hot}")
     hv, q, history, history_len = _sample_case(31 + d, S, N, d, V, gain, one_hot)
     ctx = _ctx(16, 4, V)
-    flagged = sum(_compare_sample(orc, ctx, hv, q, history, history_len, SAMPLER, rd) for rd in (0, 5))
-    assert flagged <= S
+    for rd in (0, 5):
+        _compare_sample(orc, ctx, hv, q, history, history_len, SAMPLER, rd)
     ctx.close()
 
 

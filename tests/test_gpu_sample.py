@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import mtp_synth as syn
-from tests.gpu_harness import log
+from tests.gpu_harness import log, record
 
 pytestmark = pytest.mark.gpu
 
@@ -54,6 +54,8 @@ def _compare(orc, gpu, sv, sp, round_=0, max_flag_frac=0.1):
     clean = fl == 0
     bad = np.nonzero(clean & ((n_g != n_o) | np.any(t_g != t_o, axis=1)))[0]
     log(f"  S={len(fl)} flagged={int((~clean).sum())} accept_mean={n_o.mean():.3f} mismatches_on_clean={len(bad)}")
+    record(f"sampling verify round {round_}", compared=int(clean.sum()), flagged=int((~clean).sum()),
+           mismatches_on_clean=len(bad), accept_mean=float(n_o.mean()))
     assert len(bad) == 0, (bad[:5], t_g[bad[:3]], t_o[bad[:3]], n_g[bad[:3]], n_o[bad[:3]])
     assert (~clean).mean() <= max_flag_frac
     return n_o
@@ -68,31 +70,43 @@ def test_c5_exact_sampling_verify_matches_oracle(orc):
 
 
 def test_c5_one_hot_drafts_matches_oracle(orc):
-    log("case c5 one-hot q: S=32 N=4 V=248320")
-    w = syn.c5_sample(one_hot=True)
+    """One-hot q (deterministic drafts, the audit page's own rule).  Drafts
+    sampled from the unfiltered softmax mostly land on tokens the min-p cut
+    removes (rejected outright); greedy drafts (each row's top logit) are
+    accepted often, so both branches of the accept test run."""
+    log("case c5 one-hot q: S=32 N=4 V=248320, sampled drafts, then greedy drafts")
     g = GpuSampler(32, 4, 248320)
+    w = syn.c5_sample(one_hot=True)
     _compare(orc, g, w.sample, w.sample.sampler)
+    w = syn.c5_sample(one_hot=True, draft_mode="argmax")
+    n_o = _compare(orc, g, w.sample, w.sample.sampler)
+    assert (n_o > 0).sum() >= 4          # the accept branch ran (8 of 32 sequences accept in the oracle)
 
 
-@pytest.mark.parametrize("name,over", [
-    ("top-k 40", dict(top_k=40)),
-    ("top-k 1", dict(top_k=1)),
-    ("no penalties", dict(penalty_last_n=0)),
-    ("no min-p, no top-p (full softmax rows)", dict(min_p=0.0, top_p=1.0)),
-    ("top-p only (radix-selected cut)", dict(min_p=0.0, top_p=0.9)),
-    ("warmer temperature, ~1000 candidates per row", dict(temp=1.2, min_p=0.02)),
-    ("frequency penalty, long window", dict(freq_penalty=0.3, penalty_last_n=200)),
+# Each variant keeps its oracle's near-boundary flags rare (at most 10% of
+# the sequences): a top-p cut that falls deep in a broad row's tail lands
+# within the oracle's rounding window often, so the broad variants cut
+# nearer the head (peakier rows, or a lower top-p) while still running the
+# candidate form they are there for.
+@pytest.mark.parametrize("name,over,var", [
+    ("top-k 40", dict(top_k=40), 3.0),
+    ("top-k 1", dict(top_k=1), 3.0),
+    ("no penalties", dict(penalty_last_n=0), 3.0),
+    ("no min-p, no top-p (full softmax rows)", dict(min_p=0.0, top_p=1.0), 3.0),
+    ("top-p only: 9000 survivors, radix-selected cut over the list", dict(min_p=0.0, top_p=0.9), 6.0),
+    ("warmer temperature, ~1000-1800 sorted candidates per row", dict(temp=1.2, min_p=0.02, top_p=0.6), 3.0),
+    ("frequency penalty, long window", dict(freq_penalty=0.3, penalty_last_n=200), 3.0),
 ])
-def test_sampling_chain_variants_match_oracle(orc, name, over):
+def test_sampling_chain_variants_match_oracle(orc, name, over, var):
     log(f"case sample variant: {name}")
     base = dict(temp=0.6, top_p=0.95, min_p=0.05, rep_penalty=1.08, presence_penalty=0.4, freq_penalty=0.0,
                 top_k=0, penalty_last_n=64, seed=99)
     base.update(over)
     sp = syn.Sampler(**base)
-    sv = syn.make_sample_verify(17, 12, 3, 9000, sampler=sp, hist=300)
-    sv.history_len[:] = np.array([300, 0, 5, 64, 299, 1, 100, 200, 150, 250, 30, 64], np.int32)
-    g = GpuSampler(12, 3, 9000)
-    _compare(orc, g, sv, sp, max_flag_frac=0.5)
+    sv = syn.make_sample_verify(17, 24, 3, 9000, sampler=sp, hist=300, logit_var=var)
+    sv.history_len[:] = np.resize(np.array([300, 0, 5, 64, 299, 1, 100, 200, 150, 250, 30, 64], np.int32), 24)
+    g = GpuSampler(24, 3, 9000)
+    _compare(orc, g, sv, sp)
 
 
 @pytest.mark.parametrize("name,V,over", [
@@ -114,8 +128,8 @@ def test_broad_rows_in_every_candidate_form_match_oracle(orc, name, V, over):
     sp = syn.Sampler(**base)
     sv = syn.make_sample_verify(23, 6, 3, V, sampler=sp, hist=64)
     g = GpuSampler(6, 3, V)
-    _compare(orc, g, sv, sp, max_flag_frac=0.5)
-    _compare(orc, g, sv, sp, round_=3, max_flag_frac=0.5)
+    _compare(orc, g, sv, sp)
+    _compare(orc, g, sv, sp, round_=3)
 
 
 def test_vocabulary_not_a_multiple_of_four_matches_oracle(orc):
@@ -126,7 +140,7 @@ def test_vocabulary_not_a_multiple_of_four_matches_oracle(orc):
                      top_k=0, penalty_last_n=64, seed=77)
     sv = syn.make_sample_verify(29, 6, 3, 20001, sampler=sp, hist=64)
     g = GpuSampler(6, 3, 20001)
-    _compare(orc, g, sv, sp, max_flag_frac=0.5)
+    _compare(orc, g, sv, sp)
 
 
 def test_drafts_outside_vocabulary_are_rejected(orc):
@@ -137,6 +151,29 @@ def test_drafts_outside_vocabulary_are_rejected(orc):
     g = GpuSampler(4, 2, 50)
     n_o = _compare(orc, g, sv, sp)
     assert n_o[0] == 0 and n_o[1] == 0 and n_o[3] == 0
+
+
+def test_empty_distribution_rows_match_oracle(orc):
+    """Rows with no finite maximum (every logit -inf) give an empty
+    distribution: the draft is rejected and the draw emits -1, as in the
+    oracle; one-hot and general q."""
+    log("case empty rows: S=3 N=2 V=50, an all -inf row in each sequence")
+    V = 50
+    sp = syn.Sampler(temp=1.0, top_p=0.95, min_p=0.05, rep_penalty=1.0, presence_penalty=0.0, penalty_last_n=0,
+                     seed=5)
+    p = np.zeros((3, 3, V), np.float32)
+    drafts = np.array([[4, 5], [7, 8], [9, 10]], np.int32)
+    for s in range(3):
+        for i in range(2):
+            p[s, i, drafts[s, i]] = 60.0
+    p[0, 0] = -np.inf
+    p[1, 1] = -np.inf
+    p[2, 2] = -np.inf
+    g = GpuSampler(3, 2, V)
+    for q in (None, np.zeros((3, 2, V), np.float32)):
+        sv = syn.SampleVerifyInputs(p, q, drafts, np.zeros((3, 1), np.int32), np.zeros(3, np.int32), sp)
+        n_o = _compare(orc, g, sv, sp)
+        assert n_o.tolist() == [0, 1, 2]
 
 
 def test_monte_carlo_total_variation_on_gpu(orc):

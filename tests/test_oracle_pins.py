@@ -936,3 +936,32 @@ def test_monte_carlo_total_variation_exact_vs_greedy_match(orc):
     assert tv_exact_q < 2 * floor, (tv_exact_q, floor)
     assert tv_exact_greedy < 2 * floor, (tv_exact_greedy, floor)
     assert tv_gm > 10 * floor, (tv_gm, floor)
+
+
+def test_empty_distribution_rows_reject_and_draw_nothing(orc):
+    """A row none of whose tokens survives the chain (every logit -inf, so no
+    finite maximum) has an empty distribution: its draft is rejected (the
+    accept test compares against p(d) = 0) and a draw from it yields -1.
+    Sequence 0: row 0 empty (one-hot q) -> rejected at 0, token -1.
+    Sequence 1: row 1 empty, general q -> draft 0 accepted (p(d) ~ 1), draft
+    1 rejected, residual draw empty.  Sequence 2: both drafts accepted, the
+    bonus row empty -> -1 at position 2, n_accept 2."""
+    V = 50
+    sp = _sp(min_p=0.05, top_p=0.95, penalty_last_n=0)
+    p = np.zeros((3, 3, V), np.float32)
+    drafts = np.array([[4, 5], [7, 8], [9, 10]], np.int32)
+    for s in range(3):
+        for i in range(2):
+            p[s, i, drafts[s, i]] = 60.0          # p(d) = 1 up to exp(-60)
+    p[0, 0] = -np.inf
+    p[1, 1] = -np.inf
+    p[2, 2] = -np.inf
+    t, n, fl = orc.verify_sample(p, None, drafts, np.zeros((3, 0), np.int32), np.zeros(3, np.int32), sp, 0)
+    assert n.tolist() == [0, 1, 2]
+    assert t.tolist() == [[-1, -1, -1], [7, -1, -1], [9, 10, -1]]
+    q = np.zeros((3, 2, V), np.float32)           # uniform q: p(d) = 1 > u q(d) accepts the planted drafts
+    t2, n2, _ = orc.verify_sample(p, q, drafts, np.zeros((3, 0), np.int32), np.zeros(3, np.int32), sp, 0)
+    assert n2.tolist() == [0, 1, 2]
+    assert t2[0, 0] == -1 and t2[1].tolist() == [7, -1, -1] and t2[2].tolist() == [9, 10, -1]
+    pe, _ = orc.sample_dist(p[0, 0], [], sp)
+    assert (pe == 0).all()
