@@ -311,6 +311,7 @@ def bench_hidden(args, dev):
 
 
 ATTN_SOURCES = ["attn_kernels.hip", "dev_common.h", "mtp_internal.h"]
+MM_SOURCES = ["mfma_kernels.hip", "widen.h", "dev_common.h", "mtp_internal.h"]
 
 
 def counters_file(kernel, workload):
@@ -412,8 +413,9 @@ def bench_draft(args, dev):
                 "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
                 "traffic": head_traffic_from_counters(cf, sources), "traffic_source": cf.name,
                 "bytes_per_launch": bytes_per_launch, "avg_launch_ms": avg, "launches": n}
-    r_head = roofline(head_name, "head_kernel" if "head_kernel (" in head_name else head_name.split()[0],
-                      head_ms, head_n, head_launch_bytes, HEAD_SOURCES)
+    head_key = head_name.split()[0]
+    r_head = roofline(head_name, head_key, head_ms, head_n, head_launch_bytes,
+                      MM_SOURCES if head_key == "mm_head_kernel" else HEAD_SOURCES)
     # one attention launch reads one block's visible K and V of every sequence
     r_attn = roofline(attn_name, attn_name.split()[0], attn_ms, attn_n, kvb // m.n_blocks, ATTN_SOURCES)
     if attn_ms > head_ms:

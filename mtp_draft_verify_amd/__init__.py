@@ -27,7 +27,7 @@ MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
            "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_verify_sample_hidden", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
            "mtp_last_error")
-MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY, MTP_PROF_MERGE = 0, 1, 2, 3, 4
+MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY, MTP_PROF_MERGE, MTP_PROF_N = 0, 1, 2, 3, 4, 5
 
 
 class MTPError(RuntimeError):

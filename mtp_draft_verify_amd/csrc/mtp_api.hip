@@ -91,7 +91,7 @@ struct mtp_ctx {
     // past kMaxGraphs; an evicted graph may still be queued on the stream, so
     // it is destroyed only once an event recorded behind it has completed
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[7]; hipGraph_t g; hipGraphExec_t exec; uint64_t last_use; };
+    struct Graph { int key[8]; hipGraph_t g; hipGraphExec_t exec; uint64_t last_use; };
     std::vector<Graph> graphs;
     uint64_t use_clock = 0;
     struct Retired { hipGraph_t g; hipGraphExec_t exec; hipEvent_t done; };
@@ -478,6 +478,7 @@ struct ChainShape {
     int S, N, split[MTP_N_SRC];
     int logits;     // the caller asked for draft logits
     int conf;       // the caller asked for per-step confidence / the p_min trim
+    int stream_kv;  // a step's visible KV exceeds kStreamKvBytes (non-temporal KV loads)
 };
 
 // Enqueue the whole draft chain (N steps of a1..a7, then the hand-off of the
@@ -541,6 +542,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                     aa.theta = d.rope_theta;
                     aa.scale = d.attn_scale; aa.Hq = d.n_head_q; aa.Hkv = d.n_head_kv; aa.hd = d.head_dim;
                     aa.S = S; aa.src = src; aa.step = k; aa.seqs = dp; aa.part = c->part;
+                    aa.stream_kv = sh.stream_kv;
                     e = launch_attn(d.kv_dtype, aa, sh.split[src], st);
                 }
             }
@@ -636,7 +638,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
 
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
-    const int key[7] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf};
+    const int key[8] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf, sh.stream_kv};
     ++c->use_clock;
     reap_graphs(c, false);
     for (auto &g : c->graphs)
@@ -722,7 +724,8 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
     CallIO *hio = (CallIO *)hb;
     SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
     std::memset(hio, 0, sizeof(CallIO));
-    ChainShape sh{n_seq, n_steps, {0, 0, 0}, out_logits != nullptr, out_conf != nullptr};
+    ChainShape sh{n_seq, n_steps, {0, 0, 0}, out_logits != nullptr, out_conf != nullptr, 0};
+    int64_t kv_step_bytes = 0;          // visible K + V bytes one draft step reads
     for (int s = 0; s < n_seq; ++s) {
         const mtp_seq &sq = seqs[s];
         SeqParams &p = hp[s];
@@ -735,7 +738,10 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
             if (rc) return rc;
             sh.split[src] = std::max(sh.split[src], p.src[src].n_split);
         }
+        for (int l = 0; l < d.n_blocks; ++l)
+            kv_step_bytes += (int64_t)p.src[d.block_src[l]].n_vis * d.n_head_kv * d.head_dim * 2 * elem_size(d.kv_dtype);
     }
+    sh.stream_kv = kv_step_bytes > kStreamKvBytes;
     // grids are sized for a power-of-two split count so one captured chain
     // serves a range of context lengths (surplus workgroups exit at once)
     for (int src = 0; src < MTP_N_SRC; ++src)

@@ -139,7 +139,13 @@ struct AttnArgs {
     int32_t Hq, Hkv, hd, S, src, step;
     const SeqParams *seqs;
     float *part;            // [S, Hq, MTP_MAX_SPLITS, kPartHead + hd]  (m, l, pad, pad, o[hd])
+    int32_t stream_kv;      // a step's KV exceeds the last-level cache: non-temporal KV loads
 };
+
+// KV bytes per draft step above which the attention streams its KV with
+// non-temporal loads: past this a step's KV cannot stay in the device's
+// 256 MiB last-level cache until the next step reads it again.
+static constexpr int64_t kStreamKvBytes = (int64_t)192 << 20;
 
 struct MergeArgs {
     const float *part;
