@@ -225,6 +225,26 @@ int mtp_draft_block_conf(mtp_ctx *ctx, int32_t n_seq, const mtp_seq *seqs, const
 int mtp_verify_greedy(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, int32_t n_vocab, const float *logits,
                       const int32_t *drafts, int32_t *out_tokens, int32_t *out_n_accept);
 
+/* Greedy verify for callers that cannot allocate device memory (code under
+   HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): the same operation, kernels and results as
+   mtp_verify_greedy, without a context.  Its scratch (one argmax key per
+   verified row) is a static device array of MTP_NOALLOC_MAX_ROWS keys
+   (128 KiB) that every GPU the library runs on keeps until the process
+   ends; nothing is allocated or freed, and the call clears the keys it uses
+   with a kernel (no memset).  All calls on one GPU share that array: calls
+   that overlap on one GPU (on different streams, or from several threads)
+   race and must be serialised by the caller.
+     hip_stream  a hipStream_t (NULL = the null stream) of the current device
+     logits, drafts, out_tokens, out_n_accept: as for mtp_verify_greedy
+   Returns MTP_E_SHAPE, with nothing enqueued, when n_seq * (n_draft + 1)
+   exceeds MTP_NOALLOC_MAX_ROWS; MTP_E_DEVICE if the scratch array's device
+   address cannot be looked up. */
+#define MTP_NOALLOC_MAX_ROWS 16384
+int mtp_verify_greedy_noalloc(void *hip_stream, int32_t n_seq, int32_t n_draft, int32_t n_vocab,
+                              const float *logits, const int32_t *drafts, int32_t *out_tokens,
+                              int32_t *out_n_accept);
+
 /* The target's LM head, for the verify from hidden states: row-major
    [n_vocab, d] bf16 weights (dtype MTP_BF16; others are MTP_E_DTYPE) and
    the gain of the target's final RMSNorm. */

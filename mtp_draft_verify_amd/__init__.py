@@ -26,7 +26,8 @@ MAX_BLOCKS = 8
 MAX_SPLITS = 128
 EXPORTS = ("mtp_ctx_create", "mtp_ctx_destroy", "mtp_draft_block", "mtp_draft_block_conf", "mtp_verify_greedy",
            "mtp_verify_greedy_hidden", "mtp_verify_sample", "mtp_verify_sample_hidden", "mtp_strerror", "mtp_check_desc", "mtp_profile_enable", "mtp_profile_read",
-           "mtp_last_error")
+           "mtp_last_error", "mtp_verify_greedy_noalloc")
+NOALLOC_MAX_ROWS = 16384
 MTP_PROF_HEAD, MTP_PROF_ATTN, MTP_PROF_GEMV, MTP_PROF_VERIFY, MTP_PROF_MERGE, MTP_PROF_N = 0, 1, 2, 3, 4, 5
 
 
@@ -103,6 +104,8 @@ def lib() -> C.CDLL:
         L.mtp_draft_block_conf.restype = C.c_int
         L.mtp_verify_greedy.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
         L.mtp_verify_greedy.restype = C.c_int
+        L.mtp_verify_greedy_noalloc.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P]
+        L.mtp_verify_greedy_noalloc.restype = C.c_int
         L.mtp_verify_greedy_hidden.argtypes = [P, C.c_int32, C.c_int32, C.POINTER(LmHead), P, P, P, P]
         L.mtp_verify_greedy_hidden.restype = C.c_int
         L.mtp_verify_sample.argtypes = [P, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, C.c_int32, P,
@@ -200,6 +203,16 @@ def make_lm_head(w, g_final, d: int, n_vocab: int, dtype: int = MTP_BF16, rms_ep
     h.w, h.g_final = _ptr(w), _ptr(g_final)
     h.d, h.n_vocab, h.dtype, h.rms_eps = int(d), int(n_vocab), int(dtype), float(rms_eps)
     return h
+
+
+def mtp_verify_greedy_noalloc(stream, logits, drafts, out_tokens, out_n_accept) -> None:
+    """The greedy verify without a context (static scratch, no allocation);
+    stream: a torch stream, a raw handle, or None (torch's current stream)."""
+    S, R, V = logits.shape
+    rc = lib().mtp_verify_greedy_noalloc(_stream_handle(stream), S, R - 1, V, _ptr(logits), _ptr(drafts),
+                                         _ptr(out_tokens), _ptr(out_n_accept))
+    if rc != MTP_OK:
+        raise MTPError(rc, "mtp_verify_greedy_noalloc")
 
 
 def mtp_verify_greedy_hidden(ctx: int, n_seq: int, n_draft: int, head: LmHead, hidden, drafts, out_tokens,

@@ -17,7 +17,7 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libmtp.so"
 BUILD = PKG / "_build"
 SOURCES = ["mtp_api.hip", "gemv_kernels.hip", "head_kernels.hip", "attn_kernels.hip", "misc_kernels.hip",
-           "verify_kernels.hip", "sample_kernels.hip", "mfma_kernels.hip", "hv_kernels.hip"]
+           "verify_kernels.hip", "sample_kernels.hip", "mfma_kernels.hip", "hv_kernels.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", str(PKG.parent / "include")]

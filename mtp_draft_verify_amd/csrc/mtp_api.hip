@@ -789,6 +789,29 @@ extern "C" int mtp_verify_greedy(mtp_ctx *c, int32_t n_seq, int32_t n_draft, int
     return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch", e);
 }
 
+extern "C" int mtp_verify_greedy_noalloc(void *hip_stream, int32_t n_seq, int32_t n_draft, int32_t n_vocab,
+                                         const float *logits, const int32_t *drafts, int32_t *out_tokens,
+                                         int32_t *out_n_accept) {
+    if (n_seq < 1 || n_draft < 0 || n_vocab < 1) return MTP_E_SHAPE;
+    const int64_t rows = (int64_t)n_seq * (n_draft + 1);
+    if (rows > MTP_NOALLOC_MAX_ROWS) {
+        std::snprintf(g_last_error, sizeof(g_last_error),
+                      "mtp_verify_greedy_noalloc: %lld verified rows exceed the static scratch of %d rows",
+                      (long long)rows, MTP_NOALLOC_MAX_ROWS);
+        return MTP_E_SHAPE;
+    }
+    if (!logits || (n_draft > 0 && !drafts) || !out_tokens || !out_n_accept) return MTP_E_INVAL;
+    uint64_t *keys = nullptr;
+    hipError_t e = noalloc_scratch(&keys);
+    if (e != hipSuccess) return hip_fail("scratch symbol lookup", e);
+    const hipStream_t st = (hipStream_t)hip_stream;
+    // the keys start at zero: an earlier call may have been cut short
+    e = launch_clear_u64(keys, rows, st);
+    if (e == hipSuccess) e = launch_verify_greedy(logits, drafts, n_seq, n_draft, n_vocab, keys, out_tokens,
+                                                  out_n_accept, st);
+    return e == hipSuccess ? MTP_OK : hip_fail("greedy verify launch (no-alloc)", e);
+}
+
 // Checks of a caller's LM head and hidden rows shared by both hidden-state
 // verifies; the head must fit the staging plane allocated at create.
 static int prepare_hidden_head(mtp_ctx *c, int32_t n_seq, int32_t n_draft, const mtp_lm_head *head,

@@ -208,6 +208,10 @@ hipError_t launch_verify_hidden(const HvArgs &a, int32_t rows, hipStream_t st);
 hipError_t launch_verify_prefix(const int32_t *drafts, int32_t S, int32_t N, uint64_t *keys, int32_t *out_tokens,
                                 int32_t *out_n_accept, hipStream_t st);
 
+// device address of the current device's static key scratch of
+// mtp_verify_greedy_noalloc (MTP_NOALLOC_MAX_ROWS keys)
+hipError_t noalloc_scratch(uint64_t **out);
+
 // verify
 hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int32_t S, int32_t N, int32_t V,
                                 uint64_t *keys, int32_t *out_tokens, int32_t *out_n_accept, hipStream_t st);
