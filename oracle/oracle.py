@@ -17,13 +17,17 @@ import numpy as np
 import mtp_synth as syn
 
 HERE = Path(__file__).resolve().parent
-LIB_PATH = HERE / "libmtp_oracle.so"
+# MTP_ORACLE_LIB names another build of the same sources (the sanitizer
+# build of oracle/sanitize_check.py); by default the optimised one below
+LIB_PATH = Path(os.environ.get("MTP_ORACLE_LIB", str(HERE / "libmtp_oracle.so")))
 SOURCES = [HERE / "mtp_oracle.c", HERE / "mtp_oracle.h"]
 MAXB = 8
 
 
 def build(force: bool = True) -> Path:
     """Compile the oracle with gcc (-O2, OpenMP, no fast-math, no FMA contraction)."""
+    if "MTP_ORACLE_LIB" in os.environ:
+        return LIB_PATH         # an externally built variant: used as it is
     if force or not LIB_PATH.exists() or any(s.stat().st_mtime > LIB_PATH.stat().st_mtime for s in SOURCES):
         tmp = LIB_PATH.with_suffix(".so.tmp")
         cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
