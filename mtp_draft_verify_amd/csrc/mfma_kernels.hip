@@ -250,7 +250,9 @@ __global__ __launch_bounds__(256) void mm_splitk_reduce(GemvArgs a, const float 
 // h' = W_post f runs in the same workgroups over the same staged f.
 // ============================================================================
 static constexpr int kHeadUnit = 8;     // K steps per unit: 16 rows x 256 columns
-static constexpr int kHeadDepth = 4;    // units in flight per wave
+// Units in flight per wave (a bf16 unit carries 8 KiB, a Q8_0 unit 4 KiB of
+// quants and 256 B of scales; 8 Q8_0 units in flight measured no faster).
+template <typename HT> struct HeadDepth { static constexpr int value = 4; };
 
 template <typename HT>
 struct HeadUnit;
@@ -343,38 +345,56 @@ __device__ __forceinline__ float sc_at(const u32x4_t &v, int k) {
 template <typename HT>
 __device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4_t (&xv)[2 * kHeadUnit],
                                               f32x4_t &acc_h, f32x4_t &acc_l) {
+    if constexpr (sizeof(HT) == 2) {
 #pragma unroll
-    for (int k = 0; k < kHeadUnit; ++k) {
-        const bf16x8_t xh = __builtin_bit_cast(bf16x8_t, xv[2 * k]);
-        const bf16x8_t xl = __builtin_bit_cast(bf16x8_t, xv[2 * k + 1]);
-        if constexpr (sizeof(HT) == 2) {
+        for (int k = 0; k < kHeadUnit; ++k) {
             const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, u.w[k]);
-            acc_h = mfma(xh, wv, acc_h);
-            acc_l = mfma(xl, wv, acc_l);
-        } else {
-            // Each block's products are scaled before the next block starts:
-            // the empty volatile asm statements keep their order, which
-            // keeps one block's conversion and MFMA results live at a time.
-            u32x2_t q = u.w[k];
+            acc_h = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k]), wv, acc_h);
+            acc_l = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 1]), wv, acc_l);
+        }
+    } else {
+        // A block's products are scaled into the accumulators, in block
+        // order, once the next block's quants are converted and its MFMAs
+        // issued, so each block's MFMA latency is covered by the next
+        // block's work.  The empty volatile asm statements keep that order
+        // (left free, the compiler hoists every block's conversion and runs
+        // out of registers), so two blocks' results are live at a time.
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t ph, pl;
+        {
+            u32x2_t q = u.w[0];
             asm volatile("" : "+v"(q));
             const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4_t ph = mfma(xh, wv, z), pl = mfma(xl, wv, z);
+            ph = mfma(__builtin_bit_cast(bf16x8_t, xv[0]), wv, z);
+            pl = mfma(__builtin_bit_cast(bf16x8_t, xv[1]), wv, z);
+        }
+#pragma unroll
+        for (int k = 0; k < kHeadUnit; ++k) {
+            f32x4_t nh = z, nl = z;
+            if (k + 1 < kHeadUnit) {
+                u32x2_t q = u.w[k + 1];
+                asm volatile("" : "+v"(q), "+v"(ph), "+v"(pl));
+                const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
+                nh = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 2]), wv, z);
+                nl = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 3]), wv, z);
+            }
             const float sc = sc_at(u.sc, k);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 acc_h[i] = fmaf(sc, ph[i], acc_h[i]);
                 acc_l[i] = fmaf(sc, pl[i], acc_l[i]);
             }
-            asm volatile("" : "+v"(acc_h), "+v"(acc_l));
+            asm volatile("" : "+v"(acc_h), "+v"(acc_l), "+v"(nh), "+v"(nl));
+            ph = nh;
+            pl = nl;
         }
     }
 }
 
 // The 16-row tiles [T0, T1) of one workgroup: wave w takes T0 + w, T0 + w + 4,
-// ...  Units go through a ring of kHeadDepth raw units (loaded kHeadDepth
-// units ahead); unit u + 1 is transposed into operand order while unit u's
-// MFMAs run.  UPT units make a tile and kHeadDepth is a multiple of UPT, so
+// ...  Units go through a ring of DEPTH raw units (loaded DEPTH units
+// ahead); unit u + 1 is transposed into operand order while unit u's
+// MFMAs run.  UPT units make a tile and DEPTH is a multiple of UPT, so
 // a tile's epilogue sits at a fixed ring position; loads and stores are
 // unconditional (tiles past the wave's last one load the matrix's first unit
 // and store to `sink`), which keeps the loop body straight-line and lets the
@@ -388,9 +408,10 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
                            const u32x4_t *bsm, u32x4_t *tr, float *out, int64_t out_stride, uint64_t (&best)[4],
                            float (&cm)[4], float (&cs)[4], Stage &&stage) {
     const bool conf = HEAD && a.conf != nullptr;
-    constexpr int TPI = kHeadDepth / UPT;   // tiles per loop iteration
-    static_assert(kHeadDepth % UPT == 0, "ring must hold whole tiles");
-    static_assert(kHeadDepth % 2 == 0, "operand buffers alternate with the ring position");
+    constexpr int DEPTH = HeadDepth<HT>::value;
+    constexpr int TPI = DEPTH / UPT;        // tiles per loop iteration
+    static_assert(DEPTH % UPT == 0, "ring must hold whole tiles");
+    static_assert(DEPTH % 2 == 0, "operand buffers alternate with the ring position");
     const int d = a.d, S = a.S;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -401,21 +422,21 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
         const bool real = i < nt;
         raw_load_unit<HT>(W, qs, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
     };
-    RawUnit<HT> raw[kHeadDepth];
+    RawUnit<HT> raw[DEPTH];
     HeadUnit<HT> op[2];
 #pragma unroll
-    for (int p = 0; p < kHeadDepth; ++p) load(p / UPT, p % UPT, raw[p]);
+    for (int p = 0; p < DEPTH; ++p) load(p / UPT, p % UPT, raw[p]);
     stage();                                // the activations, while the first weights arrive
     transpose_unit<HT>(raw[0], tr, lane, op[0]);
     load(TPI, 0, raw[0]);
     f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < nit; ++it) {
 #pragma unroll
-        for (int p = 0; p < kHeadDepth; ++p) {
+        for (int p = 0; p < DEPTH; ++p) {
             const int i = it * TPI + p / UPT, c = p % UPT;
             // unit u + 1 into operand order, then its ring slot refills with
-            // unit u + 1 + kHeadDepth
-            const int pn = (p + 1) % kHeadDepth;
+            // unit u + 1 + DEPTH
+            const int pn = (p + 1) % DEPTH;
             const int un_i = it * TPI + (p + 1) / UPT + TPI, un_c = pn % UPT;
             // this unit's activation operands first: they arrive while the
             // next unit is transposed
