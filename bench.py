@@ -204,12 +204,26 @@ def bench_sample(args, dev):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    bytes_step = 2 * (p.numel() + q.numel()) * 4
+    # algorithmic bytes: the p and q logit rows, each read once per call
+    bytes_step = (p.numel() + q.numel()) * 4
+    n_diag = min(args.steps, 50)
+    ctx.profile(1 << mtp.MTP_PROF_VERIFY)
+    for _ in range(n_diag):
+        step()
+    v_ms, v_n = ctx.profile_read(mtp.MTP_PROF_VERIFY)
+    ctx.profile(0)
+    avg_ms = v_ms / max(v_n, 1)
+    achieved = bytes_step / (avg_ms * 1e-3) / 1e9
     out = {"metric": "verified draft tokens/s of exact temperature>0 verify", "value": S * (R - 1) / (ms * 1e-3),
            "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": WORKLOADS["c5"][1], "n_seq": S, "n_draft": R - 1, "n_vocab": V},
-           "hbm_gbps_step": bytes_step / (ms * 1e-3) / 1e9, "accepted_per_round": float(na.float().mean())}
+           "hbm_gbps_step": bytes_step / (ms * 1e-3) / 1e9, "accepted_per_round": float(na.float().mean()),
+           "roofline": {"bound": "hbm", "kernel": "sample_chunk_kernel + sample_row_kernel + sample_seq_kernel "
+                                                 "(one mtp_verify_sample call)",
+                        "timing": f"HIP events around each call over {n_diag} calls after the timed region",
+                        "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                        "traffic": None, "bytes_per_launch": bytes_step, "avg_launch_ms": avg_ms, "launches": v_n}}
     ctx.close()
     print(json.dumps(out), flush=True)
 

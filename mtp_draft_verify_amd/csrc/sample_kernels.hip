@@ -11,10 +11,14 @@
 // Kernels (rows = S*(N+1) target rows followed by S*N draft rows):
 //   topk   (only when top_k > 0) one workgroup per row: radix select of the
 //          k-th largest raw (logit, -id) key
-//   max    per (row, 16384-token chunk): max of the penalised, tempered logit
-//   cand   per (row, chunk): tokens with exp(v - M) >= min_p join the row's
-//          candidate list (order fixed later by sorting)
-//   row    one workgroup per row: up to 4096 candidates are sorted by (prob
+//   chunk  per (row, 8192-token chunk), one read of the logits: the chunk's
+//          max of the penalised, tempered logits v goes into the row max
+//          (atomic max; the row max published so far comes back), then every
+//          token with exp(v - ref) >= min_p, ref = the larger of the two
+//          maxima, joins the row's list with its v.  ref never exceeds the
+//          row max M, so the list is a superset of the min-p survivors
+//   row    one workgroup per row: each listed v becomes e = exp(v - M), or 0
+//          when it does not survive min-p; up to 4096 survivors are sorted by (prob
 //          desc, id asc), with cumulative sums in a fixed tree order, top-p
 //          cut and normaliser; more candidates that still fit the row's list
 //          keep it unsorted (list form: the top-p threshold key by radix
@@ -31,7 +35,7 @@
 
 namespace mtp {
 
-static constexpr int kChunk = 16384;
+static constexpr int kChunk = 8192;     // tokens per chunk workgroup, held in registers
 static constexpr int32_t kImplicitForm = -1, kListForm = -2;
 static constexpr int kMaxCtx = 1024;
 static constexpr int kMaxDrafts = 64;     // drafts per sequence (the context's max_steps bound)
@@ -307,20 +311,25 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
     if (threadIdx.x == 0) a.topk_key[row] = K;
 }
 
-// pass 1: row max of the chain values
+// The single pass over the logits: the chunk's row max contribution, then
+// its part of a superset of the row's min-p survivors (token, v).
 template <int E>
-__global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chunk) {
+__global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
     constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     __shared__ float red[4];
+    __shared__ float ref_sh;
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
-    // the first batch does not depend on the context: request it first
-    float raw[2][KB][E];
+    // the whole chunk in registers: the first batch does not depend on the
+    // context, so it is requested before the context is read
+    float raw[NB][KB][E];
     load_batch<E, KB>(rr.z, c0, c1, raw[0]);
     int n_ctx;
     load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
+#pragma unroll
+    for (int b = 1; b < NB; ++b) load_batch<E, KB>(rr.z, c0 + b * BT, c1, raw[b]);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     // Context tokens take the full chain; every other token's value is
     // fl(z / temp), which does not decrease as z grows, so the largest of
@@ -328,16 +337,14 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
     // running max of z (after the top-k test).
     float mx = -INFINITY, mz = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int b0 = c0 + b * BT;
-        if (b + 1 < NB) load_batch<E, KB>(rr.z, b0 + BT, c1, raw[(b + 1) & 1]);
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int k = 0; k < KB; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int t = b0 + E * ((int)threadIdx.x + kBlock * k) + e;
+                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
                 if (t < c1) {
-                    const float z = raw[b & 1][k][e];
+                    const float z = raw[b][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
                     if (member) {
                         const float v = raw_value(a, z, t, true, cl, n_ctx, tk);
@@ -347,73 +354,87 @@ __global__ __launch_bounds__(256) void sample_max_kernel(SampleArgs a, int n_chu
                     }
                 }
             }
-    }
     if (mz > -INFINITY) mx = fmaxf(mx, chain_value(a, mz, 0));
     mx = block_max(mx, red);
-    if (threadIdx.x == 0 && mx > -INFINITY) atomicMax(&a.row_maxkey[row], fkey(mx));
-}
-
-// pass 2: min-p survivors join the candidate list
-template <int E>
-__global__ __launch_bounds__(256) void sample_cand_kernel(SampleArgs a, int n_chunk) {
-    constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
-    __shared__ CtxLds cl;
-    const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
-    const RowRef rr = row_ref(a, row);
-    const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
-    float raw[2][KB][E];
-    load_batch<E, KB>(rr.z, c0, c1, raw[0]);
-    int n_ctx;
-    load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
-    const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
-    const float M = fkey_inv(a.row_maxkey[row]);
-    // A token outside the context keeps when expf(fl(z / temp) - M) >=
-    // min_p.  With fp32 rounding and expf's error that needs z / temp >=
-    // M + ln(min_p) - 1e-5 (1 + |M|) at the least, so a raw logit below
-    // zlo = temp * (M + ln(min_p) - 0.01 - 1e-5 |M|) (rounded down) cannot
-    // keep and skips the exact test; every other token takes it unchanged.
+    if (threadIdx.x == 0) {
+        float ref = mx;
+        if (mx > -INFINITY) {
+            const uint32_t old = atomicMax(&a.row_maxkey[row], fkey(mx));
+            if (old != 0u) ref = fmaxf(mx, fkey_inv(old));
+        }
+        ref_sh = ref;
+    }
+    __syncthreads();
+    const float ref = ref_sh;
+    // exp(fl(v - M)) >= min_p implies exp(fl(v - ref)) >= min_p for ref <= M
+    // (rounding and exp do not decrease with their argument), so testing
+    // against ref keeps every survivor.  A token outside the context passes
+    // only if z / temp >= ref + ln(min_p) - 1e-5 (1 + |ref|) at the least
+    // (fp32 rounding and expf's error), so a raw logit below zlo = temp *
+    // (ref + ln(min_p) - 0.01 - 1e-5 |ref|) (rounded down) skips the test.
     float zlo = -INFINITY;
-    if (a.min_p > 0.f && M > -INFINITY) {
-        const double zl = (double)a.temp * ((double)M + a.ln_min_p - 0.01 - 1e-5 * fabs((double)M));
+    if (a.min_p > 0.f && ref > -INFINITY) {
+        const double zl = (double)a.temp * ((double)ref + a.ln_min_p - 0.01 - 1e-5 * fabs((double)ref));
         zlo = nextafterf((float)zl, -INFINITY);
     }
-    const int lane = threadIdx.x & 63;
+    // which of the thread's NB * KB * E tokens are listed (bit = position)
+    static_assert(NB * KB * E <= 32, "one keep bit per token of the thread");
+    uint32_t kmask = 0u;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int b0 = c0 + b * BT;
-        if (b + 1 < NB) load_batch<E, KB>(rr.z, b0 + BT, c1, raw[(b + 1) & 1]);
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int k = 0; k < KB; ++k)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int t = b0 + E * ((int)threadIdx.x + kBlock * k) + e;
-                bool keep = false;
-                float ev = 0.f;
+                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
                 if (t < c1) {
-                    const float z = raw[b & 1][k][e];
+                    const float z = raw[b][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
                     if (member || z >= zlo) {
                         const float v = raw_value(a, z, t, member, cl, n_ctx, tk);
-                        if (v == v) {
-                            ev = expf(v - M);
-                            keep = ev >= a.min_p;
-                        }
+                        if (v == v && expf(v - ref) >= a.min_p) kmask |= 1u << ((b * KB + k) * E + e);
                     }
                 }
-                // one slot reservation per wave: the survivors of the wave
-                // take consecutive slots in lane order
-                const uint64_t mask = __ballot(keep);
-                if (mask == 0ull) continue;             // wave-uniform
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&a.cand_n[row], __popcll(mask));
-                base = __shfl(base, 0);
-                const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-                if (keep && slot < a.cap) {
-                    a.cand_id[(int64_t)row * a.cap + slot] = t;
-                    a.cand_v[(int64_t)row * a.cap + slot] = ev;
-                }
             }
+    // Slots: an exclusive prefix sum of the threads' counts over the
+    // workgroup and one reservation per chunk, so no wave waits on an atomic
+    // inside the token loop (the listed superset can be ten times the
+    // survivors).  Slot order within the list does not matter: the row
+    // kernel sorts it or sums it in fixed point.
+    __shared__ int wtot[4], wbase_sh;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int cnt = __popc(kmask);
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
     }
+    if (lane == 63) wtot[wid] = incl;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int tot = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
+        wbase_sh = tot > 0 ? atomicAdd(&a.cand_n[row], tot) : 0;
+    }
+    __syncthreads();
+    int slot = wbase_sh + incl - cnt;
+    for (int w = 0; w < wid; ++w) slot += wtot[w];
+    if (kmask == 0u) return;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                if (!((kmask >> ((b * KB + k) * E + e)) & 1u)) continue;
+                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
+                const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                if (slot < a.cap) {
+                    a.cand_id[(int64_t)row * a.cap + slot] = t;
+                    a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, raw[b][k][e], t, member, cl, n_ctx, tk);
+                }
+                ++slot;
+            }
 }
 
 // ---------------------------------------------------------------------------
@@ -431,7 +452,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     __shared__ uint64_t keys[kSortMax];
     __shared__ float part[kPrefixBlocks];
     __shared__ float red[NT / 64];
-    __shared__ int cut_sh;
+    __shared__ int cut_sh, nkey_sh;
     __shared__ uint64_t hist[256], scal[4], red64[NT / 64];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
@@ -440,7 +461,25 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     RowState st;
     st.M = M;
     st.pad = 0;
-    if (n_all == 0) {
+    // The chunk pass listed a superset of the min-p survivors with their
+    // chain values v: each entry becomes e = exp(v - M) when it survives and
+    // 0 when it does not (an entry of weight 0 takes part in no sum and no
+    // draw).  The survivors are counted; beyond the list's slots the row
+    // takes the implicit form below, which does not read the list.
+    int n_surv = 0;
+    if (n_all > 0 && n_all <= a.cap) {
+        float *lv = a.cand_v + (int64_t)row * a.cap;
+        float cnt = 0.f;
+        for (int j = tid; j < n_all; j += NT) {
+            const float e = expf(lv[j] - M);
+            const bool keep = e >= a.min_p && e > 0.f;     // a zero weight is never drawn
+            lv[j] = keep ? e : 0.f;
+            cnt += keep ? 1.f : 0.f;
+        }
+        n_surv = (int)block_sum<NT>(cnt, red);     // exact: at most 65536 ones
+        __syncthreads();                           // the rewritten list is visible to the whole workgroup
+    }
+    if (n_all == 0 || (n_all <= a.cap && n_surv == 0)) {
         // no token survives (a row without a finite maximum): the row's
         // distribution is empty, every probability reads 0 and a draw from it
         // emits -1
@@ -452,13 +491,18 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
         }
         return;
     }
-    if (n_all <= min(kSortMax, a.cap)) {
-        // ---- compact form: sort the candidates ----
-        const int n = n_all;
+    if (n_all <= a.cap && n_surv <= kSortMax) {
+        // ---- compact form: sort the survivors ----
+        const int n = n_surv;
         int np2 = 1;
         while (np2 < n) np2 <<= 1;
-        for (int j = tid; j < np2; j += NT)
-            keys[j] = j < n ? tok_key(a.cand_v[(int64_t)row * a.cap + j], a.cand_id[(int64_t)row * a.cap + j]) : 0ull;
+        if (tid == 0) nkey_sh = 0;
+        __syncthreads();
+        for (int j = tid; j < n_all; j += NT) {
+            const float e = a.cand_v[(int64_t)row * a.cap + j];
+            if (e > 0.f) keys[atomicAdd(&nkey_sh, 1)] = tok_key(e, a.cand_id[(int64_t)row * a.cap + j]);
+        }
+        for (int j = n + tid; j < np2; j += NT) keys[j] = 0ull;
         __syncthreads();
         for (int k = 2; k <= np2; k <<= 1) {           // bitonic sort, descending
             for (int j = k >> 1; j > 0; j >>= 1) {
@@ -519,8 +563,9 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     const double scale = 1099511627776.0;   // 2^40: fixed-point weights (e <= 1), exact sums in any order
     if (n_all <= a.cap) {
         // ---- list form: every min-p survivor is in the row's (unordered)
-        // list; the top-p threshold is a radix select over the list, and
-        // the sums are fixed-point so that they do not depend on its order
+        // list (beside entries of weight 0); the top-p threshold is a radix
+        // select over the list, and the sums are fixed-point so that they do
+        // not depend on its order
         const int n = n_all;
         const int32_t *lid = a.cand_id + (int64_t)row * a.cap;
         const float *lv = a.cand_v + (int64_t)row * a.cap;
@@ -725,13 +770,8 @@ hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st) {
     }
     // 4 logits per load when every row starts on a 16-byte boundary
     const bool v4 = a.V % 4 == 0 && ((uintptr_t)a.p_logits & 15) == 0 && ((uintptr_t)a.q_logits & 15) == 0;
-    if (v4) {
-        hipLaunchKernelGGL(sample_max_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-        hipLaunchKernelGGL(sample_cand_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    } else {
-        hipLaunchKernelGGL(sample_max_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-        hipLaunchKernelGGL(sample_cand_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    }
+    if (v4) hipLaunchKernelGGL(sample_chunk_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    else hipLaunchKernelGGL(sample_chunk_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
     hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kRowThreads), 0, st, a);
     hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();
