@@ -54,8 +54,12 @@ static_assert(sizeof(CallIO) == 64, "the parameter block layout is fixed");
 // Per-workgroup partials of the draft confidence: (max, sum exp(z - max))
 // of the workgroup's logits, per (step, sequence) in slots [kConfSlots].
 static constexpr int kConfSlots = 2048;
-// A split partial row: m, l, two pad floats, then acc[hd] (16-byte aligned).
-static constexpr int kPartHead = 4;
+// A split partial row: m, l, 30 pad floats, then acc[hd].  The 128-byte
+// header keeps every row and every 64- or 256-byte piece of acc that a
+// merge workgroup reads inside whole 128-byte lines (head_dim is a multiple
+// of 64); with a 16-byte header those pieces straddled lines and the merge
+// fetched 1.7x (four dims per lane) to 3.4x (one dim per lane) its bytes.
+static constexpr int kPartHead = 32;
 struct ConfPart {
     float m, s;
 };
@@ -138,7 +142,7 @@ struct AttnArgs {
     float eps, theta, scale;
     int32_t Hq, Hkv, hd, S, src, step;
     const SeqParams *seqs;
-    float *part;            // [S, Hq, MTP_MAX_SPLITS, kPartHead + hd]  (m, l, pad, pad, o[hd])
+    float *part;            // [S, Hq, MTP_MAX_SPLITS, kPartHead + hd]  (m, l, pad..., o[hd])
     int32_t stream_kv;      // a step's KV exceeds the last-level cache: non-temporal KV loads
 };
 
