@@ -609,7 +609,13 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     constexpr int DC = 16 * DPT, SL = 16, U = MTP_MAX_SPLITS / SL;
     __shared__ float sm[SL][16], sl[SL][16];
     __shared__ float sa[SL][16][DPT];
-    const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
+    // Workgroup w takes (sequence, head) w % n_sh and dim chunk w / n_sh:
+    // consecutive workgroups go to different XCDs, so all chunks of one
+    // head then share an XCD and its L2 fetches the head's partial rows
+    // once (the chunk-fastest order fetched their header lines once per XCD).
+    const int n_sh = a.S * a.Hq;
+    const int sh = blockIdx.x % n_sh, chunk = blockIdx.x / n_sh;
+    const int s = sh / a.Hq, h = sh - s * a.Hq;
     const int tid = threadIdx.x, dl = tid % 16, slice = tid / 16;
     const int hd = a.hd;
     const int dim = chunk * DC + DPT * dl;      // hd is a multiple of 64
@@ -652,9 +658,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     if (a.hd % 64) return hipErrorInvalidValue;
     if (a.S == 1) {
-        hipLaunchKernelGGL(merge_kernel<1>, dim3(a.hd / 16, a.Hq, a.S), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL(merge_kernel<1>, dim3((a.hd / 16) * a.Hq * a.S), dim3(kBlock), 0, st, a);
     } else {
-        hipLaunchKernelGGL(merge_kernel<4>, dim3(a.hd / 64, a.Hq, a.S), dim3(kBlock), 0, st, a);
+        hipLaunchKernelGGL(merge_kernel<4>, dim3((a.hd / 64) * a.Hq * a.S), dim3(kBlock), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -299,7 +299,9 @@ __device__ __forceinline__ void raw_load_unit(const void *W, const uint16_t *qs,
         const int8_t *wc = (const int8_t *)W + 256 * c + 16 * col16;
 #pragma unroll
         for (int q = 0; q < 4; ++q) u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * q + rq, rows - 1) * d);
-        u.sc = ld_nt4(qs + (int64_t)min(row0 + col16, rows - 1) * (d / 32) + c * kHeadUnit);
+        // plain load: the tile's other units read the rest of these 128-byte
+        // lines of scales, which a non-temporal load would let L2 drop
+        u.sc = ld_global<u32x4_t>(qs + (int64_t)min(row0 + col16, rows - 1) * (d / 32) + c * kHeadUnit);
     }
 }
 
