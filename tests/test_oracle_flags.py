@@ -89,7 +89,7 @@ def test_top_p_flag_window(orc, frac, flagged):
     top_p = a - frac * 1e-5
     kept = 1 if frac > 0 else 2
     p, fl = orc.sample_dist(z, [], _sp(top_p=top_p))
-    assert bool(fl & NEAR_TOPP) == flagged, (offset, fl)
+    assert bool(fl & NEAR_TOPP) == flagged, (frac, fl)
     assert fl & ~NEAR_TOPP == 0
     assert int((p > 0).sum()) == kept
 
