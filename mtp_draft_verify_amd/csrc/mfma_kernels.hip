@@ -272,36 +272,37 @@ __device__ __forceinline__ int bslot(int t, int h, int g, int s) { return ((2 * 
 // Weights of unit c (steps 8c .. 8c+7, 256 columns) of the 16-row tile at
 // row0, as loaded.  A wave load that touches 16 rows (the operand order, lane
 // l holds row l % 16) streams at ~5.2 TB/s on gfx950, one that touches 4 rows
-// x 256 contiguous bytes at ~7.0 TB/s, so the unit is loaded in that second
-// form and put into operand order through a small LDS tile (transpose_unit).
-// Rows are clamped into the matrix (rows past the end are computed but never
-// stored).
+// x 256 contiguous bytes at ~7.0 TB/s, so a bf16 unit is loaded in that
+// second form and put into operand order through a small LDS tile
+// (transpose_unit); rows are clamped into the matrix (rows past the end are
+// computed but never stored).  A Q8_0 unit comes from the head's unit-order
+// copy, where it is one contiguous run already in operand order: four 1 KiB
+// wave loads of quants and one of its 256 bytes of scales, no transpose.
 template <typename HT>
 struct RawUnit;
 template <> struct RawUnit<uint16_t> {
     u32x4_t r[8];           // load q: rows 4 (q % 4) + lane / 16, columns 128 (q / 4) + 8 (lane % 16)
 };
 template <> struct RawUnit<int8_t> {
-    u32x4_t r[4];           // load q: rows 4 q + lane / 16, columns 16 (lane % 16) .. + 15
+    u32x4_t r[4];           // load p: K steps 2p and 2p + 1 of the lane's operand
     u32x4_t sc;             // fp16 scales of the lane's row j16 for the unit's 8 blocks
 };
 
 template <typename HT>
-__device__ __forceinline__ void raw_load_unit(const void *W, const uint16_t *qs, int rows, int d, int row0, int c,
-                                              int lane, RawUnit<HT> &u) {
-    const int rq = lane >> 4, col16 = lane & 15;
+__device__ __forceinline__ void raw_load_unit(const void *W, int rows, int d, int row0, int c, int lane,
+                                              RawUnit<HT> &u) {
     if constexpr (sizeof(HT) == 2) {
+        const int rq = lane >> 4, col16 = lane & 15;
         const uint16_t *wc = (const uint16_t *)W + 256 * c + 8 * col16;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * (q & 3) + rq, rows - 1) * d + 128 * (q >> 2));
     } else {
-        const int8_t *wc = (const int8_t *)W + 256 * c + 16 * col16;
+        // W: the unit-order copy, padded to whole tiles (row0 is a tile start)
+        const uint8_t *ub = (const uint8_t *)W + ((int64_t)(row0 >> 4) * (d >> 8) + c) * kQ8UnitBytes;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * q + rq, rows - 1) * d);
-        // plain load: the tile's other units read the rest of these 128-byte
-        // lines of scales, which a non-temporal load would let L2 drop
-        u.sc = ld_global<u32x4_t>(qs + (int64_t)min(row0 + col16, rows - 1) * (d / 32) + c * kHeadUnit);
+        for (int p = 0; p < 4; ++p) u.r[p] = ld_nt4(ub + 1024 * p + 16 * lane);
+        u.sc = ld_nt4(ub + 4096 + 16 * (lane & 15));
     }
 }
 
@@ -325,11 +326,12 @@ __device__ __forceinline__ void transpose_unit(const RawUnit<HT> &raw, u32x4_t *
             for (int kk = 0; kk < 4; ++kk) u.w[4 * hf + kk] = tr[j16 * kTrStride + 4 * kk + g];
         }
     } else {
+        // already in operand order: the 16-byte load p holds steps 2p, 2p + 1
 #pragma unroll
-        for (int q = 0; q < 4; ++q) wrow[4 * q * kTrStride] = raw.r[q];
-        const u32x2_t *rd = (const u32x2_t *)(tr + j16 * kTrStride) + g;
-#pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) u.w[k] = rd[4 * k];
+        for (int k = 0; k < kHeadUnit; ++k) {
+            const u32x4_t &r = raw.r[k >> 1];
+            u.w[k] = (k & 1) ? u32x2_t{r[2], r[3]} : u32x2_t{r[0], r[1]};
+        }
         u.sc = raw.sc;
     }
 }
@@ -406,7 +408,7 @@ __device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4
 // stage() (the workgroup's activation staging, with its barriers) runs once
 // the ring's first loads are issued.
 template <typename HT, int UPT, bool HEAD, bool LOGITS, typename Stage>
-__device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs, int rows, int T0, int T1,
+__device__ void head_tiles(const HeadArgs &a, const void *W, int rows, int T0, int T1,
                            const u32x4_t *bsm, u32x4_t *tr, float *out, int64_t out_stride, uint64_t (&best)[4],
                            float (&cm)[4], float (&cs)[4], Stage &&stage) {
     const bool conf = HEAD && a.conf != nullptr;
@@ -422,7 +424,7 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
     const int nit = (nt + TPI - 1) / TPI;
     auto load = [&](int i, int c, RawUnit<HT> &dst) {
         const bool real = i < nt;
-        raw_load_unit<HT>(W, qs, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
+        raw_load_unit<HT>(W, rows, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
     };
     RawUnit<HT> raw[DEPTH];
     HeadUnit<HT> op[2];
@@ -473,10 +475,10 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
             // issue order within the unit: activation reads, the next unit's
             // transpose, its ring refill, then the MFMAs (left alone, the
             // compiler reads each activation operand just before its MFMA)
-            constexpr int n_tr = sizeof(HT) == 2 ? 16 : 4 + kHeadUnit;
             constexpr int n_ld = sizeof(HT) == 2 ? 8 : 5;
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kHeadUnit, 0);     // LDS reads: activations
-            __builtin_amdgcn_sched_group_barrier(0x300, n_tr, 0);              // LDS writes / reads: transpose
+            if constexpr (sizeof(HT) == 2)
+                __builtin_amdgcn_sched_group_barrier(0x300, 16, 0);            // LDS writes / reads: transpose
             __builtin_amdgcn_sched_group_barrier(0x020, n_ld, 0);              // global loads
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * kHeadUnit, 0);     // MFMA
             __builtin_amdgcn_sched_barrier(0);  // keep each unit's transpose and loads next to its MFMAs
@@ -484,14 +486,129 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, const uint16_t *qs,
     }
 }
 
-// One workgroup per CU at d = 1024 (the LDS holds one), so the register file
-// may hold one wave per SIMD: the activation operands of a whole unit are
-// read ahead of its MFMAs.
+// Q8_0 units in flight per wave in the Q8_0 head (a multiple of 4, so of
+// every units-per-tile count).
+static constexpr int kQ8Depth = 4;
+
+// MFMAs of one Q8_0 unit, straight from the ring: per block the hi and lo
+// activation products go into one accumulation (hi first), which the block's
+// scale then adds to the tile's running sums, in block order.  xb: the
+// unit's first activation slot.  The schedule is pinned block by block (the
+// empty volatile asm statements: each block's operands are complete there
+// and nothing of a later block moves above it): the next block's activations
+// are read while this block converts its quants and issues its MFMAs, and a
+// block is scaled in while the next one's MFMAs run.  Left free, the
+// compiler converts and reads ahead for every block at once and the wave
+// needs more than its half of the register file.
+__device__ __forceinline__ void q8_unit_mma(const RawUnit<int8_t> &u, const u32x4_t *xb, f32x4_t &acc) {
+    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t xh = xb[0], xl = xb[64];
+    f32x4_t pp = z;
+    float spp = 0.f;
+#pragma unroll
+    for (int k = 0; k < kHeadUnit; ++k) {
+        const u32x4_t &r = u.r[k >> 1];
+        u32x2_t q = (k & 1) ? u32x2_t{r[2], r[3]} : u32x2_t{r[0], r[1]};
+        asm volatile("" : "+v"(q), "+v"(xh), "+v"(xl) : : "memory");
+        u32x4_t nxh = xh, nxl = xl;
+        if (k + 1 < kHeadUnit) {
+            nxh = xb[128 * (k + 1)];
+            nxl = xb[128 * (k + 1) + 64];
+        }
+        const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
+        f32x4_t pk = mfma(__builtin_bit_cast(bf16x8_t, xh), wv, z);
+        pk = mfma(__builtin_bit_cast(bf16x8_t, xl), wv, pk);
+        if (k > 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = fmaf(spp, pp[i], acc[i]);
+        }
+        pp = pk;
+        spp = sc_at(u.sc, k);
+        xh = nxh;
+        xl = nxl;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(spp, pp[i], acc[i]);
+    // the unit's scaling is done here: sunk to the tile's end, it would keep
+    // every unit's scales out of the ring slots being refilled
+    asm volatile("" : "+v"(acc));
+}
+
+// The 16-row tiles [T0, T1) of one workgroup for a Q8_0 head: wave w takes
+// T0 + w, T0 + w + 4, ...; its units (UPT per tile) stream through a ring of
+// kQ8Depth slots, each refilled as soon as its unit's MFMAs are issued.  The
+// unit-order copy is already in operand order, so nothing goes through LDS
+// but the activations.  Loads past the wave's last unit read the first unit
+// of the matrix and their results are never stored (as in head_tiles).
+template <int UPT, bool LOGITS, typename Stage>
+__device__ void q8_head_tiles(const HeadArgs &a, int T0, int T1, const u32x4_t *bsm, float *out, int64_t out_stride,
+                              uint64_t (&best)[4], float (&cm)[4], float (&cs)[4], Stage &&stage) {
+    static_assert(kQ8Depth % UPT == 0, "ring must hold whole tiles");
+    constexpr int TPI = kQ8Depth / UPT;     // tiles per loop iteration
+    const bool conf = a.conf != nullptr;
+    const int d = a.d, S = a.S;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j16 = lane & 15, g = lane >> 4;
+    const int nt = T1 - T0 > wid ? (T1 - T0 - wid + 3) / 4 : 0;
+    const int nit = (nt + TPI - 1) / TPI;
+    auto load = [&](int i, int c, RawUnit<int8_t> &dst) {
+        const bool real = i < nt;
+        raw_load_unit<int8_t>(a.head_qt, a.V, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
+    };
+    RawUnit<int8_t> raw[kQ8Depth];
+#pragma unroll
+    for (int p = 0; p < kQ8Depth; ++p) load(p / UPT, p % UPT, raw[p]);
+    stage();                                // the activations, while the first weights arrive
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < nit; ++it) {
+#pragma unroll
+        for (int p = 0; p < kQ8Depth; ++p) {
+            const int i = it * TPI + p / UPT, c = p % UPT;
+            // the activations are the same for every tile: left visible, the
+            // compiler hoists all of them out of the loop and spills.  Only the
+            // lane's base offset is hidden; the rest stays an immediate.
+            int lb = bslot(0, 0, g, j16);
+            asm volatile("" : "+v"(lb));
+            q8_unit_mma(raw[p], bsm + lb + bslot(c * kHeadUnit, 0, 0, 0), acc);
+            load(i + TPI, c, raw[p]);
+            if (c == UPT - 1) {
+                // lane (j16, g) holds row 16 tile + j16 for sequences 4g .. 4g+3
+                const int r = 16 * (T0 + wid + 4 * i) + j16;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int sq = 4 * g + q;
+                    const bool ok = i < nt && sq < S && r < a.V;
+                    const uint64_t k = ok ? argmax_key(acc[q], (uint32_t)r) : 0ull;
+                    best[q] = k > best[q] ? k : best[q];
+                    if (conf && ok) conf_add(cm[q], cs[q], acc[q]);
+                    if (LOGITS) *(ok ? out + (int64_t)sq * out_stride + r : a.sink + lane) = acc[q];
+                }
+                acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+            __builtin_amdgcn_sched_barrier(0);  // no instruction moves across units
+        }
+    }
+}
+
+// A bf16 unit loaded straight in operand order (lane l: row l % 16, 8
+// columns per step): the post-projection of the Q8_0 head, whose few units do
+// not need the faster row-block loads and whose workgroups keep no transpose
+// tile.
+__device__ __forceinline__ void direct_load_unit(const void *W, int rows, int d, int row0, int c, int lane,
+                                                 HeadUnit<uint16_t> &u) {
+    const uint16_t *wr = (const uint16_t *)W + (int64_t)min(row0 + (lane & 15), rows - 1) * d + 256 * c + 8 * (lane >> 4);
+#pragma unroll
+    for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt4(wr + 32 * k);
+}
+
+// The several-sequence LM head.  A Q8_0 head keeps no transpose tile, so two workgroups fit a CU and each
+// wave has half the register file.
 template <typename HT, int UPT, bool LOGITS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mm_head_kernel(HeadArgs a,
-                                                                                                 int tiles_per_wg) {
+__device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg) {
+    constexpr bool Q8 = sizeof(HT) == 1;
     extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
-    __shared__ u32x4_t mm_tr[4][kTrSlots];  // one weight transpose tile per wave
+    __shared__ u32x4_t mm_tr[Q8 ? 1 : 4 * kTrSlots];    // one weight transpose tile per wave (bf16)
     __shared__ float rsw[4][16];            // per-wave partial sums of squares of each sequence
     __shared__ uint64_t wbest[4][16];
     __shared__ float wcm[4][16], wcs[4][16];
@@ -511,16 +628,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int s = tid & 15;
         const float *xs = a.x + (int64_t)min(s, S - 1) * d;
         float v[NIT][8], gv[NIT][8];
+        auto load_gain = [&](int k) {
+            const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
+            const int col = 32 * t + 8 * g;
+            const float4 g0 = *(const float4 *)(a.g_final + col), g1 = *(const float4 *)(a.g_final + col + 4);
+            gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
+            gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
+        };
 #pragma unroll
         for (int k = 0; k < NIT; ++k) {
             const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
             const int col = 32 * t + 8 * g;
             const float4 x0 = *(const float4 *)(xs + col), x1 = *(const float4 *)(xs + col + 4);
-            const float4 g0 = *(const float4 *)(a.g_final + col), g1 = *(const float4 *)(a.g_final + col + 4);
             v[k][0] = x0.x; v[k][1] = x0.y; v[k][2] = x0.z; v[k][3] = x0.w;
             v[k][4] = x1.x; v[k][5] = x1.y; v[k][6] = x1.z; v[k][7] = x1.w;
-            gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
-            gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
+            load_gain(k);
         }
         float ss = 0.f;
 #pragma unroll
@@ -557,16 +679,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // projection costs a unit of streaming per wave and no extra latency.
     const int n_post_tiles = (a.dh + 15) / 16;
     const bool post_unit = wid < UPT;
-    RawUnit<uint16_t> praw;
-    if (hb < n_post_tiles && post_unit) raw_load_unit<uint16_t>(a.w_post, nullptr, a.dh, d, 16 * hb, wid, lane, praw);
+    std::conditional_t<Q8, HeadUnit<uint16_t>, RawUnit<uint16_t>> praw;
+    auto load_post = [&](int tb) {
+        if constexpr (Q8) direct_load_unit(a.w_post, a.dh, d, 16 * tb, wid, lane, praw);
+        else raw_load_unit<uint16_t>(a.w_post, a.dh, d, 16 * tb, wid, lane, praw);
+    };
+    // (the Q8_0 kernel's half register file has no room to hold them through
+    // the head: it requests them after)
+    if (!Q8 && hb < n_post_tiles && post_unit) load_post(hb);
     {
         float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : a.sink;
         const int64_t logits_stride = (int64_t)a.n_steps * a.V;
         const int n_tiles = (a.V + 15) / 16;
         const int T0 = hb * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
-        const void *W = sizeof(HT) == 1 ? (const void *)a.head_q : a.head;
-        head_tiles<HT, UPT, true, LOGITS>(a, W, a.head_qs, a.V, T0, T1, mm_bsm, mm_tr[wid], logits, logits_stride,
-                                          best, cm, cs, stage);
+        if constexpr (Q8)
+            q8_head_tiles<UPT, LOGITS>(a, T0, T1, mm_bsm, logits, logits_stride, best, cm, cs, stage);
+        else
+            head_tiles<HT, UPT, true, LOGITS>(a, a.head, a.V, T0, T1, mm_bsm, mm_tr + wid * kTrSlots, logits,
+                                              logits_stride, best, cm, cs, stage);
         // best over the 16 rows of each lane group: xor-shuffles within 16 lanes
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -609,11 +739,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
     const int j16 = lane & 15, g = lane >> 4;
     for (int tb = hb; tb < n_post_tiles; tb += (int)gridDim.x) {
-        if (tb != hb && post_unit) raw_load_unit<uint16_t>(a.w_post, nullptr, a.dh, d, 16 * tb, wid, lane, praw);
+        if ((Q8 || tb != hb) && post_unit) load_post(tb);
         f32x4_t ph = {0.f, 0.f, 0.f, 0.f}, pl = {0.f, 0.f, 0.f, 0.f};
         if (post_unit) {
             HeadUnit<uint16_t> u;
-            transpose_unit<uint16_t>(praw, mm_tr[wid], lane, u);
+            if constexpr (Q8) u = praw;
+            else transpose_unit<uint16_t>(praw, mm_tr + wid * kTrSlots, lane, u);
             u32x4_t xv[2 * kHeadUnit];
             const u32x4_t *xb = mm_bsm + bslot(wid * kHeadUnit, 0, g, j16);
 #pragma unroll
@@ -636,6 +767,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         __syncthreads();
     }
+}
+
+// bf16: one workgroup per CU at d = 1024 (the LDS holds one), so the register
+// file may hold one wave per SIMD: the activation operands of a whole unit
+// are read ahead of its MFMAs.
+template <typename HT, int UPT, bool LOGITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mm_head_kernel(HeadArgs a,
+                                                                                                 int tiles_per_wg) {
+    mm_head_body<HT, UPT, LOGITS>(a, tiles_per_wg);
+}
+
+// Q8_0: two workgroups per CU, two waves per SIMD.
+template <int UPT, bool LOGITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mm_q8_head_kernel(HeadArgs a,
+                                                                                                    int tiles_per_wg) {
+    mm_head_body<int8_t, UPT, LOGITS>(a, tiles_per_wg);
 }
 
 // ----------------------------------------------------------------------------
@@ -699,29 +846,35 @@ hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart,
 
 bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a) {
     const int upt = a.d / (32 * kHeadUnit);
-    return w_dtype == MTP_BF16 && (head_dtype == MTP_BF16 || head_dtype == MTP_Q8_0) && a.S >= kMmMinSeqs &&
+    return w_dtype == MTP_BF16 && (head_dtype == MTP_BF16 || (head_dtype == MTP_Q8_0 && a.head_qt)) && a.S >= kMmMinSeqs &&
            a.S <= 16 && a.d % (32 * kHeadUnit) == 0 && (upt == 1 || upt == 2 || upt == 4) && a.sink;
+}
+
+template <typename K>
+static hipError_t launch_head_k(K kernel, const HeadArgs &a, int tiles_per_wg, dim3 grid, size_t lds, hipStream_t st) {
+    hipError_t e = allow_dynamic_lds(kernel, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, st, a, tiles_per_wg);
+    return hipGetLastError();
 }
 
 template <typename HT, int UPT>
 static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 grid, size_t lds, bool logits,
                                    hipStream_t st) {
-    if (logits) {
-        hipError_t e = allow_dynamic_lds(mm_head_kernel<HT, UPT, true>, lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((mm_head_kernel<HT, UPT, true>), grid, dim3(256), lds, st, a, tiles_per_wg);
+    if constexpr (sizeof(HT) == 1) {
+        return logits ? launch_head_k(mm_q8_head_kernel<UPT, true>, a, tiles_per_wg, grid, lds, st)
+                      : launch_head_k(mm_q8_head_kernel<UPT, false>, a, tiles_per_wg, grid, lds, st);
     } else {
-        hipError_t e = allow_dynamic_lds(mm_head_kernel<HT, UPT, false>, lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((mm_head_kernel<HT, UPT, false>), grid, dim3(256), lds, st, a, tiles_per_wg);
+        return logits ? launch_head_k(mm_head_kernel<HT, UPT, true>, a, tiles_per_wg, grid, lds, st)
+                      : launch_head_k(mm_head_kernel<HT, UPT, false>, a, tiles_per_wg, grid, lds, st);
     }
-    return hipGetLastError();
 }
 
 // Head workgroups of a launch and the 16-row tiles each takes.
-static void mm_head_grid(const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
-    // dynamic activation halves + the static transpose tiles and reduction slots
-    const size_t lds = sizeof(u32x4_t) * ((size_t)128 * (a.d / 32) + 4 * kTrSlots + 4 * 64) + 2048;
+static void mm_head_grid(int head_dtype, const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
+    // dynamic activation halves + the static transpose tiles (bf16) and reduction slots
+    const size_t tr = head_dtype == MTP_Q8_0 ? 1 : 4 * kTrSlots;
+    const size_t lds = sizeof(u32x4_t) * ((size_t)128 * (a.d / 32) + tr + 4 * 64) + 2048;
     const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
     const int n_tiles = (a.V + 15) / 16;
     n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
@@ -729,9 +882,9 @@ static void mm_head_grid(const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
     n_wg = (n_tiles + tiles_per_wg - 1) / tiles_per_wg;
 }
 
-int mm_head_groups(const HeadArgs &a) {
+int mm_head_groups(int head_dtype, const HeadArgs &a) {
     int n_wg, tpw;
-    mm_head_grid(a, n_wg, tpw);
+    mm_head_grid(head_dtype, a, n_wg, tpw);
     return n_wg;
 }
 
@@ -741,7 +894,7 @@ hipError_t launch_mm_head(int head_dtype, const HeadArgs &a_in, bool logits, hip
     const size_t lds = sizeof(u32x4_t) * (size_t)128 * KS;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     int n_wg, tiles_per_wg;
-    mm_head_grid(a, n_wg, tiles_per_wg);
+    mm_head_grid(head_dtype, a, n_wg, tiles_per_wg);
     a.n_head_wg = n_wg;
     const dim3 grid(n_wg);
 #define MTP_MMH(HT, U)                                                                                 \

@@ -41,6 +41,60 @@ hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, i
     return hipGetLastError();
 }
 
+// Q8_0 blocks -> unit order (layout in mtp_internal.h): one thread per
+// 16-byte piece of the output.
+__global__ void q8_unit_order_kernel(const uint8_t *blocks, int64_t rows, int32_t cols, int64_t n_pieces,
+                                     uint8_t *out) {
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= n_pieces) return;
+    constexpr int kPieces = kQ8UnitBytes / 16;
+    const int upc = cols / 256, nblk = cols / 32;
+    const int64_t unit = id / kPieces;
+    const int w = (int)(id - unit * kPieces);
+    const int64_t t = unit / upc;
+    const int c = (int)(unit - t * upc);
+    auto byte_at = [&](int64_t row, int b, int off) -> uint32_t { return blocks[(row * nblk + b) * 34 + off]; };
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (w < 256) {
+        const int p = w >> 6, l = w & 63, g = l >> 4, j = l & 15;
+        const int64_t row = 16 * t + j;
+        if (row < rows) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int b = 8 * c + 2 * p + h;
+#pragma unroll
+                for (int wd = 0; wd < 2; ++wd) {
+                    const int off = 2 + 8 * g + 4 * wd;
+                    v[2 * h + wd] = byte_at(row, b, off) | (byte_at(row, b, off + 1) << 8) |
+                                    (byte_at(row, b, off + 2) << 16) | (byte_at(row, b, off + 3) << 24);
+                }
+            }
+        }
+    } else {
+        const int j = w - 256;
+        const int64_t row = 16 * t + j;
+        if (row < rows) {
+#pragma unroll
+            for (int k = 0; k < 8; k += 2)
+                v[k / 2] = byte_at(row, 8 * c + k, 0) | (byte_at(row, 8 * c + k, 1) << 8) |
+                           (byte_at(row, 8 * c + k + 1, 0) << 16) | (byte_at(row, 8 * c + k + 1, 1) << 24);
+        }
+    }
+    *(uint4 *)(out + id * 16) = make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+size_t q8_unit_order_bytes(int64_t rows, int32_t cols) {
+    return (size_t)((rows + 15) / 16) * (size_t)(cols / 256) * kQ8UnitBytes;
+}
+
+hipError_t launch_q8_unit_order(const uint8_t *blocks, int64_t rows, int32_t cols, uint8_t *out, hipStream_t st) {
+    if (cols % 256 != 0) return hipErrorInvalidValue;
+    const int64_t n_pieces = (int64_t)(q8_unit_order_bytes(rows, cols) / 16);
+    hipLaunchKernelGGL(q8_unit_order_kernel, dim3((unsigned)((n_pieces + 255) / 256)), dim3(256), 0, st, blocks, rows,
+                       cols, n_pieces, out);
+    return hipGetLastError();
+}
+
 __global__ void clear_u64_kernel(uint64_t *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0ull;

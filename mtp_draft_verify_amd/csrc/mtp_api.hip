@@ -79,6 +79,7 @@ struct mtp_ctx {
     double *inv_freq = nullptr;         // [head_dim / 2] RoPE frequencies
     int8_t *head_q = nullptr;           // Q8_0 head re-laid out: int8 plane
     uint16_t *head_qs = nullptr;        //   and fp16 scale plane
+    uint8_t *head_qt = nullptr;         // Q8_0 head in unit order (several-sequence head)
     // per-call parameter block: CallIO then SeqParams[max_seqs], at one fixed
     // device address; staged through a ring of pinned host slots
     uint8_t *d_block = nullptr;
@@ -220,7 +221,7 @@ static void free_ctx(mtp_ctx *c) {
         (void)hipGraphDestroy(g.g);
     }
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->d_block,
+    void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->head_qt, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane,
                     c->o_op, c->u_op, c->x_op, c->kpart, c->hv_logits};
     for (void *b : bufs)
@@ -309,6 +310,10 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         if (ok && d.head_dtype == MTP_Q8_0)
             ok = dalloc(&c->head_q, (size_t)d.n_vocab * d.d_model) &&
                  dalloc(&c->head_qs, (size_t)d.n_vocab * (d.d_model / 32));
+        // the several-sequence head streams the Q8_0 head in unit order: each
+        // 16-row x 256-column unit is one contiguous run already in operand order
+        if (ok && d.head_dtype == MTP_Q8_0 && d.max_seqs >= kMmMinSeqs && d.d_model % 256 == 0)
+            ok = dalloc(&c->head_qt, q8_unit_order_bytes(d.n_vocab, d.d_model));
         if (ok) ok = hipHostMalloc((void **)&c->h_block, c->block_bytes * kParamSlots) == hipSuccess;
         if (ok) ok = hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking) == hipSuccess;
         for (int i = 0; ok && i < kParamSlots; ++i)
@@ -340,6 +345,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         if (e != hipSuccess) { free_ctx(c); return hip_fail("rope table kernel", e); }
         if (d.head_dtype == MTP_Q8_0) {
             e = launch_q8_repack((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_q, c->head_qs, c->stream);
+            if (e == hipSuccess && c->head_qt)
+                e = launch_q8_unit_order((const uint8_t *)c->w.head, d.n_vocab, d.d_model, c->head_qt, c->stream);
             if (e != hipSuccess) { free_ctx(c); return hip_fail("Q8_0 re-layout kernel", e); }
         }
     }
@@ -598,7 +605,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
         if (e == hipSuccess) {
             HeadArgs ha{};
             ha.x = c->x; ha.g_final = c->w.g_final; ha.eps = d.rms_eps; ha.d = D; ha.S = S; ha.V = V;
-            ha.head = c->w.head; ha.head_q = c->head_q; ha.head_qs = c->head_qs;
+            ha.head = c->w.head; ha.head_q = c->head_q; ha.head_qs = c->head_qs; ha.head_qt = c->head_qt;
             // one sequence: one workgroup per compute unit, each streaming a
             // contiguous block of rows with the next rows always in flight
             const int64_t wg_cap = S == 1 ? c->n_cu : 2048;
@@ -623,7 +630,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                 e = launch_cand_head(d.head_dtype, d.w_dtype, ha, n_post_wg, sh.logits, st);
             } else {
                 const bool mm = mm_head_supported(d.head_dtype, d.w_dtype, ha);
-                n_part = mm ? mm_head_groups(ha) : ha.n_head_wg;
+                n_part = mm ? mm_head_groups(d.head_dtype, ha) : ha.n_head_wg;
                 e = mm ? launch_mm_head(d.head_dtype, ha, sh.logits, st)
                        : launch_head(d.head_dtype, d.w_dtype, ha, n_post_wg, sh.logits, st);
             }

@@ -116,6 +116,7 @@ struct HeadArgs {
     const void *head;       // bf16 / f32 [V, d]
     const int8_t *head_q;   // Q8_0 plane [V, d]
     const uint16_t *head_qs;    // Q8_0 scales [V, d/32]
+    const uint8_t *head_qt; // Q8_0 head in unit order (several-sequence head), or null
     int32_t rows_per_wg, n_head_wg;
     uint64_t *keys;         // [S] argmax keys (cleared before)
     const CallIO *io;       // io->out_logits (nullable), io->out_h_last (nullable)
@@ -168,6 +169,17 @@ hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *i
                                 hipStream_t st);
 hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
                             hipStream_t st);
+// Unit order of a Q8_0 matrix [rows, cols] (cols % 256 == 0) for the
+// several-sequence head: unit (t, c) = rows 16t .. 16t+15 x columns 256c ..
+// 256c+255 is kQ8UnitBytes contiguous bytes at (t * cols / 256 + c) *
+// kQ8UnitBytes.  Bytes 1024 p + 16 l (p < 4, lane l = 16 g + j) hold the 8
+// quants of row 16t + j at columns 256c + 32 (2p) + 8g .. +7, then those at
+// 256c + 32 (2p + 1) + 8g .. +7: a wave's 16-byte load at its lane offset is
+// two K steps of the matrix-core operand.  Bytes 4096 + 16 j hold the fp16
+// scales of row 16t + j's blocks 8c .. 8c+7.  Rows past the end are zero.
+static constexpr int kQ8UnitBytes = 4352;
+size_t q8_unit_order_bytes(int64_t rows, int32_t cols);
+hipError_t launch_q8_unit_order(const uint8_t *blocks, int64_t rows, int32_t cols, uint8_t *out, hipStream_t st);
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st);
 hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_t n_part, int64_t step_stride,
                               const CallIO *io, hipStream_t st);
@@ -193,7 +205,7 @@ hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart,
                           hipStream_t st);
 bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a);
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a, bool logits, hipStream_t st);
-int mm_head_groups(const HeadArgs &a);   // head workgroups (confidence partials) of one launch
+int mm_head_groups(int head_dtype, const HeadArgs &a);   // head workgroups (confidence partials) of one launch
 
 // verify from hidden states: the target's final norm + LM head + argmax over
 // rows [row0, row0 + R) of hidden, in passes of up to 64 rows

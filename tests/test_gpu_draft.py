@@ -69,6 +69,20 @@ def test_c4_q8_head_small_context(orc):
     _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
 
 
+def test_q8_head_ragged_vocab_several_and_one_sequence(orc):
+    """The several-sequence Q8_0 head streams the head's unit-order copy,
+    whose last 16-row tile is padded with zero rows when V % 16 != 0; the
+    one-sequence head reads the row-major plane.  Both against the oracle,
+    and the same sequence alone and in the batch gives the same ids."""
+    log("case q8 ragged: V=262144-123, ctx=1500, S=5 and S=1, N=3")
+    w = syn.c4_longctx_q8(n_vocab=262144 - 123, ctx=1500, n_seq=5, n_steps=3)
+    g = GpuDrafter(w.model, 5, 3)
+    batch = g.run(w.draft)
+    _check(w, batch, orc.draft_block(w.model, w.draft))
+    one = g.run(w.draft, seq_idx=[3])
+    assert np.array_equal(one["drafts"][0], batch["drafts"][3])
+
+
 def test_chained_equals_step_by_step_on_gpu():
     """One N-step call == N one-step calls chained through (token, h), bit for
     bit (the fused-vs-sequential check of the evaluation record)."""
