@@ -16,6 +16,7 @@
 // Each output column is a separate dot product, so a sequence gets the same
 // bits whatever else is in the batch.
 #include <algorithm>
+#include <type_traits>
 
 #include "widen.h"
 
@@ -41,20 +42,38 @@ __device__ __forceinline__ void split_bf16(const float (&v)[8], u32x4_t &hi, u32
     lo = __builtin_bit_cast(u32x4_t, l);
 }
 
-// 8 Q8_0 quants (one lane's share of a step) as exact bf16 values.
+// Signed byte B of w as fp32, in one instruction (the convert's own byte
+// select and sign extension; left to itself the compiler extracts bytes 1
+// and 3 with an extra 16-bit shift each).
+template <int B>
+__device__ __forceinline__ float sbyte_to_f32(uint32_t w) {
+    float f;
+    if constexpr (B == 0)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(f) : "v"(w));
+    else if constexpr (B == 1)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(f) : "v"(w));
+    else if constexpr (B == 2)
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(f) : "v"(w));
+    else
+        asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(f) : "v"(w));
+    return f;
+}
+
+// 8 Q8_0 quants (one lane's share of a step) as exact bf16 values: each
+// integer goes to fp32 exactly and every |q| <= 128 has at most 8
+// significant bits, so the pairwise fp32 -> bf16 conversion (one
+// instruction per pair on gfx950) is exact too.
 __device__ __forceinline__ u32x4_t q8_to_bf16(const u32x2_t q) {
-    u32x4_t r;
+    bf16x8_t r;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t w = q[h];
-        const uint32_t f0 = __float_as_uint((float)(int8_t)(w & 0xFF));
-        const uint32_t f1 = __float_as_uint((float)(int8_t)((w >> 8) & 0xFF));
-        const uint32_t f2 = __float_as_uint((float)(int8_t)((w >> 16) & 0xFF));
-        const uint32_t f3 = __float_as_uint((float)(int8_t)(w >> 24));
-        r[2 * h + 0] = (f0 >> 16) | (f1 & 0xFFFF0000u);
-        r[2 * h + 1] = (f2 >> 16) | (f3 & 0xFFFF0000u);
+        r[4 * h + 0] = (__bf16)sbyte_to_f32<0>(w);
+        r[4 * h + 1] = (__bf16)sbyte_to_f32<1>(w);
+        r[4 * h + 2] = (__bf16)sbyte_to_f32<2>(w);
+        r[4 * h + 3] = (__bf16)sbyte_to_f32<3>(w);
     }
-    return r;
+    return __builtin_bit_cast(u32x4_t, r);
 }
 
 __device__ __forceinline__ u32x4_t ld_nt4(const void *p) { return __builtin_nontemporal_load((const u32x4_t *)p); }
@@ -268,6 +287,11 @@ template <> struct HeadUnit<int8_t> {
 // 1 KiB block per (t, h) in lane order, so a wave reads it with a single
 // conflict-free ds_read_b128 at a compile-time offset from its lane base.
 __device__ __forceinline__ int bslot(int t, int h, int g, int s) { return ((2 * t + h) * 4 + g) * 16 + s; }
+// Packed form for at most 8 sequences: one block per step t whose operand
+// rows j < 8 hold the hi half of sequence j and rows j >= 8 the lo half of
+// sequence j - 8, so one MFMA forms both halves' products (in separate
+// output rows, added once per tile).
+__device__ __forceinline__ int pslot(int t, int g, int j) { return (t * 4 + g) * 16 + j; }
 
 // Weights of unit c (steps 8c .. 8c+7, 256 columns) of the 16-row tile at
 // row0, as loaded.  A wave load that touches 16 rows (the operand order, lane
@@ -487,7 +511,7 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, int rows, int T0, i
 }
 
 // Q8_0 units in flight per wave in the Q8_0 head (a multiple of 4, so of
-// every units-per-tile count).
+// every units-per-tile count; 8 measured slower than 4 at 8 sequences).
 static constexpr int kQ8Depth = 4;
 
 // MFMAs of one Q8_0 unit, straight from the ring: per block the hi and lo
@@ -500,24 +524,29 @@ static constexpr int kQ8Depth = 4;
 // block is scaled in while the next one's MFMAs run.  Left free, the
 // compiler converts and reads ahead for every block at once and the wave
 // needs more than its half of the register file.
+// PACK: the activations in the packed form (one MFMA per block; a lane's
+// results are the hi or the lo products of its four sequences).
+template <bool PACK>
 __device__ __forceinline__ void q8_unit_mma(const RawUnit<int8_t> &u, const u32x4_t *xb, f32x4_t &acc) {
+    constexpr int XS = PACK ? 64 : 128;     // slots per step
     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    u32x4_t xh = xb[0], xl = xb[64];
+    u32x4_t xh = xb[0], xl = PACK ? xh : xb[64];
     f32x4_t pp = z;
     float spp = 0.f;
 #pragma unroll
     for (int k = 0; k < kHeadUnit; ++k) {
         const u32x4_t &r = u.r[k >> 1];
         u32x2_t q = (k & 1) ? u32x2_t{r[2], r[3]} : u32x2_t{r[0], r[1]};
-        asm volatile("" : "+v"(q), "+v"(xh), "+v"(xl) : : "memory");
+        if constexpr (PACK) asm volatile("" : "+v"(q), "+v"(xh) : : "memory");
+        else asm volatile("" : "+v"(q), "+v"(xh), "+v"(xl) : : "memory");
         u32x4_t nxh = xh, nxl = xl;
         if (k + 1 < kHeadUnit) {
-            nxh = xb[128 * (k + 1)];
-            nxl = xb[128 * (k + 1) + 64];
+            nxh = xb[XS * (k + 1)];
+            if constexpr (!PACK) nxl = xb[XS * (k + 1) + 64];
         }
         const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
         f32x4_t pk = mfma(__builtin_bit_cast(bf16x8_t, xh), wv, z);
-        pk = mfma(__builtin_bit_cast(bf16x8_t, xl), wv, pk);
+        if constexpr (!PACK) pk = mfma(__builtin_bit_cast(bf16x8_t, xl), wv, pk);
         if (k > 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = fmaf(spp, pp[i], acc[i]);
@@ -539,12 +568,17 @@ __device__ __forceinline__ void q8_unit_mma(const RawUnit<int8_t> &u, const u32x
 // kQ8Depth slots, each refilled as soon as its unit's MFMAs are issued.  The
 // unit-order copy is already in operand order, so nothing goes through LDS
 // but the activations.  Loads past the wave's last unit read the first unit
-// of the matrix and their results are never stored (as in head_tiles).
-template <int UPT, bool LOGITS, typename Stage>
+// of the matrix and their results are never stored (as in head_tiles).  The
+// last ring pass is peeled: it refills nothing, and before it last() requests
+// what the workgroup needs after the head (the post-projection's weights),
+// into the registers the ring is about to free.
+template <int UPT, bool LOGITS, bool PACK, typename StageLoad, typename StageFinish, typename Last>
 __device__ void q8_head_tiles(const HeadArgs &a, int T0, int T1, const u32x4_t *bsm, float *out, int64_t out_stride,
-                              uint64_t (&best)[4], float (&cm)[4], float (&cs)[4], Stage &&stage) {
-    static_assert(kQ8Depth % UPT == 0, "ring must hold whole tiles");
-    constexpr int TPI = kQ8Depth / UPT;     // tiles per loop iteration
+                              uint64_t (&best)[4], float (&cm)[4], float (&cs)[4], StageLoad &&stage_load,
+                              StageFinish &&stage_finish, Last &&last) {
+    constexpr int DEPTH = kQ8Depth;
+    static_assert(DEPTH % UPT == 0, "ring must hold whole tiles");
+    constexpr int TPI = DEPTH / UPT;        // tiles per loop iteration
     const bool conf = a.conf != nullptr;
     const int d = a.d, S = a.S;
     const int lane = threadIdx.x & 63;
@@ -556,39 +590,51 @@ __device__ void q8_head_tiles(const HeadArgs &a, int T0, int T1, const u32x4_t *
         const bool real = i < nt;
         raw_load_unit<int8_t>(a.head_qt, a.V, d, real ? 16 * (T0 + wid + 4 * i) : 0, real ? c : 0, lane, dst);
     };
-    RawUnit<int8_t> raw[kQ8Depth];
+    RawUnit<int8_t> raw[DEPTH];
+    stage_load();                           // x and the gain (from L2) ahead of the weights
+    asm volatile("" : : : "memory");        // keeps them first in the load queue
 #pragma unroll
-    for (int p = 0; p < kQ8Depth; ++p) load(p / UPT, p % UPT, raw[p]);
-    stage();                                // the activations, while the first weights arrive
+    for (int p = 0; p < DEPTH; ++p) load(p / UPT, p % UPT, raw[p]);
+    stage_finish();                         // the activations, while the first weights arrive
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it < nit; ++it) {
+    auto pass = [&](int it, auto refill) {
 #pragma unroll
-        for (int p = 0; p < kQ8Depth; ++p) {
+        for (int p = 0; p < DEPTH; ++p) {
             const int i = it * TPI + p / UPT, c = p % UPT;
             // the activations are the same for every tile: left visible, the
             // compiler hoists all of them out of the loop and spills.  Only the
             // lane's base offset is hidden; the rest stays an immediate.
-            int lb = bslot(0, 0, g, j16);
+            int lb = PACK ? pslot(0, g, j16) : bslot(0, 0, g, j16);
             asm volatile("" : "+v"(lb));
-            q8_unit_mma(raw[p], bsm + lb + bslot(c * kHeadUnit, 0, 0, 0), acc);
-            load(i + TPI, c, raw[p]);
+            q8_unit_mma<PACK>(raw[p], bsm + lb + (PACK ? pslot(c * kHeadUnit, 0, 0) : bslot(c * kHeadUnit, 0, 0, 0)),
+                              acc);
+            if constexpr (decltype(refill)::value) load(i + TPI, c, raw[p]);
             if (c == UPT - 1) {
-                // lane (j16, g) holds row 16 tile + j16 for sequences 4g .. 4g+3
+                // lane (j16, g) holds row 16 tile + j16 for sequences 4g .. 4g+3;
+                // packed: lanes g < 2 the hi products, lanes g + 2 the lo ones
                 const int r = 16 * (T0 + wid + 4 * i) + j16;
+                f32x4_t zt = acc;
+                if constexpr (PACK) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) zt[q] = acc[q] + __shfl_xor(acc[q], 32);
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int sq = 4 * g + q;
-                    const bool ok = i < nt && sq < S && r < a.V;
-                    const uint64_t k = ok ? argmax_key(acc[q], (uint32_t)r) : 0ull;
+                    const bool ok = (!PACK || g < 2) && i < nt && sq < S && r < a.V;
+                    const uint64_t k = ok ? argmax_key(zt[q], (uint32_t)r) : 0ull;
                     best[q] = k > best[q] ? k : best[q];
-                    if (conf && ok) conf_add(cm[q], cs[q], acc[q]);
-                    if (LOGITS) *(ok ? out + (int64_t)sq * out_stride + r : a.sink + lane) = acc[q];
+                    if (conf && ok) conf_add(cm[q], cs[q], zt[q]);
+                    if (LOGITS) *(ok ? out + (int64_t)sq * out_stride + r : a.sink + lane) = zt[q];
                 }
                 acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
             }
             __builtin_amdgcn_sched_barrier(0);  // no instruction moves across units
         }
-    }
+    };
+    for (int it = 0; it + 1 < nit; ++it) pass(it, std::true_type{});
+    last();
+    if (nit > 0) pass(nit - 1, std::false_type{});
 }
 
 // A bf16 unit loaded straight in operand order (lane l: row l % 16, 8
@@ -604,9 +650,10 @@ __device__ __forceinline__ void direct_load_unit(const void *W, int rows, int d,
 
 // The several-sequence LM head.  A Q8_0 head keeps no transpose tile, so two workgroups fit a CU and each
 // wave has half the register file.
-template <typename HT, int UPT, bool LOGITS>
+template <typename HT, int UPT, bool LOGITS, bool PACK>
 __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg) {
     constexpr bool Q8 = sizeof(HT) == 1;
+    static_assert(Q8 || !PACK, "the packed activations serve the Q8_0 head");
     extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
     __shared__ u32x4_t mm_tr[Q8 ? 1 : 4 * kTrSlots];    // one weight transpose tile per wave (bf16)
     __shared__ float rsw[4][16];            // per-wave partial sums of squares of each sequence
@@ -623,18 +670,15 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
     // its 16 * UPT column groups of x and of the gain at once, sums its
     // squares, and the 16 threads of a sequence (4 lanes of each wave) add
     // theirs in a fixed order, so the stage costs one memory round trip.
-    auto stage = [&]() {
-        constexpr int NIT = 2 * UPT;        // KS * 64 / 256 slots per thread
-        const int s = tid & 15;
-        const float *xs = a.x + (int64_t)min(s, S - 1) * d;
-        float v[NIT][8], gv[NIT][8];
-        auto load_gain = [&](int k) {
-            const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
-            const int col = 32 * t + 8 * g;
-            const float4 g0 = *(const float4 *)(a.g_final + col), g1 = *(const float4 *)(a.g_final + col + 4);
-            gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
-            gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
-        };
+    // (stage_load requests x and the gain; stage_finish waits for them and
+    // fills the LDS.  The Q8_0 kernel requests its first weights between the
+    // two, so that its staging waits for x alone, not for those weights.)
+    constexpr int NIT = 2 * UPT;            // KS * 64 / 256 slots per thread
+    const int s_st = tid & 15;
+    const int sx = PACK ? (s_st & 7) : s_st;    // the sequence this thread stages (packed: rows s, s + 8)
+    float v[NIT][8], gv[NIT][8];
+    auto stage_load = [&]() {
+        const float *xs = a.x + (int64_t)min(sx, S - 1) * d;
 #pragma unroll
         for (int k = 0; k < NIT; ++k) {
             const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
@@ -642,8 +686,13 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
             const float4 x0 = *(const float4 *)(xs + col), x1 = *(const float4 *)(xs + col + 4);
             v[k][0] = x0.x; v[k][1] = x0.y; v[k][2] = x0.z; v[k][3] = x0.w;
             v[k][4] = x1.x; v[k][5] = x1.y; v[k][6] = x1.z; v[k][7] = x1.w;
-            load_gain(k);
+            const float4 g0 = *(const float4 *)(a.g_final + col), g1 = *(const float4 *)(a.g_final + col + 4);
+            gv[k][0] = g0.x; gv[k][1] = g0.y; gv[k][2] = g0.z; gv[k][3] = g0.w;
+            gv[k][4] = g1.x; gv[k][5] = g1.y; gv[k][6] = g1.z; gv[k][7] = g1.w;
         }
+    };
+    auto stage_finish = [&]() {
+        const int s = s_st;
         float ss = 0.f;
 #pragma unroll
         for (int k = 0; k < NIT; ++k)
@@ -658,16 +707,24 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
         for (int k = 0; k < NIT; ++k) {
             const int it = tid + 256 * k, t = it >> 6, g = (it >> 4) & 3;
             u32x4_t hi = {0, 0, 0, 0}, lo = {0, 0, 0, 0};
-            if (s < S) {
+            if (sx < S) {
                 float f[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] = v[k][e] * r * gv[k][e];
                 split_bf16(f, hi, lo);
             }
-            mm_bsm[bslot(t, 0, g, s)] = hi;
-            mm_bsm[bslot(t, 1, g, s)] = lo;
+            if constexpr (PACK) {
+                mm_bsm[pslot(t, g, s)] = s < 8 ? hi : lo;
+            } else {
+                mm_bsm[bslot(t, 0, g, s)] = hi;
+                mm_bsm[bslot(t, 1, g, s)] = lo;
+            }
         }
         __syncthreads();
+    };
+    auto stage = [&]() {
+        stage_load();
+        stage_finish();
     };
 
     uint64_t best[4] = {0ull, 0ull, 0ull, 0ull};   // sequences 4g .. 4g+3 of this lane
@@ -685,15 +742,19 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
         else raw_load_unit<uint16_t>(a.w_post, a.dh, d, 16 * tb, wid, lane, praw);
     };
     // (the Q8_0 kernel's half register file has no room to hold them through
-    // the head: it requests them after)
-    if (!Q8 && hb < n_post_tiles && post_unit) load_post(hb);
+    // the head: it requests them before its last ring pass)
+    auto post_first = [&]() {
+        if (hb < n_post_tiles && post_unit) load_post(hb);
+    };
+    if (!Q8) post_first();
     {
         float *logits = a.io->out_logits ? a.io->out_logits + (int64_t)a.step * a.V : a.sink;
         const int64_t logits_stride = (int64_t)a.n_steps * a.V;
         const int n_tiles = (a.V + 15) / 16;
         const int T0 = hb * tiles_per_wg, T1 = min(n_tiles, T0 + tiles_per_wg);
         if constexpr (Q8)
-            q8_head_tiles<UPT, LOGITS>(a, T0, T1, mm_bsm, logits, logits_stride, best, cm, cs, stage);
+            q8_head_tiles<UPT, LOGITS, PACK>(a, T0, T1, mm_bsm, logits, logits_stride, best, cm, cs, stage_load,
+                                             stage_finish, post_first);
         else
             head_tiles<HT, UPT, true, LOGITS>(a, a.head, a.V, T0, T1, mm_bsm, mm_tr + wid * kTrSlots, logits,
                                               logits_stride, best, cm, cs, stage);
@@ -739,27 +800,37 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
     float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
     const int j16 = lane & 15, g = lane >> 4;
     for (int tb = hb; tb < n_post_tiles; tb += (int)gridDim.x) {
-        if ((Q8 || tb != hb) && post_unit) load_post(tb);
+        if (tb != hb && post_unit) load_post(tb);
         f32x4_t ph = {0.f, 0.f, 0.f, 0.f}, pl = {0.f, 0.f, 0.f, 0.f};
         if (post_unit) {
             HeadUnit<uint16_t> u;
             if constexpr (Q8) u = praw;
             else transpose_unit<uint16_t>(praw, mm_tr + wid * kTrSlots, lane, u);
-            u32x4_t xv[2 * kHeadUnit];
-            const u32x4_t *xb = mm_bsm + bslot(wid * kHeadUnit, 0, g, j16);
+            if constexpr (PACK) {
+                // hi products in lanes g < 2, lo products in lanes g + 2
+                const u32x4_t *xb = mm_bsm + pslot(wid * kHeadUnit, g, j16);
 #pragma unroll
-            for (int k = 0; k < kHeadUnit; ++k) {
-                xv[2 * k] = xb[128 * k];
-                xv[2 * k + 1] = xb[128 * k + 64];
+                for (int k = 0; k < kHeadUnit; ++k)
+                    ph = mfma(__builtin_bit_cast(bf16x8_t, xb[64 * k]), __builtin_bit_cast(bf16x8_t, u.w[k]), ph);
+            } else {
+                u32x4_t xv[2 * kHeadUnit];
+                const u32x4_t *xb = mm_bsm + bslot(wid * kHeadUnit, 0, g, j16);
+#pragma unroll
+                for (int k = 0; k < kHeadUnit; ++k) {
+                    xv[2 * k] = xb[128 * k];
+                    xv[2 * k + 1] = xb[128 * k + 64];
+                }
+                head_unit_mma<uint16_t>(u, xv, ph, pl);
             }
-            head_unit_mma<uint16_t>(u, xv, ph, pl);
         }
-        post_part[wid][lane] = ph + pl;
+        post_part[wid][lane] = PACK ? ph : ph + pl;
         __syncthreads();
-        if (wid == 0) {
+        if (wid == 0 && (!PACK || lane < 32)) {
             // lane (j16, g) holds row 16 tb + j16 for sequences 4g .. 4g+3
-            f32x4_t z = post_part[0][lane];
-            for (int w = 1; w < UPT; ++w) z += post_part[w][lane];
+            // (packed: hi + lo of the same wave first, as unpacked)
+            auto part = [&](int w) { return PACK ? post_part[w][lane] + post_part[w][lane + 32] : post_part[w][lane]; };
+            f32x4_t z = part(0);
+            for (int w = 1; w < UPT; ++w) z += part(w);
             const int r = 16 * tb + j16;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -775,14 +846,15 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
 template <typename HT, int UPT, bool LOGITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void mm_head_kernel(HeadArgs a,
                                                                                                  int tiles_per_wg) {
-    mm_head_body<HT, UPT, LOGITS>(a, tiles_per_wg);
+    mm_head_body<HT, UPT, LOGITS, false>(a, tiles_per_wg);
 }
 
-// Q8_0: two workgroups per CU, two waves per SIMD.
-template <int UPT, bool LOGITS>
+// Q8_0: two workgroups per CU, two waves per SIMD; PACK for at most 8
+// sequences.
+template <int UPT, bool LOGITS, bool PACK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mm_q8_head_kernel(HeadArgs a,
                                                                                                     int tiles_per_wg) {
-    mm_head_body<int8_t, UPT, LOGITS>(a, tiles_per_wg);
+    mm_head_body<int8_t, UPT, LOGITS, PACK>(a, tiles_per_wg);
 }
 
 // ----------------------------------------------------------------------------
@@ -862,8 +934,11 @@ template <typename HT, int UPT>
 static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 grid, size_t lds, bool logits,
                                    hipStream_t st) {
     if constexpr (sizeof(HT) == 1) {
-        return logits ? launch_head_k(mm_q8_head_kernel<UPT, true>, a, tiles_per_wg, grid, lds, st)
-                      : launch_head_k(mm_q8_head_kernel<UPT, false>, a, tiles_per_wg, grid, lds, st);
+        if (a.S <= 8)
+            return logits ? launch_head_k(mm_q8_head_kernel<UPT, true, true>, a, tiles_per_wg, grid, lds, st)
+                          : launch_head_k(mm_q8_head_kernel<UPT, false, true>, a, tiles_per_wg, grid, lds, st);
+        return logits ? launch_head_k(mm_q8_head_kernel<UPT, true, false>, a, tiles_per_wg, grid, lds, st)
+                      : launch_head_k(mm_q8_head_kernel<UPT, false, false>, a, tiles_per_wg, grid, lds, st);
     } else {
         return logits ? launch_head_k(mm_head_kernel<HT, UPT, true>, a, tiles_per_wg, grid, lds, st)
                       : launch_head_k(mm_head_kernel<HT, UPT, false>, a, tiles_per_wg, grid, lds, st);
@@ -871,11 +946,19 @@ static hipError_t launch_mm_head_t(const HeadArgs &a, int tiles_per_wg, dim3 gri
 }
 
 // Head workgroups of a launch and the 16-row tiles each takes.
+// Dynamic LDS of a launch: the staged activations.
+static size_t mm_head_lds(int head_dtype, const HeadArgs &a) {
+    const bool pack = head_dtype == MTP_Q8_0 && a.S <= 8;
+    return sizeof(u32x4_t) * (size_t)(pack ? 64 : 128) * (a.d / 32);
+}
+
 static void mm_head_grid(int head_dtype, const HeadArgs &a, int &n_wg, int &tiles_per_wg) {
-    // dynamic activation halves + the static transpose tiles (bf16) and reduction slots
-    const size_t tr = head_dtype == MTP_Q8_0 ? 1 : 4 * kTrSlots;
-    const size_t lds = sizeof(u32x4_t) * ((size_t)128 * (a.d / 32) + tr + 4 * 64) + 2048;
-    const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(4, (160 * 1024) / lds));
+    // activations + the static transpose tiles (bf16) and reduction slots; the
+    // Q8_0 kernel's registers hold two workgroups per CU at most
+    const bool q8 = head_dtype == MTP_Q8_0;
+    const size_t tr = q8 ? 1 : 4 * kTrSlots;
+    const size_t lds = mm_head_lds(head_dtype, a) + sizeof(u32x4_t) * (tr + 4 * 64) + 2048;
+    const int per_cu = (int)std::max<size_t>(1, std::min<size_t>(q8 ? 2 : 4, (160 * 1024) / lds));
     const int n_tiles = (a.V + 15) / 16;
     n_wg = std::min(256 * per_cu, (n_tiles + 3) / 4);
     tiles_per_wg = (n_tiles + n_wg - 1) / n_wg;
@@ -890,8 +973,8 @@ int mm_head_groups(int head_dtype, const HeadArgs &a) {
 
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a_in, bool logits, hipStream_t st) {
     HeadArgs a = a_in;
-    const int KS = a.d / 32, upt = a.d / (32 * kHeadUnit);
-    const size_t lds = sizeof(u32x4_t) * (size_t)128 * KS;
+    const int upt = a.d / (32 * kHeadUnit);
+    const size_t lds = mm_head_lds(head_dtype, a);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     int n_wg, tiles_per_wg;
     mm_head_grid(head_dtype, a, n_wg, tiles_per_wg);

@@ -69,18 +69,25 @@ def test_c4_q8_head_small_context(orc):
     _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
 
 
-def test_q8_head_ragged_vocab_several_and_one_sequence(orc):
+def _rows(out, idx):
+    return {k: (v[idx] if isinstance(v, np.ndarray) else v) for k, v in out.items()}
+
+
+def test_q8_head_ragged_vocab_packed_unpacked_and_one_sequence(orc):
     """The several-sequence Q8_0 head streams the head's unit-order copy,
-    whose last 16-row tile is padded with zero rows when V % 16 != 0; the
-    one-sequence head reads the row-major plane.  Both against the oracle,
-    and the same sequence alone and in the batch gives the same ids."""
-    log("case q8 ragged: V=262144-123, ctx=1500, S=5 and S=1, N=3")
-    w = syn.c4_longctx_q8(n_vocab=262144 - 123, ctx=1500, n_seq=5, n_steps=3)
-    g = GpuDrafter(w.model, 5, 3)
-    batch = g.run(w.draft)
-    _check(w, batch, orc.draft_block(w.model, w.draft))
-    one = g.run(w.draft, seq_idx=[3])
-    assert np.array_equal(one["drafts"][0], batch["drafts"][3])
+    whose last 16-row tile is padded with zero rows when V % 16 != 0.  Up
+    to 8 sequences share each MFMA between the activations' hi and lo
+    halves (packed), 9 to 16 take one MFMA per half (unpacked), and one
+    sequence runs the row-major one-sequence head.  All three against the
+    oracle on the same sequences."""
+    log("case q8 ragged: V=262144-123, ctx=1500, N=3; S=12 (unpacked), 5 (packed), 1")
+    w = syn.c4_longctx_q8(n_vocab=262144 - 123, ctx=1500, n_seq=12, n_steps=3)
+    ref = orc.draft_block(w.model, w.draft)
+    g = GpuDrafter(w.model, 12, 3)
+    _check(w, g.run(w.draft), ref)
+    few = [3, 7, 0, 11, 5]
+    _check(w, g.run(w.draft, seq_idx=few), _rows(ref, few))
+    _check(w, g.run(w.draft, seq_idx=[6]), _rows(ref, [6]))
 
 
 def test_chained_equals_step_by_step_on_gpu():
