@@ -212,7 +212,7 @@ def bench_sample(args, dev):
         step()
     v_ms, v_n = ctx.profile_read(mtp.MTP_PROF_VERIFY)
     ctx.profile(0)
-    avg_ms = v_ms / max(v_n, 1)
+    avg_ms = v_ms / n_diag                  # the call's kernels, summed
     achieved = bytes_step / (avg_ms * 1e-3) / 1e9
     out = {"metric": "verified draft tokens/s of exact temperature>0 verify", "value": S * (R - 1) / (ms * 1e-3),
            "unit": "draft tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -221,7 +221,7 @@ def bench_sample(args, dev):
            "hbm_gbps_step": bytes_step / (ms * 1e-3) / 1e9, "accepted_per_round": float(na.float().mean()),
            "roofline": {"bound": "hbm", "kernel": "sample_chunk_kernel + sample_row_kernel + sample_seq_kernel "
                                                  "(one mtp_verify_sample call)",
-                        "timing": f"HIP events around each call over {n_diag} calls after the timed region",
+                        "timing": f"start/stop HIP events of each kernel launch, summed per call, over {n_diag} calls after the timed region",
                         "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                         "traffic": None, "bytes_per_launch": bytes_step, "avg_launch_ms": avg_ms, "launches": v_n}}
     ctx.close()
@@ -268,7 +268,7 @@ def bench_hidden(args, dev):
         step()
     v_ms, v_n = ctx.profile_read(mtp.MTP_PROF_VERIFY)
     ctx.profile(0)
-    avg_ms = v_ms / max(v_n, 1)
+    avg_ms = v_ms / n_diag                  # the call's kernels, summed
     alg_bytes = V * d * 2 + S * R * d * 4         # the head once + the hidden rows
     achieved = alg_bytes / (avg_ms * 1e-3) / 1e9
     out = {"metric": "verified rows/s of greedy verify from hidden states (fused target head + argmax)",
@@ -278,7 +278,7 @@ def bench_hidden(args, dev):
            "config": {"workload": WORKLOADS["c8"][1], "n_seq": S, "rows_per_seq": R, "d": d, "n_vocab": V},
            "roofline": {"bound": "hbm", "kernel": "hv_prep_kernel + hv_head_kernel + verify_prefix_kernel "
                                                  "(one entry-point call)",
-                        "timing": f"HIP events around each call over {n_diag} calls after the timed region",
+                        "timing": f"start/stop HIP events of each kernel launch, summed per call, over {n_diag} calls after the timed region",
                         "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": achieved / PEAK_HBM_GBPS,
                         "traffic": head_traffic_from_counters(HV_COUNTERS_FILE, HV_SOURCES),
@@ -374,10 +374,11 @@ def bench_draft(args, dev):
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
-    # Kernel timing: the same steps again with HIP events around every launch
-    # of one kernel class on the library's stream (events make the library
-    # launch the chain kernel by kernel instead of replaying its captured
-    # graph; the kernels themselves are the same).
+    # Kernel timing: the same steps again, each launch of one kernel class
+    # carrying start/stop HIP events that the runtime sets when the kernel
+    # starts and finishes running on the library's stream (timing makes the
+    # library launch the chain kernel by kernel instead of replaying its
+    # captured graph; the kernels themselves are the same).
     def class_time(cls, n):
         ctx.profile(1 << cls)
         for _ in range(n):
@@ -411,6 +412,8 @@ def bench_draft(args, dev):
         head_launch_bytes -= m.n_centroids * m.d_model * (4 if m.w_dtype == syn.F32 else 2)
     if m.n_centroids:
         head_name = "cand_head_kernel (centroid head candidate rows + argmax + post-proj)"
+    elif S >= 2 and m.head_dtype == syn.Q8_0:
+        head_name = "mm_q8_head_kernel (final RMSNorm + matrix-core Q8_0 LM head + argmax + post-proj)"
     elif S >= 2 and m.head_dtype != syn.F32:
         head_name = "mm_head_kernel (final RMSNorm + matrix-core LM head + argmax + post-proj)"
     else:
@@ -422,14 +425,14 @@ def bench_draft(args, dev):
         avg = total_ms / max(n, 1)
         ach = bytes_per_launch / (avg * 1e-3) / 1e9
         cf = counters_file(key, args.workload)
-        return {"bound": "hbm", "kernel": name, "timing": f"HIP events around each launch over {args.steps} "
+        return {"bound": "hbm", "kernel": name, "timing": f"start/stop HIP events of each launch over {args.steps} "
                 "steps after the timed region, on the library's stream",
                 "achieved": ach, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
                 "traffic": head_traffic_from_counters(cf, sources), "traffic_source": cf.name,
                 "bytes_per_launch": bytes_per_launch, "avg_launch_ms": avg, "launches": n}
     head_key = head_name.split()[0]
     r_head = roofline(head_name, head_key, head_ms, head_n, head_launch_bytes,
-                      MM_SOURCES if head_key == "mm_head_kernel" else HEAD_SOURCES)
+                      MM_SOURCES if head_key in ("mm_head_kernel", "mm_q8_head_kernel") else HEAD_SOURCES)
     # one attention launch reads one block's visible K and V of every sequence
     r_attn = roofline(attn_name, attn_name.split()[0], attn_ms, attn_n, kvb // m.n_blocks, ATTN_SOURCES)
     if attn_ms > head_ms:

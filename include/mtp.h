@@ -324,10 +324,12 @@ int mtp_verify_sample_hidden(mtp_ctx *ctx, int32_t n_seq, int32_t n_draft, const
 /* Optional HIP-event timing of the kernels one context launches, for
    measurement tools.  mtp_profile_enable waits for the stream, clears all
    counters and enables the classes whose bit (1 << class) is set in mask
-   (0 disables timing).  While enabled, every launch of an enabled class is
-   bracketed by two events on the context's stream.  mtp_profile_read waits
-   for the stream, returns the summed duration (ms) and launch count of one
-   class since the last enable/read, and resets that class. */
+   (0 disables timing).  While enabled, calls launch their kernels one by one
+   (not as a replayed graph) and every kernel of an enabled class carries a
+   start and a stop event that the runtime sets when that kernel starts and
+   finishes running, so a duration holds no dispatch time.  mtp_profile_read
+   waits for the stream, returns the summed duration (ms) and the number of
+   kernels of one class since the last enable/read, and resets that class. */
 typedef enum mtp_prof_class {
     MTP_PROF_HEAD = 0,      /* final norm + LM head + argmax + post-projection */
     MTP_PROF_ATTN = 1,      /* split-K attention (partials per split) */

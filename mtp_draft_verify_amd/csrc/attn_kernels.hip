@@ -524,15 +524,15 @@ hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream
     const int G = a.Hq / a.Hkv;
 #define MTP_ATTN_CASE(KT, HDV, GV)                                                                  \
     if (a.hd == HDV && G == GV) {                                                                   \
-        hipLaunchKernelGGL((attn_kernel<KT, HDV / 16, GV>), grid, dim3(kBlock), 0, st, a);          \
+        mtp_launch((attn_kernel<KT, HDV / 16, GV>), grid, dim3(kBlock), 0, st, a);          \
         return hipGetLastError();                                                                   \
     }
 #define MTP_ATTN_MM(HDV, GV)                                                                        \
     if (a.hd == HDV && G == GV) {                                                                   \
         if (a.stream_kv)                                                                            \
-            hipLaunchKernelGGL((attn_mm_kernel<HDV, GV, true>), grid, dim3(kBlock), 0, st, a);      \
+            mtp_launch((attn_mm_kernel<HDV, GV, true>), grid, dim3(kBlock), 0, st, a);      \
         else                                                                                        \
-            hipLaunchKernelGGL((attn_mm_kernel<HDV, GV, false>), grid, dim3(kBlock), 0, st, a);     \
+            mtp_launch((attn_mm_kernel<HDV, GV, false>), grid, dim3(kBlock), 0, st, a);     \
         return hipGetLastError();                                                                   \
     }
     if (kv_dtype == MTP_BF16) {
@@ -658,9 +658,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 hipError_t launch_merge(const MergeArgs &a, hipStream_t st) {
     if (a.hd % 64) return hipErrorInvalidValue;
     if (a.S == 1) {
-        hipLaunchKernelGGL(merge_kernel<1>, dim3((a.hd / 16) * a.Hq * a.S), dim3(kBlock), 0, st, a);
+        mtp_launch(merge_kernel<1>, dim3((a.hd / 16) * a.Hq * a.S), dim3(kBlock), 0, st, a);
     } else {
-        hipLaunchKernelGGL(merge_kernel<4>, dim3((a.hd / 64) * a.Hq * a.S), dim3(kBlock), 0, st, a);
+        mtp_launch(merge_kernel<4>, dim3((a.hd / 64) * a.Hq * a.S), dim3(kBlock), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -329,7 +329,7 @@ static hipError_t launch_gemv_nv(int in_mode, int epi, const GemvArgs &a, int n_
     if (in_mode == I && epi == E) {                                                                     \
         hipError_t e0 = allow_dynamic_lds(gemv_kernel<WT, NV, I, E, ONE>, lds);                         \
         if (e0 != hipSuccess) return e0;                                                                \
-        hipLaunchKernelGGL((gemv_kernel<WT, NV, I, E, ONE>), dim3(n_wg), dim3(kBlock), lds, st, a);    \
+        mtp_launch((gemv_kernel<WT, NV, I, E, ONE>), dim3(n_wg), dim3(kBlock), lds, st, a);    \
         return hipGetLastError();                                                                       \
     }
     MTP_GEMV_CASE(IN_EMBED, EPI_STORE)

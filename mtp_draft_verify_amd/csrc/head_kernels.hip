@@ -279,7 +279,7 @@ static hipError_t launch_head_c(const HeadArgs &a, int w_dtype, int n_post_wg, h
     if (nv <= N) {                                                                                     \
         hipError_t e0 = allow_dynamic_lds(head_kernel<HT, N, ONE, CONF, LOGITS>, lds);                 \
         if (e0 != hipSuccess) return e0;                                                               \
-        hipLaunchKernelGGL((head_kernel<HT, N, ONE, CONF, LOGITS>), grid, dim3(kBlock), lds, st, a,     \
+        mtp_launch((head_kernel<HT, N, ONE, CONF, LOGITS>), grid, dim3(kBlock), lds, st, a,     \
                            w_dtype);                                                                   \
         return hipGetLastError();                                                                      \
     }
@@ -449,7 +449,7 @@ static hipError_t launch_cand_t(const HeadArgs &a_in, int w_dtype, int n_post_wg
     if (nv <= N) {                                                                                     \
         hipError_t e0 = allow_dynamic_lds(cand_head_kernel<HT, N, CONF>, lds);                         \
         if (e0 != hipSuccess) return e0;                                                               \
-        hipLaunchKernelGGL((cand_head_kernel<HT, N, CONF>), grid, dim3(kBlock), lds, st, a, w_dtype, chunks); \
+        mtp_launch((cand_head_kernel<HT, N, CONF>), grid, dim3(kBlock), lds, st, a, w_dtype, chunks); \
         return hipGetLastError();                                                                      \
     }
     MTP_CAND_CASE(1)

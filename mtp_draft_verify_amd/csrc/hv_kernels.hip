@@ -311,7 +311,7 @@ size_t hv_plane_bytes(int32_t d) { return sizeof(u32x4_t) * (size_t)hv_chunk_slo
 
 template <int RG, bool LOGITS>
 static hipError_t launch_hv_pass(const HvArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(hv_prep_kernel<RG>, dim3(16 * RG), dim3(256), 0, st, a);
+    mtp_launch(hv_prep_kernel<RG>, dim3(16 * RG), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t lds = 2 * sizeof(u32x4_t) * (size_t)hv_chunk_slots<RG>();
@@ -324,7 +324,7 @@ static hipError_t launch_hv_pass(const HvArgs &a, hipStream_t st) {
     int n_wg = std::min(256 * per_cu, n_groups);
     const int gpw = (n_groups + n_wg - 1) / n_wg;
     n_wg = (n_groups + gpw - 1) / gpw;
-    hipLaunchKernelGGL((hv_head_kernel<RG, kHvTW, LOGITS>), dim3(n_wg), dim3(256), lds, st, a, gpw);
+    mtp_launch((hv_head_kernel<RG, kHvTW, LOGITS>), dim3(n_wg), dim3(256), lds, st, a, gpw);
     return hipGetLastError();
 }
 

@@ -884,10 +884,10 @@ hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart,
         const dim3 grid((a.M + 15) / 16, nsplit);
 #define MTP_MM_SPLIT(I, E)                                                                             \
         if (in_mode == I && epi == E) {                                                                \
-            hipLaunchKernelGGL((mm_gemv_kernel<4, I, E, true>), grid, dim3(256), 0, st, a, kpart);     \
+            mtp_launch((mm_gemv_kernel<4, I, E, true>), grid, dim3(256), 0, st, a, kpart);     \
             hipError_t e0 = hipGetLastError();                                                         \
             if (e0 != hipSuccess) return e0;                                                           \
-            hipLaunchKernelGGL((mm_splitk_reduce<E>), dim3((a.S * a.M + 255) / 256), dim3(256), 0, st, \
+            mtp_launch((mm_splitk_reduce<E>), dim3((a.S * a.M + 255) / 256), dim3(256), 0, st, \
                                a, (const float *)kpart, nsplit);                                        \
             return hipGetLastError();                                                                  \
         }
@@ -899,7 +899,7 @@ hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart,
     const dim3 grid((a.M + 15) / 16);
 #define MTP_MM_CASE(NW, I, E)                                                                          \
     if (nw == NW && in_mode == I && epi == E) {                                                        \
-        hipLaunchKernelGGL((mm_gemv_kernel<NW, I, E, false>), grid, dim3(NW * 64), 0, st, a,           \
+        mtp_launch((mm_gemv_kernel<NW, I, E, false>), grid, dim3(NW * 64), 0, st, a,           \
                            (float *)nullptr);                                                          \
         return hipGetLastError();                                                                      \
     }
@@ -926,7 +926,7 @@ template <typename K>
 static hipError_t launch_head_k(K kernel, const HeadArgs &a, int tiles_per_wg, dim3 grid, size_t lds, hipStream_t st) {
     hipError_t e = allow_dynamic_lds(kernel, lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kernel, grid, dim3(256), lds, st, a, tiles_per_wg);
+    mtp_launch(kernel, grid, dim3(256), lds, st, a, tiles_per_wg);
     return hipGetLastError();
 }
 

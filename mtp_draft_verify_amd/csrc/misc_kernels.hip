@@ -14,7 +14,7 @@ __global__ void finish_drafts_kernel(const uint64_t *keys, int32_t S, const Call
 
 hipError_t launch_finish_drafts(const uint64_t *keys, int32_t S, const CallIO *io, int32_t stride, int32_t col,
                                 hipStream_t st) {
-    hipLaunchKernelGGL(finish_drafts_kernel, dim3((S + 63) / 64), dim3(64), 0, st, keys, S, io, stride, col);
+    mtp_launch(finish_drafts_kernel, dim3((S + 63) / 64), dim3(64), 0, st, keys, S, io, stride, col);
     return hipGetLastError();
 }
 
@@ -37,7 +37,7 @@ __global__ void q8_repack_kernel(const uint8_t *blocks, int64_t n_blocks, int8_t
 hipError_t launch_q8_repack(const uint8_t *blocks, int64_t rows, int32_t cols, int8_t *q, uint16_t *s,
                             hipStream_t st) {
     const int64_t nb = rows * (cols / 32);
-    hipLaunchKernelGGL(q8_repack_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, blocks, nb, q, s);
+    mtp_launch(q8_repack_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, blocks, nb, q, s);
     return hipGetLastError();
 }
 
@@ -90,7 +90,7 @@ size_t q8_unit_order_bytes(int64_t rows, int32_t cols) {
 hipError_t launch_q8_unit_order(const uint8_t *blocks, int64_t rows, int32_t cols, uint8_t *out, hipStream_t st) {
     if (cols % 256 != 0) return hipErrorInvalidValue;
     const int64_t n_pieces = (int64_t)(q8_unit_order_bytes(rows, cols) / 16);
-    hipLaunchKernelGGL(q8_unit_order_kernel, dim3((unsigned)((n_pieces + 255) / 256)), dim3(256), 0, st, blocks, rows,
+    mtp_launch(q8_unit_order_kernel, dim3((unsigned)((n_pieces + 255) / 256)), dim3(256), 0, st, blocks, rows,
                        cols, n_pieces, out);
     return hipGetLastError();
 }
@@ -101,7 +101,7 @@ __global__ void clear_u64_kernel(uint64_t *p, int64_t n) {
 }
 
 hipError_t launch_clear_u64(uint64_t *p, int64_t n, hipStream_t st) {
-    hipLaunchKernelGGL(clear_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+    mtp_launch(clear_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(256) void conf_finish_kernel(const ConfPart *part, 
 hipError_t launch_conf_finish(const ConfPart *part, int32_t S, int32_t N, int32_t n_part, int64_t step_stride,
                               const CallIO *io, hipStream_t st) {
     if (N > 64 || n_part > kConfSlots) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(conf_finish_kernel, dim3(S), dim3(256), 0, st, part, N, n_part, step_stride, io);
+    mtp_launch(conf_finish_kernel, dim3(S), dim3(256), 0, st, part, N, n_part, step_stride, io);
     return hipGetLastError();
 }
 
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void centroid_topk_kernel(const float *cl, int
 hipError_t launch_centroid_topk(const float *cl, int32_t n_centroids, int32_t k, int32_t S, int32_t *cand,
                                 hipStream_t st) {
     if (n_centroids > kMaxCentroids || k < 1 || k > n_centroids || k > kMaxCentroidTopK) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(centroid_topk_kernel, dim3(S), dim3(256), 0, st, cl, n_centroids, k, cand);
+    mtp_launch(centroid_topk_kernel, dim3(S), dim3(256), 0, st, cl, n_centroids, k, cand);
     return hipGetLastError();
 }
 
@@ -276,7 +276,7 @@ __global__ void fill_logits_kernel(const CallIO *io, int32_t S, int32_t N, int32
 
 hipError_t launch_fill_logits(const CallIO *io, int32_t S, int32_t N, int32_t V, int32_t step, float v,
                               hipStream_t st) {
-    hipLaunchKernelGGL(fill_logits_kernel, dim3(1024), dim3(256), 0, st, io, S, N, V, step, v);
+    mtp_launch(fill_logits_kernel, dim3(1024), dim3(256), 0, st, io, S, N, V, step, v);
     return hipGetLastError();
 }
 
@@ -287,7 +287,7 @@ __global__ void rope_init_kernel(double *inv_freq, int32_t hd, double theta) {
 }
 
 hipError_t launch_rope_init(double *inv_freq, int32_t hd, float theta, hipStream_t st) {
-    hipLaunchKernelGGL(rope_init_kernel, dim3((hd / 2 + 63) / 64), dim3(64), 0, st, inv_freq, hd, (double)theta);
+    mtp_launch(rope_init_kernel, dim3((hd / 2 + 63) / 64), dim3(64), 0, st, inv_freq, hd, (double)theta);
     return hipGetLastError();
 }
 

@@ -363,27 +363,46 @@ extern "C" void mtp_ctx_destroy(mtp_ctx *c) {
 // ---------------------------------------------------------------------------
 // optional event timing
 // ---------------------------------------------------------------------------
-namespace {
-struct ProfScope {
+namespace mtp {
+struct LaunchTimer {
     mtp_ctx *c;
     int cls;
-    std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
-    ProfScope(mtp_ctx *ctx, int k) : c(ctx), cls(k) {
-        if (!(c->prof_mask & (1 << cls))) return;
-        if (c->prof_pool.empty()) {
-            hipEvent_t a, b;
-            if (hipEventCreate(&a) != hipSuccess) return;
-            if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
-            c->prof_pool.emplace_back(a, b);
+};
+thread_local LaunchTimer *g_launch_timer = nullptr;
+
+bool launch_timer_take(LaunchTimer *t, hipEvent_t *start, hipEvent_t *stop) {
+    mtp_ctx *c = t->c;
+    if (c->prof_pool.empty()) {
+        hipEvent_t a, b;
+        if (hipEventCreate(&a) != hipSuccess) return false;
+        if (hipEventCreate(&b) != hipSuccess) {
+            (void)hipEventDestroy(a);
+            return false;
         }
-        ev = c->prof_pool.back();
-        c->prof_pool.pop_back();
-        (void)hipEventRecord(ev.first, c->stream);
+        c->prof_pool.emplace_back(a, b);
+    }
+    *start = c->prof_pool.back().first;
+    *stop = c->prof_pool.back().second;
+    c->prof_pool.pop_back();
+    return true;
+}
+
+void launch_timer_done(LaunchTimer *t, hipEvent_t start, hipEvent_t stop) {
+    t->c->prof_pending[t->cls].emplace_back(start, stop);
+}
+}  // namespace mtp
+
+namespace {
+// Times every kernel launched in its scope as class k (when k is enabled).
+struct ProfScope {
+    LaunchTimer timer;
+    LaunchTimer *prev;
+    bool on;
+    ProfScope(mtp_ctx *ctx, int k) : timer{ctx, k}, prev(g_launch_timer), on((ctx->prof_mask >> k) & 1) {
+        if (on) g_launch_timer = &timer;
     }
     ~ProfScope() {
-        if (!ev.first) return;
-        (void)hipEventRecord(ev.second, c->stream);
-        c->prof_pending[cls].push_back(ev);
+        if (on) g_launch_timer = prev;
     }
 };
 }  // namespace
@@ -773,7 +792,7 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
 
     hipError_t e;
     if (c->prof_mask) {
-        e = enqueue_chain(c, sh, c->stream);        // event timing needs individual launches
+        e = enqueue_chain(c, sh, c->stream);        // kernel timing takes individual launches
     } else {
         hipGraphExec_t exec = chain_graph(c, sh);
         e = exec ? hipGraphLaunch(exec, c->stream) : enqueue_chain(c, sh, c->stream);

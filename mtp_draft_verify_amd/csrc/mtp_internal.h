@@ -1,5 +1,6 @@
 // mtp_internal.h -- structures shared by the host runtime and the kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -159,6 +160,31 @@ struct MergeArgs {
     int32_t Hq, Hkv, hd, S, src;
     const SeqParams *seqs;
 };
+
+// Kernel timing (mtp_profile_enable).  While a timed kernel class is being
+// enqueued on this thread, g_launch_timer is set and every launch takes a
+// start and a stop event of its own, which the runtime sets when that
+// kernel starts and finishes running (no dispatch time between them).
+struct LaunchTimer;
+extern thread_local LaunchTimer *g_launch_timer;
+bool launch_timer_take(LaunchTimer *t, hipEvent_t *start, hipEvent_t *stop);
+void launch_timer_done(LaunchTimer *t, hipEvent_t start, hipEvent_t stop);
+
+// Every kernel of the library is launched through here (arguments converted
+// to the kernel's parameter types).
+template <typename... P, typename... A>
+inline void mtp_launch(void (*kernel)(P...), const dim3 &grid, const dim3 &block, size_t shmem, hipStream_t st,
+                       A &&...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    LaunchTimer *t = g_launch_timer;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (t && launch_timer_take(t, &e0, &e1)) {
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, st, e0, e1, 0u, static_cast<P>(args)...);
+        launch_timer_done(t, e0, e1);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, st, static_cast<P>(args)...);
+    }
+}
 
 // launchers (defined with their kernels; all enqueue on `st`)
 hipError_t launch_gemv(int w_dtype, int in_mode, int epi, const GemvArgs &a, int n_wg, hipStream_t st);

@@ -765,15 +765,15 @@ hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st) {
     const int n_chunk = (a.V + kChunk - 1) / kChunk;
     if ((int64_t)rows * n_chunk > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (a.top_k > 0) {
-        hipLaunchKernelGGL(sample_topk_kernel, dim3(rows), dim3(kBlock), 0, st, a);
+        mtp_launch(sample_topk_kernel, dim3(rows), dim3(kBlock), 0, st, a);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     // 4 logits per load when every row starts on a 16-byte boundary
     const bool v4 = a.V % 4 == 0 && ((uintptr_t)a.p_logits & 15) == 0 && ((uintptr_t)a.q_logits & 15) == 0;
-    if (v4) hipLaunchKernelGGL(sample_chunk_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    else hipLaunchKernelGGL(sample_chunk_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
-    hipLaunchKernelGGL(sample_row_kernel, dim3(rows), dim3(kRowThreads), 0, st, a);
-    hipLaunchKernelGGL(sample_seq_kernel, dim3(a.S), dim3(kRowThreads), 0, st, a);
+    if (v4) mtp_launch(sample_chunk_kernel<4>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    else mtp_launch(sample_chunk_kernel<1>, dim3(rows * n_chunk), dim3(kBlock), 0, st, a, n_chunk);
+    mtp_launch(sample_row_kernel, dim3(rows), dim3(kRowThreads), 0, st, a);
+    mtp_launch(sample_seq_kernel, dim3(a.S), dim3(kRowThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int3
     const int64_t n_chunk = (V + kVerifyChunk - 1) / kVerifyChunk;
     const int64_t n_wg = n_chunk * (int64_t)(N + 1) * S;
     if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(verify_argmax_kernel, dim3((unsigned)n_wg), dim3(kBlock), 0, st, logits, (int32_t)n_chunk, V,
+    mtp_launch(verify_argmax_kernel, dim3((unsigned)n_wg), dim3(kBlock), 0, st, logits, (int32_t)n_chunk, V,
                        keys);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -94,7 +94,7 @@ hipError_t launch_verify_greedy(const float *logits, const int32_t *drafts, int3
 
 hipError_t launch_verify_prefix(const int32_t *drafts, int32_t S, int32_t N, uint64_t *keys, int32_t *out_tokens,
                                 int32_t *out_n_accept, hipStream_t st) {
-    hipLaunchKernelGGL(verify_prefix_kernel, dim3((S + 63) / 64), dim3(64), 0, st, drafts, S, N, keys, out_tokens,
+    mtp_launch(verify_prefix_kernel, dim3((S + 63) / 64), dim3(64), 0, st, drafts, S, N, keys, out_tokens,
                        out_n_accept);
     return hipGetLastError();
 }

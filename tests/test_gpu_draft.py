@@ -194,7 +194,7 @@ def test_captured_chain_replays_match_direct_launches():
         g.ctx.profile(0)
         replay = g.run(w.draft, last_tok=(w.draft.last_tok + shift) % w.model.n_vocab,
                        h_prev=w.draft.h_prev * (1 + 0.1 * shift))
-        g.ctx.profile(1 << mtp.MTP_PROF_GEMV)     # event timing forces individual launches
+        g.ctx.profile(1 << mtp.MTP_PROF_GEMV)     # kernel timing launches kernel by kernel
         direct = g.run(w.draft, last_tok=(w.draft.last_tok + shift) % w.model.n_vocab,
                        h_prev=w.draft.h_prev * (1 + 0.1 * shift))
         g.ctx.profile(0)
