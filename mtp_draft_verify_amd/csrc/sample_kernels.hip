@@ -174,16 +174,65 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t *red) {
 struct CtxLds {
     int32_t tok[kMaxCtx];
     uint32_t bits[kChunk / 32];
+    uint16_t cnt[kChunk];   // occurrences in the context of the token at each chunk position (where bits is set)
 };
 
-__device__ void load_ctx(const SampleArgs &a, int s, int i, int c0, int nbits, CtxLds &cl, int &n_ctx) {
-    n_ctx = ctx_len(a, s, i);
+// Scalar load of a value whose address is the same in every lane.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
+// The penalty context of row (s, i), in two parts around the chunk's logit
+// loads.  A wave's vector loads return in order, so context reads issued
+// behind the logits would wait for all of them: ctx_request reads the
+// context's length (one scalar load) and requests its tokens (thread j
+// holds tokens j, j + kBlock, ...) before the logits are requested;
+// ctx_store then writes them to LDS (cl.tok) with the bitmap of those
+// inside the chunk [c0, c0 + nbits) and their counts.
+struct CtxReq {
+    int32_t t[kMaxCtx / kBlock];
+    int n;
+};
+
+__device__ __forceinline__ void ctx_request(const SampleArgs &a, int s, int i, CtxReq &r) {
+    const int hlen = a.history_len ? min(max(ld_uniform(a.history_len + s), 0), a.hstride) : 0;
+    const int total = hlen + i;
+    r.n = a.last_n <= 0 ? 0 : min(a.last_n, total);
+    const int p0 = total - r.n;             // the context's first position
+#pragma unroll
+    for (int u = 0; u < kMaxCtx / kBlock; ++u) {
+        const int j = (int)threadIdx.x + kBlock * u;
+        r.t[u] = 0;
+        if (j < r.n) {
+            const int pos = p0 + j;
+            r.t[u] = pos < hlen ? a.history[(int64_t)s * a.hstride + pos] : a.drafts[(int64_t)s * a.N + (pos - hlen)];
+        }
+    }
+}
+
+__device__ void ctx_store(const CtxReq &r, int c0, int nbits, CtxLds &cl) {
     for (int w = threadIdx.x; w < kChunk / 32; w += kBlock) cl.bits[w] = 0u;
     __syncthreads();
-    for (int j = threadIdx.x; j < n_ctx; j += kBlock) {
-        const int32_t t = ctx_token(a, s, i, n_ctx, j);
-        cl.tok[j] = t;
-        if (t >= c0 && t < c0 + nbits) atomicOr(&cl.bits[(t - c0) >> 5], 1u << ((t - c0) & 31));
+#pragma unroll
+    for (int u = 0; u < kMaxCtx / kBlock; ++u) {
+        const int j = (int)threadIdx.x + kBlock * u, t = r.t[u];
+        if (j < r.n) {
+            cl.tok[j] = t;
+            if (t >= c0 && t < c0 + nbits) atomicOr(&cl.bits[(t - c0) >> 5], 1u << ((t - c0) & 31));
+        }
+    }
+    __syncthreads();
+    // each in-chunk occurrence counts its token once (equal tokens store
+    // equal counts), so a penalised logit later costs one LDS read
+#pragma unroll
+    for (int u = 0; u < kMaxCtx / kBlock; ++u) {
+        const int j = (int)threadIdx.x + kBlock * u, t = r.t[u];
+        if (j < r.n && t >= c0 && t < c0 + nbits) {
+            int c = 0;
+            for (int jj = 0; jj < r.n; ++jj) c += cl.tok[jj] == t;
+            cl.cnt[t - c0] = (uint16_t)c;
+        }
     }
     __syncthreads();
 }
@@ -217,18 +266,13 @@ __device__ __forceinline__ int sorted_count(const int32_t *tok, int n, int32_t t
     return c;
 }
 
-__device__ __forceinline__ int ctx_count(const CtxLds &cl, int n_ctx, int32_t t) {
-    int c = 0;
-    for (int j = 0; j < n_ctx; ++j) c += cl.tok[j] == t;
-    return c;
-}
-
 // value of token t of a row (raw logit `raw`) after top-k and penalties (NaN
-// when top-k drops it)
+// when top-k drops it); member: t is in the penalty context, whose counts
+// ctx_store left per position of the chunk starting at c0
 __device__ __forceinline__ float raw_value(const SampleArgs &a, float raw, int32_t t, bool member, const CtxLds &cl,
-                                           int n_ctx, uint64_t topk_key) {
+                                           int c0, uint64_t topk_key) {
     if (a.top_k > 0 && tok_key(raw, t) < topk_key) return __int_as_float(0x7FC00000);
-    return chain_value(a, raw, member ? ctx_count(cl, n_ctx, t) : 0);
+    return chain_value(a, raw, member ? (int)cl.cnt[t - c0] : 0);
 }
 
 // The chunk passes walk their kChunk tokens in batches of KB = 32 / E loads
@@ -314,7 +358,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
 // The single pass over the logits: the chunk's row max contribution, then
 // its part of a superset of the row's min-p survivors (token, v).
 template <int E>
-__global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
     constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     __shared__ float red[4];
@@ -322,14 +366,14 @@ __global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_c
     const int row = blockIdx.x / n_chunk, chunk = blockIdx.x - row * n_chunk;
     const RowRef rr = row_ref(a, row);
     const int c0 = chunk * kChunk, c1 = min(a.V, c0 + kChunk);
-    // the whole chunk in registers: the first batch does not depend on the
-    // context, so it is requested before the context is read
+    // the penalty context's tokens are requested first, then the whole chunk
+    // (into registers)
+    CtxReq creq;
+    ctx_request(a, rr.s, rr.i, creq);
     float raw[NB][KB][E];
-    load_batch<E, KB>(rr.z, c0, c1, raw[0]);
-    int n_ctx;
-    load_ctx(a, rr.s, rr.i, c0, c1 - c0, cl, n_ctx);
 #pragma unroll
-    for (int b = 1; b < NB; ++b) load_batch<E, KB>(rr.z, c0 + b * BT, c1, raw[b]);
+    for (int b = 0; b < NB; ++b) load_batch<E, KB>(rr.z, c0 + b * BT, c1, raw[b]);
+    ctx_store(creq, c0, c1 - c0, cl);
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     // Context tokens take the full chain; every other token's value is
     // fl(z / temp), which does not decrease as z grows, so the largest of
@@ -347,7 +391,7 @@ __global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_c
                     const float z = raw[b][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
                     if (member) {
-                        const float v = raw_value(a, z, t, true, cl, n_ctx, tk);
+                        const float v = raw_value(a, z, t, true, cl, c0, tk);
                         if (v == v) mx = fmaxf(mx, v);
                     } else if (!(a.top_k > 0 && tok_key(z, t) < tk)) {
                         mz = fmaxf(mz, z);
@@ -391,7 +435,7 @@ __global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_c
                     const float z = raw[b][k][e];
                     const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
                     if (member || z >= zlo) {
-                        const float v = raw_value(a, z, t, member, cl, n_ctx, tk);
+                        const float v = raw_value(a, z, t, member, cl, c0, tk);
                         if (v == v && expf(v - ref) >= a.min_p) kmask |= 1u << ((b * KB + k) * E + e);
                     }
                 }
@@ -431,7 +475,7 @@ __global__ __launch_bounds__(256) void sample_chunk_kernel(SampleArgs a, int n_c
                 const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
                 if (slot < a.cap) {
                     a.cand_id[(int64_t)row * a.cap + slot] = t;
-                    a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, raw[b][k][e], t, member, cl, n_ctx, tk);
+                    a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, raw[b][k][e], t, member, cl, c0, tk);
                 }
                 ++slot;
             }
@@ -445,12 +489,10 @@ static constexpr int kSortMax = 4096;
 // broad row (more candidates than kSortMax) makes them walk the whole
 // vocabulary several times, so they take 16 waves.
 static constexpr int kRowThreads = 1024;
-static constexpr int kPrefixBlocks = 256;   // blocks of the sorted candidates' prefix sums
 
 __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     constexpr int NT = kRowThreads;
     __shared__ uint64_t keys[kSortMax];
-    __shared__ float part[kPrefixBlocks];
     __shared__ float red[NT / 64];
     __shared__ int cut_sh, nkey_sh;
     __shared__ uint64_t hist[256], scal[4], red64[NT / 64];
@@ -517,26 +559,36 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
                 __syncthreads();
             }
         }
-        // inclusive prefix sums of e in sorted order: contiguous per-thread
-        // blocks, then a serial scan of the block totals (fixed order)
-        // (kPrefixBlocks contiguous blocks, whatever the workgroup size)
-        constexpr int PB = kPrefixBlocks;
-        const int per = (n + PB - 1) / PB;
-        const int b0 = tid < PB ? tid * per : n, b1 = min(n, b0 + per);
-        float run = 0.f;
-        for (int j = b0; j < b1; ++j) run += fkey_inv((uint32_t)(keys[j] >> 32));
-        if (tid < PB) part[tid] = run;
+        // prefix sums of e in sorted order, in a fixed order: thread tid sums
+        // its contiguous block of `per` entries, the block sums are scanned
+        // within each wave (shuffles) and across the waves (LDS), and the
+        // top-p cut and the kept prefix's normaliser both come from that one
+        // running sum
+        const int per = (n + NT - 1) / NT;
+        const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+        const int lane = tid & 63, wid = tid >> 6;
+        float bs = 0.f;
+        for (int j = b0; j < b1; ++j) bs += fkey_inv((uint32_t)(keys[j] >> 32));
+        float inc = bs;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(inc, off);
+            if (lane >= off) inc += y;
+        }
+        float excl = __shfl_up(inc, 1);
+        if (lane == 0) excl = 0.f;
+        if (lane == 63) red[wid] = inc;
         if (tid == 0) cut_sh = n - 1;
         __syncthreads();
-        if (tid == 0) {
-            float acc = 0.f;
-            for (int b = 0; b < PB; ++b) { const float t = part[b]; part[b] = acc; acc += t; }
-            red[0] = acc;
+        float base = 0.f, Z2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w) {
+            if (w < wid) base += red[w];
+            Z2 += red[w];
         }
-        __syncthreads();
-        const float Z2 = red[0];
-        if (a.top_p < 1.f && tid < PB) {
-            float cum = part[tid];
+        const float start = base + excl;    // the sum of all entries before this thread's block
+        if (a.top_p < 1.f) {
+            float cum = start;
             for (int j = b0; j < b1; ++j) {
                 cum += fkey_inv((uint32_t)(keys[j] >> 32));
                 if (cum / Z2 >= a.top_p) { atomicMin(&cut_sh, j); break; }
@@ -544,11 +596,10 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
         }
         __syncthreads();
         const int cut = cut_sh;
-        // normaliser of the kept prefix, in the same summation order
-        if (tid == 0) {
-            const int tb = cut / per;
-            float z = part[tb];
-            for (int j = tb * per; j <= cut; ++j) z += fkey_inv((uint32_t)(keys[j] >> 32));
+        // normaliser of the kept prefix: the running sum at the cut
+        if (cut >= b0 && cut < b1) {
+            float z = start;
+            for (int j = b0; j <= cut; ++j) z += fkey_inv((uint32_t)(keys[j] >> 32));
             st.Z = z;
             st.tau = keys[cut];
             st.n_keep = cut + 1;
