@@ -90,6 +90,18 @@ def test_q8_head_ragged_vocab_packed_unpacked_and_one_sequence(orc):
     _check(w, g.run(w.draft, seq_idx=[6]), _rows(ref, [6]))
 
 
+@pytest.mark.parametrize("d_model,n_seq", [(256, 5), (256, 12), (512, 7), (512, 11), (288, 6)])
+def test_q8_head_widths(orc, d_model, n_seq):
+    """The several-sequence Q8_0 head at one and two 256-column units per
+    tile (d = 256, 512; packed at <= 8 sequences, unpacked above), and at a
+    width that is not a multiple of 256 (d = 288: no unit-order copy, the
+    row-major head instead), on a ragged vocabulary."""
+    log(f"case q8 width: d={d_model}, S={n_seq}, V=30011, ctx=700, N=3")
+    w = syn.c4_longctx_q8(d_model=d_model, n_vocab=30011, ctx=700, n_seq=n_seq, n_steps=3)
+    g = GpuDrafter(w.model, n_seq, 3)
+    _check(w, g.run(w.draft), orc.draft_block(w.model, w.draft))
+
+
 def test_chained_equals_step_by_step_on_gpu():
     """One N-step call == N one-step calls chained through (token, h), bit for
     bit (the fused-vs-sequential check of the evaluation record)."""
