@@ -269,18 +269,15 @@ __global__ __launch_bounds__(256) void mm_splitk_reduce(GemvArgs a, const float 
 // h' = W_post f runs in the same workgroups over the same staged f.
 // ============================================================================
 static constexpr int kHeadUnit = 8;     // K steps per unit: 16 rows x 256 columns
-// Units in flight per wave (a bf16 unit carries 8 KiB, a Q8_0 unit 4 KiB of
-// quants and 256 B of scales; 8 Q8_0 units in flight measured no faster).
-template <typename HT> struct HeadDepth { static constexpr int value = 4; };
+// bf16 units in flight per wave in head_tiles (a unit carries 8 KiB)
+static constexpr int kHeadDepth = 4;
 
+// A bf16 unit in operand order: step k of lane (g, j16) holds row j16's
+// 8 columns 32k + 8g .. +7.
 template <typename HT>
 struct HeadUnit;
 template <> struct HeadUnit<uint16_t> {
     u32x4_t w[kHeadUnit];
-};
-template <> struct HeadUnit<int8_t> {
-    u32x2_t w[kHeadUnit];
-    u32x4_t sc;             // fp16 scales of the lane's row for the unit's 8 blocks
 };
 
 // Staged-activation slot of (step t, half h, lane group g, sequence s): one
@@ -339,24 +336,15 @@ static constexpr int kTrSlots = 16 * kTrStride;
 
 template <typename HT>
 __device__ __forceinline__ void transpose_unit(const RawUnit<HT> &raw, u32x4_t *tr, int lane, HeadUnit<HT> &u) {
+    static_assert(sizeof(HT) == 2, "bf16 units only: Q8_0 units load in operand order");
     const int j16 = lane & 15, g = lane >> 4;
     u32x4_t *wrow = tr + (lane >> 4) * kTrStride + j16;
-    if constexpr (sizeof(HT) == 2) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) wrow[4 * q * kTrStride] = raw.r[4 * hf + q];
+        for (int q = 0; q < 4; ++q) wrow[4 * q * kTrStride] = raw.r[4 * hf + q];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) u.w[4 * hf + kk] = tr[j16 * kTrStride + 4 * kk + g];
-        }
-    } else {
-        // already in operand order: the 16-byte load p holds steps 2p, 2p + 1
-#pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) {
-            const u32x4_t &r = raw.r[k >> 1];
-            u.w[k] = (k & 1) ? u32x2_t{r[2], r[3]} : u32x2_t{r[0], r[1]};
-        }
-        u.sc = raw.sc;
+        for (int kk = 0; kk < 4; ++kk) u.w[4 * hf + kk] = tr[j16 * kTrStride + 4 * kk + g];
     }
 }
 
@@ -365,57 +353,20 @@ __device__ __forceinline__ float sc_at(const u32x4_t &v, int k) {
     return half_to_f((uint16_t)((k & 1) ? (w >> 16) : (w & 0xFFFF)));
 }
 
-// MFMAs of one unit with its activation operands xv (hi, lo per step, read
-// from LDS beforehand); acc_h / acc_l carry the tile's running sums.  The
-// activations are the A operand (rows = sequences) and the weights the B
+// MFMAs of one bf16 unit with its activation operands xv (hi, lo per step,
+// read from LDS beforehand); acc_h / acc_l carry the tile's running sums.
+// The activations are the A operand (rows = sequences) and the weights the B
 // operand (columns = vocabulary rows), so a lane's four results share its
-// weight row j16 and one Q8_0 scale per block.
+// weight row j16.
 template <typename HT>
 __device__ __forceinline__ void head_unit_mma(const HeadUnit<HT> &u, const u32x4_t (&xv)[2 * kHeadUnit],
                                               f32x4_t &acc_h, f32x4_t &acc_l) {
-    if constexpr (sizeof(HT) == 2) {
+    static_assert(sizeof(HT) == 2, "bf16 units only");
 #pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) {
-            const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, u.w[k]);
-            acc_h = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k]), wv, acc_h);
-            acc_l = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 1]), wv, acc_l);
-        }
-    } else {
-        // A block's products are scaled into the accumulators, in block
-        // order, once the next block's quants are converted and its MFMAs
-        // issued, so each block's MFMA latency is covered by the next
-        // block's work.  The empty volatile asm statements keep that order
-        // (left free, the compiler hoists every block's conversion and runs
-        // out of registers), so two blocks' results are live at a time.
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        f32x4_t ph, pl;
-        {
-            u32x2_t q = u.w[0];
-            asm volatile("" : "+v"(q));
-            const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
-            ph = mfma(__builtin_bit_cast(bf16x8_t, xv[0]), wv, z);
-            pl = mfma(__builtin_bit_cast(bf16x8_t, xv[1]), wv, z);
-        }
-#pragma unroll
-        for (int k = 0; k < kHeadUnit; ++k) {
-            f32x4_t nh = z, nl = z;
-            if (k + 1 < kHeadUnit) {
-                u32x2_t q = u.w[k + 1];
-                asm volatile("" : "+v"(q), "+v"(ph), "+v"(pl));
-                const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, q8_to_bf16(q));
-                nh = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 2]), wv, z);
-                nl = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 3]), wv, z);
-            }
-            const float sc = sc_at(u.sc, k);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc_h[i] = fmaf(sc, ph[i], acc_h[i]);
-                acc_l[i] = fmaf(sc, pl[i], acc_l[i]);
-            }
-            asm volatile("" : "+v"(acc_h), "+v"(acc_l), "+v"(nh), "+v"(nl));
-            ph = nh;
-            pl = nl;
-        }
+    for (int k = 0; k < kHeadUnit; ++k) {
+        const bf16x8_t wv = __builtin_bit_cast(bf16x8_t, u.w[k]);
+        acc_h = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k]), wv, acc_h);
+        acc_l = mfma(__builtin_bit_cast(bf16x8_t, xv[2 * k + 1]), wv, acc_l);
     }
 }
 
@@ -436,7 +387,8 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, int rows, int T0, i
                            const u32x4_t *bsm, u32x4_t *tr, float *out, int64_t out_stride, uint64_t (&best)[4],
                            float (&cm)[4], float (&cs)[4], Stage &&stage) {
     const bool conf = HEAD && a.conf != nullptr;
-    constexpr int DEPTH = HeadDepth<HT>::value;
+    static_assert(sizeof(HT) == 2, "bf16 heads only: the Q8_0 head runs q8_head_tiles");
+    constexpr int DEPTH = kHeadDepth;
     constexpr int TPI = DEPTH / UPT;        // tiles per loop iteration
     static_assert(DEPTH % UPT == 0, "ring must hold whole tiles");
     static_assert(DEPTH % 2 == 0, "operand buffers alternate with the ring position");
@@ -499,10 +451,9 @@ __device__ void head_tiles(const HeadArgs &a, const void *W, int rows, int T0, i
             // issue order within the unit: activation reads, the next unit's
             // transpose, its ring refill, then the MFMAs (left alone, the
             // compiler reads each activation operand just before its MFMA)
-            constexpr int n_ld = sizeof(HT) == 2 ? 8 : 5;
+            constexpr int n_ld = 8;
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kHeadUnit, 0);     // LDS reads: activations
-            if constexpr (sizeof(HT) == 2)
-                __builtin_amdgcn_sched_group_barrier(0x300, 16, 0);            // LDS writes / reads: transpose
+            __builtin_amdgcn_sched_group_barrier(0x300, 16, 0);                // LDS writes / reads: transpose
             __builtin_amdgcn_sched_group_barrier(0x020, n_ld, 0);              // global loads
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * kHeadUnit, 0);     // MFMA
             __builtin_amdgcn_sched_barrier(0);  // keep each unit's transpose and loads next to its MFMAs
