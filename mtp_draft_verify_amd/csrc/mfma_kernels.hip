@@ -599,13 +599,13 @@ __device__ __forceinline__ void direct_load_unit(const void *W, int rows, int d,
     for (int k = 0; k < kHeadUnit; ++k) u.w[k] = ld_nt4(wr + 32 * k);
 }
 
-// The several-sequence LM head.  A Q8_0 head keeps no transpose tile, so two workgroups fit a CU and each
-// wave has half the register file.
+// The several-sequence LM head.  A Q8_0 head keeps no transpose tile, so two
+// workgroups fit a CU and each wave has half the register file.
 template <typename HT, int UPT, bool LOGITS, bool PACK>
 __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg) {
     constexpr bool Q8 = sizeof(HT) == 1;
     static_assert(Q8 || !PACK, "the packed activations serve the Q8_0 head");
-    extern __shared__ u32x4_t mm_bsm[];     // [KS][2][4][16] activation halves
+    extern __shared__ u32x4_t mm_bsm[];     // activation halves: [KS][2][4][16] (bslot), packed [KS][4][16] (pslot)
     __shared__ u32x4_t mm_tr[Q8 ? 1 : 4 * kTrSlots];    // one weight transpose tile per wave (bf16)
     __shared__ float rsw[4][16];            // per-wave partial sums of squares of each sequence
     __shared__ uint64_t wbest[4][16];

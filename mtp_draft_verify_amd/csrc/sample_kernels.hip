@@ -275,11 +275,11 @@ __device__ __forceinline__ float raw_value(const SampleArgs &a, float raw, int32
     return chain_value(a, raw, member ? (int)cl.cnt[t - c0] : 0);
 }
 
-// The chunk passes walk their kChunk tokens in batches of KB = 32 / E loads
-// per thread, each load E consecutive logits (E = 4 when rows are 16-byte
-// aligned: one wave load then moves 1 KiB): all of a batch's logits are
-// requested at once (clamped into the chunk), the first batch before the
-// context is read, each next one before the current one is used.
+// The chunk kernel holds its kChunk tokens in registers, in batches of
+// KB = 32 / E loads per thread, each load E consecutive logits (E = 4 when
+// rows are 16-byte aligned: one wave load then moves 1 KiB).  Every batch is
+// requested at once (clamped into the chunk), right after the context's
+// tokens.
 template <int E> struct ChunkShape {
     static constexpr int KB = E == 4 ? 4 : 8;           // loads per thread per batch
     static constexpr int BT = E * kBlock * KB;          // tokens per batch
