@@ -508,15 +508,39 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     // 0 when it does not (an entry of weight 0 takes part in no sum and no
     // draw).  The survivors are counted; beyond the list's slots the row
     // takes the implicit form below, which does not read the list.
+    // A list of at most RU * NT entries stays in registers through the
+    // count: it always takes the compact form, which then needs no second
+    // read of it.  A longer one is rewritten in place.
+    constexpr int RU = 4;
+    static_assert(RU * NT <= kSortMax, "a list held in registers is always sorted");
+    const bool inreg = n_all <= RU * NT;
+    float er[RU];
+    int32_t ir[RU];
+    if (tid == 0) nkey_sh = 0;
     int n_surv = 0;
     if (n_all > 0 && n_all <= a.cap) {
         float *lv = a.cand_v + (int64_t)row * a.cap;
+        const int32_t *li = a.cand_id + (int64_t)row * a.cap;
         float cnt = 0.f;
-        for (int j = tid; j < n_all; j += NT) {
-            const float e = expf(lv[j] - M);
+        auto filter = [&](float v) {
+            const float e = expf(v - M);
             const bool keep = e >= a.min_p && e > 0.f;     // a zero weight is never drawn
-            lv[j] = keep ? e : 0.f;
             cnt += keep ? 1.f : 0.f;
+            return keep ? e : 0.f;
+        };
+        if (inreg) {
+#pragma unroll
+            for (int u = 0; u < RU; ++u) {
+                const int j = tid + NT * u;
+                er[u] = 0.f;
+                ir[u] = 0;
+                if (j < n_all) {
+                    er[u] = filter(lv[j]);
+                    ir[u] = li[j];
+                }
+            }
+        } else {
+            for (int j = tid; j < n_all; j += NT) lv[j] = filter(lv[j]);
         }
         n_surv = (int)block_sum<NT>(cnt, red);     // exact: at most 65536 ones
         __syncthreads();                           // the rewritten list is visible to the whole workgroup
@@ -538,25 +562,63 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
         const int n = n_surv;
         int np2 = 1;
         while (np2 < n) np2 <<= 1;
-        if (tid == 0) nkey_sh = 0;
-        __syncthreads();
-        for (int j = tid; j < n_all; j += NT) {
-            const float e = a.cand_v[(int64_t)row * a.cap + j];
-            if (e > 0.f) keys[atomicAdd(&nkey_sh, 1)] = tok_key(e, a.cand_id[(int64_t)row * a.cap + j]);
+        if (inreg) {
+#pragma unroll
+            for (int u = 0; u < RU; ++u)
+                if (er[u] > 0.f) keys[atomicAdd(&nkey_sh, 1)] = tok_key(er[u], ir[u]);
+        } else {
+            for (int j = tid; j < n_all; j += NT) {
+                const float e = a.cand_v[(int64_t)row * a.cap + j];
+                if (e > 0.f) keys[atomicAdd(&nkey_sh, 1)] = tok_key(e, a.cand_id[(int64_t)row * a.cap + j]);
+            }
         }
+        if (np2 <= 128) np2 = 128;                     // the one-wave sort below takes 128 keys
         for (int j = n + tid; j < np2; j += NT) keys[j] = 0ull;
         __syncthreads();
-        for (int k = 2; k <= np2; k <<= 1) {           // bitonic sort, descending
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int x = tid; x < np2; x += NT) {
-                    const int y = x ^ j;
-                    if (y > x) {
-                        const bool desc = (x & k) == 0;
-                        const uint64_t kx = keys[x], ky = keys[y];
-                        if (desc ? (kx < ky) : (kx > ky)) { keys[x] = ky; keys[y] = kx; }
+        if (np2 == 128) {
+            // bitonic sort, descending, in one wave's registers: key x = lane +
+            // 64 h; partners 64 apart sit in the same lane, closer ones are
+            // exchanged across lanes (no barrier per stage)
+            if (tid < 64) {
+                uint64_t v[2] = {keys[tid], keys[tid + 64]};
+#pragma unroll
+                for (int k = 2; k <= 128; k <<= 1)
+#pragma unroll
+                    for (int j = k >> 1; j > 0; j >>= 1) {
+                        if (j == 64) {
+                            // pair (tid, tid + 64): the lower index sits in v[0]
+                            const bool desc = (tid & k) == 0;
+                            const uint64_t hi = v[0] > v[1] ? v[0] : v[1], lo = v[0] > v[1] ? v[1] : v[0];
+                            v[0] = desc ? hi : lo;
+                            v[1] = desc ? lo : hi;
+                        } else {
+#pragma unroll
+                            for (int h = 0; h < 2; ++h) {
+                                const int x = tid + 64 * h;
+                                const uint64_t o = shfl_xor_u64(v[h], j);
+                                const bool desc = (x & k) == 0, first = (x & j) == 0;
+                                const uint64_t hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
+                                v[h] = (desc == first) ? hi : lo;
+                            }
+                        }
                     }
+                keys[tid] = v[0];
+                keys[tid + 64] = v[1];
+            }
+            __syncthreads();
+        } else {
+            for (int k = 2; k <= np2; k <<= 1) {       // bitonic sort, descending
+                for (int j = k >> 1; j > 0; j >>= 1) {
+                    for (int x = tid; x < np2; x += NT) {
+                        const int y = x ^ j;
+                        if (y > x) {
+                            const bool desc = (x & k) == 0;
+                            const uint64_t kx = keys[x], ky = keys[y];
+                            if (desc ? (kx < ky) : (kx > ky)) { keys[x] = ky; keys[y] = kx; }
+                        }
+                    }
+                    __syncthreads();
                 }
-                __syncthreads();
             }
         }
         // prefix sums of e in sorted order, in a fixed order: thread tid sums
