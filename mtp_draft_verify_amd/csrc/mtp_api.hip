@@ -278,7 +278,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         const size_t fit = ((size_t)8 << 20) / rows;
         const size_t cap = std::max<size_t>(4096, std::min<size_t>(65536, fit)) & ~(size_t)255;
         c->s_cap = (int32_t)std::min<size_t>(cap, (size_t)d.n_vocab);
-        ok = ok && dalloc(&c->s_maxkey, rows) && dalloc(&c->s_topk, rows) && dalloc(&c->s_cand_n, rows) &&
+        ok = ok && dalloc(&c->s_maxkey, rows * kRowCtrStride) && dalloc(&c->s_topk, rows) &&
+             dalloc(&c->s_cand_n, rows * kRowCtrStride) &&
              dalloc(&c->s_cand_id, rows * c->s_cap) && dalloc(&c->s_cand_v, rows * c->s_cap) &&
              dalloc((uint8_t **)&c->s_state, rows * sample_row_state_bytes());
     }
@@ -327,8 +328,8 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
     {
         const size_t rows = S * (2 * (size_t)d.max_steps + 1);
         hipError_t e = hipMemset(c->vkeys, 0, sizeof(uint64_t) * S * R);
-        if (e == hipSuccess) e = hipMemset(c->s_maxkey, 0, sizeof(uint32_t) * rows);
-        if (e == hipSuccess) e = hipMemset(c->s_cand_n, 0, sizeof(int32_t) * rows);
+        if (e == hipSuccess) e = hipMemset(c->s_maxkey, 0, sizeof(uint32_t) * rows * kRowCtrStride);
+        if (e == hipSuccess) e = hipMemset(c->s_cand_n, 0, sizeof(int32_t) * rows * kRowCtrStride);
         if (e != hipSuccess) { free_ctx(c); return hip_fail("hipMemset (verify scratch)", e); }
     }
     if (c->has_weights) {

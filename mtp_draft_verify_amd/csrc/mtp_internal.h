@@ -270,15 +270,19 @@ struct SampleArgs {
     int32_t top_k, last_n;
     uint64_t seed, round;
     // scratch, per row (S*(N+1) target rows, then S*N draft rows)
-    uint32_t *row_maxkey;   // zero between calls
+    uint32_t *row_maxkey;   // [rows * kRowCtrStride], zero between calls
     uint64_t *topk_key;
-    int32_t *cand_n;        // zero between calls
+    int32_t *cand_n;        // [rows * kRowCtrStride], zero between calls
     int32_t *cand_id;       // [rows, cap]
     float *cand_v;          // [rows, cap]
     void *row_state;        // [rows] RowState
     int32_t cap;
     int32_t *out_tokens, *out_n_accept;
 };
+// Every chunk workgroup of a row updates the row's max and list length with
+// device-scope atomics; atomics on one line are applied one after another,
+// so each row's counter sits alone on a 256-byte stretch (row r at r * 64).
+static constexpr int kRowCtrStride = 64;
 hipError_t launch_verify_sample(const SampleArgs &a, hipStream_t st);
 size_t sample_row_state_bytes();
 

@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
 // The single pass over the logits: the chunk's row max contribution, then
 // its part of a superset of the row's min-p survivors (token, v).
 template <int E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
     constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     __shared__ float red[4];
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     if (threadIdx.x == 0) {
         float ref = mx;
         if (mx > -INFINITY) {
-            const uint32_t old = atomicMax(&a.row_maxkey[row], fkey(mx));
+            const uint32_t old = atomicMax(&a.row_maxkey[row * kRowCtrStride], fkey(mx));
             if (old != 0u) ref = fmaxf(mx, fkey_inv(old));
         }
         ref_sh = ref;
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     __syncthreads();
     if (threadIdx.x == 0) {
         const int tot = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
-        wbase_sh = tot > 0 ? atomicAdd(&a.cand_n[row], tot) : 0;
+        wbase_sh = tot > 0 ? atomicAdd(&a.cand_n[row * kRowCtrStride], tot) : 0;
     }
     __syncthreads();
     int slot = wbase_sh + incl - cnt;
@@ -498,8 +498,8 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
     __shared__ uint64_t hist[256], scal[4], red64[NT / 64];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
-    const int n_all = a.cand_n[row];
-    const float M = fkey_inv(a.row_maxkey[row]);
+    const int n_all = a.cand_n[row * kRowCtrStride];
+    const float M = fkey_inv(a.row_maxkey[row * kRowCtrStride]);
     RowState st;
     st.M = M;
     st.pad = 0;
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
             for (int j = tid; j < st.n_keep; j += NT)
                 consider(a.cand_id[(int64_t)prow * a.cap + j], a.cand_v[(int64_t)prow * a.cap + j] / st.Z);
         } else if (st.n_keep == kListForm) {
-            const int n = a.cand_n[prow];
+            const int n = a.cand_n[prow * kRowCtrStride];
             for (int j = tid; j < n; j += NT) {
                 const int32_t t = a.cand_id[(int64_t)prow * a.cap + j];
                 const float e = a.cand_v[(int64_t)prow * a.cap + j];
@@ -863,13 +863,13 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
     if (tid == 0) a.out_n_accept[s] = n_acc;
     // clear this sequence's row scratch for the next call
     for (int i = tid; i < R; i += NT) {
-        a.row_maxkey[s * R + i] = 0u;
-        a.cand_n[s * R + i] = 0;
+        a.row_maxkey[(s * R + i) * kRowCtrStride] = 0u;
+        a.cand_n[(s * R + i) * kRowCtrStride] = 0;
     }
     if (a.q_logits)
         for (int i = tid; i < N; i += NT) {
-            a.row_maxkey[a.S * R + s * N + i] = 0u;
-            a.cand_n[a.S * R + s * N + i] = 0;
+            a.row_maxkey[(a.S * R + s * N + i) * kRowCtrStride] = 0u;
+            a.cand_n[(a.S * R + s * N + i) * kRowCtrStride] = 0;
         }
 }
 
