@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(SampleArgs a) {
 // The single pass over the logits: the chunk's row max contribution, then
 // its part of a superset of the row's min-p survivors (token, v).
 template <int E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 : 3))) void sample_chunk_kernel(SampleArgs a, int n_chunk) {
     constexpr int KB = ChunkShape<E>::KB, BT = ChunkShape<E>::BT, NB = ChunkShape<E>::NB;
     __shared__ CtxLds cl;
     __shared__ float red[4];
@@ -374,6 +374,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
 #pragma unroll
     for (int b = 0; b < NB; ++b) load_batch<E, KB>(rr.z, c0 + b * BT, c1, raw[b]);
     ctx_store(creq, c0, c1 - c0, cl);
+    // which of the thread's NB * KB * E tokens are in the context (bit =
+    // position, as for kmask below): read from the bitmap once, so the
+    // passes below test a register instead of waiting on LDS per token.  A
+    // load's E tokens start at a multiple of E and share one bitmap word.
+    static_assert(NB * KB * E <= 32, "one bit per token of the thread");
+    uint32_t mmask = 0u;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+            const int off = b * BT + E * ((int)threadIdx.x + kBlock * k);
+            const uint32_t w = cl.bits[off >> 5] >> (off & 31);
+            mmask |= (w & ((1u << E) - 1u)) << ((b * KB + k) * E);
+        }
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
     // Context tokens take the full chain; every other token's value is
     // fl(z / temp), which does not decrease as z grows, so the largest of
@@ -389,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
                 const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
                 if (t < c1) {
                     const float z = raw[b][k][e];
-                    const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                    const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
                     if (member) {
                         const float v = raw_value(a, z, t, true, cl, c0, tk);
                         if (v == v) mx = fmaxf(mx, v);
@@ -422,7 +436,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
         zlo = nextafterf((float)zl, -INFINITY);
     }
     // which of the thread's NB * KB * E tokens are listed (bit = position)
-    static_assert(NB * KB * E <= 32, "one keep bit per token of the thread");
     uint32_t kmask = 0u;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -433,7 +446,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
                 const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
                 if (t < c1) {
                     const float z = raw[b][k][e];
-                    const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                    const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
                     if (member || z >= zlo) {
                         const float v = raw_value(a, z, t, member, cl, c0, tk);
                         if (v == v && expf(v - ref) >= a.min_p) kmask |= 1u << ((b * KB + k) * E + e);
@@ -472,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) void s
             for (int e = 0; e < E; ++e) {
                 if (!((kmask >> ((b * KB + k) * E + e)) & 1u)) continue;
                 const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
-                const bool member = (cl.bits[(t - c0) >> 5] >> ((t - c0) & 31)) & 1u;
+                const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
                 if (slot < a.cap) {
                     a.cand_id[(int64_t)row * a.cap + slot] = t;
                     a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, raw[b][k][e], t, member, cl, c0, tk);
