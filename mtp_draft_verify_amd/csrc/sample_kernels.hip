@@ -31,6 +31,8 @@
 //          next call
 // All floating point is fp32; every sum runs in a fixed order, so a call is
 // deterministic.
+#include <cfloat>
+
 #include "dev_common.h"
 
 namespace mtp {
@@ -389,29 +391,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 
             mmask |= (w & ((1u << E) - 1u)) << ((b * KB + k) * E);
         }
     const uint64_t tk = a.top_k > 0 ? a.topk_key[row] : 0;
-    // Context tokens take the full chain; every other token's value is
-    // fl(z / temp), which does not decrease as z grows, so the largest of
-    // them is the value of the largest raw logit: those tokens only need a
-    // running max of z (after the top-k test).
-    float mx = -INFINITY, mz = -INFINITY;
+    // Positions p = (b * KB + k) * E + e of the thread's tokens: `ok` holds
+    // those that are tokens of the row (the last chunk's loads are clamped)
+    // and survive top-k; of them, context tokens (memb) take the full chain
+    // and every other token (plain) is valued fl(z / temp).
+    constexpr int NP = NB * KB * E;
+    constexpr uint32_t kAll = (uint32_t)((1ull << NP) - 1u);
+    auto tok_at = [&](int b, int k, int e) { return c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e; };
+    uint32_t ok = kAll;
+    if (c1 - c0 < kChunk || a.top_k > 0) {
+        ok = 0u;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int k = 0; k < KB; ++k)
+            for (int k = 0; k < KB; ++k)
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
-                if (t < c1) {
-                    const float z = raw[b][k][e];
-                    const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
-                    if (member) {
-                        const float v = raw_value(a, z, t, true, cl, c0, tk);
-                        if (v == v) mx = fmaxf(mx, v);
-                    } else if (!(a.top_k > 0 && tok_key(z, t) < tk)) {
-                        mz = fmaxf(mz, z);
-                    }
+                for (int e = 0; e < E; ++e) {
+                    const int t = tok_at(b, k, e);
+                    const bool keep = t < c1 && !(a.top_k > 0 && tok_key(raw[b][k][e], t) < tk);
+                    ok |= (uint32_t)keep << ((b * KB + k) * E + e);
                 }
-            }
+    }
+    const uint32_t memb = ok & mmask, plain = ok & ~mmask;
+    // fl(z / temp) does not decrease as z grows, so the largest plain value
+    // is that of the largest plain raw logit: those tokens only need a
+    // running max of z.
+    float mz = -INFINITY;
+    if (plain == kAll) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e) mz = fmaxf(mz, raw[b][k][e]);
+    } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    mz = fmaxf(mz, (plain >> ((b * KB + k) * E + e)) & 1u ? raw[b][k][e] : -INFINITY);
+    }
+    float mx = -INFINITY;
+    if (memb) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if ((memb >> ((b * KB + k) * E + e)) & 1u) {
+                        const float v = raw_value(a, raw[b][k][e], tok_at(b, k, e), true, cl, c0, tk);
+                        if (v == v) mx = fmaxf(mx, v);
+                    }
+    }
+    const float mz_thread = mz;
     if (mz > -INFINITY) mx = fmaxf(mx, chain_value(a, mz, 0));
     mx = block_max(mx, red);
     if (threadIdx.x == 0) {
@@ -426,33 +461,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 
     const float ref = ref_sh;
     // exp(fl(v - M)) >= min_p implies exp(fl(v - ref)) >= min_p for ref <= M
     // (rounding and exp do not decrease with their argument), so testing
-    // against ref keeps every survivor.  A token outside the context passes
-    // only if z / temp >= ref + ln(min_p) - 1e-5 (1 + |ref|) at the least
-    // (fp32 rounding and expf's error), so a raw logit below zlo = temp *
-    // (ref + ln(min_p) - 0.01 - 1e-5 |ref|) (rounded down) skips the test.
-    float zlo = -INFINITY;
+    // against ref keeps every survivor.  A plain token passes only if
+    // z / temp >= ref + ln(min_p) - 1e-5 (1 + |ref|) at the least (fp32
+    // rounding and expf's error), so every plain token with a raw logit of at
+    // least zlo = temp * (ref + ln(min_p) - 0.01 - 1e-5 |ref|) (rounded down)
+    // is listed, untested: the list stays a superset, and the row kernel
+    // takes the exact decision.  A token of value -inf never survives (its
+    // weight is 0), so zlo is at least -FLT_MAX.
+    float zlo = -FLT_MAX;
     if (a.min_p > 0.f && ref > -INFINITY) {
         const double zl = (double)a.temp * ((double)ref + a.ln_min_p - 0.01 - 1e-5 * fabs((double)ref));
-        zlo = nextafterf((float)zl, -INFINITY);
+        zlo = fmaxf(nextafterf((float)zl, -INFINITY), -FLT_MAX);
     }
-    // which of the thread's NB * KB * E tokens are listed (bit = position)
+    // which of the thread's tokens are listed (bit = position)
     uint32_t kmask = 0u;
+    if (mz_thread >= zlo) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int k = 0; k < KB; ++k)
+            for (int k = 0; k < KB; ++k)
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
-                if (t < c1) {
-                    const float z = raw[b][k][e];
-                    const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
-                    if (member || z >= zlo) {
-                        const float v = raw_value(a, z, t, member, cl, c0, tk);
+                for (int e = 0; e < E; ++e) kmask |= (uint32_t)(raw[b][k][e] >= zlo) << ((b * KB + k) * E + e);
+        kmask &= plain;
+    }
+    if (memb) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int k = 0; k < KB; ++k)
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if ((memb >> ((b * KB + k) * E + e)) & 1u) {
+                        const float v = raw_value(a, raw[b][k][e], tok_at(b, k, e), true, cl, c0, tk);
                         if (v == v && expf(v - ref) >= a.min_p) kmask |= 1u << ((b * KB + k) * E + e);
                     }
-                }
-            }
+    }
     // Slots: an exclusive prefix sum of the threads' counts over the
     // workgroup and one reservation per chunk, so no wave waits on an atomic
     // inside the token loop (the listed superset can be ten times the
