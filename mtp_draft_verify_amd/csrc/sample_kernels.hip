@@ -519,22 +519,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 
     __syncthreads();
     int slot = wbase_sh + incl - cnt;
     for (int w = 0; w < wid; ++w) slot += wtot[w];
-    if (kmask == 0u) return;
+    // each thread walks the set bits of its kmask (the slots follow position
+    // order); the listed value is picked out of the registers by position
+    for (uint32_t m = kmask; m != 0u; m &= m - 1u) {
+        const int p = __builtin_ctz(m);
+        float z = 0.f;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int k = 0; k < KB; ++k)
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                if (!((kmask >> ((b * KB + k) * E + e)) & 1u)) continue;
-                const int t = c0 + b * BT + E * ((int)threadIdx.x + kBlock * k) + e;
-                const bool member = (mmask >> ((b * KB + k) * E + e)) & 1u;
-                if (slot < a.cap) {
-                    a.cand_id[(int64_t)row * a.cap + slot] = t;
-                    a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, raw[b][k][e], t, member, cl, c0, tk);
-                }
-                ++slot;
-            }
+        for (int q = 0; q < NP; ++q) z = p == q ? raw[q / (KB * E)][(q / E) % KB][q % E] : z;
+        const int t = tok_at(p / (KB * E), (p / E) % KB, p % E);
+        if (slot < a.cap) {
+            a.cand_id[(int64_t)row * a.cap + slot] = t;
+            a.cand_v[(int64_t)row * a.cap + slot] = raw_value(a, z, t, (mmask >> p) & 1u, cl, c0, tk);
+        }
+        ++slot;
+    }
 }
 
 // ---------------------------------------------------------------------------
