@@ -239,9 +239,53 @@ __device__ void ctx_store(const CtxReq &r, int c0, int nbits, CtxLds &cl) {
     __syncthreads();
 }
 
-// sort a context list of n <= kMaxCtx tokens ascending in place (LDS, bitonic)
+__device__ __forceinline__ int32_t shfl_xor_key(int32_t v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int m) { return shfl_xor_u64(v, m); }
+
+// Bitonic sort of 128 keys held by one wave (key x = lane + 64 h in v[h]),
+// descending when DESC, else ascending.  Partners 64 apart sit in one lane
+// and closer ones are exchanged across lanes, so no stage needs a barrier.
+template <bool DESC, typename T>
+__device__ __forceinline__ void wave_sort128(T (&v)[2], int lane) {
+#pragma unroll
+    for (int k = 2; k <= 128; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            if (j == 64) {
+                // only in the last merge (k = 128): one direction for all pairs
+                const T hi = v[0] > v[1] ? v[0] : v[1], lo = v[0] > v[1] ? v[1] : v[0];
+                v[0] = DESC ? hi : lo;
+                v[1] = DESC ? lo : hi;
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int x = lane + 64 * h;
+                    const T o = shfl_xor_key(v[h], j);
+                    const bool up = ((x & k) == 0) != DESC;     // x's block is sorted ascending
+                    const bool first = (x & j) == 0;            // x is the lower of the pair
+                    const T hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
+                    v[h] = (up == first) ? lo : hi;
+                }
+            }
+        }
+}
+
+// sort a context list of n <= kMaxCtx tokens ascending in place (LDS):
+// up to 128 in one wave's registers, more by a bitonic network over the
+// workgroup.  The list is visible to the workgroup on entry and on return.
 template <int NT>
 __device__ void sort_ctx(int32_t *tok, int n) {
+    if (n <= 128) {
+        if (threadIdx.x < 64) {
+            const int l = threadIdx.x;
+            int32_t v[2] = {l < n ? tok[l] : 0x7FFFFFFF, l + 64 < n ? tok[l + 64] : 0x7FFFFFFF};
+            wave_sort128<false>(v, l);
+            if (l < n) tok[l] = v[0];
+            if (l + 64 < n) tok[l + 64] = v[1];
+        }
+        __syncthreads();
+        return;
+    }
     int np2 = 1;
     while (np2 < n) np2 <<= 1;
     for (int j = n + threadIdx.x; j < np2; j += NT) tok[j] = 0x7FFFFFFF;
@@ -630,32 +674,10 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
         for (int j = n + tid; j < np2; j += NT) keys[j] = 0ull;
         __syncthreads();
         if (np2 == 128) {
-            // bitonic sort, descending, in one wave's registers: key x = lane +
-            // 64 h; partners 64 apart sit in the same lane, closer ones are
-            // exchanged across lanes (no barrier per stage)
+            // sorted descending in one wave's registers
             if (tid < 64) {
                 uint64_t v[2] = {keys[tid], keys[tid + 64]};
-#pragma unroll
-                for (int k = 2; k <= 128; k <<= 1)
-#pragma unroll
-                    for (int j = k >> 1; j > 0; j >>= 1) {
-                        if (j == 64) {
-                            // pair (tid, tid + 64): the lower index sits in v[0]
-                            const bool desc = (tid & k) == 0;
-                            const uint64_t hi = v[0] > v[1] ? v[0] : v[1], lo = v[0] > v[1] ? v[1] : v[0];
-                            v[0] = desc ? hi : lo;
-                            v[1] = desc ? lo : hi;
-                        } else {
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {
-                                const int x = tid + 64 * h;
-                                const uint64_t o = shfl_xor_u64(v[h], j);
-                                const bool desc = (x & k) == 0, first = (x & j) == 0;
-                                const uint64_t hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
-                                v[h] = (desc == first) ? hi : lo;
-                            }
-                        }
-                    }
+                wave_sort128<true>(v, tid);
                 keys[tid] = v[0];
                 keys[tid + 64] = v[1];
             }
@@ -812,17 +834,33 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
 // ---------------------------------------------------------------------------
 // per-sequence accept / resample
 // ---------------------------------------------------------------------------
-// probability of token t under row `row` (its RowState already final), t
-// occurring cnt times in the row's context
+// Probability of token t under row `row` (its RowState final), t occurring
+// cnt times in the row's context, in two halves: tok_prob_load issues the
+// reads (the row's state, its logit at t and top-k key), tok_prob_value
+// finishes once the count is known.
+struct TokProbIn {
+    RowState st;
+    float raw;
+    uint64_t tk;
+    bool in_vocab;
+};
+__device__ __forceinline__ TokProbIn tok_prob_load(const SampleArgs &a, int row, int32_t t) {
+    TokProbIn r;
+    r.in_vocab = t >= 0 && t < a.V;
+    r.st = ((const RowState *)a.row_state)[row];
+    r.raw = r.in_vocab ? row_ref(a, row).z[t] : 0.f;
+    r.tk = a.top_k > 0 ? a.topk_key[row] : 0;
+    return r;
+}
+__device__ __forceinline__ float tok_prob_value(const SampleArgs &a, const TokProbIn &r, int32_t t, int cnt) {
+    if (!r.in_vocab) return 0.f;
+    if (a.top_k > 0 && tok_key(r.raw, t) < r.tk) return 0.f;
+    const float e = expf(chain_value(a, r.raw, cnt) - r.st.M);
+    if (!(e >= a.min_p) || tok_key(e, t) < r.st.tau) return 0.f;
+    return e / r.st.Z;
+}
 __device__ float row_prob_cnt(const SampleArgs &a, int row, int32_t t, int cnt) {
-    if (t < 0 || t >= a.V) return 0.f;
-    const RowRef rr = row_ref(a, row);
-    const RowState st = ((const RowState *)a.row_state)[row];
-    const float raw = rr.z[t];
-    if (a.top_k > 0 && tok_key(raw, t) < a.topk_key[row]) return 0.f;
-    const float e = expf(chain_value(a, raw, cnt) - st.M);
-    if (!(e >= a.min_p) || tok_key(e, t) < st.tau) return 0.f;
-    return e / st.Z;
+    return tok_prob_value(a, tok_prob_load(a, row, t), t, cnt);
 }
 // the same with the row's context as a sorted list
 __device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t *ctx_tok, int n_ctx) {
@@ -832,27 +870,63 @@ __device__ float row_prob(const SampleArgs &a, int row, int32_t t, const int32_t
 
 __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
     constexpr int NT = kRowThreads;
+    __shared__ int32_t seq_tok[kMaxCtx + kMaxDrafts];
     __shared__ int32_t ctx_tok[kMaxCtx];
     __shared__ uint64_t best_w[NT / 64];
     __shared__ int accept[kMaxDrafts];
+    __shared__ RowState pstate[kMaxDrafts + 1];
     const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int N = a.N, R = N + 1;
+    // Every row's penalty context lies in positions [p_lo, hlen + N) of
+    // history[s] ++ drafts[s]: read once into LDS.  Row i's context starts
+    // at hlen + i - n_ctx(i), which does not decrease with i.
+    const int hlen = hist_len(a, s);
+    const int p_lo = hlen - ctx_len(a, s, 0);
+    const int n_seq = hlen + N - p_lo;
     // The accept test of draft i needs only the final states of its p and q
     // rows, the draft's count in row i's context and its own uniform, none
-    // of the earlier outcomes: all the tests run at once, one wave per draft.
-    for (int i = wid; i < N; i += NT / 64) {
-        const int32_t d = a.drafts[(int64_t)s * N + i];
-        const int n_ctx = ctx_len(a, s, i);
+    // of the earlier outcomes: all the tests run at once, one wave per draft
+    // (the reads at the draft are issued with the context's).
+    constexpr int kWaves = NT / 64;
+    static_assert(kMaxDrafts <= 4 * kWaves, "drafts per wave");
+    int32_t dr[4];
+    TokProbIn pin[4], qin[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = wid + kWaves * u;
+        dr[u] = i < N ? a.drafts[(int64_t)s * N + i] : -1;
+    }
+    for (int j = tid; j < n_seq; j += NT) {
+        const int pos = p_lo + j;
+        seq_tok[j] = pos < hlen ? a.history[(int64_t)s * a.hstride + pos] : a.drafts[(int64_t)s * N + (pos - hlen)];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = wid + kWaves * u;
+        if (i < N) {
+            pin[u] = tok_prob_load(a, s * R + i, dr[u]);
+            if (a.q_logits) qin[u] = tok_prob_load(a, a.S * R + s * N + i, dr[u]);
+        }
+    }
+    // the bonus row's state, for the draw below
+    if (tid == 0) pstate[N] = ((const RowState *)a.row_state)[s * R + N];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int i = wid + kWaves * u;
+        if (i >= N) continue;
+        const int32_t d = dr[u];
+        const int n_ctx = ctx_len(a, s, i), c0 = hlen + i - n_ctx - p_lo;
         float c = 0.f;
         if (d >= 0 && d < a.V)
-            for (int j = lane; j < n_ctx; j += 64) c += ctx_token(a, s, i, n_ctx, j) == d ? 1.f : 0.f;
+            for (int j = lane; j < n_ctx; j += 64) c += seq_tok[c0 + j] == d ? 1.f : 0.f;
         const int cnt = (int)wave_sum(c);         // exact: at most kMaxCtx ones
         if (lane == 0) {
-            const float pd = row_prob_cnt(a, s * R + i, d, cnt);
-            const float qd = a.q_logits ? row_prob_cnt(a, a.S * R + s * N + i, d, cnt)
-                                        : ((d >= 0 && d < a.V) ? 1.f : 0.f);
-            const float u = counter_uniform(a.seed, s, a.round, i, 0, 0);
-            accept[i] = (u * qd < pd) ? 1 : 0;
+            const float pd = tok_prob_value(a, pin[u], d, cnt);
+            const float qd = a.q_logits ? tok_prob_value(a, qin[u], d, cnt) : ((d >= 0 && d < a.V) ? 1.f : 0.f);
+            const float uu = counter_uniform(a.seed, s, a.round, i, 0, 0);
+            accept[i] = (uu * qd < pd) ? 1 : 0;
+            pstate[i] = pin[u].st;
         }
     }
     __syncthreads();
@@ -862,15 +936,15 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
     for (int j = tid; j < n_acc; j += NT) a.out_tokens[(int64_t)s * R + j] = a.drafts[(int64_t)s * N + j];
     {
         const int prow = s * R + i;
-        const int n_ctx = ctx_len(a, s, i);
-        for (int j = tid; j < n_ctx; j += NT) ctx_tok[j] = ctx_token(a, s, i, n_ctx, j);
+        const int n_ctx = ctx_len(a, s, i), c0 = hlen + i - n_ctx - p_lo;
+        for (int j = tid; j < n_ctx; j += NT) ctx_tok[j] = seq_tok[c0 + j];
         __syncthreads();
         sort_ctx<NT>(ctx_tok, n_ctx);
         const int32_t d = i < N ? a.drafts[(int64_t)s * N + i] : -1;
         const int qrow = a.q_logits ? a.S * R + s * N + i : -1;
         // draw from max(p - q, 0) (rejection at row i) or from p_N (bonus)
         const uint64_t stream = i < N ? 1 : 2;
-        const RowState st = ((const RowState *)a.row_state)[prow];
+        const RowState st = pstate[i];
         uint64_t best = 0;
         auto consider = [&](int32_t t, float pt) {
             float r = pt;
@@ -899,8 +973,7 @@ __global__ __launch_bounds__(kRowThreads) void sample_seq_kernel(SampleArgs a) {
         }
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
-            const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), m) << 32) |
-                               (uint32_t)__shfl_xor((int)(uint32_t)best, m);
+            const uint64_t o = shfl_xor_u64(best, m);
             best = o > best ? o : best;
         }
         if (lane == 0) best_w[wid] = best;
