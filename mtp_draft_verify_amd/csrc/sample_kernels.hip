@@ -242,32 +242,92 @@ __device__ void ctx_store(const CtxReq &r, int c0, int nbits, CtxLds &cl) {
 __device__ __forceinline__ int32_t shfl_xor_key(int32_t v, int m) { return __shfl_xor(v, m); }
 __device__ __forceinline__ uint64_t shfl_xor_key(uint64_t v, int m) { return shfl_xor_u64(v, m); }
 
-// Bitonic sort of 128 keys held by one wave (key x = lane + 64 h in v[h]),
-// descending when DESC, else ascending.  Partners 64 apart sit in one lane
-// and closer ones are exchanged across lanes, so no stage needs a barrier.
+// Bitonic sorting network, descending when DESC: stage (k, j) orders each
+// pair (x, x ^ j) of the keys the way x's block of k keys runs.  A wave holds
+// the 128 keys x = xb + lane + 64 h (xb a multiple of 128) in v[h]; a stage
+// with j <= 64 runs inside the wave: partners 64 apart sit in one lane,
+// closer ones are exchanged across lanes, so it needs no barrier.
 template <bool DESC, typename T>
-__device__ __forceinline__ void wave_sort128(T (&v)[2], int lane) {
+__device__ __forceinline__ void wave_stage(T (&v)[2], int lane, int xb, int k, int j) {
+    if (j == 64) {
+        // (x, x + 64), k >= 128: both in the same block of k
+        const bool up = (((xb + lane) & k) == 0) != DESC;
+        const T hi = v[0] > v[1] ? v[0] : v[1], lo = v[0] > v[1] ? v[1] : v[0];
+        v[0] = up ? lo : hi;
+        v[1] = up ? hi : lo;
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int x = xb + lane + 64 * h;
+            const T o = shfl_xor_key(v[h], j);
+            const bool up = ((x & k) == 0) != DESC;     // x's block is sorted ascending
+            const bool first = (x & j) == 0;            // x is the lower of the pair
+            const T hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
+            v[h] = (up == first) ? lo : hi;
+        }
+    }
+}
+// the wave's 128 keys sorted (blocks up to k = 128)
+template <bool DESC, typename T>
+__device__ __forceinline__ void wave_sort128(T (&v)[2], int lane, int xb = 0) {
 #pragma unroll
     for (int k = 2; k <= 128; k <<= 1)
 #pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j == 64) {
-                // only in the last merge (k = 128): one direction for all pairs
-                const T hi = v[0] > v[1] ? v[0] : v[1], lo = v[0] > v[1] ? v[1] : v[0];
-                v[0] = DESC ? hi : lo;
-                v[1] = DESC ? lo : hi;
-            } else {
+        for (int j = k >> 1; j > 0; j >>= 1) wave_stage<DESC>(v, lane, xb, k, j);
+}
+
+// Descending sort of keys[0, np2) in LDS (256 <= np2 <= 2048, a power of
+// two, padded with zeros) by np2 / 128 waves of the workgroup, 128 keys per
+// wave in registers: stages with partners more than 64 apart exchange through
+// LDS, alternating between keys[0, 2048) and keys[2048, 4096), one workgroup
+// barrier each; the others run inside the waves.  Every thread of the
+// workgroup calls it; keys is visible to the workgroup on entry and on return.
+__device__ void block_sort_desc(uint64_t *keys, int np2) {
+    const int lane = threadIdx.x & 63, xb = 128 * (threadIdx.x >> 6);
+    const bool act = xb < np2;
+    uint64_t v[2] = {0ull, 0ull};
+    if (act) {
+        v[0] = keys[xb + lane];
+        v[1] = keys[xb + lane + 64];
+        wave_sort128<true>(v, lane, xb);
+    }
+    int buf = 0;
+    for (int k = 256; k <= np2; k <<= 1) {
+        for (int j = k >> 1; j >= 128; j >>= 1) {
+            uint64_t *bk = keys + 2048 * buf;
+            if (act) {
+                bk[xb + lane] = v[0];
+                bk[xb + lane + 64] = v[1];
+            }
+            __syncthreads();
+            if (act) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const int x = lane + 64 * h;
-                    const T o = shfl_xor_key(v[h], j);
-                    const bool up = ((x & k) == 0) != DESC;     // x's block is sorted ascending
-                    const bool first = (x & j) == 0;            // x is the lower of the pair
-                    const T hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
+                    const int x = xb + lane + 64 * h;
+                    const uint64_t o = bk[x ^ j];
+                    const bool up = (x & k) != 0, first = (x & j) == 0;
+                    const uint64_t hi = v[h] > o ? v[h] : o, lo = v[h] > o ? o : v[h];
                     v[h] = (up == first) ? lo : hi;
                 }
             }
+            buf ^= 1;
         }
+        if (act) {
+            wave_stage<true>(v, lane, xb, k, 64);
+            wave_stage<true>(v, lane, xb, k, 32);
+            wave_stage<true>(v, lane, xb, k, 16);
+            wave_stage<true>(v, lane, xb, k, 8);
+            wave_stage<true>(v, lane, xb, k, 4);
+            wave_stage<true>(v, lane, xb, k, 2);
+            wave_stage<true>(v, lane, xb, k, 1);
+        }
+    }
+    __syncthreads();
+    if (act) {
+        keys[xb + lane] = v[0];
+        keys[xb + lane + 64] = v[1];
+    }
+    __syncthreads();
 }
 
 // sort a context list of n <= kMaxCtx tokens ascending in place (LDS):
@@ -682,6 +742,8 @@ __global__ __launch_bounds__(kRowThreads) void sample_row_kernel(SampleArgs a) {
                 keys[tid + 64] = v[1];
             }
             __syncthreads();
+        } else if (np2 <= 2048) {
+            block_sort_desc(keys, np2);
         } else {
             for (int k = 2; k <= np2; k <<= 1) {       // bitonic sort, descending
                 for (int j = k >> 1; j > 0; j >>= 1) {
