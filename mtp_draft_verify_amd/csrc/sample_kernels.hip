@@ -600,13 +600,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 
                         if (v == v && expf(v - ref) >= a.min_p) kmask |= 1u << ((b * KB + k) * E + e);
                     }
     }
-    // Slots: an exclusive prefix sum of the threads' counts over the
-    // workgroup and one reservation per chunk, so no wave waits on an atomic
-    // inside the token loop (the listed superset can be ten times the
-    // survivors).  Slot order within the list does not matter: the row
+    // Slots: an exclusive prefix sum of the threads' counts over the wave
+    // and one reservation per wave (each row's counter has a line of its
+    // own), so no wave waits on an atomic inside the token loop or on the
+    // other waves.  Slot order within the list does not matter: the row
     // kernel sorts it or sums it in fixed point.
-    __shared__ int wtot[4], wbase_sh;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int cnt = __popc(kmask);
     int incl = cnt;
 #pragma unroll
@@ -614,15 +613,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(E == 4 ? 6 
         const int y = __shfl_up(incl, off);
         if (lane >= off) incl += y;
     }
-    if (lane == 63) wtot[wid] = incl;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int tot = (wtot[0] + wtot[1]) + (wtot[2] + wtot[3]);
-        wbase_sh = tot > 0 ? atomicAdd(&a.cand_n[row * kRowCtrStride], tot) : 0;
-    }
-    __syncthreads();
-    int slot = wbase_sh + incl - cnt;
-    for (int w = 0; w < wid; ++w) slot += wtot[w];
+    const int wtot = __shfl(incl, 63);
+    if (wtot == 0) return;
+    int wbase = 0;
+    if (lane == 0) wbase = atomicAdd(&a.cand_n[row * kRowCtrStride], wtot);
+    int slot = __shfl(wbase, 0) + incl - cnt;
     // each thread walks the set bits of its kmask (the slots follow position
     // order); the listed value is picked out of the registers by position
     for (uint32_t m = kmask; m != 0u; m &= m - 1u) {
