@@ -736,21 +736,14 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
                 wcm[wid][4 * (lane >> 4) + q] = cm[q];
                 wcs[wid][4 * (lane >> 4) + q] = cs[q];
             }
-        __syncthreads();
-        if (tid < S) {
-            uint64_t k = wbest[0][tid];
-            for (int w = 1; w < 4; ++w) k = wbest[w][tid] > k ? wbest[w][tid] : k;
-            atomicMax((unsigned long long *)&a.keys[tid], (unsigned long long)k);
-            if (conf) {
-                float m = wcm[0][tid], sm = wcs[0][tid];
-                for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w][tid], wcs[w][tid]);
-                a.conf[(int64_t)tid * kConfSlots + hb] = ConfPart{m, sm};
-            }
-        }
     }
+    // The post-projection tile(s) of this workgroup: tb = hb, hb + the grid,
+    // ...  Each wave multiplies its unit as soon as its head tiles are done
+    // and leaves the partial sums in LDS; the first tile shares the barrier of
+    // the argmax reduction, so its sum and store go out beside the atomics.
     float *h_out = (a.step == a.n_steps - 1 && a.io->out_h_last) ? a.io->out_h_last : a.h_out;
     const int j16 = lane & 15, g = lane >> 4;
-    for (int tb = hb; tb < n_post_tiles; tb += (int)gridDim.x) {
+    auto post_mma = [&](int tb) {
         if (tb != hb && post_unit) load_post(tb);
         f32x4_t ph = {0.f, 0.f, 0.f, 0.f}, pl = {0.f, 0.f, 0.f, 0.f};
         if (post_unit) {
@@ -775,7 +768,8 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
             }
         }
         post_part[wid][lane] = PACK ? ph : ph + pl;
-        __syncthreads();
+    };
+    auto post_store = [&](int tb) {
         if (wid == 0 && (!PACK || lane < 32)) {
             // lane (j16, g) holds row 16 tb + j16 for sequences 4g .. 4g+3
             // (packed: hi + lo of the same wave first, as unpacked)
@@ -787,7 +781,25 @@ __device__ __forceinline__ void mm_head_body(const HeadArgs &a, int tiles_per_wg
             for (int q = 0; q < 4; ++q)
                 if (r < a.dh && 4 * g + q < S) h_out[(int64_t)(4 * g + q) * a.dh + r] = z[q];
         }
+    };
+    if (hb < n_post_tiles) post_mma(hb);
+    __syncthreads();
+    if (tid < S) {
+        uint64_t k = wbest[0][tid];
+        for (int w = 1; w < 4; ++w) k = wbest[w][tid] > k ? wbest[w][tid] : k;
+        atomicMax((unsigned long long *)&a.keys[tid], (unsigned long long)k);
+        if (a.conf) {
+            float m = wcm[0][tid], sm = wcs[0][tid];
+            for (int w = 1; w < 4; ++w) conf_merge(m, sm, wcm[w][tid], wcs[w][tid]);
+            a.conf[(int64_t)tid * kConfSlots + hb] = ConfPart{m, sm};
+        }
+    }
+    if (hb < n_post_tiles) post_store(hb);
+    for (int tb = hb + (int)gridDim.x; tb < n_post_tiles; tb += (int)gridDim.x) {
+        __syncthreads();        // the previous tile's partial sums are read
+        post_mma(tb);
         __syncthreads();
+        post_store(tb);
     }
 }
 
