@@ -319,11 +319,16 @@ __device__ __forceinline__ void raw_load_unit(const void *W, int rows, int d, in
         for (int q = 0; q < 8; ++q)
             u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * (q & 3) + rq, rows - 1) * d + 128 * (q >> 2));
     } else {
-        // W: the unit-order copy, padded to whole tiles (row0 is a tile start)
+        // W: the unit-order copy, padded to whole tiles (row0 is a tile start).
+        // Plain (cached) loads: a draft step's KV stream is non-temporal, so
+        // part of the head (285 MB at V = 262144, d = 1024) is still in the
+        // last-level cache when the next step reads it (8 sequences x 131072
+        // cells: 51.6 us non-temporal, 48.8 us plain; with plain KV loads as
+        // well the head takes 55.4 us).
         const uint8_t *ub = (const uint8_t *)W + ((int64_t)(row0 >> 4) * (d >> 8) + c) * kQ8UnitBytes;
 #pragma unroll
-        for (int p = 0; p < 4; ++p) u.r[p] = ld_nt4(ub + 1024 * p + 16 * lane);
-        u.sc = ld_nt4(ub + 4096 + 16 * (lane & 15));
+        for (int p = 0; p < 4; ++p) u.r[p] = *(const u32x4_t *)(ub + 1024 * p + 16 * lane);
+        u.sc = *(const u32x4_t *)(ub + 4096 + 16 * (lane & 15));
     }
 }
 
