@@ -320,11 +320,13 @@ __device__ __forceinline__ void raw_load_unit(const void *W, int rows, int d, in
             u.r[q] = ld_nt4(wc + (int64_t)min(row0 + 4 * (q & 3) + rq, rows - 1) * d + 128 * (q >> 2));
     } else {
         // W: the unit-order copy, padded to whole tiles (row0 is a tile start).
-        // Plain (cached) loads: a draft step's KV stream is non-temporal, so
-        // part of the head (285 MB at V = 262144, d = 1024) is still in the
-        // last-level cache when the next step reads it (8 sequences x 131072
-        // cells: 51.6 us non-temporal, 48.8 us plain; with plain KV loads as
-        // well the head takes 55.4 us).
+        // Plain (cached) loads, measured in the draft round of 8 sequences x
+        // 131072 cells (285 MB head, V = 262144, d = 1024): 51.6 us with
+        // non-temporal loads, 48.8 us plain.  With plain KV loads in the
+        // round as well the head takes 55.4 us, so the gain goes with the KV
+        // stream's non-temporal loads leaving the last-level cache to the
+        // head between steps; holding a fixed 140-240 MB of it cached (the
+        // rest non-temporal) gains nothing more.
         const uint8_t *ub = (const uint8_t *)W + ((int64_t)(row0 >> 4) * (d >> 8) + c) * kQ8UnitBytes;
 #pragma unroll
         for (int p = 0; p < 4; ++p) u.r[p] = *(const u32x4_t *)(ub + 1024 * p + 16 * lane);
