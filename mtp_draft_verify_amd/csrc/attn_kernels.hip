@@ -230,19 +230,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // ----------------------------------------------------------------------------
 // bf16 KV: scores on the matrix cores, softmax and P.V on the vector ALUs
 // ----------------------------------------------------------------------------
-// Workgroup = (split, kv head, sequence) as above; each wave owns 16-cell
-// tiles w, w+4, ... of the split.  Per tile the G query heads meet the 16
-// K rows in v_mfma_f32_16x16x32_bf16 (A = K, cells as rows, straight from
-// HBM; B = the scaled query as bf16 hi and lo halves, 2G of the 16
-// columns), so a score costs no vector work.  Lane j < G of each 16-lane
-// row then owns head j for 4 cells: it adds the lo column, keeps the online
-// softmax (m, l) in base 2 and publishes p through LDS; every lane then
-// accumulates P.V for its HD/64 dims of all G heads from the tile's V rows,
-// which it loads as one coalesced 512-byte row per cell.  The next tile's
-// K and V are loaded before the current one is used; loads past the
-// wave's last tile re-read its first tile (cached) so the loop body stays
-// straight-line.  Positions past the split end are clamped to its last
-// position (never an unseen cell) and masked to -inf.
+// Workgroup = (split, kv head group, sequence), serving nh kv heads of the
+// group (nh = the sequence's heads_wg: 1, or 2 at long context).  Its four
+// waves are dealt out head-fastest: wave w serves kv head w % nh of the
+// group and the split's 16-cell tiles w / nh, w / nh + 4 / nh, ...  With
+// nh = 2 the waves of a workgroup read both heads' halves of the same cell
+// rows together, one contiguous run of 2 * hd * 2 bytes per cell.  Per tile
+// the G query heads of a wave's kv head meet the 16 K rows in
+// v_mfma_f32_16x16x32_bf16 (A = K, cells as rows, straight from HBM; B =
+// the scaled query as bf16 hi and lo halves, 2G of the 16 columns), so a
+// score costs no vector work.  Lane j < G of each 16-lane row then owns
+// head j for 4 cells: it adds the lo column, keeps the online softmax
+// (m, l) in base 2; every lane then accumulates P.V for its HD/64 dims of
+// all G heads from the tile's V rows, which it loads as one coalesced row
+// per cell.  The next tile's K and V are loaded before the current one is
+// used.  Positions past the split end are clamped to its last position
+// (never an unseen cell) and masked to -inf.  NHM is the largest nh the
+// instantiation serves; a sequence with nh = 1 takes the same operations in
+// the same order in either instantiation.
 // STREAM: the KV a draft step reads is far larger than the last-level
 // cache, so nothing read now is still cached when the next step reads it:
 // the tile loads are non-temporal (measured with loads alone over 8 x 131072
@@ -275,34 +280,40 @@ __device__ __forceinline__ void bf16_pair(uint32_t w, float &lo, float &hi) {
     hi = __uint_as_float(w & 0xFFFF0000u);
 }
 
-template <int HD, int G, bool STREAM>
-__global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
-    constexpr int KS = HD / 32, DPL = HD / 64;
-    static_assert(2 * G <= 16, "hi and lo query columns must fit one MFMA tile");
-    __shared__ __attribute__((aligned(16))) float qs[G][HD];
-    __shared__ __attribute__((aligned(16))) float cs[HD / 2], sn[HD / 2];
-    __shared__ float wm[4][G], wl[4][G];
-    __shared__ float wacc[4][G][HD];
-    __shared__ abf16x8_t qbs[KS][64];
+// LDS of one attention workgroup, sized for NHM kv heads
+template <int HD, int G, int NHM>
+struct AttnSmem {
+    static constexpr int KS = HD / 32;
+    alignas(16) float qs[G * NHM][HD];
+    alignas(16) float cs[HD / 2];
+    alignas(16) float sn[HD / 2];
+    float wm[4][G], wl[4][G];
+    float wacc[4][G][HD];
+    abf16x8_t qbs[NHM][KS][64];
+};
 
-    const bool kv_fast = a.S == 1;
-    const int kvh = kv_fast ? blockIdx.x : blockIdx.y, split = kv_fast ? blockIdx.y : blockIdx.x, s = blockIdx.z;
+// One workgroup's split for NH kv heads (NH <= NHM, compile time).
+template <int HD, int G, int NH, int NHM, bool STREAM>
+__device__ __forceinline__ void attn_mm_body(const AttnArgs &a, AttnSmem<HD, G, NHM> &sm, int kvg, int split, int s) {
+    constexpr int KS = HD / 32, DPL = HD / 64;
     const SeqParams &sqp = a.seqs[s];
     const SrcParams &sp = sqp.src[a.src];
-    if (split >= sp.n_split) return;
+    constexpr int nh = NH, wph = 4 / NH, nqh = G * NH;     // kv heads, waves per kv head, query heads
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hw = wid % NH, wt = wid / NH;                     // head in the group, first tile
+    const int kvh = kvg * nh + hw;
     const int j16 = lane & 15, g = lane >> 4;
     const int pbeg = split * sp.split_len;
     const int npos = min(sp.split_len, sp.n_vis - pbeg);
     const int ntile = (npos + 15) / 16;
-    const int nt = ntile > wid ? (ntile - wid + 3) / 4 : 0;     // this wave's tiles
+    const int nt = ntile > wt ? (ntile - wt + wph - 1) / wph : 0;   // this wave's tiles
 
     const uint16_t *kb = (const uint16_t *)sp.k + (int64_t)kvh * HD;
     const uint16_t *vb = (const uint16_t *)sp.v + (int64_t)kvh * HD;
     auto cell_of = [&](int pi) { return src_cell(sp, pbeg + min(pi, npos - 1)); };
     auto load = [&](int i, AttnTile<HD, G> &t) {
-        const int p0 = i < nt ? 16 * (wid + 4 * i) : 16 * wid;
+        const int p0 = i < nt ? 16 * (wt + wph * i) : 16 * wt;
         const uint16_t *kp = kb + (int64_t)cell_of(p0 + j16) * sp.cell_stride + 8 * g;
 #pragma unroll
         for (int u = 0; u < KS; ++u) t.k[u] = kv_load<STREAM, u32x4_t>(kp + 32 * u);
@@ -317,14 +328,14 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
 
     // --- prologue: per-head q RMSNorm; RoPE follows in the operand build ---
     constexpr int QPL = (HD + 63) / 64;
-    constexpr int GW = (G + 3) / 4;
+    constexpr int GW = (G * NH + 3) / 4;
     float qv[GW][QPL], gq[QPL];
 #pragma unroll
     for (int i = 0; i < QPL; ++i) gq[i] = (lane + 64 * i < HD) ? a.g_q[lane + 64 * i] : 0.f;
 #pragma unroll
     for (int jj = 0; jj < GW; ++jj) {
         const int j = wid + 4 * jj;
-        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvh * G + min(j, G - 1)) * HD;
+        const float *qh = a.q + ((int64_t)s * a.Hq + (int64_t)kvg * nqh + min(j, nqh - 1)) * HD;
 #pragma unroll
         for (int i = 0; i < QPL; ++i) qv[jj][i] = (lane + 64 * i < HD) ? qh[lane + 64 * i] : 0.f;
     }
@@ -336,13 +347,13 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
         const double red = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
         float sv, cv;
         sincosf((float)red, &sv, &cv);
-        cs[tid] = cv;
-        sn[tid] = sv;
+        sm.cs[tid] = cv;
+        sm.sn[tid] = sv;
     }
 #pragma unroll
     for (int jj = 0; jj < GW; ++jj) {
         const int j = wid + 4 * jj;
-        if (j < G) {
+        if (j < nqh) {
             float ss = 0.f;
 #pragma unroll
             for (int i = 0; i < QPL; ++i) ss = fmaf(qv[jj][i], qv[jj][i], ss);
@@ -350,28 +361,30 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
             const float r = 1.0f / sqrtf(ss / (float)HD + a.eps);
 #pragma unroll
             for (int i = 0; i < QPL; ++i)
-                if (lane + 64 * i < HD) qs[j][lane + 64 * i] = qv[jj][i] * r * gq[i];
+                if (lane + 64 * i < HD) sm.qs[j][lane + 64 * i] = qv[jj][i] * r * gq[i];
         }
     }
     __syncthreads();
 
-    // B operand: column h < G holds the hi half of query head h after RoPE,
-    // column 8 + h its lo half (scaled by scale * log2(e)); the other
-    // columns are zero.  Each wave builds KS / 4 of the KS steps and puts
-    // them in LDS, where every wave reads the whole operand back.  A lane's
-    // 8 values of a step are 8 consecutive dims inside one rotation half
-    // (which half depends on the step only); it reads them and their
-    // partners from a clamped head row with 16-byte LDS reads and zeroes
-    // dead columns afterwards: a per-lane guard on the reads would turn into
-    // a branch and a wait around each of them.
+    // B operand of each kv head of the workgroup: column h < G holds the hi
+    // half of its query head h after RoPE, column 8 + h its lo half (scaled
+    // by scale * log2(e)); the other columns are zero.  Each wave builds
+    // nh * KS / 4 of the nh * KS steps and puts them in LDS, where every wave
+    // reads its head's operand back.  A lane's 8 values of a step are 8
+    // consecutive dims inside one rotation half (which half depends on the
+    // step only); it reads them and their partners from a clamped head row
+    // with 16-byte LDS reads and zeroes dead columns afterwards: a per-lane
+    // guard on the reads would turn into a branch and a wait around each of
+    // them.
     {
         const int h = j16 & 7;
         const bool live = h < G;
-        const float *qrow = qs[min(h, G - 1)];
         const float sc = a.scale * kLog2e;
 #pragma unroll
-        for (int uu = 0; uu < KS / 4; ++uu) {
-            const int u = wid * (KS / 4) + uu;
+        for (int uu = 0; uu < NH * KS / 4; ++uu) {
+            const int v = wid * (NH * KS / 4) + uu;
+            const int hb = v / KS, u = v % KS;
+            const float *qrow = sm.qs[hb * G + min(h, G - 1)];
             const bool first = 32 * u < HD / 2;             // rotation half, uniform per step
             const int c0 = (32 * u + 8 * g) % (HD / 2);
             float x0[8], x1[8], cv[8], sv[8];
@@ -382,23 +395,23 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
             };
             rd8(qrow + c0, x0);
             rd8(qrow + c0 + HD / 2, x1);
-            rd8(cs + c0, cv);
-            rd8(sn + c0, sv);
+            rd8(sm.cs + c0, cv);
+            rd8(sm.sn + c0, sv);
             abf16x8_t qv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float r0 = x0[e] * cv[e] - x1[e] * sv[e], r1 = x0[e] * sv[e] + x1[e] * cv[e];
                 const float x = live ? (first ? r0 : r1) * sc : 0.f;
-                const __bf16 hb = (__bf16)x;
-                qv[e] = j16 < 8 ? hb : (__bf16)(x - (float)hb);
+                const __bf16 hbf = (__bf16)x;
+                qv[e] = j16 < 8 ? hbf : (__bf16)(x - (float)hbf);
             }
-            qbs[u][lane] = qv;
+            sm.qbs[hb][u][lane] = qv;
         }
     }
     __syncthreads();
     abf16x8_t qb[KS];
 #pragma unroll
-    for (int u = 0; u < KS; ++u) qb[u] = qbs[u][lane];
+    for (int u = 0; u < KS; ++u) qb[u] = sm.qbs[hw][u][lane];
 
     float m = -INFINITY, l = 0.f;           // head j16 (lanes j16 < G)
     float acc[G][DPL];
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
         const f32x4_t d = d0 + d1;
         // lane (j16 < G, g): head j16, cells 4g .. 4g+3; its lo column sits
         // 8 lanes away in the same row (a rotate by 8 either way)
-        const int pt = 16 * (wid + 4 * i) + 4 * g;
+        const int pt = 16 * (wt + wph * i) + 4 * g;
         float sc[4], mt = -INFINITY;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -488,29 +501,31 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
     if (i + 1 < nt) tile(i + 1, buf[1]);
     if (i + 2 < nt) tile(i + 2, buf[0]);
 
-    // --- merge the four waves' states -> one partial per query head --------
+    // --- merge the states of each kv head's waves -> one partial per query head
     if (j16 < G && g == 0) {
-        wm[wid][j16] = m;
-        wl[wid][j16] = l;
+        sm.wm[wid][j16] = m;
+        sm.wl[wid][j16] = l;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) wacc[wid][h][DPL * lane + e] = acc[h][e];
+        for (int e = 0; e < DPL; ++e) sm.wacc[wid][h][DPL * lane + e] = acc[h][e];
     __syncthreads();
-    for (int i = tid; i < G * HD; i += kBlock) {
+    for (int i = tid; i < nqh * HD; i += kBlock) {
         const int j = i / HD, c = i - j * HD;
+        const int hh = j / G, jh = j - hh * G;          // kv head in the workgroup, query head of it
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][j]);
+        for (int k = 0; k < wph; ++k) M = fmaxf(M, sm.wm[hh + nh * k][jh]);
         float L = 0.f, av = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float wt = wm[w][j] == -INFINITY ? 0.f : exp2f(wm[w][j] - M);
-            L = fmaf(wl[w][j], wt, L);
-            av = fmaf(wacc[w][j][c], wt, av);
+        for (int k = 0; k < wph; ++k) {
+            const int w = hh + nh * k;
+            const float wt = sm.wm[w][jh] == -INFINITY ? 0.f : exp2f(sm.wm[w][jh] - M);
+            L = fmaf(sm.wl[w][jh], wt, L);
+            av = fmaf(sm.wacc[w][jh][c], wt, av);
         }
-        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvh * G + j) * MTP_MAX_SPLITS + split) * (HD + kPartHead);
+        float *pp = a.part + (((int64_t)s * a.Hq + (int64_t)kvg * nqh + j) * MTP_MAX_SPLITS + split) * (HD + kPartHead);
         pp[kPartHead + c] = av;
         if (c == 0) {
             pp[0] = M;
@@ -519,32 +534,71 @@ __global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
     }
 }
 
+template <int HD, int G, int NHM, bool STREAM>
+__global__ __launch_bounds__(256) void attn_mm_kernel(AttnArgs a) {
+    static_assert(2 * G <= 16, "hi and lo query columns must fit one MFMA tile");
+    static_assert(NHM == 1 || NHM == 2, "one or two kv heads per workgroup");
+    static_assert((HD / 32) % 4 == 0, "every wave builds the same number of operand steps");
+    __shared__ AttnSmem<HD, G, NHM> sm;
+    // Grid: (kv head, split) for one sequence, so the kv heads of a split run
+    // together; (split, kv head, sequence) for several; and (split, sequence,
+    // kv head) when some sequence's workgroups serve two kv heads.  There the
+    // second kv head's workgroups of such a sequence have nothing to do: they
+    // come last instead of between the working ones, and the grid leaves
+    // them out when every sequence of the launch serves two.
+    int kvg, split, s;
+    if (NHM == 2) {
+        split = blockIdx.x; s = blockIdx.y; kvg = blockIdx.z;
+    } else if (a.S == 1) {
+        kvg = blockIdx.x; split = blockIdx.y; s = 0;
+    } else {
+        split = blockIdx.x; kvg = blockIdx.y; s = blockIdx.z;
+    }
+    const SrcParams &sp = a.seqs[s].src[a.src];
+    if (split >= sp.n_split) return;
+    if (NHM == 2 && sp.heads_wg == 2) {             // uniform per workgroup
+        if (2 * kvg < a.Hkv) attn_mm_body<HD, G, (NHM == 2 ? 2 : 1), NHM, STREAM>(a, sm, kvg, split, s);
+    } else {
+        attn_mm_body<HD, G, 1, NHM, STREAM>(a, sm, kvg, split, s);
+    }
+}
+
 hipError_t launch_attn(int kv_dtype, const AttnArgs &a, int max_split, hipStream_t st) {
     const dim3 grid = a.S == 1 ? dim3(a.Hkv, max_split, 1) : dim3(max_split, a.Hkv, a.S);
+    const dim3 grid_wide(max_split, a.S, a.wide == 2 ? a.Hkv / 2 : a.Hkv);
     const int G = a.Hq / a.Hkv;
 #define MTP_ATTN_CASE(KT, HDV, GV)                                                                  \
     if (a.hd == HDV && G == GV) {                                                                   \
         mtp_launch((attn_kernel<KT, HDV / 16, GV>), grid, dim3(kBlock), 0, st, a);          \
         return hipGetLastError();                                                                   \
     }
+#define MTP_ATTN_MM_NH(HDV, GV, NHV)                                                                \
+    if (a.stream_kv)                                                                                \
+        mtp_launch((attn_mm_kernel<HDV, GV, NHV, true>), NHV == 2 ? grid_wide : grid, dim3(kBlock), 0, st, a); \
+    else                                                                                            \
+        mtp_launch((attn_mm_kernel<HDV, GV, NHV, false>), NHV == 2 ? grid_wide : grid, dim3(kBlock), 0, st, a); \
+    return hipGetLastError();
 #define MTP_ATTN_MM(HDV, GV)                                                                        \
     if (a.hd == HDV && G == GV) {                                                                   \
-        if (a.stream_kv)                                                                            \
-            mtp_launch((attn_mm_kernel<HDV, GV, true>), grid, dim3(kBlock), 0, st, a);      \
-        else                                                                                        \
-            mtp_launch((attn_mm_kernel<HDV, GV, false>), grid, dim3(kBlock), 0, st, a);     \
-        return hipGetLastError();                                                                   \
+        if (a.wide) { MTP_ATTN_MM_NH(HDV, GV, 2) }                                                  \
+        MTP_ATTN_MM_NH(HDV, GV, 1)                                                                  \
+    }
+#define MTP_ATTN_MM1(HDV, GV)                                                                       \
+    if (a.hd == HDV && G == GV) {                                                                   \
+        MTP_ATTN_MM_NH(HDV, GV, 1)                                                                  \
     }
     if (kv_dtype == MTP_BF16) {
         MTP_ATTN_MM(256, 4)
         MTP_ATTN_MM(256, 2)
         MTP_ATTN_MM(256, 1)
-        MTP_ATTN_MM(256, 8)
+        MTP_ATTN_MM1(256, 8)      // two heads of 8 query heads each would not fit two waves per SIMD
         MTP_ATTN_MM(128, 8)
         MTP_ATTN_MM(128, 4)
         MTP_ATTN_MM(128, 2)
         MTP_ATTN_MM(128, 1)
     }
+#undef MTP_ATTN_MM_NH
+#undef MTP_ATTN_MM1
 #undef MTP_ATTN_MM
     if (kv_dtype == MTP_BF16) {
         MTP_ATTN_CASE(uint16_t, 256, 4)

@@ -92,7 +92,7 @@ struct mtp_ctx {
     // past kMaxGraphs; an evicted graph may still be queued on the stream, so
     // it is destroyed only once an event recorded behind it has completed
     hipStream_t cap_stream = nullptr;
-    struct Graph { int key[8]; hipGraph_t g; hipGraphExec_t exec; uint64_t last_use; };
+    struct Graph { int key[11]; hipGraph_t g; hipGraphExec_t exec; uint64_t last_use; };
     std::vector<Graph> graphs;
     uint64_t use_clock = 0;
     struct Retired { hipGraph_t g; hipGraphExec_t exec; hipEvent_t done; };
@@ -439,9 +439,11 @@ extern "C" int mtp_profile_read(mtp_ctx *c, int cls, double *total_ms, int64_t *
 // draft chain
 // ---------------------------------------------------------------------------
 // Split-K geometry of one sequence's visible cells: at most MTP_MAX_SPLITS
-// power-of-two splits of at least 64 cells (one 16-cell tile per wave).  It
-// depends on the sequence alone (and on whether it is alone in the batch),
-// so a sequence gets the same partition whatever else is in the batch.  In a
+// power-of-two splits of at least 64 cells (one 16-cell tile per wave), and
+// at most MTP_MAX_SPLITS / 2 when its workgroups serve two kv heads each
+// (kWideCtx).  It depends on the sequence alone (and on whether it is alone
+// in the batch), so a sequence gets the same partition and the same
+// arithmetic whatever else is in the batch.  In a
 // batch, sequences of 2048 or more visible cells split no finer than 128
 // cells, so that each wave overlaps one tile's loads with the other's
 // arithmetic; workgroups are plentiful there (measured, attention + merge:
@@ -477,7 +479,9 @@ static int src_geometry(const mtp_model_desc &d, const mtp_seq &sq, int src, boo
         p.c0 = first;
         p.n_vis = p.n_sink + (sq.attn_pos - first + 1);
     }
-    const int64_t per = (p.n_vis + MTP_MAX_SPLITS - 1) / MTP_MAX_SPLITS;
+    p.heads_wg = attn_heads_per_wg(d.kv_dtype, d.head_dim, d.n_head_q, d.n_head_kv, p.n_vis);
+    const int64_t max_split = p.heads_wg == 2 ? MTP_MAX_SPLITS / 2 : MTP_MAX_SPLITS;
+    const int64_t per = (p.n_vis + max_split - 1) / max_split;
     const int64_t min_split = (batched && p.n_vis >= 2048) ? 128 : 64;
     p.split_len = (int32_t)std::max<int64_t>(min_split, pow2ceil(per));
     p.n_split = (p.n_vis + p.split_len - 1) / p.split_len;
@@ -506,6 +510,7 @@ struct ChainShape {
     int logits;     // the caller asked for draft logits
     int conf;       // the caller asked for per-step confidence / the p_min trim
     int stream_kv;  // a step's visible KV exceeds kStreamKvBytes (non-temporal KV loads)
+    int wide[MTP_N_SRC];    // sequences whose attention workgroups serve two kv heads: 0 none, 1 some, 2 all
 };
 
 // Enqueue the whole draft chain (N steps of a1..a7, then the hand-off of the
@@ -570,6 +575,7 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
                     aa.scale = d.attn_scale; aa.Hq = d.n_head_q; aa.Hkv = d.n_head_kv; aa.hd = d.head_dim;
                     aa.S = S; aa.src = src; aa.step = k; aa.seqs = dp; aa.part = c->part;
                     aa.stream_kv = sh.stream_kv;
+                    aa.wide = sh.wide[src];
                     e = launch_attn(d.kv_dtype, aa, sh.split[src], st);
                 }
             }
@@ -665,7 +671,8 @@ static hipError_t enqueue_chain(mtp_ctx *c, const ChainShape &sh, hipStream_t st
 
 // The captured chain for a launch shape (built on first use).
 static hipGraphExec_t chain_graph(mtp_ctx *c, const ChainShape &sh) {
-    const int key[8] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf, sh.stream_kv};
+    const int key[11] = {sh.S, sh.N, sh.split[0], sh.split[1], sh.split[2], sh.logits, sh.conf, sh.stream_kv,
+                         sh.wide[0], sh.wide[1], sh.wide[2]};
     ++c->use_clock;
     reap_graphs(c, false);
     for (auto &g : c->graphs)
@@ -751,7 +758,7 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
     CallIO *hio = (CallIO *)hb;
     SeqParams *hp = (SeqParams *)(hb + sizeof(CallIO));
     std::memset(hio, 0, sizeof(CallIO));
-    ChainShape sh{n_seq, n_steps, {0, 0, 0}, out_logits != nullptr, out_conf != nullptr, 0};
+    ChainShape sh{n_seq, n_steps, {0, 0, 0}, out_logits != nullptr, out_conf != nullptr, 0, {0, 0, 0}};
     int64_t kv_step_bytes = 0;          // visible K + V bytes one draft step reads
     for (int s = 0; s < n_seq; ++s) {
         const mtp_seq &sq = seqs[s];
@@ -764,11 +771,14 @@ extern "C" int mtp_draft_block_conf(mtp_ctx *c, int32_t n_seq, const mtp_seq *se
             int rc = src_geometry(d, sq, src, n_seq > 1, p.src[src]);
             if (rc) return rc;
             sh.split[src] = std::max(sh.split[src], p.src[src].n_split);
+            sh.wide[src] += p.src[src].heads_wg == 2;       // counted here, coded after the loop
         }
         for (int l = 0; l < d.n_blocks; ++l)
             kv_step_bytes += (int64_t)p.src[d.block_src[l]].n_vis * d.n_head_kv * d.head_dim * 2 * elem_size(d.kv_dtype);
     }
     sh.stream_kv = kv_step_bytes > kStreamKvBytes;
+    for (int src = 0; src < MTP_N_SRC; ++src)
+        sh.wide[src] = sh.wide[src] == 0 ? 0 : sh.wide[src] == n_seq ? 2 : 1;
     // grids are sized for a power-of-two split count so one captured chain
     // serves a range of context lengths (surplus workgroups exit at once)
     for (int src = 0; src < MTP_N_SRC; ++src)

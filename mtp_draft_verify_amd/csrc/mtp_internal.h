@@ -22,6 +22,8 @@ struct SrcParams {
     int32_t c0;
     int32_t split_len;
     int32_t n_split;
+    int32_t heads_wg;       // kv heads one attention workgroup serves (1, or 2 at long context)
+    int32_t pad;
 };
 
 struct SeqParams {
@@ -146,7 +148,28 @@ struct AttnArgs {
     const SeqParams *seqs;
     float *part;            // [S, Hq, MTP_MAX_SPLITS, kPartHead + hd]  (m, l, pad..., o[hd])
     int32_t stream_kv;      // a step's KV exceeds the last-level cache: non-temporal KV loads
+    int32_t wide;           // sequences with heads_wg 2 for this source: 0 none, 1 some, 2 all
 };
+
+// Visible cells from which a sequence's bf16 attention workgroups serve two
+// kv heads each (the waves then read whole cell rows of both heads together)
+// and its split count is at most 64.  Measured over 8 sequences x 131072
+// cells, 2 kv heads x 256 dims: 328.5 us per launch with one head and
+// 1024-cell splits, 324.5 us with two heads and 2048-cell splits; with
+// 4096-cell splits 344 us.  Shorter contexts keep one head per workgroup
+// (one sequence over 8192 cells: 8.4 -> 11.8 us with two).
+static constexpr int32_t kWideCtx = 65536;
+
+// kv heads per attention workgroup for a sequence of n_vis visible cells:
+// 2 on the bf16 matrix-core path at long context with an even kv head count
+// (not at head_dim 256 with 8 query heads per kv head, whose registers would
+// not fit two waves per SIMD).
+inline int attn_heads_per_wg(int kv_dtype, int hd, int n_head_q, int n_head_kv, int64_t n_vis) {
+    const int G = n_head_kv > 0 ? n_head_q / n_head_kv : 0;
+    const bool mm = kv_dtype == MTP_BF16 && ((hd == 256 && (G == 1 || G == 2 || G == 4)) ||
+                                             (hd == 128 && (G == 1 || G == 2 || G == 4 || G == 8)));
+    return (mm && n_head_kv % 2 == 0 && n_vis >= kWideCtx) ? 2 : 1;
+}
 
 // KV bytes per draft step above which the attention streams its KV with
 // non-temporal loads: past this a step's KV cannot stay in the device's

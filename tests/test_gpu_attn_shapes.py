@@ -76,3 +76,32 @@ def test_degenerate_and_boundary_contexts_match_oracle(orc, kv, wd, hd, hq, hkv)
         one = g.run(dr, seq_idx=[s])
         c1 = compare_draft(m, one, orc.draft_block(m, dr, seq_idx=[s]), [0])
         assert c1.near_ties == 0
+
+
+# bf16 shapes whose long-context sequences run two kv heads per workgroup
+WIDE_CASES = [c for c in CASES if c[0] == syn.BF16 and c[4] % 2 == 0 and not (c[2] == 256 and c[3] // c[4] == 8)]
+
+
+@pytest.mark.parametrize("kv,wd,hd,hq,hkv", WIDE_CASES,
+                         ids=[f"bf16-hd{c[2]}-hq{c[3]}-hkv{c[4]}" for c in WIDE_CASES])
+def test_two_heads_per_workgroup_long_context_matches_oracle(orc, kv, wd, hd, hq, hkv):
+    """From 65536 visible cells a sequence's attention workgroups serve two
+    kv heads each, over at most 64 splits: 70001 cells split into 35 splits
+    of 2048, the last holding 369 cells.  Alone (one-sequence grid), and in a
+    batch beside a 3000-cell sequence that keeps one head per workgroup in
+    the same launch."""
+    name = f"hd={hd} Hq={hq} Hkv={hkv}"
+    log(f"case two kv heads per workgroup: {name}, ctx 70001 alone and with 3000")
+    m = syn.make_model(61 + hd + 7 * hq + hkv, d_model=256, d_hprev=256, n_blocks=1, n_head_q=hq, n_head_kv=hkv,
+                       head_dim=hd, d_ff=512, n_vocab=4096, w_dtype=wd, head_dtype=wd, kv_dtype=kv)
+    dr = syn.make_draft_inputs(13 + hd, m, [70001, 3000], 3)
+    g = GpuDrafter(m, 2, 3)
+    c = compare_draft(m, g.run(dr), orc.draft_block(m, dr))
+    log(f"  batch: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
+        f"max_h_err={c.max_h_err:.3g}")
+    assert c.near_ties <= 1
+    one = g.run(dr, seq_idx=[0])
+    c1 = compare_draft(m, one, orc.draft_block(m, dr, seq_idx=[0]), [0])
+    log(f"  alone: near_ties={c1.near_ties} max_logit_err={c1.max_logit_err:.3g}")
+    assert c1.near_ties <= 1
+    g.close()

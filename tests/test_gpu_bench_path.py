@@ -86,10 +86,12 @@ def test_c4_full_size_131072_cells_sampled_sequences(orc):
 
 
 def test_long_ragged_context_alone_and_in_a_batch(orc):
-    """100003 visible cells split into 1024-cell splits (98 splits, the last
-    675 cells): each wave of a full split walks 16 tiles, the steady-state
-    loop several times, and the last split is ragged.  Alone (one-sequence
-    paths) and beside a 131072-cell and a 5000-cell sequence (batch paths)."""
+    """100003 visible cells split into 2048-cell splits (49 splits, the last
+    1699 cells) whose workgroups serve both kv heads: each wave of a full
+    split walks 64 tiles, the steady-state loop many times, and the last
+    split is ragged.  Alone (one-sequence paths) and beside a 131072-cell
+    and a 5000-cell sequence (batch paths; the 5000-cell one keeps one kv
+    head per workgroup in the same launch)."""
     log("case long ragged context: 100003 cells alone and with 131072 / 5000")
     m = syn.make_model(57, d_model=256, d_hprev=256, n_blocks=1, n_head_q=8, n_head_kv=2, head_dim=256, d_ff=512,
                        n_vocab=4096, w_dtype=syn.BF16, head_dtype=syn.BF16, kv_dtype=syn.BF16)
@@ -100,6 +102,23 @@ def test_long_ragged_context_alone_and_in_a_batch(orc):
     _check("ctx 100003 in a batch of 3, no logits", m, g.run(dr, want_logits=False), o)
     one = g.run(dr, seq_idx=[0])
     _check("ctx 100003 alone", m, one, orc.draft_block(m, dr, seq_idx=[0]), [0])
+    g.close()
+
+
+def test_short_sequences_same_bits_beside_a_long_one():
+    """A sequence's attention arithmetic depends on that sequence alone:
+    short sequences give the same bits in a batch whose launches also run a
+    long (two kv heads per workgroup) sequence as in a batch without it."""
+    log("case short sequences beside a long one: same bits")
+    m = syn.make_model(63, d_model=256, d_hprev=256, n_blocks=2, n_head_q=8, n_head_kv=2, head_dim=256, d_ff=512,
+                       n_vocab=4096, w_dtype=syn.BF16, head_dtype=syn.BF16, kv_dtype=syn.BF16)
+    dr = syn.make_draft_inputs(65, m, [3000, 131072, 5000], 3)
+    g = GpuDrafter(m, 3, 3)
+    full = g.run(dr)
+    short = g.run(dr, seq_idx=[0, 2])
+    for k, s in enumerate((0, 2)):
+        for key in ("drafts", "logits", "h_last"):
+            assert np.array_equal(short[key][k], full[key][s]), (s, key)
     g.close()
 
 
