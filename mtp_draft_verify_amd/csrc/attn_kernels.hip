@@ -280,7 +280,17 @@ __device__ __forceinline__ void bf16_pair(uint32_t w, float &lo, float &hi) {
     hi = __uint_as_float(w & 0xFFFF0000u);
 }
 
-// LDS of one attention workgroup, sized for NHM kv heads
+// K tile staging in LDS: each wave's 16 rows of hd bf16, rows padded by 16
+// bytes so that a wave's operand-order reads (16 rows x 16 bytes per lane
+// group) fall on 16 different 4-bank groups.
+template <int HD>
+struct KStage {
+    static constexpr int ROWB = 2 * HD + 16;
+    alignas(16) char w[4][16 * ROWB];
+};
+
+// LDS of one attention workgroup, sized for NHM kv heads.  The K staging is
+// used only by the main loop and the wave partials only after it.
 template <int HD, int G, int NHM>
 struct AttnSmem {
     static constexpr int KS = HD / 32;
@@ -288,7 +298,10 @@ struct AttnSmem {
     alignas(16) float cs[HD / 2];
     alignas(16) float sn[HD / 2];
     float wm[4][G], wl[4][G];
-    float wacc[4][G][HD];
+    union {
+        KStage<HD> kst;
+        float wacc[4][G][HD];
+    };
     abf16x8_t qbs[NHM][KS][64];
 };
 
@@ -312,15 +325,34 @@ __device__ __forceinline__ void attn_mm_body(const AttnArgs &a, AttnSmem<HD, G, 
     const uint16_t *kb = (const uint16_t *)sp.k + (int64_t)kvh * HD;
     const uint16_t *vb = (const uint16_t *)sp.v + (int64_t)kvh * HD;
     auto cell_of = [&](int pi) { return src_cell(sp, pbeg + min(pi, npos - 1)); };
+    // STREAM: K rows are loaded whole, instruction q taking rows RPI q ..
+    // RPI q + RPI - 1 of the tile, lane l the 16-byte chunk l % CPR of row
+    // RPI q + l / CPR, and go into operand order through LDS (measured with
+    // loads alone, 8 sequences x 131072 cells: 322 us with the 16 rows x 64
+    // bytes per instruction that the operand order needs, 315 us this way
+    // with the LDS transpose; in the kernel, 16 sequences of 4096-32768
+    // cells 39.8 -> 38.0 us).  Otherwise each lane loads its operand (row j16,
+    // 16 bytes per step) directly: with one or two tiles per wave the LDS
+    // round trip would sit on the critical path (one sequence over 8192
+    // cells 7.8 -> 8.3 us with it).
+    constexpr int CPR = HD / 8, RPI = 64 / CPR;
+    const int krow = STREAM ? lane / CPR : j16, kchunk = lane % CPR;
     auto load = [&](int i, AttnTile<HD, G> &t) {
         const int p0 = i < nt ? 16 * (wt + wph * i) : 16 * wt;
-        const uint16_t *kp = kb + (int64_t)cell_of(p0 + j16) * sp.cell_stride + 8 * g;
+        if constexpr (STREAM) {
 #pragma unroll
-        for (int u = 0; u < KS; ++u) t.k[u] = kv_load<STREAM, u32x4_t>(kp + 32 * u);
+            for (int q = 0; q < KS; ++q)
+                t.k[q] = kv_load<STREAM, u32x4_t>(kb + (int64_t)cell_of(p0 + RPI * q + krow) * sp.cell_stride + 8 * kchunk);
+        } else {
+            const uint16_t *kp = kb + (int64_t)cell_of(p0 + krow) * sp.cell_stride + 8 * g;
+#pragma unroll
+            for (int u = 0; u < KS; ++u) t.k[u] = kv_load<STREAM, u32x4_t>(kp + 32 * u);
+        }
 #pragma unroll
         for (int c = 0; c < 16; ++c)
             t.v[c] = kv_load<STREAM, typename VRow<DPL>::T>(vb + (int64_t)cell_of(p0 + c) * sp.cell_stride + DPL * lane);
     };
+    char *kst = sm.kst.w[wid];
     // the first two tiles do not depend on the query: request them first
     AttnTile<HD, G> buf[2];
     if (nt > 0) load(0, buf[0]);
@@ -434,12 +466,27 @@ __device__ __forceinline__ void attn_mm_body(const AttnArgs &a, AttnSmem<HD, G, 
         return __uint_as_float(r[0]) + __uint_as_float(r[1]);
     };
     auto tile = [&](int i, const AttnTile<HD, G> &t) {
+        // STREAM: K through the wave's LDS rows into operand order (step u of
+        // lane (j16, g) is row j16, dims 32 u + 8 g .. + 7).  A wave's LDS
+        // operations complete in order, so the next tile's stores cannot
+        // overtake these reads.
+        constexpr int ROWB = KStage<HD>::ROWB;
+        u32x4_t ko[KS];
+        if constexpr (STREAM) {
+#pragma unroll
+            for (int q = 0; q < KS; ++q) *(u32x4_t *)(kst + (RPI * q + krow) * ROWB + 16 * kchunk) = t.k[q];
+#pragma unroll
+            for (int u = 0; u < KS; ++u) ko[u] = *(const u32x4_t *)(kst + j16 * ROWB + 64 * u + 16 * g);
+        } else {
+#pragma unroll
+            for (int u = 0; u < KS; ++u) ko[u] = t.k[u];
+        }
         // two independent MFMA chains over the even / odd head-dim steps
         f32x4_t d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < KS; u += 2) {
-            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, t.k[u]), qb[u], d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, t.k[u + 1]), qb[u + 1], d1, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, ko[u]), qb[u], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(abf16x8_t, ko[u + 1]), qb[u + 1], d1, 0, 0, 0);
         }
         const f32x4_t d = d0 + d1;
         // lane (j16 < G, g): head j16, cells 4g .. 4g+3; its lo column sits
@@ -490,10 +537,14 @@ __device__ __forceinline__ void attn_mm_body(const AttnArgs &a, AttnSmem<HD, G, 
     // conditions; the last one to three tiles are peeled, so no load is
     // issued past the wave's last tile.
     int i = 0;
+    // (STREAM: the scheduling fences keep the next tile's loads behind the
+    // current tile, whose staged K then reuses the registers its raw K held)
     for (; i + 3 < nt; i += 2) {
         tile(i, buf[0]);
+        if constexpr (STREAM) __builtin_amdgcn_sched_barrier(0);
         load(i + 2, buf[0]);
         tile(i + 1, buf[1]);
+        if constexpr (STREAM) __builtin_amdgcn_sched_barrier(0);
         load(i + 3, buf[1]);
     }
     if (i < nt) tile(i, buf[0]);
@@ -502,6 +553,7 @@ __device__ __forceinline__ void attn_mm_body(const AttnArgs &a, AttnSmem<HD, G, 
     if (i + 2 < nt) tile(i + 2, buf[0]);
 
     // --- merge the states of each kv head's waves -> one partial per query head
+    __syncthreads();                        // the wave partials reuse the K staging
     if (j16 < G && g == 0) {
         sm.wm[wid][j16] = m;
         sm.wl[wid][j16] = l;
