@@ -105,3 +105,26 @@ def test_two_heads_per_workgroup_long_context_matches_oracle(orc, kv, wd, hd, hq
     log(f"  alone: near_ties={c1.near_ties} max_logit_err={c1.max_logit_err:.3g}")
     assert c1.near_ties <= 1
     g.close()
+
+
+def test_two_heads_per_workgroup_over_a_wrapping_swa_ring_matches_oracle(orc):
+    """A sliding window of 70000 cells over a ring of the same capacity, with
+    attn_pos past the capacity: the window wraps around the ring inside one
+    of its 2048-cell splits, and the sequence's workgroups serve both kv
+    heads.  Beside a 3000-cell sequence, whose window (all of its positions)
+    keeps one head per workgroup, and alone."""
+    log("case two kv heads per workgroup over a wrapping 70000-cell SWA ring")
+    m = syn.make_model(67, d_model=256, d_hprev=256, n_blocks=2, n_head_q=8, n_head_kv=2, head_dim=256, d_ff=512,
+                       n_vocab=4096, w_dtype=syn.BF16, head_dtype=syn.BF16, kv_dtype=syn.BF16, swa_window=70000,
+                       block_src=[syn.KV_SWA, syn.KV_FULL])
+    dr = syn.make_draft_inputs(69, m, [100001, 3000], 3)
+    g = GpuDrafter(m, 2, 3)
+    c = compare_draft(m, g.run(dr), orc.draft_block(m, dr))
+    log(f"  batch: steps={c.compared_steps} near_ties={c.near_ties} max_logit_err={c.max_logit_err:.3g} "
+        f"max_h_err={c.max_h_err:.3g}")
+    assert c.near_ties <= 1
+    one = g.run(dr, seq_idx=[0])
+    c1 = compare_draft(m, one, orc.draft_block(m, dr, seq_idx=[0]), [0])
+    log(f"  alone: near_ties={c1.near_ties} max_logit_err={c1.max_logit_err:.3g}")
+    assert c1.near_ties <= 1
+    g.close()
