@@ -237,9 +237,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 // nh = 2 the waves of a workgroup read both heads' halves of the same cell
 // rows together, one contiguous run of 2 * hd * 2 bytes per cell.  Per tile
 // the G query heads of a wave's kv head meet the 16 K rows in
-// v_mfma_f32_16x16x32_bf16 (A = K, cells as rows, straight from HBM; B =
-// the scaled query as bf16 hi and lo halves, 2G of the 16 columns), so a
-// score costs no vector work.  Lane j < G of each 16-lane row then owns
+// v_mfma_f32_16x16x32_bf16 (A = K, cells as rows, loaded in operand order,
+// or through LDS when streaming; B = the scaled query as bf16 hi and lo
+// halves, 2G of the 16 columns), so a score costs no vector work.  Lane j < G of each 16-lane row then owns
 // head j for 4 cells: it adds the lo column, keeps the online softmax
 // (m, l) in base 2; every lane then accumulates P.V for its HD/64 dims of
 // all G heads from the tile's V rows, which it loads as one coalesced row
