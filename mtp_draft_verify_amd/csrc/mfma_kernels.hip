@@ -125,14 +125,13 @@ __device__ __forceinline__ void mm_load_x(const GemvArgs &a, int s, int col, flo
     for (int i = 0; i < 8; ++i) x[i] = a.embed_scale * e[i];
 }
 
-// SPLIT: workgroup (tile, ks) takes only the ks-th run of NW * kMmSteps
-// steps and writes its partial tile to kpart[ks][s][row]; mm_splitk_reduce
-// then sums the runs in order and applies the epilogue.  For long rows over
-// few row tiles (M = 1024: 64 tiles), where one workgroup per tile would
-// leave most CUs idle and read all activations per tile.
-template <int NW, int IN, int EPI, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *kpart) {
-    static_assert(!(SPLIT && IN == IN_NORM), "a split run cannot see the whole row's norm");
+// ROWS < 16: a workgroup's tile holds ROWS weight rows (operand rows ROWS ..
+// 15 are zero), so short matrices spread over more workgroups (M = 1024 in
+// 16-row tiles would leave three CUs in four idle).  Each output row is its
+// own MFMA dot product: its value does not depend on the tile height.
+template <int NW, int IN, int EPI, int ROWS>
+__global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in) {
+    static_assert(ROWS == 16 || ROWS == 8 || ROWS == 4 || ROWS == 2, "a tile is a power-of-two part of an operand");
     GemvArgs a = a_in;
     if (IN == IN_EMBED) {   // caller buffers of this call
         a.tok_in = a.step == 0 ? a.io->last_tok : nullptr;
@@ -144,10 +143,9 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *
     const int K = a.K, M = a.M, S = a.S, KS = K / 32;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int j16 = lane & 15, g = lane >> 4;
-    const int R0 = blockIdx.x * 16;
-    const int T0 = SPLIT ? (int)blockIdx.y * NW * kMmSteps : 0;     // first step of this run
+    const int R0 = blockIdx.x * ROWS;
 
-    if (IN == IN_EMBED && blockIdx.x == 0 && blockIdx.y == 0 && tid < S) {
+    if (IN == IN_EMBED && blockIdx.x == 0 && tid < S) {
         if (a.drafts_out) a.drafts_out[(int64_t)tid * a.drafts_stride + a.drafts_col] = key_index(a.key_in[tid]);
         if (a.key_reset) a.key_reset[tid] = 0ull;
     }
@@ -156,11 +154,12 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *
     u32x4_t wa[kMmSteps];
     {
         const int row = R0 + j16;
+        const bool rok = j16 < ROWS && row < M;
         const uint16_t *wr = (const uint16_t *)a.W + (int64_t)row * K + 8 * g;
 #pragma unroll
         for (int i = 0; i < kMmSteps; ++i) {
-            const int t = T0 + wid + NW * i;
-            wa[i] = (row < M && t < KS) ? ld_nt4(wr + 32 * t) : u32x4_t{0, 0, 0, 0};
+            const int t = wid + NW * i;
+            wa[i] = (rok && t < KS) ? ld_nt4(wr + 32 * t) : u32x4_t{0, 0, 0, 0};
         }
     }
     // activations of sequence j16 at the same columns
@@ -169,7 +168,7 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *
     float gn[IN == IN_NORM ? kMmSteps : 1][8];
 #pragma unroll
     for (int i = 0; i < kMmSteps; ++i) {
-        const int t = T0 + wid + NW * i;
+        const int t = wid + NW * i;
         const int col = 32 * t + 8 * g;
         if (sok && t < KS) {
             if (IN != IN_EMBED && a.src_op) {
@@ -218,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *
     f32x4_t acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kMmSteps; ++i) {
-        if (T0 + wid + NW * i >= KS) break;     // wave-uniform
+        if (wid + NW * i >= KS) break;     // wave-uniform
         u32x4_t bh, bl;
         split_bf16(x[i], bh, bl);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, wa[i]);
@@ -231,34 +230,15 @@ __global__ __launch_bounds__(NW * 64) void mm_gemv_kernel(GemvArgs a_in, float *
     for (int o = tid; o < 256; o += NW * 64) {
         const int s = o >> 4, rho = o & 15;
         const int row = R0 + rho;
-        if (s >= S || row >= M) continue;
+        if (s >= S || rho >= ROWS || row >= M) continue;
         const int l = s + 16 * (rho >> 2), q = rho & 3;
         float y = 0.f;
         for (int w = 0; w < NW; ++w) y += red[w][l][q];
-        if (SPLIT) {
-            kpart[((int64_t)blockIdx.y * S + s) * M + row] = y;
-            continue;
-        }
         float *dp = a.dst + (int64_t)s * a.dst_stride + row;
         const float out = EPI == EPI_STORE ? y : EPI == EPI_ADD ? *dp + y : silu_f(y);
         *dp = out;
         if (a.dst_op) a.dst_op[op_index(row, s)] = out;
     }
-}
-
-// Sum of the split runs of a split GEMV, in run order, then the epilogue:
-// one thread per (sequence, row).
-template <int EPI>
-__global__ __launch_bounds__(256) void mm_splitk_reduce(GemvArgs a, const float *kpart, int nsplit) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.S * a.M) return;
-    const int s = i / a.M, row = i - s * a.M;
-    float y = 0.f;
-    for (int ks = 0; ks < nsplit; ++ks) y += kpart[((int64_t)ks * a.S + s) * a.M + row];
-    float *dp = a.dst + (int64_t)s * a.dst_stride + row;
-    const float out = EPI == EPI_ADD ? *dp + y : y;
-    *dp = out;
-    if (a.dst_op) a.dst_op[op_index(row, s)] = out;
 }
 
 // ============================================================================
@@ -834,45 +814,34 @@ bool mm_gemv_supported(int w_dtype, const GemvArgs &a) {
     return w_dtype == MTP_BF16 && a.S >= kMmMinSeqs && a.S <= 16 && a.K % 32 == 0 && a.K <= 16 * kMmSteps * 32;
 }
 
-int mm_gemv_splits(int in_mode, const GemvArgs &a) {
-    // Split plain rows longer than two runs of a 4-wave workgroup when the
-    // row tiles alone would not fill the chip.  Measured at 16 sequences,
-    // M = 1024: K = 4096 goes from 9.7 us to 4.7 + 4.2 (sum of the runs);
-    // K = 2048 would not gain, and the pre-projection (K = 3840) got slower
-    // (11.6 -> 9.8 + 4.6 us): its embedding gather is a dependent load that
-    // the split does not shorten.
-    const int run = 4 * kMmSteps * 32;
-    if (in_mode != IN_PLAIN || a.K <= 2 * run || a.M > 2048) return 1;
-    return (a.K + run - 1) / run;
+// Weight rows per workgroup tile: halved from 16 (down to 2) while the
+// matrix has fewer than 256 tiles, one per CU.  Measured against 16-row tiles
+// with the M = 1024 down projection split over K (4 runs + a reduce): rounds
+// of 8 sequences x 131072 cells 5.99 -> 5.96 ms, 16 sequences over SWA + full
+// KV 1.213 -> 1.185 ms, 8 sequences over a sink + window 0.789 -> 0.755 ms;
+// with 512 tiles as the target (2- and 4-row tiles) all three got slower
+// (6.13, 1.357, 0.893 ms).
+static int mm_gemv_rows(const GemvArgs &a) {
+    int rows = 16;
+    while (rows > 2 && (a.M + rows - 1) / rows < 256) rows /= 2;
+    return rows;
 }
 
-hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart, int64_t kpart_floats,
-                          hipStream_t st) {
+hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, hipStream_t st) {
     const int KS = a.K / 32;
-    const int nsplit = mm_gemv_splits(in_mode, a);
-    if (nsplit > 1 && kpart && (int64_t)nsplit * a.S * a.M <= kpart_floats) {
-        const dim3 grid((a.M + 15) / 16, nsplit);
-#define MTP_MM_SPLIT(I, E)                                                                             \
-        if (in_mode == I && epi == E) {                                                                \
-            mtp_launch((mm_gemv_kernel<4, I, E, true>), grid, dim3(256), 0, st, a, kpart);     \
-            hipError_t e0 = hipGetLastError();                                                         \
-            if (e0 != hipSuccess) return e0;                                                           \
-            mtp_launch((mm_splitk_reduce<E>), dim3((a.S * a.M + 255) / 256), dim3(256), 0, st, \
-                               a, (const float *)kpart, nsplit);                                        \
-            return hipGetLastError();                                                                  \
-        }
-        MTP_MM_SPLIT(IN_PLAIN, EPI_ADD)
-#undef MTP_MM_SPLIT
-        return hipErrorInvalidValue;
-    }
     const int nw = KS <= 4 * kMmSteps ? 4 : KS <= 8 * kMmSteps ? 8 : 16;
-    const dim3 grid((a.M + 15) / 16);
-#define MTP_MM_CASE(NW, I, E)                                                                          \
-    if (nw == NW && in_mode == I && epi == E) {                                                        \
-        mtp_launch((mm_gemv_kernel<NW, I, E, false>), grid, dim3(NW * 64), 0, st, a,           \
-                           (float *)nullptr);                                                          \
+    const int rows = mm_gemv_rows(a);
+    const dim3 grid((a.M + rows - 1) / rows);
+#define MTP_MM_CASE_R(NW, I, E, R)                                                                     \
+    if (nw == NW && in_mode == I && epi == E && rows == R) {                                           \
+        mtp_launch((mm_gemv_kernel<NW, I, E, R>), grid, dim3(NW * 64), 0, st, a);               \
         return hipGetLastError();                                                                      \
     }
+#define MTP_MM_CASE(NW, I, E)   \
+    MTP_MM_CASE_R(NW, I, E, 16) \
+    MTP_MM_CASE_R(NW, I, E, 8)  \
+    MTP_MM_CASE_R(NW, I, E, 4)  \
+    MTP_MM_CASE_R(NW, I, E, 2)
 #define MTP_MM_NW(NW)                          \
     MTP_MM_CASE(NW, IN_EMBED, EPI_STORE)       \
     MTP_MM_CASE(NW, IN_NORM, EPI_STORE)        \
@@ -883,6 +852,7 @@ hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart,
     MTP_MM_NW(16)
 #undef MTP_MM_NW
 #undef MTP_MM_CASE
+#undef MTP_MM_CASE_R
     return hipErrorInvalidValue;
 }
 

@@ -69,8 +69,6 @@ struct mtp_ctx {
     // draft scratch
     float *x = nullptr, *q = nullptr, *o = nullptr, *u = nullptr, *h = nullptr, *part = nullptr;
     float *o_op = nullptr, *u_op = nullptr, *x_op = nullptr;    // o, u, x in operand order (several sequences)
-    float *kpart = nullptr;             // partial tiles of split several-sequence GEMVs
-    int64_t kpart_floats = 0;
     float *sink = nullptr;              // [64] stores that carry nothing land here
     ConfPart *conf_part = nullptr;      // [max_steps][max_seqs][kConfSlots] confidence partials
     float *cl = nullptr;                // [max_seqs, n_centroids] centroid logits (centroid head)
@@ -223,7 +221,7 @@ static void free_ctx(mtp_ctx *c) {
     if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
     void *bufs[] = {c->x, c->q, c->o, c->u, c->h, c->part, c->sink, c->conf_part, c->cl, c->cand, c->dkeys, c->inv_freq, c->head_q, c->head_qs, c->head_qt, c->d_block,
                     c->vkeys, c->s_maxkey, c->s_topk, c->s_cand_n, c->s_cand_id, c->s_cand_v, c->s_state, c->hv_plane,
-                    c->o_op, c->u_op, c->x_op, c->kpart, c->hv_logits};
+                    c->o_op, c->u_op, c->x_op, c->hv_logits};
     for (void *b : bufs)
         if (b) (void)hipFree(b);
     if (c->h_block) (void)hipHostFree(c->h_block);
@@ -300,7 +298,6 @@ extern "C" int mtp_ctx_create(const mtp_model_desc *desc, const mtp_weights *wei
         ok = ok && dalloc(&c->x, S * d.d_model) && dalloc(&c->q, S * qd) && dalloc(&c->o, S * qd) &&
              dalloc(&c->u, S * d.d_ff) && dalloc(&c->h, S * d.d_hprev) &&
              dalloc(&c->o_op, 16 * qd) && dalloc(&c->u_op, 16 * (size_t)d.d_ff) && dalloc(&c->x_op, 16 * (size_t)d.d_model) &&
-             dalloc(&c->kpart, (size_t)(c->kpart_floats = kMaxKSplits * std::min<int64_t>(S, 16) * d.d_model)) &&
              dalloc(&c->part, S * d.n_head_q * MTP_MAX_SPLITS * (size_t)(d.head_dim + kPartHead)) &&
              dalloc(&c->dkeys, 2 * S) && dalloc(&c->inv_freq, (size_t)d.head_dim / 2) && dalloc(&c->sink, 64) &&
              dalloc(&c->conf_part, (size_t)d.max_steps * S * kConfSlots);
@@ -496,7 +493,7 @@ static int gemv_rows_per_wg(int M) {
 
 static hipError_t run_gemv(mtp_ctx *c, int in_mode, int epi, GemvArgs a, hipStream_t st) {
     ProfScope ps(c, MTP_PROF_GEMV);
-    if (mm_gemv_supported(c->desc.w_dtype, a)) return launch_mm_gemv(in_mode, epi, a, c->kpart, c->kpart_floats, st);
+    if (mm_gemv_supported(c->desc.w_dtype, a)) return launch_mm_gemv(in_mode, epi, a, st);
     if (a.src_op || a.dst_op) return hipErrorInvalidValue;     // operand order is a matrix-core path layout
     a.rows_per_wg = gemv_rows_per_wg(a.M);
     const int n_wg = (a.M + a.rows_per_wg - 1) / a.rows_per_wg;

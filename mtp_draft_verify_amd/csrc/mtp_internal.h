@@ -246,12 +246,7 @@ hipError_t launch_cand_head(int head_dtype, int w_dtype, const HeadArgs &a, int 
 // several sequences: GEMVs and the LM head on the matrix cores
 static constexpr int kMmMinSeqs = 2;
 bool mm_gemv_supported(int w_dtype, const GemvArgs &a);
-// K runs a several-sequence GEMV is split into (1 = not split); the split
-// form needs kpart scratch of runs * S * M floats (else it runs unsplit)
-int mm_gemv_splits(int in_mode, const GemvArgs &a);
-static constexpr int kMaxKSplits = 4;   // K <= 4096 on the matrix-core GEMV path
-hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, float *kpart, int64_t kpart_floats,
-                          hipStream_t st);
+hipError_t launch_mm_gemv(int in_mode, int epi, const GemvArgs &a, hipStream_t st);
 bool mm_head_supported(int head_dtype, int w_dtype, const HeadArgs &a);
 hipError_t launch_mm_head(int head_dtype, const HeadArgs &a, bool logits, hipStream_t st);
 int mm_head_groups(int head_dtype, const HeadArgs &a);   // head workgroups (confidence partials) of one launch
